@@ -1,0 +1,185 @@
+/*
+ * eagle3.h -- C ABI of libeagle3.so: one verify step of an EAGLE-3 draft
+ * token tree on an AMD Instinct MI355X (gfx950), plus the EAGLE-3 draft head.
+ *
+ * Sources, by page and section:
+ *   [lesson] "EAGLE-3 speculative decoding: the tree-verifier method" (course
+ *            lesson): "Verify-accept semantics" (a draft token is accepted when
+ *            it equals the target's highest-probability token given the tokens
+ *            before it; scan stops at the first miss and the target's token
+ *            there is appended), "Tree draft vs chain draft" (the target checks
+ *            the whole tree in one forward pass under a mask that lets each
+ *            token see only its ancestors).
+ *   [news]   News write-up of "EAGLE-3: Scaling up Inference Acceleration of
+ *            Large Language Models via Training-Time Test": the draft-stage
+ *            paragraphs (low/mid/high features l, m, h fused by an FC from 3k to
+ *            k; concatenation with the embedding of the token one step ahead;
+ *            an FC to k; a single-layer transformer; the target's LM head), and
+ *            the note that each forward of the target reads all its parameters.
+ *
+ * Conventions for every entry point:
+ *   - All tensor arguments are DEVICE pointers owned by the caller, dense
+ *     row-major with the shapes given below. Floating-point tensors are bf16
+ *     (raw 16-bit patterns) or fp32 as selected by the `dtype` argument; they
+ *     must be 16-byte aligned. Index tensors are int32, masks uint64.
+ *   - The library never allocates or frees device memory. Scratch comes from
+ *     the caller through a `ws` pointer sized by the matching *_workspace()
+ *     query (same arguments). It keeps no state between calls.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *     the call returns without synchronising.
+ *   - Errors found on the host are returned before anything is launched:
+ *       EAGLE3_ERR_ARG          null pointer, negative size, misalignment
+ *       EAGLE3_ERR_UNSUPPORTED  a shape or option this build does not handle
+ *       EAGLE3_ERR_WORKSPACE    ws smaller than the *_workspace() query
+ *     A launch failure returns EAGLE3_ERR_HIP. Data errors (a parent[] that is
+ *     not a tree in topological order, an id out of range) are reported
+ *     through the optional device status arrays; without them the outputs of
+ *     bad data are unspecified but every memory access stays in bounds.
+ *   - No call throws; every call is safe to make from several host threads on
+ *     different streams.
+ *
+ * Tree conventions (reading of [lesson]): node 0 of every tree is the root,
+ * the last committed token; parent[0] = -1 and 0 <= parent[n] < n for n > 0.
+ * T = number of nodes including the root; T <= 64 * W where W is the number
+ * of 64-bit mask words per node (W = 1 or 2).
+ */
+#ifndef EAGLE3_H
+#define EAGLE3_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum eagle3_status {
+    EAGLE3_OK = 0,
+    EAGLE3_ERR_ARG = -1,
+    EAGLE3_ERR_UNSUPPORTED = -2,
+    EAGLE3_ERR_TREE = -3,
+    EAGLE3_ERR_RANGE = -4,
+    EAGLE3_ERR_HIP = -5,
+    EAGLE3_ERR_WORKSPACE = -6
+};
+
+enum eagle3_dtype { EAGLE3_F32 = 0, EAGLE3_BF16 = 1 };
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char *eagle3_status_string(int status);
+
+/* ABI version: bumped whenever a signature or layout below changes. */
+int eagle3_abi_version(void);
+
+/*
+ * Ancestor bitmask of every node ([lesson] "Tree draft vs chain draft": a node
+ * sees only its ancestors; reading: and itself).
+ *   parent  [B, T] int32
+ *   mask    [B, T, W] uint64 out: bit (t % 64) of word t / 64 of node n is set
+ *           iff t is n or an ancestor of n
+ *   depth   [B, T] int32 out (nullable): number of ancestors excluding n
+ *   status  [B] int32 out (nullable): EAGLE3_OK, or EAGLE3_ERR_TREE when the
+ *           sequence's parent[] breaks the tree conventions (its mask is then
+ *           unspecified)
+ * Needs 1 <= T <= 64 * W, W in {1, 2}.
+ */
+int eagle3_tree_mask(const int32_t *parent, int B, int T, int W,
+                     uint64_t *mask, int32_t *depth, int32_t *status, void *stream);
+
+/*
+ * Tree attention ([lesson] "Tree draft vs chain draft"; GQA reading: query
+ * head h reads KV head h / (Hq / Hkv)). For sequence b, query node i, head h:
+ *   keys = the b-th prefix (prefix_len[b] positions, paged) followed by the
+ *          tree keys t = 0..Tk-1 whose bit is set in mask[b][i];
+ *   out  = softmax(scale * q . k) . v over those keys; lse = ln sum exp.
+ * Layouts:
+ *   q        [B, Tq, Hq, D]            k_tree, v_tree [B, Tk, Hkv, D]
+ *   k_cache  [num_blocks, Hkv, block_size, D]   (key rows, D contiguous)
+ *   v_cache  [num_blocks, Hkv, D, block_size]   (value columns, slot contiguous)
+ *   block_table [B, max_blocks] int32: physical block of logical block j of
+ *            sequence b; entries past ceil(prefix_len[b] / block_size) are
+ *            never read
+ *   prefix_len [B] int32, each in [0, max_blocks * block_size]
+ *   mask     [B, Tq, W] uint64 over the Tk tree keys (from eagle3_tree_mask
+ *            when the queries are the tree nodes themselves, Tq == Tk), or
+ *            NULL together with parent [B, Tq] (Tq == Tk) to build it on the fly
+ *   out      [B, Tq, Hq, D]; lse [B, Tq, Hq] fp32 (nullable), natural log
+ * Supported: bf16 with D = 128; fp32 with D = 64 or 128; block_size 16;
+ * Tk <= 64 * W, W in {1, 2}; Hq % Hkv == 0. A query row that sees no key gets
+ * out = 0 and lse = -inf. Slots of the cache past prefix_len are never read.
+ * split_keys: prefix keys per work-group split (multiple of 64), 0 = chosen by
+ * the library from B, Hkv and max_blocks. Results do not depend on the call's
+ * batch composition, but may differ in the last bits between split choices.
+ */
+typedef struct eagle3_tree_attn_args {
+    int dtype;
+    int B, Tq, Tk, Hq, Hkv, D, W;
+    float scale;
+    const void *q;
+    const void *k_tree;
+    const void *v_tree;
+    const void *k_cache;
+    const void *v_cache;
+    int num_blocks, block_size;
+    const int32_t *block_table;
+    int max_blocks;
+    const int32_t *prefix_len;
+    const uint64_t *mask;
+    const int32_t *parent;
+    void *out;
+    float *lse;
+    int split_keys;
+} eagle3_tree_attn_args;
+
+size_t eagle3_tree_attn_workspace(const eagle3_tree_attn_args *a);
+int eagle3_tree_attn(const eagle3_tree_attn_args *a, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * RMSNorm over the last dimension (reading: the hidden state is normalised
+ * before the LM head, as in Llama): y = x / sqrt(mean(x^2) + eps) * gamma.
+ *   x, y [M, K]; gamma [K] (nullable: 1). In-place (x == y) is allowed.
+ * Supported: K % 8 == 0.
+ */
+int eagle3_rmsnorm(const void *x, const void *gamma, int M, int K, float eps,
+                   int dtype, void *y, void *stream);
+
+/*
+ * LM head with a fused per-row selection; the [M, N] logits are never stored
+ * ([lesson] "Verify-accept semantics": the target's argmax at each node;
+ * [news]: the draft also uses the target's LM head).
+ *   hidden [M, K]; w [N, K] (vocabulary-major)
+ *   idx [M, topk] int32, val [M, topk] fp32: the topk largest logits of each
+ *        row in the order (logit descending, id ascending), so idx[m][0] is
+ *        the lowest id attaining the maximum
+ *   gap [M] fp32 (nullable): top1 - top2, top2 the largest logit over the
+ *        other ids (0 on an exact tie)
+ *   lse [M] fp32 (nullable): ln sum_v exp(logit_v)
+ * Supported: 1 <= topk <= 16; K % 64 == 0; N >= 2. Logits are accumulated in
+ * fp32 (bf16 products are exact in fp32).
+ */
+size_t eagle3_lmhead_workspace(int M, int N, int K, int topk, int dtype);
+int eagle3_lmhead_argmax(const void *hidden, const void *w, int M, int N, int K, int topk, int dtype,
+                         int32_t *idx, float *val, float *gap, float *lse,
+                         void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Greedy acceptance on a tree ([lesson] "Verify-accept semantics", applied to
+ * every root-to-leaf path). A non-root node is accepted when its parent is
+ * accepted and tokens[n] == target_idx[parent[n]]; the root always is.
+ * accept_len = depth of the deepest accepted node; among equally deep ones the
+ * lowest index is the end node (reading). Outputs:
+ *   accept_len [B] int32
+ *   path       [B, T] int32: root, ..., end node; -1 after
+ *   out_tokens [B, T] int32: tokens of path[1..accept_len], then
+ *              target_idx[end] (the target's own token); -1 after
+ * Inputs: tokens, target_idx [B, T] int32; exactly one of parent [B, T] or
+ * mask [B, T, W] (from eagle3_tree_mask) non-NULL. T <= 64 * W, W in {1, 2}.
+ */
+int eagle3_accept_path(const int32_t *tokens, const int32_t *parent, const uint64_t *mask, int W,
+                       const int32_t *target_idx, int B, int T,
+                       int32_t *accept_len, int32_t *path, int32_t *out_tokens, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* EAGLE3_H */

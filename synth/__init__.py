@@ -326,9 +326,11 @@ def _select_kv(kv: PagedKV, sel: np.ndarray) -> PagedKV:
     return PagedKV(kv.k_cache, kv.v_cache, kv.block_table[sel].copy(), kv.prefix_len[sel].copy(), kv.block_size)
 
 
-def lm_head_weight(shape_or_wid, seed: int, V: int, K: int, std: float = 0.02) -> np.ndarray:
+def lm_head_weight(shape_or_wid, V: int, K: int, std: float = 0.02) -> np.ndarray:
+    """LM-head matrix [V, K] (vocabulary-major), N(0, std^2) in bf16. The model
+    is fixed per workload: seeds vary the inputs, not the weights."""
     wid = shape_or_wid.wid if hasattr(shape_or_wid, "wid") else int(shape_or_wid)
-    return normal_bf16(child_rng(wid, seed, C_WLM), (V, K), std=std)
+    return normal_bf16(child_rng(wid, 0, C_WLM), (V, K), std=std)
 
 
 def plant_tokens(parent: np.ndarray, target_idx: np.ndarray, p_seq, plant_u, plant_id) -> np.ndarray:

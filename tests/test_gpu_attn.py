@@ -1,0 +1,147 @@
+"""GPU parity of tree attention against the oracle (same seeded inputs).
+
+bf16: normwise relative error <= 2e-2 per output tensor (storage rounding of
+bf16 is 2^-9 relative, P is rounded to bf16 before the PV product), lse within
+2e-3. fp32: <= 1e-5. Invariances that must hold bit-exactly on the GPU too:
+K/V of a non-ancestor never changes a node's output; the physical order of
+cache blocks does not matter."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from _gpu import dev, host, normwise_rel
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import tree_draft_verification_amd as t
+    return t
+
+
+def gpu_attn(lib, inp, mask=None, parent=None, split_keys=0, want_lse=True):
+    # every device tensor is bound to a name: the args struct holds raw pointers
+    q, kt, vt = dev(inp.q), dev(inp.k_tree), dev(inp.v_tree)
+    kc, vc = dev(inp.kv.k_cache), dev(inp.kv.v_cache)
+    bt, pl = dev(inp.kv.block_table), dev(inp.kv.prefix_len)
+    mk = None if mask is None else dev(mask)
+    pa = None if parent is None else dev(parent)
+    B, Tq, Hq, D = q.shape
+    out = torch.empty_like(q)
+    lse = torch.empty((B, Tq, Hq), dtype=torch.float32, device="cuda") if want_lse else None
+    args = lib.tree_attn_args(q, kt, vt, kc, vc, bt, pl, out, mask=mk, parent=pa, lse=lse, split_keys=split_keys)
+    ws_n = lib.eagle3_tree_attn_workspace(args)
+    ws = torch.empty(max(ws_n, 256), dtype=torch.uint8, device="cuda")
+    lib.eagle3_tree_attn(args, ws)
+    torch.cuda.synchronize()
+    return host(out), (host(lse) if want_lse else None)
+
+
+def make(wid, B, T, Hq, Hkv, plen, dtype="bf16", D=128, seed=0, depth=7, Tq=None):
+    rng = np.random.default_rng(wid * 10 + seed)
+    n = T - 1
+    parent = np.stack([synth.topk_tree(rng, n, min(depth, n), 10) if n > 0 else np.array([-1], np.int32)
+                       for _ in range(B)])
+    inp = synth.attn_inputs(wid, seed, B, Tq or T, T, Hq, Hkv, D, plen, dtype)
+    return parent, inp
+
+
+CASES = [
+    # B, T, Hq, Hkv, prefix lengths, split_keys
+    (3, 61, 8, 2, [0, 37, 1100], 0),
+    (3, 61, 8, 2, [0, 37, 1100], 64),
+    (3, 61, 8, 2, [5, 700, 130], 256),
+    (2, 61, 32, 4, [300, 64], 0),        # G = 8: two row blocks
+    (1, 16, 4, 4, [129], 0),             # MHA, small tree
+    (2, 1, 8, 2, [17, 0], 0),            # root only
+    (2, 100, 4, 1, [40, 90], 0),         # W = 2
+]
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+@pytest.mark.parametrize("mode", ["mask", "parent"])
+def test_bf16_parity(orc, lib, case, mode):
+    B, T, Hq, Hkv, plen, split = CASES[case]
+    parent, inp = make(100 + case, B, T, Hq, Hkv, plen)
+    W = (T + 63) // 64
+    mask, _ = orc.tree_mask(parent, W)
+    ref, ref_lse = orc.tree_attn(inp.q, inp.k_tree, inp.v_tree, inp.kv, mask)
+    if mode == "mask":
+        got, lse = gpu_attn(lib, inp, mask=mask, split_keys=split)
+    else:
+        got, lse = gpu_attn(lib, inp, parent=parent, split_keys=split)
+    rel, mx = normwise_rel(got, ref)
+    assert rel <= 2e-2, (rel, mx)
+    assert np.all(np.isfinite(lse))
+    assert np.abs(lse - ref_lse).max() <= 2e-3
+
+
+def test_bf16_draft_step_form(orc, lib):
+    """Tq frontier queries over Tk = 70 draft-tree keys (W = 2)."""
+    B, Tq, Tk, Hq, Hkv = 4, 10, 70, 8, 2
+    inp = synth.attn_inputs(120, 0, B, Tq, Tk, Hq, Hkv, 128, [1024, 500, 33, 0], "bf16")
+    rng = np.random.default_rng(0)
+    vis = rng.random((B, Tq, Tk)) < 0.3
+    vis[:, :, 0] = True
+    mask = np.zeros((B, Tq, 2), np.uint64)
+    for t in range(Tk):
+        mask[..., t // 64] |= vis[..., t].astype(np.uint64) << np.uint64(t % 64)
+    ref, ref_lse = orc.tree_attn(inp.q, inp.k_tree, inp.v_tree, inp.kv, mask)
+    got, lse = gpu_attn(lib, inp, mask=mask)
+    rel, mx = normwise_rel(got, ref)
+    assert rel <= 2e-2, (rel, mx)
+    assert np.abs(lse - ref_lse).max() <= 2e-3
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_f32_parity(orc, lib, D):
+    B, T, Hq, Hkv = 2, 16, 4, 4
+    parent, inp = make(130, B, T, Hq, Hkv, [150, 0], dtype="f32", D=D, depth=4)
+    mask, _ = orc.tree_mask(parent)
+    ref, ref_lse = orc.tree_attn(inp.q, inp.k_tree, inp.v_tree, inp.kv, mask)
+    got, lse = gpu_attn(lib, inp, mask=mask)
+    rel, mx = normwise_rel(got, ref)
+    assert rel <= 1e-5, (rel, mx)
+    assert np.abs(lse - ref_lse).max() <= 1e-5
+
+
+def test_non_ancestor_perturbation_bit_identical(orc, lib):
+    B, T, Hq, Hkv = 2, 61, 8, 2
+    parent, inp = make(140, B, T, Hq, Hkv, [200, 90])
+    mask, _ = orc.tree_mask(parent)
+    base, _ = gpu_attn(lib, inp, mask=mask)
+    rng = np.random.default_rng(1)
+    for b in range(B):
+        i = int(rng.integers(1, T))
+        vis = np.array([(int(mask[b, i, 0]) >> t) & 1 for t in range(T)], bool)
+        inp2 = synth.AttnInputs(inp.q, inp.k_tree.copy(), inp.v_tree.copy(), inp.kv)
+        noise = synth.f32_to_bf16(synth.normal_f32(rng, inp2.k_tree[b, ~vis].shape, 3.0))
+        inp2.k_tree[b, ~vis] = noise
+        inp2.v_tree[b, ~vis] = noise[..., ::-1]
+        got, _ = gpu_attn(lib, inp2, mask=mask)
+        assert np.array_equal(got[b, i], base[b, i])
+
+
+def test_block_order_bit_identical(orc, lib):
+    B, T, Hq, Hkv = 2, 61, 8, 2
+    parent, inp = make(150, B, T, Hq, Hkv, [333, 1000])
+    mask, _ = orc.tree_mask(parent)
+    base, base_lse = gpu_attn(lib, inp, mask=mask)
+    kv = inp.kv
+    perm = np.random.default_rng(2).permutation(kv.num_blocks)
+    inv = np.argsort(perm)
+    moved = synth.PagedKV(kv.k_cache[inv].copy(), kv.v_cache[inv].copy(), perm[kv.block_table].astype(np.int32),
+                          kv.prefix_len, kv.block_size)
+    got, got_lse = gpu_attn(lib, synth.AttnInputs(inp.q, inp.k_tree, inp.v_tree, moved), mask=mask)
+    assert np.array_equal(got, base) and np.array_equal(got_lse, base_lse)
+
+
+def test_deterministic(orc, lib):
+    B, T, Hq, Hkv = 1, 61, 32, 8
+    parent, inp = make(160, B, T, Hq, Hkv, [1024])
+    mask, _ = orc.tree_mask(parent)
+    a, la = gpu_attn(lib, inp, mask=mask)
+    b, lb = gpu_attn(lib, inp, mask=mask)
+    assert np.array_equal(a, b) and np.array_equal(la, lb)

@@ -1,0 +1,113 @@
+"""End-to-end verify step on the GPU (mask -> attention -> RMSNorm -> LM-head
+argmax -> acceptance) against the oracle on the same seeded inputs.
+
+* attention output: normwise <= 2e-2 (bf16);
+* per-node argmax: identical wherever the oracle's top-2 gap >= 1e-3;
+* accept_len, path, out_tokens: identical for every sequence that is not
+  flagged (a sequence is flagged when one of its oracle-accepted nodes has a
+  top-2 gap < 1e-3); flagged sequences are counted.
+Draft tokens are planted from the ORACLE's argmax.
+Full-size workloads run the GPU over the whole batch and the oracle on
+sampled sequences (each sequence's results depend on that sequence only)."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from _gpu import dev, host, normwise_rel
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import tree_draft_verification_amd as t
+    return t
+
+
+def subset(inp: synth.VerifyInputs, sel) -> synth.VerifyInputs:
+    kv = inp.kv
+    kv2 = synth.PagedKV(kv.k_cache, kv.v_cache, kv.block_table[sel].copy(), kv.prefix_len[sel].copy(), kv.block_size)
+    return dataclasses.replace(inp, parent=inp.parent[sel], kv=kv2, q=inp.q[sel], k_tree=inp.k_tree[sel],
+                               v_tree=inp.v_tree[sel], p_seq=inp.p_seq[sel], plant_u=inp.plant_u[sel],
+                               plant_id=inp.plant_id[sel])
+
+
+def run_gpu(lib, inp, W_lm, tokens, split_keys=0):
+    s = inp.shape
+    B, T = inp.parent.shape
+    kc, vc = dev(inp.kv.k_cache), dev(inp.kv.v_cache)
+    bt, pl = dev(inp.kv.block_table), dev(inp.kv.prefix_len)
+    w = dev(W_lm)
+    step = lib.VerifyStep(B, T, s.Hq, s.Hkv, s.D, W_lm.shape[0], kc, vc, bt, pl, w, split_keys=split_keys)
+    parent, q, kt, vt, tok = dev(inp.parent), dev(inp.q), dev(inp.k_tree), dev(inp.v_tree), dev(tokens)
+    step.run(parent, q, kt, vt, tok)
+    torch.cuda.synchronize()
+    return dict(attn=host(step.attn), idx=host(step.idx).reshape(B, T), gap=host(step.gap).reshape(B, T),
+                accept_len=host(step.accept_len), path=host(step.path), out_tokens=host(step.out_tokens))
+
+
+def check(ref, got, sel=None):
+    sel = np.arange(got["idx"].shape[0]) if sel is None else np.asarray(sel)
+    rel, mx = normwise_rel(got["attn"][sel], ref["attn"])
+    assert rel <= 2e-2, (rel, mx)
+    clean = ref["gap"] >= 1e-3
+    assert np.array_equal(got["idx"][sel][clean], ref["idx"][clean])
+    ok = ~ref["flagged"]
+    for k in ("accept_len", "path", "out_tokens"):
+        assert np.array_equal(got[k][sel][ok], ref[k][ok]), k
+    return int(ref["flagged"].sum())
+
+
+SMALL = synth.VerifyShape("small", 20, B=4, Hq=8, Hkv=2, D=128, V=3001, n_drafts=60, depth=7, prefix=(0, 700),
+                          p_match=(0.6, 0.95))
+
+
+@pytest.mark.parametrize("seed", range(3))
+@pytest.mark.parametrize("split_keys", [0, 128])
+def test_verify_small(orc, lib, seed, split_keys):
+    inp = synth.verify_inputs(SMALL, seed)
+    W = synth.lm_head_weight(SMALL, SMALL.V, SMALL.K)
+    ref = orc.verify_step(inp, W)
+    got = run_gpu(lib, inp, W, ref["tokens"], split_keys)
+    check(ref, got)
+
+
+def test_verify_all_match_and_all_mismatch(orc, lib):
+    inp = synth.verify_inputs(SMALL, 7)
+    W = synth.lm_head_weight(SMALL, SMALL.V, SMALL.K)
+    fw = orc.verify_forward(inp, W)
+    full = synth.plant_tokens(inp.parent, fw["idx"], np.ones(SMALL.B), inp.plant_u, inp.plant_id)
+    got = run_gpu(lib, inp, W, full)
+    _, depth = orc.tree_mask(inp.parent)
+    flagged = orc.flags(inp.parent, full, fw["idx"], fw["gap"])
+    for b in range(SMALL.B):
+        if not flagged[b]:
+            assert got["accept_len"][b] == depth[b].max()        # full depth accepted
+    none = (fw["idx"][np.arange(SMALL.B)[:, None], np.maximum(inp.parent, 0)] + 1) % SMALL.V
+    got = run_gpu(lib, inp, W, none.astype(np.int32))
+    assert np.all(got["accept_len"] == 0)                         # exactly one token
+    assert np.all((got["out_tokens"] >= 0).sum(axis=1) == 1)
+
+
+FULL = [("llama8b-b1", None), ("llama8b-b64", "sample"), ("llama70b-b8", "sample")]
+
+
+@pytest.mark.parametrize("name,mode", FULL)
+def test_verify_full_size(orc, lib, name, mode):
+    shape = synth.VERIFY_SHAPES[name]
+    inp = synth.verify_inputs(shape, 0)
+    W = synth.lm_head_weight(shape, shape.V, shape.K)
+    if mode is None:
+        sel = np.arange(shape.B)
+    else:  # first, last and longest-prefix sequences
+        sel = np.unique([0, shape.B - 1, int(np.argmax(inp.kv.prefix_len))])[:3 if shape.B > 8 else 1]
+    sub = subset(inp, sel)
+    ref = orc.verify_step(sub, W)
+    tokens = inp.plant_id.copy()
+    tokens[sel] = ref["tokens"]
+    got = run_gpu(lib, inp, W, tokens)
+    n_flag = check(ref, got, sel)
+    print(f"{name}: sequences checked {len(sel)}, flagged {n_flag}, tau {got['accept_len'][sel] + 1}")

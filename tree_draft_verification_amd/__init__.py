@@ -1,0 +1,9 @@
+"""EAGLE-3 draft-tree verification on AMD Instinct MI355X (gfx950).
+
+The compute lives in libeagle3.so (HIP kernels behind the C ABI declared in
+include/eagle3.h); ``binding`` wraps each entry point with the same name and
+``verify`` strings the calls of one verify step together on one stream.
+"""
+from . import binding  # noqa: F401  (raises ImportError when the library is missing)
+from .binding import *  # noqa: F401,F403
+from .verify import VerifyStep  # noqa: F401

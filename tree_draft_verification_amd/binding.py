@@ -1,0 +1,164 @@
+"""ctypes binding of libeagle3.so: one Python function per C entry point,
+same names, argument marshalling only (torch tensors -> device pointers,
+the current torch stream -> hipStream_t). Every computation runs in the HIP
+kernels; when the library is missing this module raises at import.
+Structures built here (TreeAttnArgs) hold raw device pointers: the caller
+keeps the tensors alive until the enqueued work has finished.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libeagle3.so")
+
+OK, ERR_ARG, ERR_UNSUPPORTED, ERR_TREE, ERR_RANGE, ERR_HIP, ERR_WORKSPACE = 0, -1, -2, -3, -4, -5, -6
+F32, BF16 = 0, 1
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m tree_draft_verification_amd.build` "
+                      "(there is no fallback path)")
+_lib = ctypes.CDLL(LIB_PATH)
+
+P, I, F, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+
+
+class TreeAttnArgs(ctypes.Structure):
+    _fields_ = [
+        ("dtype", I), ("B", I), ("Tq", I), ("Tk", I), ("Hq", I), ("Hkv", I), ("D", I), ("W", I),
+        ("scale", F),
+        ("q", P), ("k_tree", P), ("v_tree", P), ("k_cache", P), ("v_cache", P),
+        ("num_blocks", I), ("block_size", I),
+        ("block_table", P), ("max_blocks", I), ("prefix_len", P),
+        ("mask", P), ("parent", P), ("out", P), ("lse", P),
+        ("split_keys", I),
+    ]
+
+
+def _sig(name, res, *args):
+    fn = getattr(_lib, name)
+    fn.restype = res
+    fn.argtypes = list(args)
+    return fn
+
+
+_status_string = _sig("eagle3_status_string", ctypes.c_char_p, I)
+_abi_version = _sig("eagle3_abi_version", I)
+_tree_mask = _sig("eagle3_tree_mask", I, P, I, I, I, P, P, P, P)
+_tree_attn_ws = _sig("eagle3_tree_attn_workspace", SZ, ctypes.POINTER(TreeAttnArgs))
+_tree_attn = _sig("eagle3_tree_attn", I, ctypes.POINTER(TreeAttnArgs), P, SZ, P)
+_rmsnorm = _sig("eagle3_rmsnorm", I, P, P, I, I, F, I, P, P)
+_lmhead_ws = _sig("eagle3_lmhead_workspace", SZ, I, I, I, I, I)
+_lmhead = _sig("eagle3_lmhead_argmax", I, P, P, I, I, I, I, I, P, P, P, P, P, SZ, P)
+_accept = _sig("eagle3_accept_path", I, P, P, P, I, P, I, I, P, P, P, P)
+
+
+class Eagle3Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {eagle3_status_string(status)} ({status})")
+        self.status = status
+
+
+def _check(rc: int, where: str):
+    if rc != OK:
+        raise Eagle3Error(rc, where)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def eagle3_status_string(status: int) -> str:
+    return _status_string(status).decode()
+
+
+def eagle3_abi_version() -> int:
+    return _abi_version()
+
+
+def eagle3_tree_mask(parent, W, mask, depth=None, status=None, stream=None):
+    B, T = parent.shape
+    _check(_tree_mask(_ptr(parent), B, T, W, _ptr(mask), _ptr(depth), _ptr(status), _stream(stream)),
+           "eagle3_tree_mask")
+
+
+def tree_attn_args(q, k_tree, v_tree, k_cache, v_cache, block_table, prefix_len, out, mask=None, parent=None,
+                   lse=None, scale=None, split_keys=0) -> TreeAttnArgs:
+    B, Tq, Hq, D = q.shape
+    Tk, Hkv = k_tree.shape[1], k_tree.shape[2]
+    W = mask.shape[-1] if mask is not None else (Tq + 63) // 64
+    a = TreeAttnArgs()
+    a.dtype = _dtype(q)
+    a.B, a.Tq, a.Tk, a.Hq, a.Hkv, a.D, a.W = B, Tq, Tk, Hq, Hkv, D, W
+    a.scale = float(scale if scale is not None else D ** -0.5)
+    a.q, a.k_tree, a.v_tree = _ptr(q), _ptr(k_tree), _ptr(v_tree)
+    a.k_cache, a.v_cache = _ptr(k_cache), _ptr(v_cache)
+    a.num_blocks, a.block_size = k_cache.shape[0], k_cache.shape[2]
+    a.block_table, a.max_blocks, a.prefix_len = _ptr(block_table), block_table.shape[1], _ptr(prefix_len)
+    a.mask, a.parent, a.out, a.lse = _ptr(mask), _ptr(parent), _ptr(out), _ptr(lse)
+    a.split_keys = int(split_keys)
+    return a
+
+
+def eagle3_tree_attn_workspace(args: TreeAttnArgs) -> int:
+    return int(_tree_attn_ws(ctypes.byref(args)))
+
+
+def eagle3_tree_attn(args: TreeAttnArgs, ws=None, ws_bytes=None, stream=None):
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size() if isinstance(ws, torch.Tensor) else 0
+    _check(_tree_attn(ctypes.byref(args), _ptr(ws), ws_bytes, _stream(stream)), "eagle3_tree_attn")
+
+
+def eagle3_rmsnorm(x, y, gamma=None, eps=1e-5, stream=None):
+    K = x.shape[-1]
+    M = x.numel() // K
+    _check(_rmsnorm(_ptr(x), _ptr(gamma), M, K, float(eps), _dtype(x), _ptr(y), _stream(stream)), "eagle3_rmsnorm")
+
+
+def eagle3_lmhead_workspace(M, N, K, topk, dtype) -> int:
+    return int(_lmhead_ws(M, N, K, topk, dtype))
+
+
+def eagle3_lmhead_argmax(hidden, w, topk, idx, val=None, gap=None, lse=None, ws=None, stream=None):
+    K = hidden.shape[-1]
+    M = hidden.numel() // K
+    N = w.shape[0]
+    ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
+    _check(_lmhead(_ptr(hidden), _ptr(w), M, N, K, topk, _dtype(hidden), _ptr(idx), _ptr(val), _ptr(gap), _ptr(lse),
+                   _ptr(ws), ws_bytes, _stream(stream)), "eagle3_lmhead_argmax")
+
+
+def eagle3_accept_path(tokens, target_idx, accept_len, path, out_tokens, parent=None, mask=None, stream=None):
+    B, T = tokens.shape
+    W = mask.shape[-1] if mask is not None else (T + 63) // 64
+    _check(_accept(_ptr(tokens), _ptr(parent), _ptr(mask), W, _ptr(target_idx), B, T, _ptr(accept_len), _ptr(path),
+                   _ptr(out_tokens), _stream(stream)), "eagle3_accept_path")
+
+
+def exported_symbols():
+    """Names this binding resolved from the library (for load checks)."""
+    return sorted(n for n in dir(_lib) if n.startswith("eagle3_"))

@@ -1,0 +1,79 @@
+// Internal helpers of libeagle3.so (gfx950 only). Not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "eagle3.h"
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
+typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2_t;
+
+#define E3_LAUNCH_CHECK()                                          \
+    do {                                                           \
+        if (hipGetLastError() != hipSuccess) return EAGLE3_ERR_HIP; \
+    } while (0)
+
+static inline bool e3_aligned16(const void *p) { return (((uintptr_t)p) & 15u) == 0; }
+static inline hipStream_t e3_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
+
+__device__ __forceinline__ float e3_bf16_to_f32(uint16_t u) { return __uint_as_float(((uint32_t)u) << 16); }
+
+// fp32 -> bf16, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t e3_f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)0x7fc0;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// two fp32 -> packed bf16 pair (lo in bits 0..15)
+__device__ __forceinline__ uint32_t e3_pack_bf16x2(float lo, float hi) {
+    return (uint32_t)e3_f32_to_bf16(lo) | ((uint32_t)e3_f32_to_bf16(hi) << 16);
+}
+
+// (value, index) order used by every selection: larger value first, then lower index.
+__device__ __forceinline__ bool e3_better(float va, int ia, float vb, int ib) {
+    return va > vb || (va == vb && ia < ib);
+}
+
+// insert (v, i) into the sorted list (L[0] best); drops the worst entry.
+template <int KK>
+__device__ __forceinline__ void e3_topk_insert(float (&lv)[KK], int (&li)[KK], float v, int i) {
+#pragma unroll
+    for (int s = 0; s < KK; ++s) {
+        if (e3_better(v, i, lv[s], li[s])) {
+            float tv = lv[s]; int ti = li[s];
+            lv[s] = v; li[s] = i;
+            v = tv; i = ti;
+        }
+    }
+}
+
+template <int KK>
+__device__ __forceinline__ void e3_topk_init(float (&lv)[KK], int (&li)[KK]) {
+#pragma unroll
+    for (int s = 0; s < KK; ++s) { lv[s] = -INFINITY; li[s] = 0x7fffffff; }
+}
+
+// merge the list held by lane (lane ^ mask) into this lane's list
+template <int KK>
+__device__ __forceinline__ void e3_topk_merge_xor(float (&lv)[KK], int (&li)[KK], int mask) {
+    float ov[KK]; int oi[KK];
+#pragma unroll
+    for (int s = 0; s < KK; ++s) { ov[s] = __shfl_xor(lv[s], mask); oi[s] = __shfl_xor(li[s], mask); }
+#pragma unroll
+    for (int s = 0; s < KK; ++s) e3_topk_insert<KK>(lv, li, ov[s], oi[s]);
+}
+
+// log-sum-exp pair (max, sum of exp(x - max)) combination
+__device__ __forceinline__ void e3_lse_combine(float &m, float &s, float m2, float s2) {
+    float mn = fmaxf(m, m2);
+    if (mn == -INFINITY) { m = mn; s = 0.f; return; }
+    s = s * __expf(m - mn) + s2 * __expf(m2 - mn);
+    m = mn;
+}

@@ -1,0 +1,531 @@
+// Tree attention: every draft-tree node attends to its sequence's paged KV
+// prefix plus its own ancestors (course lesson "EAGLE-3 speculative decoding:
+// the tree-verifier method", section "Tree draft vs chain draft": one target
+// pass over the whole tree, masked so a token sees only its ancestors).
+// GQA reading: query head h uses KV head h / (Hq / Hkv).
+//
+// bf16, D = 128 (MFMA path). One work-group per (prefix split, KV head,
+// sequence, block of 256 query rows); a query row is (node, head-in-group),
+// so the G query heads sharing a KV head share every K/V tile read.
+//   - K/V tiles of 64 keys are copied from the paged cache into LDS with
+//     16-byte loads; each 16-token cache block is one contiguous 4 KB run for
+//     K ([block, head, slot, d]) and for V ([block, head, d, slot]). The V
+//     layout keeps keys contiguous per dimension, which is what the PV
+//     product needs as its contraction operand.
+//   - Each wave owns 32 query rows. S^T = K . Q^T by MFMA 32x32x16, so every
+//     lane holds one query's scores: the softmax max and sum are in-lane plus
+//     one exchange between the two half-waves. Online softmax in fp32 (exp2,
+//     log2(e) folded into the scale). O^T += V^T . P^T by MFMA with P in bf16.
+//   - Prefix keys are split across work-groups when there are too few
+//     (sequence, head) pairs to fill the chip; the split holding the end of
+//     the prefix also processes the tree keys under the ancestor mask.
+//     Split partials (normalised O, max, sum) are merged in split order by a
+//     second kernel, so results are deterministic.
+// fp32 (any D <= 128): one 64-lane wave per query row, lanes over keys for
+// the scores and over dimensions for P.V; for small models.
+#include "common.h"
+
+namespace {
+
+constexpr int KT = 64;       // keys per tile
+constexpr int DH = 128;      // head dim of the MFMA path
+constexpr int KS_LD = DH + 8;  // LDS row stride (elements) of the K tile
+constexpr int VT_LD = KT + 8;  // LDS row stride (elements) of the V^T tile
+constexpr int ROWS_PER_WG = 256;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+struct AttnParams {
+    const uint16_t *q, *k_tree, *v_tree, *k_cache, *v_cache;
+    const int32_t *block_table, *prefix_len;
+    const uint64_t *mask;
+    const int32_t *parent;
+    uint16_t *out;
+    float *lse;
+    float *ws_o;   // [B, Hkv, nsplit, Rpad, D]
+    float *ws_ml;  // [B, Hkv, nsplit, Rpad, 2]
+    int B, Tq, Tk, Hq, Hkv, W, G, R, Rpad, nrb, nsplit, split_keys, max_blocks, num_blocks;
+    float scale_log2;
+};
+
+// prefix length as the kernels use it: clamped to the block table's capacity
+// (and 0 with an empty pool), so bad data can never index out of bounds
+__device__ __forceinline__ int clamped_len(const int32_t *prefix_len, int b, int max_blocks, int bs, int num_blocks) {
+    const int L = prefix_len[b];
+    if (num_blocks <= 0) return 0;
+    return max(0, min(L, max_blocks * bs));
+}
+
+__device__ __forceinline__ int clamped_block(const int32_t *btab, int j, int num_blocks) {
+    return min(max(btab[j], 0), num_blocks - 1);
+}
+
+// ancestor words of node t of sequence b (mask given or walked from parent[])
+__device__ __forceinline__ void query_mask(const AttnParams &p, int b, int t, uint64_t &w0, uint64_t &w1) {
+    w0 = 0; w1 = 0;
+    if (p.mask) {
+        const uint64_t *m = p.mask + ((size_t)b * p.Tq + t) * p.W;
+        w0 = m[0];
+        if (p.W > 1) w1 = m[1];
+    } else {
+        int cur = t;
+        for (int steps = 0; steps < p.Tq && cur >= 0 && cur < p.Tq; ++steps) {
+            if (cur < 64) w0 |= (uint64_t)1 << cur;
+            else w1 |= (uint64_t)1 << (cur - 64);
+            cur = p.parent[(size_t)b * p.Tq + cur];
+        }
+    }
+}
+
+template <int NW>
+__global__ __launch_bounds__(NW * 64) void tree_attn_bf16_kernel(AttnParams p) {
+    __shared__ __attribute__((aligned(16))) uint16_t Ks[KT][KS_LD];
+    __shared__ __attribute__((aligned(16))) uint16_t Vt[DH][VT_LD];
+    constexpr int NT = NW * 64;
+
+    const int split = blockIdx.x / p.nrb, rb = blockIdx.x % p.nrb;
+    const int kvh = blockIdx.y, b = blockIdx.z;
+    const int L = clamped_len(p.prefix_len, b, p.max_blocks, 16, p.num_blocks);
+    const int C = p.split_keys;
+    const int nsplit_b = L > 0 ? (L + C - 1) / C : 1;
+    if (split >= nsplit_b) return;
+    const int k_begin = split * C;
+    const int k_end = min(L, k_begin + C);
+    const bool last = split == nsplit_b - 1;
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int lr = lane & 31, lh = lane >> 5;
+    const int row = rb * ROWS_PER_WG + wave * 32 + lr;  // this lane's query row
+    const bool row_ok = row < p.R;
+    const int t = row_ok ? row / p.G : 0;
+    const int hq = kvh * p.G + (row_ok ? row % p.G : 0);
+    const bool wave_active = rb * ROWS_PER_WG + wave * 32 < p.R;
+
+    // Q^T operand: d = 16 s + 8 lh + i
+    u32x4_t qb[8];
+    {
+        const uint16_t *qrow = p.q + (((size_t)b * p.Tq + t) * p.Hq + hq) * DH + 8 * lh;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            qb[s] = row_ok ? *reinterpret_cast<const u32x4_t *>(qrow + 16 * s) : u32x4_t{0u, 0u, 0u, 0u};
+        }
+    }
+    uint64_t mw0 = 0, mw1 = 0;
+    if (last && row_ok) query_mask(p, b, t, mw0, mw1);
+
+    f32x16_t ot[4];
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ot[db][r] = 0.f;
+    float m_run = -INFINITY, l_run = 0.f;
+
+    const int32_t *btab = p.block_table + (size_t)b * p.max_blocks;
+    const int n_prefix_tiles = (k_end - k_begin + KT - 1) / KT;
+    const int n_tree_tiles = last ? (p.Tk + KT - 1) / KT : 0;
+
+    for (int it = 0; it < n_prefix_tiles + n_tree_tiles; ++it) {
+        const bool is_tree = it >= n_prefix_tiles;
+        const int kt0 = is_tree ? (it - n_prefix_tiles) * KT : k_begin + it * KT;
+        __syncthreads();  // previous tile fully consumed
+        if (!is_tree) {
+            // K: 1024 chunks of 16 B (key = c / 16, d8 = c % 16)
+            for (int c = tid; c < KT * DH / 8; c += NT) {
+                const int key = c >> 4, d8 = (c & 15) * 8;
+                const int kg = kt0 + key;
+                u32x4_t v = {0u, 0u, 0u, 0u};
+                if (kg < k_end) {
+                    const int phys = clamped_block(btab, kg >> 4, p.num_blocks);
+                    v = *reinterpret_cast<const u32x4_t *>(
+                        p.k_cache + (((size_t)phys * p.Hkv + kvh) * 16 + (kg & 15)) * DH + d8);
+                }
+                *reinterpret_cast<u32x4_t *>(&Ks[key][d8]) = v;
+            }
+            // V: chunk c -> block j = c / 256, d = (c % 256) / 2, 8 slots (c & 1)
+            for (int c = tid; c < KT * DH / 8; c += NT) {
+                const int j = c >> 8, d = (c & 255) >> 1, half = c & 1;
+                const int kg0 = kt0 + 16 * j + 8 * half;
+                u32x4_t v = {0u, 0u, 0u, 0u};
+                if (kg0 < k_end) {
+                    const int phys = clamped_block(btab, kg0 >> 4, p.num_blocks);
+                    v = *reinterpret_cast<const u32x4_t *>(
+                        p.v_cache + (((size_t)phys * p.Hkv + kvh) * DH + d) * 16 + 8 * half);
+                    const int nvalid = k_end - kg0;  // keys past the prefix end -> 0
+                    if (nvalid < 8) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            uint32_t x = v[e];
+                            if (2 * e >= nvalid) x &= 0xffff0000u;
+                            if (2 * e + 1 >= nvalid) x &= 0x0000ffffu;
+                            v[e] = x;
+                        }
+                    }
+                }
+                *reinterpret_cast<u32x4_t *>(&Vt[d][16 * j + 8 * half]) = v;
+            }
+        } else {
+            for (int c = tid; c < KT * DH / 8; c += NT) {
+                const int key = c >> 4, d8 = (c & 15) * 8;
+                const int tk = kt0 + key;
+                u32x4_t kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
+                if (tk < p.Tk) {
+                    const size_t off = (((size_t)b * p.Tk + tk) * p.Hkv + kvh) * DH + d8;
+                    kv = *reinterpret_cast<const u32x4_t *>(p.k_tree + off);
+                    vv = *reinterpret_cast<const u32x4_t *>(p.v_tree + off);
+                }
+                *reinterpret_cast<u32x4_t *>(&Ks[key][d8]) = kv;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    Vt[d8 + 2 * e][key] = (uint16_t)(vv[e] & 0xffffu);
+                    Vt[d8 + 2 * e + 1][key] = (uint16_t)(vv[e] >> 16);
+                }
+            }
+        }
+        __syncthreads();
+        if (!wave_active) continue;
+
+        // S^T[key][query] for two 32-key blocks
+        f32x16_t st[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) st[kb][r] = 0.f;
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                const u32x4_t a = *reinterpret_cast<const u32x4_t *>(&Ks[kb * 32 + lr][16 * s + 8 * lh]);
+                st[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                                 __builtin_bit_cast(bf16x8_t, qb[s]), st[kb], 0, 0, 0);
+            }
+        }
+        // scale, mask, tile max; key of register r: 32 kb + 8 (r / 4) + 4 lh + r % 4
+        const uint64_t mword = (kt0 / 64 == 0) ? mw0 : mw1;
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int kk = kb * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+                const bool vis = is_tree ? (((mword >> kk) & 1u) && (kt0 + kk < p.Tk)) : (kt0 + kk < k_end);
+                const float sv = vis ? st[kb][r] * p.scale_log2 : -INFINITY;
+                st[kb][r] = sv;
+                tmax = fmaxf(tmax, sv);
+            }
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+        const float m_new = fmaxf(m_run, tmax);
+        const float alpha = (m_new == -INFINITY) ? 1.f : exp2f(m_run - m_new);
+        const float msub = (m_new == -INFINITY) ? 0.f : m_new;
+        float psum = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float pv = exp2f(st[kb][r] - msub);
+                st[kb][r] = pv;
+                psum += pv;
+            }
+        l_run = l_run * alpha + psum;
+        m_run = m_new;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) ot[db][r] *= alpha;
+
+        // O^T[d][query] += V^T[d][key] . P^T[key][query], 16 keys per step
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const int kb = ks >> 1, r0 = 8 * (ks & 1);
+            u32x4_t pb;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) pb[e] = e3_pack_bf16x2(st[kb][r0 + 2 * e], st[kb][r0 + 2 * e + 1]);
+#pragma unroll
+            for (int db = 0; db < 4; ++db) {
+                const uint16_t *vrow = &Vt[db * 32 + lr][16 * ks + 4 * lh];
+                const u32x2_t lo = *reinterpret_cast<const u32x2_t *>(vrow);
+                const u32x2_t hi = *reinterpret_cast<const u32x2_t *>(vrow + 8);
+                const u32x4_t a = {lo[0], lo[1], hi[0], hi[1]};
+                ot[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                                 __builtin_bit_cast(bf16x8_t, pb), ot[db], 0, 0, 0);
+            }
+        }
+    }
+    if (!row_ok) return;
+    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    // lane holds d = 32 db + 8 (r / 4) + 4 lh + r % 4 for its query
+    if (nsplit_b == 1) {
+        uint16_t *orow = p.out + (((size_t)b * p.Tq + t) * p.Hq + hq) * DH;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const int d = db * 32 + 8 * g4 + 4 * lh;
+                u32x2_t o;
+                o[0] = e3_pack_bf16x2(ot[db][4 * g4] * inv, ot[db][4 * g4 + 1] * inv);
+                o[1] = e3_pack_bf16x2(ot[db][4 * g4 + 2] * inv, ot[db][4 * g4 + 3] * inv);
+                *reinterpret_cast<u32x2_t *>(orow + d) = o;
+            }
+        if (p.lse && lh == 0)
+            p.lse[((size_t)b * p.Tq + t) * p.Hq + hq] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+    } else {
+        const size_t prow = (((size_t)b * p.Hkv + kvh) * p.nsplit + split) * p.Rpad + row;
+        float *orow = p.ws_o + prow * DH;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const int d = db * 32 + 8 * g4 + 4 * lh;
+                f32x4_t o = {ot[db][4 * g4] * inv, ot[db][4 * g4 + 1] * inv, ot[db][4 * g4 + 2] * inv,
+                             ot[db][4 * g4 + 3] * inv};
+                *reinterpret_cast<f32x4_t *>(orow + d) = o;
+            }
+        if (lh == 0) {
+            p.ws_ml[prow * 2] = m_run;
+            p.ws_ml[prow * 2 + 1] = l_tot;
+        }
+    }
+}
+
+// Merge split partials of multi-split sequences, in split order.
+__global__ __launch_bounds__(128) void tree_attn_combine_kernel(AttnParams p) {
+    const int idx = blockIdx.x;  // (b, t, hq)
+    const int hq = idx % p.Hq, t = (idx / p.Hq) % p.Tq, b = idx / (p.Hq * p.Tq);
+    const int L = clamped_len(p.prefix_len, b, p.max_blocks, 16, p.num_blocks);
+    const int nsplit_b = L > 0 ? (L + p.split_keys - 1) / p.split_keys : 1;
+    if (nsplit_b <= 1) return;
+    const int kvh = hq / p.G, row = t * p.G + hq % p.G;
+    const size_t base = ((size_t)b * p.Hkv + kvh) * p.nsplit;
+    float M = -INFINITY;
+    for (int s = 0; s < nsplit_b; ++s) M = fmaxf(M, p.ws_ml[((base + s) * p.Rpad + row) * 2]);
+    const int d = threadIdx.x;
+    float acc = 0.f, den = 0.f;
+    for (int s = 0; s < nsplit_b; ++s) {
+        const size_t prow = (base + s) * p.Rpad + row;
+        const float ms = p.ws_ml[prow * 2], ls = p.ws_ml[prow * 2 + 1];
+        const float wgt = (ms == -INFINITY) ? 0.f : ls * exp2f(ms - M);
+        acc += wgt * p.ws_o[prow * DH + d];
+        den += wgt;
+    }
+    const float o = den > 0.f ? acc / den : 0.f;
+    p.out[(((size_t)b * p.Tq + t) * p.Hq + hq) * DH + d] = e3_f32_to_bf16(o);
+    if (p.lse && d == 0)
+        p.lse[((size_t)b * p.Tq + t) * p.Hq + hq] = den > 0.f ? (M + log2f(den)) * kLn2 : -INFINITY;
+}
+
+// ---------------------------------------------------------------- fp32 path
+
+struct AttnF32 {
+    const float *q, *k_tree, *v_tree, *k_cache, *v_cache;
+    const int32_t *block_table, *prefix_len;
+    const uint64_t *mask;
+    const int32_t *parent;
+    float *out, *lse;
+    int Tq, Tk, Hq, Hkv, D, W, G, max_blocks, block_size, num_blocks;
+    float scale;
+};
+
+__global__ __launch_bounds__(64) void tree_attn_f32_kernel(AttnF32 p) {
+    __shared__ float qs[128];
+    __shared__ float ps[64];
+    __shared__ int keyref[64];  // >= 0: prefix position; < 0: -(tree key) - 1
+    const int idx = blockIdx.x;
+    const int hq = idx % p.Hq, t = (idx / p.Hq) % p.Tq, b = idx / (p.Hq * p.Tq);
+    const int kvh = hq / p.G, lane = threadIdx.x, D = p.D;
+    const int L = clamped_len(p.prefix_len, b, p.max_blocks, p.block_size, p.num_blocks);
+    const float *qrow = p.q + (((size_t)b * p.Tq + t) * p.Hq + hq) * D;
+    for (int d = lane; d < D; d += 64) qs[d] = qrow[d];
+    uint64_t w0 = 0, w1 = 0;
+    if (p.mask) {
+        const uint64_t *m = p.mask + ((size_t)b * p.Tq + t) * p.W;
+        w0 = m[0];
+        if (p.W > 1) w1 = m[1];
+    } else {
+        int cur = t;
+        for (int s = 0; s < p.Tq && cur >= 0 && cur < p.Tq; ++s) {
+            if (cur < 64) w0 |= (uint64_t)1 << cur; else w1 |= (uint64_t)1 << (cur - 64);
+            cur = p.parent[(size_t)b * p.Tq + cur];
+        }
+    }
+    __syncthreads();
+    const int32_t *btab = p.block_table + (size_t)b * p.max_blocks;
+    const int bs = p.block_size;
+    float m_run = -INFINITY, l_run = 0.f;
+    float acc0 = 0.f, acc1 = 0.f;  // d = lane, lane + 64
+    const int nkeys = L + p.Tk;
+    for (int c0 = 0; c0 < nkeys; c0 += 64) {
+        const int j = c0 + lane;
+        float s = -INFINITY;
+        int ref = 0;
+        if (j < L) {
+            const int blk = clamped_block(btab, j / bs, p.num_blocks);
+            const float *kr = p.k_cache + (((size_t)blk * p.Hkv + kvh) * bs + j % bs) * D;
+            float dot = 0.f;
+            for (int d = 0; d < D; ++d) dot = fmaf(qs[d], kr[d], dot);
+            s = dot * p.scale;
+            ref = j;
+        } else if (j < nkeys) {
+            const int tk = j - L;
+            const bool vis = tk < 64 ? ((w0 >> tk) & 1u) : ((w1 >> (tk - 64)) & 1u);
+            if (vis) {
+                const float *kr = p.k_tree + (((size_t)b * p.Tk + tk) * p.Hkv + kvh) * D;
+                float dot = 0.f;
+                for (int d = 0; d < D; ++d) dot = fmaf(qs[d], kr[d], dot);
+                s = dot * p.scale;
+            }
+            ref = -tk - 1;
+        }
+        float cmax = s;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) cmax = fmaxf(cmax, __shfl_xor(cmax, off));
+        const float m_new = fmaxf(m_run, cmax);
+        const float alpha = (m_new == -INFINITY) ? 1.f : expf(m_run - m_new);
+        const float pj = (s == -INFINITY) ? 0.f : expf(s - m_new);
+        float csum = pj;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) csum += __shfl_xor(csum, off);
+        l_run = l_run * alpha + csum;
+        m_run = m_new;
+        ps[lane] = pj;
+        keyref[lane] = ref;
+        __syncthreads();
+        acc0 *= alpha; acc1 *= alpha;
+        const int cn = min(64, nkeys - c0);
+        for (int jj = 0; jj < cn; ++jj) {
+            const float pv = ps[jj];
+            if (pv == 0.f) continue;
+            const int r = keyref[jj];
+            if (r >= 0) {
+                const int blk = clamped_block(btab, r / bs, p.num_blocks);
+                const float *vc = p.v_cache + ((size_t)blk * p.Hkv + kvh) * (size_t)D * bs + r % bs;
+                if (lane < D) acc0 = fmaf(pv, vc[(size_t)lane * bs], acc0);
+                if (lane + 64 < D) acc1 = fmaf(pv, vc[(size_t)(lane + 64) * bs], acc1);
+            } else {
+                const float *vr = p.v_tree + (((size_t)b * p.Tk + (-r - 1)) * p.Hkv + kvh) * D;
+                if (lane < D) acc0 = fmaf(pv, vr[lane], acc0);
+                if (lane + 64 < D) acc1 = fmaf(pv, vr[lane + 64], acc1);
+            }
+        }
+        __syncthreads();
+    }
+    float *orow = p.out + (((size_t)b * p.Tq + t) * p.Hq + hq) * D;
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    if (lane < D) orow[lane] = acc0 * inv;
+    if (lane + 64 < D) orow[lane + 64] = acc1 * inv;
+    if (p.lse && lane == 0) p.lse[((size_t)b * p.Tq + t) * p.Hq + hq] = l_run > 0.f ? m_run + logf(l_run) : -INFINITY;
+}
+
+// ---------------------------------------------------------------- host side
+
+struct Plan {
+    int nrb, nsplit, split_keys, nw;
+    size_t ws_bytes;
+};
+
+int check_args(const eagle3_tree_attn_args *a) {
+    if (!a) return EAGLE3_ERR_ARG;
+    if (a->B < 0 || a->Tq < 1 || a->Tk < 0 || a->Hq < 1 || a->Hkv < 1 || a->max_blocks < 1 || a->num_blocks < 0)
+        return EAGLE3_ERR_ARG;
+    if (!(a->scale > 0.f)) return EAGLE3_ERR_ARG;
+    if (a->Hq % a->Hkv != 0) return EAGLE3_ERR_UNSUPPORTED;
+    if (a->W < 1 || a->W > 2 || a->Tk > 64 * a->W) return EAGLE3_ERR_UNSUPPORTED;
+    if (a->block_size != 16) return EAGLE3_ERR_UNSUPPORTED;
+    if (a->dtype == EAGLE3_BF16) {
+        if (a->D != 128) return EAGLE3_ERR_UNSUPPORTED;
+    } else if (a->dtype == EAGLE3_F32) {
+        if (a->D < 1 || a->D > 128) return EAGLE3_ERR_UNSUPPORTED;
+    } else {
+        return EAGLE3_ERR_UNSUPPORTED;
+    }
+    if (a->split_keys < 0 || a->split_keys % KT != 0) return EAGLE3_ERR_UNSUPPORTED;
+    if (a->mask == nullptr) {
+        if (a->parent == nullptr || a->Tq != a->Tk) return EAGLE3_ERR_ARG;
+    }
+    return EAGLE3_OK;
+}
+
+Plan make_plan(const eagle3_tree_attn_args *a) {
+    Plan pl{};
+    const int G = a->Hq / a->Hkv;
+    const int R = a->Tq * G;
+    pl.nrb = (R + ROWS_PER_WG - 1) / ROWS_PER_WG;
+    const int rows0 = R < ROWS_PER_WG ? R : ROWS_PER_WG;
+    pl.nw = rows0 <= 64 ? 2 : rows0 <= 128 ? 4 : 8;
+    const long lmax = (long)a->max_blocks * a->block_size;
+    const long ktiles = lmax > 0 ? (lmax + KT - 1) / KT : 1;
+    if (a->split_keys > 0) {
+        pl.split_keys = a->split_keys;
+    } else {
+        const long base = (long)a->B * a->Hkv * pl.nrb;
+        long ns = base > 0 ? (256 + base - 1) / base : 1;
+        if (ns < 1) ns = 1;
+        if (ns > ktiles) ns = ktiles;
+        const long tiles_per = (ktiles + ns - 1) / ns;
+        pl.split_keys = (int)(tiles_per * KT);
+    }
+    pl.nsplit = (int)((lmax + pl.split_keys - 1) / pl.split_keys);
+    if (pl.nsplit < 1) pl.nsplit = 1;
+    pl.ws_bytes = 0;
+    if (a->dtype == EAGLE3_BF16 && pl.nsplit > 1) {
+        const size_t rows = (size_t)a->B * a->Hkv * pl.nsplit * (size_t)pl.nrb * ROWS_PER_WG;
+        pl.ws_bytes = ((rows * DH * 4 + 255) & ~(size_t)255) + rows * 2 * 4;
+    }
+    return pl;
+}
+
+}  // namespace
+
+extern "C" size_t eagle3_tree_attn_workspace(const eagle3_tree_attn_args *a) {
+    if (check_args(a) != EAGLE3_OK) return 0;
+    return make_plan(a).ws_bytes;
+}
+
+extern "C" int eagle3_tree_attn(const eagle3_tree_attn_args *a, void *ws, size_t ws_bytes, void *stream) {
+    const int rc = check_args(a);
+    if (rc != EAGLE3_OK) return rc;
+    if (a->B == 0) return EAGLE3_OK;
+    if (!a->q || !a->out || !a->block_table || !a->prefix_len) return EAGLE3_ERR_ARG;
+    if (a->Tk > 0 && (!a->k_tree || !a->v_tree)) return EAGLE3_ERR_ARG;
+    if (a->num_blocks > 0 && (!a->k_cache || !a->v_cache)) return EAGLE3_ERR_ARG;
+    for (const void *ptr : {a->q, a->k_tree, a->v_tree, a->k_cache, a->v_cache, (const void *)a->out})
+        if (ptr && !e3_aligned16(ptr)) return EAGLE3_ERR_ARG;
+    const Plan pl = make_plan(a);
+    if (ws_bytes < pl.ws_bytes || (pl.ws_bytes > 0 && !ws)) return EAGLE3_ERR_WORKSPACE;
+    if (pl.ws_bytes > 0 && !e3_aligned16(ws)) return EAGLE3_ERR_ARG;
+    const hipStream_t st = e3_stream(stream);
+    const int G = a->Hq / a->Hkv;
+    if (a->dtype == EAGLE3_BF16) {
+        AttnParams p;
+        p.q = (const uint16_t *)a->q; p.k_tree = (const uint16_t *)a->k_tree; p.v_tree = (const uint16_t *)a->v_tree;
+        p.k_cache = (const uint16_t *)a->k_cache; p.v_cache = (const uint16_t *)a->v_cache;
+        p.block_table = a->block_table; p.prefix_len = a->prefix_len; p.mask = a->mask; p.parent = a->parent;
+        p.out = (uint16_t *)a->out; p.lse = a->lse;
+        p.B = a->B; p.Tq = a->Tq; p.Tk = a->Tk; p.Hq = a->Hq; p.Hkv = a->Hkv; p.W = a->W; p.G = G;
+        p.R = a->Tq * G; p.nrb = pl.nrb; p.Rpad = pl.nrb * ROWS_PER_WG; p.nsplit = pl.nsplit;
+        p.split_keys = pl.split_keys; p.max_blocks = a->max_blocks; p.num_blocks = a->num_blocks;
+        p.scale_log2 = a->scale * kLog2e;
+        p.ws_o = nullptr; p.ws_ml = nullptr;
+        if (pl.ws_bytes > 0) {
+            const size_t rows = (size_t)a->B * a->Hkv * pl.nsplit * (size_t)pl.nrb * ROWS_PER_WG;
+            p.ws_o = (float *)ws;
+            p.ws_ml = (float *)((char *)ws + ((rows * DH * 4 + 255) & ~(size_t)255));
+        }
+        dim3 grid(pl.nsplit * pl.nrb, a->Hkv, a->B);
+        switch (pl.nw) {
+            case 2: tree_attn_bf16_kernel<2><<<grid, 128, 0, st>>>(p); break;
+            case 4: tree_attn_bf16_kernel<4><<<grid, 256, 0, st>>>(p); break;
+            default: tree_attn_bf16_kernel<8><<<grid, 512, 0, st>>>(p); break;
+        }
+        if (pl.nsplit > 1) tree_attn_combine_kernel<<<a->B * a->Tq * a->Hq, DH, 0, st>>>(p);
+    } else {
+        AttnF32 p;
+        p.q = (const float *)a->q; p.k_tree = (const float *)a->k_tree; p.v_tree = (const float *)a->v_tree;
+        p.k_cache = (const float *)a->k_cache; p.v_cache = (const float *)a->v_cache;
+        p.block_table = a->block_table; p.prefix_len = a->prefix_len; p.mask = a->mask; p.parent = a->parent;
+        p.out = (float *)a->out; p.lse = a->lse;
+        p.Tq = a->Tq; p.Tk = a->Tk; p.Hq = a->Hq; p.Hkv = a->Hkv; p.D = a->D; p.W = a->W; p.G = G;
+        p.max_blocks = a->max_blocks; p.block_size = a->block_size; p.num_blocks = a->num_blocks;
+        p.scale = a->scale;
+        tree_attn_f32_kernel<<<a->B * a->Tq * a->Hq, 64, 0, st>>>(p);
+    }
+    E3_LAUNCH_CHECK();
+    return EAGLE3_OK;
+}
