@@ -326,11 +326,29 @@ def _select_kv(kv: PagedKV, sel: np.ndarray) -> PagedKV:
     return PagedKV(kv.k_cache, kv.v_cache, kv.block_table[sel].copy(), kv.prefix_len[sel].copy(), kv.block_size)
 
 
-def lm_head_weight(shape_or_wid, V: int, K: int, std: float = 0.02) -> np.ndarray:
+def lm_head_weight(shape_or_wid, V: int, K: int, std: float = 0.02, threads: int | None = None) -> np.ndarray:
     """LM-head matrix [V, K] (vocabulary-major), N(0, std^2) in bf16. The model
-    is fixed per workload: seeds vary the inputs, not the weights."""
+    is fixed per workload: seeds vary the inputs, not the weights.
+
+    Rows come in blocks of 2048, block i from its own generator
+    default_rng([workload_id, 0, C_WLM, i]), so blocks can be drawn in
+    parallel threads with identical results."""
+    import concurrent.futures
+    import os
     wid = shape_or_wid.wid if hasattr(shape_or_wid, "wid") else int(shape_or_wid)
-    return normal_bf16(child_rng(wid, 0, C_WLM), (V, K), std=std)
+    out = np.empty((V, K), dtype=np.uint16)
+    RB = 2048
+
+    def block(i):
+        r0 = i * RB
+        r1 = min(V, r0 + RB)
+        rng = np.random.default_rng([wid, 0, C_WLM, i])
+        out[r0:r1] = normal_bf16(rng, (r1 - r0, K), std=std)
+
+    nthreads = threads or min(16, os.cpu_count() or 1)
+    with concurrent.futures.ThreadPoolExecutor(nthreads) as ex:
+        list(ex.map(block, range((V + RB - 1) // RB)))
+    return out
 
 
 def plant_tokens(parent: np.ndarray, target_idx: np.ndarray, p_seq, plant_u, plant_id) -> np.ndarray:

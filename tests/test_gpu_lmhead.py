@@ -40,8 +40,15 @@ def compare(orc, h, w, topk, got, want_lse, tol=1e-4):
     gi, gv, gg, gl = got
     ri, rv, rgap, rl = orc.lmhead(h, w, topk=topk + 1)
     clean = np.all(np.diff(rv, axis=1) <= -MARGIN, axis=1)
-    assert clean.mean() > 0.5
+    assert clean.mean() > (0.5 if topk <= 2 else 0.2)
     assert np.array_equal(gi[clean], ri[clean, :topk])
+    # every row: the logit of each returned id is the oracle's value at that rank
+    hf = synth.bf16_to_f32(h) if h.dtype == np.uint16 else h
+    wf = synth.bf16_to_f32(w) if w.dtype == np.uint16 else w
+    for m in range(h.shape[0]):
+        lg = wf[gi[m]].astype(np.float64) @ hf[m].astype(np.float64)
+        assert np.abs(lg - rv[m, :topk]).max() <= tol
+    assert len(set(map(tuple, [sorted(r) for r in gi]))) > 0 and all(len(set(r)) == topk for r in gi)
     assert np.abs(gv[clean] - rv[clean, :topk]).max() <= tol
     top1_clean = rgap >= MARGIN
     assert np.array_equal(gi[top1_clean, 0], ri[top1_clean, 0])

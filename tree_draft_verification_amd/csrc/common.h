@@ -31,9 +31,22 @@ __device__ __forceinline__ uint16_t e3_f32_to_bf16(float f) {
     return (uint16_t)(u >> 16);
 }
 
-// two fp32 -> packed bf16 pair (lo in bits 0..15)
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2_t;
+
+// two fp32 -> packed bf16 pair (lo in bits 0..15), round to nearest even
+// (one v_cvt_pk_bf16_f32 on gfx950)
 __device__ __forceinline__ uint32_t e3_pack_bf16x2(float lo, float hi) {
-    return (uint32_t)e3_f32_to_bf16(lo) | ((uint32_t)e3_f32_to_bf16(hi) << 16);
+    const f32x2_t v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
+// Split two fp32 values into bf16 hi + lo parts (x ~= hi + lo to about 16
+// significant bits): hi = bf16(x), lo = bf16(x - hi); x - hi is exact in fp32.
+__device__ __forceinline__ void e3_split_bf16x2(float a, float b, uint32_t &hi, uint32_t &lo) {
+    hi = e3_pack_bf16x2(a, b);
+    const float ha = __uint_as_float(hi << 16), hb = __uint_as_float(hi & 0xffff0000u);
+    lo = e3_pack_bf16x2(a - ha, b - hb);
 }
 
 // (value, index) order used by every selection: larger value first, then lower index.

@@ -15,7 +15,8 @@
 //   - Each wave owns 32 query rows. S^T = K . Q^T by MFMA 32x32x16, so every
 //     lane holds one query's scores: the softmax max and sum are in-lane plus
 //     one exchange between the two half-waves. Online softmax in fp32 (exp2,
-//     log2(e) folded into the scale). O^T += V^T . P^T by MFMA with P in bf16.
+//     log2(e) folded into the scale). O^T += V^T . P^T by MFMA with P split
+//     into bf16 hi + lo parts, so P keeps ~16 significant bits.
 //   - Prefix keys are split across work-groups when there are too few
 //     (sequence, head) pairs to fill the chip; the split holding the end of
 //     the prefix also processes the tree keys under the ancestor mask.
@@ -230,21 +231,28 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_bf16_kernel(AttnParams p) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) ot[db][r] *= alpha;
 
-        // O^T[d][query] += V^T[d][key] . P^T[key][query], 16 keys per step
+        // O^T[d][query] += V^T[d][key] . P^T[key][query], 16 keys per step.
+        // P enters as bf16 hi + lo (two MFMAs on the same V operand): a single
+        // bf16 rounding of P would leave ~2e-3 relative error in the output.
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             const int kb = ks >> 1, r0 = 8 * (ks & 1);
-            u32x4_t pb;
+            u32x4_t ph, pl;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) pb[e] = e3_pack_bf16x2(st[kb][r0 + 2 * e], st[kb][r0 + 2 * e + 1]);
+            for (int e = 0; e < 4; ++e) {
+                uint32_t h2, l2;
+                e3_split_bf16x2(st[kb][r0 + 2 * e], st[kb][r0 + 2 * e + 1], h2, l2);
+                ph[e] = h2;
+                pl[e] = l2;
+            }
 #pragma unroll
             for (int db = 0; db < 4; ++db) {
                 const uint16_t *vrow = &Vt[db * 32 + lr][16 * ks + 4 * lh];
                 const u32x2_t lo = *reinterpret_cast<const u32x2_t *>(vrow);
                 const u32x2_t hi = *reinterpret_cast<const u32x2_t *>(vrow + 8);
-                const u32x4_t a = {lo[0], lo[1], hi[0], hi[1]};
-                ot[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                                 __builtin_bit_cast(bf16x8_t, pb), ot[db], 0, 0, 0);
+                const bf16x8_t a = __builtin_bit_cast(bf16x8_t, u32x4_t{lo[0], lo[1], hi[0], hi[1]});
+                ot[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, ph), ot[db], 0, 0, 0);
+                ot[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, pl), ot[db], 0, 0, 0);
             }
         }
     }

@@ -50,20 +50,32 @@ class VerifyStep:
             self._attn_ws = torch.empty(max(256, need), dtype=torch.uint8, device=q.device)
         return a
 
-    def forward(self, parent, q, k_tree, v_tree, stream=None):
-        """Enqueue a0-a3 (mask, attention, norm, LM-head argmax)."""
+    def forward(self, parent, q, k_tree, v_tree, stream=None, events=None):
+        """Enqueue a0-a3 (mask, attention, norm, LM-head argmax). ``events``:
+        optional {"attn": (start, end), "lmhead": (start, end)} HIP events
+        recorded around those calls on the same stream."""
+        ev = events or {}
         B_.eagle3_tree_mask(parent, self.W, self.mask, self.depth, self.status, stream=stream)
         a = self._args(q, k_tree, v_tree)
+        self._record(ev, "attn", 0, stream)
         B_.eagle3_tree_attn(a, self._attn_ws, stream=stream)
+        self._record(ev, "attn", 1, stream)
         B_.eagle3_rmsnorm(self.attn.view(self.B * self.T, self.K), self.hidden, eps=self.eps, stream=stream)
+        self._record(ev, "lmhead", 0, stream)
         B_.eagle3_lmhead_argmax(self.hidden, self.w_lm, 1, self.idx, self.val, self.gap, None, self.lm_ws,
                                 stream=stream)
+        self._record(ev, "lmhead", 1, stream)
+
+    @staticmethod
+    def _record(ev, name, i, stream):
+        if name in ev:
+            ev[name][i].record(stream if stream is not None else torch.cuda.current_stream())
 
     def accept(self, tokens, stream=None):
         """Enqueue a4 (greedy acceptance) on the argmax of forward()."""
         B_.eagle3_accept_path(tokens, self.idx.view(self.B, self.T), self.accept_len, self.path, self.out_tokens,
                               mask=self.mask, stream=stream)
 
-    def run(self, parent, q, k_tree, v_tree, tokens, stream=None):
-        self.forward(parent, q, k_tree, v_tree, stream)
+    def run(self, parent, q, k_tree, v_tree, tokens, stream=None, events=None):
+        self.forward(parent, q, k_tree, v_tree, stream, events)
         self.accept(tokens, stream)
