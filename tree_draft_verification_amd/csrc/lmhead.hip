@@ -2,28 +2,41 @@
 // memory. The target's argmax at every tree node decides acceptance (course
 // lesson "EAGLE-3 speculative decoding: the tree-verifier method", section
 // "Verify-accept semantics"); the draft head's top-k uses the same head (news
-// write-up of the EAGLE-3 paper, draft-stage paragraphs).
+// write-up of the EAGLE-3 paper, draft-stage paragraphs), and every forward
+// streams the whole head from memory (the same write-up's opening remark that
+// each forward reads all parameters), so for few rows this is an HBM stream.
 //
-// Pass 1 (one work-group per 256-row vocabulary tile x 64-row hidden tile):
-//   bf16: MFMA 32x32x16. The vocabulary rows are the MFMA "row" operand and
-//   the hidden rows the "column" operand, so every accumulator register of a
-//   lane belongs to one hidden row: per-row selection needs no transposes.
-//   Each lane streams 64 contiguous bytes of its weight row per 64-wide k
-//   chunk (both operands use the same k permutation, so the contraction is
-//   unchanged), two chunks in flight. fp32: plain FMA loop (small models).
-//   The 64x256 logit tile is staged in LDS; 4 threads per row keep a sorted
-//   top-KK list (value desc, id asc) and an online (max, sum exp) pair, then
-//   merge by lane shuffles. One (list, max, sum) record per row and tile goes
-//   to the workspace.
-// Pass 2 (one work-group per row): merges the records of all tiles in a
-//   fixed order -> deterministic results.
+// Pass 1, bf16 (one work-group per 128-row vocabulary tile x 64-row hidden
+// tile, 4 waves, 2 work-groups per CU):
+//   - 64-wide k chunks of the weight tile (128 rows x 128 B) and of the hidden
+//     tile (64 rows x 128 B) go straight from global memory into a 3-stage LDS
+//     ring with 16-byte global_load_lds (no VGPR round trip); each 1 KB load
+//     instruction covers 8 full 128 B row segments. A wave waits only for the
+//     oldest stage (explicit vmcnt) and the stage hand-off uses a bare barrier
+//     (a fenced barrier would drain the stages still in flight).
+//   - 16-byte columns are XOR-swizzled by row pair, so the MFMA operand reads
+//     (ds_read_b128, 32 rows per instruction) are bank-conflict free.
+//   - Each tile starts its k sweep at a different chunk (tile * 7 mod K/64):
+//     tiles running together then read different column ranges of their rows
+//     instead of all hitting the same 128 B column of rows 8 KB apart.
+//   - MFMA 32x32x16: vocabulary rows are the "row" operand and hidden rows the
+//     "column" operand, so each accumulator register of a lane belongs to one
+//     hidden row.
+// Pass 1, fp32: plain FMA loop over a 256-row vocabulary tile (small models).
+// Epilogue (both): the logit tile is staged in LDS; a few threads per row keep
+// a sorted top-KK list (value desc, id asc) and an online (max, sum exp) pair,
+// merged by lane shuffles; one record per (row, tile) goes to the workspace.
+// Pass 2 (one work-group per row): merges all tiles' records in a fixed order,
+// so results are deterministic.
 #include "common.h"
 
 namespace {
 
-constexpr int BN = 256;  // vocabulary rows per tile
-constexpr int BK = 64;   // k per chunk (bf16 path)
-constexpr int LDP = BN + 4;
+constexpr int BN_B = 128;  // vocabulary rows per tile, bf16 path
+constexpr int BN_F = 256;  // vocabulary rows per tile, fp32 path
+constexpr int BK = 64;     // k per chunk, bf16 path
+constexpr int NSTAGE = 3;  // LDS ring depth, bf16 path
+constexpr int ROT = 7;     // chunk rotation per tile
 
 struct Partials {
     float *val;  // [M, ntiles, KK]
@@ -32,12 +45,12 @@ struct Partials {
     float *se;   // [M, ntiles]
 };
 
-// Per-row selection over an LDS tile lg[BMt][LDP]; tpr threads per row.
-template <int BMt, int KK, bool LSE>
-__device__ __forceinline__ void tile_select(const float (*lg)[LDP], int m0, int M, int n0, int N, int tile, int ntiles,
-                                            const Partials &p) {
+// Per-row selection over an LDS tile lg[BMt][BNt + 4]; 256 / BMt threads per row.
+template <int BMt, int BNt, int KK, bool LSE>
+__device__ __forceinline__ void tile_select(const float (*lg)[BNt + 4], int m0, int M, int n0, int N, int tile,
+                                            int ntiles, const Partials &p) {
     constexpr int TPR = 256 / BMt;
-    constexpr int PER = BN / TPR;
+    constexpr int PER = BNt / TPR;
     const int row = threadIdx.x / TPR, part = threadIdx.x % TPR;
     float lv[KK]; int li[KK];
     e3_topk_init<KK>(lv, li);
@@ -71,92 +84,117 @@ __device__ __forceinline__ void tile_select(const float (*lg)[LDP], int m0, int 
     }
 }
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// 16-byte column swizzle of an LDS row (row pairs share a permutation)
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
+
+// wait until at most N vector-memory operations of this wave are outstanding
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
 template <int KK, bool LSE>
 __global__ __launch_bounds__(256, 2) void lmhead_bf16_kernel(const uint16_t *__restrict__ h,
                                                              const uint16_t *__restrict__ w, int M, int N, int K,
                                                              int ntiles, Partials p) {
-    constexpr int BM = 64;
-    __shared__ float lg[BM][LDP];
+    constexpr int BM = 64, BN = BN_B, NS = NSTAGE;
+    constexpr int WST = BN * 128, HST = BM * 128;   // bytes of one stage (128 B = 64 bf16 per row)
+    constexpr int WBLK = WST / 1024;                 // 1 KB load blocks of the weight part
+    constexpr int LOADS = (WST + HST) / 1024 / 4;    // 1 KB loads per wave per stage
+    static_assert((WST + HST) % 4096 == 0, "stage must split evenly over 4 waves");
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[NS * (WST + HST)];
+    static_assert(sizeof(float) * BM * (BN + 4) <= sizeof(smem), "logit tile must fit the ring");
+
     const int mt = blockIdx.x, tile = blockIdx.y;
     const int m0 = mt * BM, n0 = tile * BN;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int lr = lane & 31, lh = lane >> 5;
 
-    const uint16_t *wrow[2];
-    const uint16_t *hrow[2];
-    bool hval[2];
+    // global source of each of this lane's loads (chunk offset added per stage):
+    // block b of a stage holds rows 8b..8b+7; lane l fills row 8b + l/8, 16-byte
+    // column l%8, which receives global column (l%8) ^ swz(row)
+    const uint16_t *src[LOADS];
+    int dst[LOADS];
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-        int v = n0 + wave * 64 + nb * 32 + lr;
-        v = v < N ? v : N - 1;  // clamped rows are computed and ignored
-        wrow[nb] = w + (size_t)v * K + lh * 32;
+    for (int j = 0; j < LOADS; ++j) {
+        const int blk = wave * LOADS + j;
+        if (blk < WBLK) {
+            const int row = blk * 8 + lane / 8;
+            const int v = min(n0 + row, N - 1);   // rows past N are computed and dropped
+            src[j] = w + (size_t)v * K + 8 * ((lane & 7) ^ swz(row));
+            dst[j] = blk * 1024;
+        } else {
+            const int row = (blk - WBLK) * 8 + lane / 8;
+            const int m = min(m0 + row, M - 1);   // rows past M are computed and dropped
+            src[j] = h + (size_t)m * K + 8 * ((lane & 7) ^ swz(row));
+            dst[j] = WST + (blk - WBLK) * 1024;
+        }
     }
+    auto issue = [&](int stage, int kc) {
+        unsigned char *base = smem + stage * (WST + HST);
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-        const int m = m0 + mb * 32 + lr;
-        hval[mb] = m < M;
-        hrow[mb] = h + (size_t)(m < M ? m : M - 1) * K + lh * 32;
-    }
+        for (int j = 0; j < LOADS; ++j)
+            __builtin_amdgcn_global_load_lds((const void *)(src[j] + kc), (lds_void_t *)(base + dst[j]), 16, 0, 0);
+    };
 
-    f32x16_t acc[2][2];
+    f32x16_t acc[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+        for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
 
-    u32x4_t a0[2][4], b0[2][4], a1[2][4], b1[2][4];
-    const u32x4_t zero = {0u, 0u, 0u, 0u};
+    const int nch = K / BK;
+    const int rot = (tile * ROT) % nch;
+#pragma unroll
+    for (int st = 0; st < NS - 1; ++st)
+        if (st < nch) issue(st, ((st + rot) % nch) * BK);
 
-    auto load = [&](u32x4_t (&a)[2][4], u32x4_t (&b)[2][4], int kc) {
+    const int vrow = wave * 32 + lr;  // this lane's weight row in the tile (MFMA row operand)
+    for (int c = 0; c < nch; ++c) {
+        if (c + NS - 2 < nch) wait_vmcnt<(NS - 2) * LOADS>();
+        else wait_vmcnt<0>();
+        // stage c has landed for every wave, and every wave is done with the
+        // buffer about to be refilled; a fenced barrier would also drain the
+        // stages still in flight, so the barrier is a bare one
+        __builtin_amdgcn_s_barrier();
+        __asm__ volatile("" ::: "memory");
+        if (c + NS - 1 < nch) issue((c + NS - 1) % NS, ((c + NS - 1 + rot) % nch) * BK);
+        const unsigned char *wb = smem + (c % NS) * (WST + HST);
+        const unsigned char *hb = wb + WST;
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
+        for (int s = 0; s < 4; ++s) {
+            // both operands take k = 32 lh + 8 s .. +7 of the chunk
+            const int col = 4 * lh + s;
+            const u32x4_t a = *reinterpret_cast<const u32x4_t *>(wb + vrow * 128 + ((col ^ swz(vrow)) << 4));
 #pragma unroll
-            for (int s = 0; s < 4; ++s) a[nb][s] = *reinterpret_cast<const u32x4_t *>(wrow[nb] + kc + 8 * s);
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-                b[mb][s] = hval[mb] ? *reinterpret_cast<const u32x4_t *>(hrow[mb] + kc + 8 * s) : zero;
-    };
-    auto compute = [&](const u32x4_t (&a)[2][4], const u32x4_t (&b)[2][4]) {
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-#pragma unroll
-            for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-                for (int mb = 0; mb < 2; ++mb)
-                    acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        __builtin_bit_cast(bf16x8_t, a[nb][s]), __builtin_bit_cast(bf16x8_t, b[mb][s]),
-                        acc[nb][mb], 0, 0, 0);
-    };
-
-    load(a0, b0, 0);
-    for (int kc = 0; kc < K; kc += 2 * BK) {
-        if (kc + BK < K) load(a1, b1, kc + BK);
-        compute(a0, b0);
-        if (kc + 2 * BK < K) load(a0, b0, kc + 2 * BK);
-        if (kc + BK < K) compute(a1, b1);
+            for (int mb = 0; mb < 2; ++mb) {
+                const int hrow = mb * 32 + lr;
+                const u32x4_t b = *reinterpret_cast<const u32x4_t *>(hb + hrow * 128 + ((col ^ swz(hrow)) << 4));
+                acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                                  __builtin_bit_cast(bf16x8_t, b), acc[mb], 0, 0, 0);
+            }
+        }
     }
-
-    // D[vocab i][hidden j]: lane holds j = lr, i = 8*(r/4) + 4*lh + r%4
+    __syncthreads();  // the ring is reused for the logit tile
+    float (*lg)[BN + 4] = reinterpret_cast<float (*)[BN + 4]>(smem);
+    // D[vocab i][hidden j]: lane holds j = lr, i = 8 (r / 4) + 4 lh + r % 4
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
+    for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                lg[mb * 32 + lr][wave * 64 + nb * 32 + 8 * (r >> 2) + 4 * lh + (r & 3)] = acc[nb][mb][r];
+        for (int r = 0; r < 16; ++r)
+            lg[mb * 32 + lr][wave * 32 + 8 * (r >> 2) + 4 * lh + (r & 3)] = acc[mb][r];
     __syncthreads();
-    tile_select<BM, KK, LSE>(lg, m0, M, n0, N, tile, ntiles, p);
+    tile_select<BM, BN, KK, LSE>(lg, m0, M, n0, N, tile, ntiles, p);
 }
 
 template <int KK, bool LSE>
 __global__ __launch_bounds__(256) void lmhead_f32_kernel(const float *__restrict__ h, const float *__restrict__ w,
                                                          int M, int N, int K, int ntiles, Partials p) {
-    constexpr int BM = 16;
-    __shared__ float lg[BM][LDP];
+    constexpr int BM = 16, BN = BN_F;
+    __shared__ float lg[BM][BN + 4];
     __shared__ float hs[BM][64];
     const int mt = blockIdx.x, tile = blockIdx.y;
     const int m0 = mt * BM, n0 = tile * BN;
@@ -185,7 +223,7 @@ __global__ __launch_bounds__(256) void lmhead_f32_kernel(const float *__restrict
 #pragma unroll
     for (int r = 0; r < BM; ++r) lg[r][t] = acc[r];
     __syncthreads();
-    tile_select<BM, KK, LSE>(lg, m0, M, n0, N, tile, ntiles, p);
+    tile_select<BM, BN, KK, LSE>(lg, m0, M, n0, N, tile, ntiles, p);
 }
 
 template <int KK, bool LSE>
@@ -256,7 +294,7 @@ Partials carve(void *ws, int M, int ntiles, int KK) {
 template <int KK, bool LSE>
 void launch(const void *hidden, const void *w, int M, int N, int K, int topk, int dtype, int32_t *idx, float *val,
             float *gap, float *lse, void *ws, hipStream_t st) {
-    const int ntiles = (N + BN - 1) / BN;
+    const int ntiles = (N + (dtype == EAGLE3_BF16 ? BN_B : BN_F) - 1) / (dtype == EAGLE3_BF16 ? BN_B : BN_F);
     const Partials p = carve(ws, M, ntiles, KK);
     if (dtype == EAGLE3_BF16) {
         dim3 grid((M + 63) / 64, ntiles);
@@ -280,7 +318,8 @@ void launch_kk(bool want_lse, const void *hidden, const void *w, int M, int N, i
 
 extern "C" size_t eagle3_lmhead_workspace(int M, int N, int K, int topk, int dtype) {
     if (M <= 0 || N <= 0 || topk < 1) return 0;
-    const int ntiles = (N + BN - 1) / BN;
+    const int bn = dtype == EAGLE3_BF16 ? BN_B : BN_F;
+    const int ntiles = (N + bn - 1) / bn;
     const int KK = kk_for(topk);
     const size_t rec = (size_t)M * ntiles;
     return align256(rec * KK * 4) + align256(rec * KK * 4) + align256(rec * 4) + align256(rec * 4);
