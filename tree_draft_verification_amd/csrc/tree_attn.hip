@@ -14,8 +14,11 @@
 //     product needs as its contraction operand.
 //   - Each wave owns 32 query rows. S^T = K . Q^T by MFMA 32x32x16, so every
 //     lane holds one query's scores: the softmax max and sum are in-lane plus
-//     one exchange between the two half-waves. Online softmax in fp32 (exp2,
-//     log2(e) folded into the scale). O^T += V^T . P^T by MFMA with P split
+//     one exchange between the two half-waves. Online softmax in fp32 with
+//     log2(e) folded into the scale, raw v_exp_f32, and a lazily refreshed
+//     running max (O is rescaled only when the max grows by more than 2^8).
+//     K rows sit in LDS in a permuted key order so that each lane's 8 scores
+//     per 16-key step are consecutive keys and the V operand is one read. O^T += V^T . P^T by MFMA with P split
 //     into bf16 hi + lo parts, so P keeps ~16 significant bits.
 //   - Prefix keys are split across work-groups when there are too few
 //     (sequence, head) pairs to fill the chip; the split holding the end of
@@ -30,8 +33,6 @@ namespace {
 
 constexpr int KT = 64;       // keys per tile
 constexpr int DH = 128;      // head dim of the MFMA path
-constexpr int KS_LD = DH + 8;  // LDS row stride (elements) of the K tile
-constexpr int VT_LD = KT + 8;  // LDS row stride (elements) of the V^T tile
 constexpr int ROWS_PER_WG = 256;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -78,11 +79,134 @@ __device__ __forceinline__ void query_mask(const AttnParams &p, int b, int t, ui
     }
 }
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+constexpr int NSTAGE = 3;                  // depth of the K/V ring
+constexpr int STAGE = 2 * KT * DH * 2;     // bytes per stage: K tile + V tile (16 KB each)
+constexpr int VOFF = KT * DH * 2;          // V tile offset inside a stage
+constexpr int MAX_SPLIT_BLOCKS = 256;      // cache blocks one split may cover (split_keys <= 4096)
+
+// 16-byte column swizzle of K rows (a tile row is one key, 256 B): K reads of
+// 16 consecutive rows then hit 16 distinct bank groups.
+__device__ __forceinline__ int kswz(int row) { return row & 15; }
+// V rows are (block, d) pairs of 32 B = 16 slots; the two 16-byte halves are
+// swapped on every other group of 8 rows, halving bank conflicts of PV reads.
+__device__ __forceinline__ int vswz(int d) { return (d >> 3) & 1; }
+// Key held by K-tile row r: bits 2 and 3 of the key swapped. The S^T
+// accumulator gives lane half h the rows 8a + 4h + c (a in {0,1}, c in 0..3)
+// of each 16-row group, i.e. keys 8h + 4a + c: eight consecutive keys, which
+// is one 16-byte half of a V row, so the PV operand is a single LDS read.
+__device__ __forceinline__ int row_key(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+enum TileKind { TILE_FULL = 0, TILE_PARTIAL = 1, TILE_TREE = 2 };
+
+// Softmax bookkeeping is in log2 units with a lazily refreshed running max:
+// m_run only moves when a score exceeds it by more than 2^8 (so exp2 values
+// stay below 256, harmless in fp32), which makes O rescaling rare.
+constexpr float kLazyMax = 8.f;
+
+// One 64-key tile for one wave: S^T = K.Q^T, online softmax, O^T += V^T.P^T.
+// kind is wave-uniform (one copy of the code serves every tile kind).
+__device__ __forceinline__ void attend_tile(int kind, const unsigned char *stage, const u32x4_t (&qb)[8],
+                                            f32x16_t (&ot)[4], float &m_run, float &l_run, int lr, int lh,
+                                            int nvalid, uint64_t mword, float scale_log2) {
+    const unsigned char *Kb = stage, *Vb = stage + VOFF;
+    f32x16_t st[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+        const int row = kb * 32 + lr;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            // lane half lh holds d = 16 s + 8 lh .. +7, i.e. 16-byte column 2 s + lh
+            const u32x4_t a = *reinterpret_cast<const u32x4_t *>(Kb + row * 256 + (((2 * s + lh) ^ kswz(row)) << 4));
+            if (s == 0) {
+                const f32x16_t z = {};
+                st[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                                 __builtin_bit_cast(bf16x8_t, qb[s]), z, 0, 0, 0);
+            } else {
+                st[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                                 __builtin_bit_cast(bf16x8_t, qb[s]), st[kb], 0, 0, 0);
+            }
+        }
+    }
+    // register r of block kb holds key 32 kb + 16 (r / 8) + 8 lh + (r % 8)
+    if (kind != TILE_FULL) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int kk = kb * 32 + 16 * (r >> 3) + 8 * lh + (r & 7);
+                const bool vis = kk < nvalid && (kind != TILE_TREE || ((mword >> kk) & 1u));
+                st[kb][r] = vis ? st[kb][r] : -INFINITY;
+            }
+    }
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, st[kb][r]);
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * scale_log2;
+    // refresh the running max only when it is exceeded by more than 2^kLazyMax
+    const bool grow = tmax > m_run + kLazyMax;
+    if (__ballot(grow)) {
+        const float m_new = grow ? tmax : m_run;
+        const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) ot[db][r] *= alpha;
+        m_run = m_new;
+    }
+    const float msub = (m_run == -INFINITY) ? 0.f : m_run;
+    float psum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const float pv = __builtin_amdgcn_exp2f(fmaf(st[kb][r], scale_log2, -msub));
+            st[kb][r] = pv;
+            psum += pv;
+        }
+    l_run += psum;
+    // 16 keys per step = one cache block of the tile; this lane's 8 P values
+    // are keys 8 lh .. 8 lh + 7 of the block. P enters as bf16 hi + lo (two
+    // MFMAs on the same V operand): a single bf16 rounding of P would leave
+    // ~2e-3 relative error in the output.
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        const int kb = ks >> 1, r0 = 8 * (ks & 1);
+        u32x4_t ph, pl;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            uint32_t h2, l2;
+            e3_split_bf16x2(st[kb][r0 + 2 * e], st[kb][r0 + 2 * e + 1], h2, l2);
+            ph[e] = h2;
+            pl[e] = l2;
+        }
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+            const int d = db * 32 + lr;
+            const u32x4_t v = *reinterpret_cast<const u32x4_t *>(Vb + ks * 4096 + d * 32 + ((lh ^ vswz(d)) << 4));
+            const bf16x8_t a = __builtin_bit_cast(bf16x8_t, v);
+            ot[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, ph), ot[db], 0, 0, 0);
+            ot[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, pl), ot[db], 0, 0, 0);
+        }
+    }
+}
+
 template <int NW>
 __global__ __launch_bounds__(NW * 64) void tree_attn_bf16_kernel(AttnParams p) {
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[KT][KS_LD];
-    __shared__ __attribute__((aligned(16))) uint16_t Vt[DH][VT_LD];
+    __shared__ __attribute__((aligned(1024))) unsigned char ring[NSTAGE * STAGE];
+    __shared__ int bids[MAX_SPLIT_BLOCKS];
     constexpr int NT = NW * 64;
+    constexpr int LOADS = 32 / NW;  // 1 KB DMA loads per wave per stage (16 for K, 16 for V)
 
     const int split = blockIdx.x / p.nrb, rb = blockIdx.x % p.nrb;
     const int kvh = blockIdx.y, b = blockIdx.z;
@@ -102,14 +226,47 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_bf16_kernel(AttnParams p) {
     const int hq = kvh * p.G + (row_ok ? row % p.G : 0);
     const bool wave_active = rb * ROWS_PER_WG + wave * 32 < p.R;
 
+    // physical ids of the cache blocks this split reads
+    const int blk0 = k_begin / 16;
+    const int nblk = (k_end - k_begin + 15) / 16;
+    const int32_t *btab = p.block_table + (size_t)b * p.max_blocks;
+    for (int i = tid; i < nblk; i += NT) bids[i] = clamped_block(btab, blk0 + i, p.num_blocks);
+
+    // this lane's part of each DMA load: element offset inside a cache block
+    // ([16 slots][128 d] for K, [128 d][16 slots] for V)
+    int dma_off[LOADS];
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) {
+        const int q = wave * LOADS + j;
+        if (q < 16) {
+            const int rib = 4 * (q & 3) + lane / 16;    // tile row in block (rows are 16-aligned per block)
+            dma_off[j] = row_key(rib) * DH + 8 * ((lane & 15) ^ kswz(rib));
+        } else {
+            const int d = 32 * ((q - 16) & 3) + lane / 2;
+            dma_off[j] = d * 16 + 8 * ((lane & 1) ^ vswz(d));
+        }
+    }
+    const size_t head_off = (size_t)kvh * 16 * DH;
+    const size_t blk_stride = (size_t)p.Hkv * 16 * DH;
+    auto issue = [&](int stage, int tile) {
+        unsigned char *base = ring + stage * STAGE;
+#pragma unroll
+        for (int j = 0; j < LOADS; ++j) {
+            const int q = wave * LOADS + j;
+            const int lb = min(4 * tile + ((q & 15) >> 2), nblk - 1);  // blocks past the prefix re-read the last
+            const uint16_t *src = (q < 16 ? p.k_cache : p.v_cache) + (size_t)bids[lb] * blk_stride + head_off +
+                                  dma_off[j];
+            __builtin_amdgcn_global_load_lds((const void *)src, (lds_void_t *)(base + q * 1024), 16, 0, 0);
+        }
+    };
+
     // Q^T operand: d = 16 s + 8 lh + i
     u32x4_t qb[8];
     {
         const uint16_t *qrow = p.q + (((size_t)b * p.Tq + t) * p.Hq + hq) * DH + 8 * lh;
 #pragma unroll
-        for (int s = 0; s < 8; ++s) {
+        for (int s = 0; s < 8; ++s)
             qb[s] = row_ok ? *reinterpret_cast<const u32x4_t *>(qrow + 16 * s) : u32x4_t{0u, 0u, 0u, 0u};
-        }
     }
     uint64_t mw0 = 0, mw1 = 0;
     if (last && row_ok) query_mask(p, b, t, mw0, mw1);
@@ -121,141 +278,75 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_bf16_kernel(AttnParams p) {
         for (int r = 0; r < 16; ++r) ot[db][r] = 0.f;
     float m_run = -INFINITY, l_run = 0.f;
 
-    const int32_t *btab = p.block_table + (size_t)b * p.max_blocks;
-    const int n_prefix_tiles = (k_end - k_begin + KT - 1) / KT;
-    const int n_tree_tiles = last ? (p.Tk + KT - 1) / KT : 0;
-
-    for (int it = 0; it < n_prefix_tiles + n_tree_tiles; ++it) {
-        const bool is_tree = it >= n_prefix_tiles;
-        const int kt0 = is_tree ? (it - n_prefix_tiles) * KT : k_begin + it * KT;
-        __syncthreads();  // previous tile fully consumed
-        if (!is_tree) {
-            // K: 1024 chunks of 16 B (key = c / 16, d8 = c % 16)
-            for (int c = tid; c < KT * DH / 8; c += NT) {
-                const int key = c >> 4, d8 = (c & 15) * 8;
-                const int kg = kt0 + key;
-                u32x4_t v = {0u, 0u, 0u, 0u};
-                if (kg < k_end) {
-                    const int phys = clamped_block(btab, kg >> 4, p.num_blocks);
-                    v = *reinterpret_cast<const u32x4_t *>(
-                        p.k_cache + (((size_t)phys * p.Hkv + kvh) * 16 + (kg & 15)) * DH + d8);
-                }
-                *reinterpret_cast<u32x4_t *>(&Ks[key][d8]) = v;
-            }
-            // V: chunk c -> block j = c / 256, d = (c % 256) / 2, 8 slots (c & 1)
-            for (int c = tid; c < KT * DH / 8; c += NT) {
-                const int j = c >> 8, d = (c & 255) >> 1, half = c & 1;
-                const int kg0 = kt0 + 16 * j + 8 * half;
-                u32x4_t v = {0u, 0u, 0u, 0u};
-                if (kg0 < k_end) {
-                    const int phys = clamped_block(btab, kg0 >> 4, p.num_blocks);
-                    v = *reinterpret_cast<const u32x4_t *>(
-                        p.v_cache + (((size_t)phys * p.Hkv + kvh) * DH + d) * 16 + 8 * half);
-                    const int nvalid = k_end - kg0;  // keys past the prefix end -> 0
-                    if (nvalid < 8) {
+    const int ntile = (k_end - k_begin + KT - 1) / KT;
+    __syncthreads();  // block ids (and the q / mask loads) are in
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            uint32_t x = v[e];
-                            if (2 * e >= nvalid) x &= 0xffff0000u;
-                            if (2 * e + 1 >= nvalid) x &= 0x0000ffffu;
-                            v[e] = x;
-                        }
-                    }
+    for (int st = 0; st < NSTAGE - 1; ++st)
+        if (st < ntile) issue(st, st);
+
+    // prefix tiles stream through the ring; the tree keys (only in the split
+    // holding the end of the prefix) follow through registers, since their V
+    // rows must be transposed into the [block][d][slot] layout
+    const int ntree = last ? (p.Tk + KT - 1) / KT : 0;
+    for (int it = 0; it < ntile + ntree; ++it) {
+        const unsigned char *stage;
+        int kind, nvalid;
+        uint64_t mword = 0;
+        if (it < ntile) {
+            if (it + NSTAGE - 2 < ntile) wait_vmcnt<(NSTAGE - 2) * LOADS>();
+            else wait_vmcnt<0>();
+            // tile it has landed for every wave and every wave is done with the
+            // buffer refilled below; a fenced barrier would drain the whole ring
+            __builtin_amdgcn_s_barrier();
+            __asm__ volatile("" ::: "memory");
+            stage = ring + (it % NSTAGE) * STAGE;
+            nvalid = k_end - (k_begin + it * KT);
+            kind = nvalid >= KT ? TILE_FULL : TILE_PARTIAL;
+            if (nvalid < KT) {
+                // last, partial tile: zero the V slots past the prefix (the
+                // cache may hold anything there, and 0 * NaN would poison the sum)
+                unsigned char *vb = ring + (it % NSTAGE) * STAGE + VOFF;
+                for (int r = tid; r < 4 * DH; r += NT) {
+                    const int jb = r / DH, d = r % DH;
+                    uint16_t *rowp = reinterpret_cast<uint16_t *>(vb + jb * 4096 + d * 32);
+                    for (int sl = 0; sl < 16; ++sl)
+                        if (16 * jb + sl >= nvalid) rowp[((sl >> 3) ^ vswz(d)) * 8 + (sl & 7)] = 0;
                 }
-                *reinterpret_cast<u32x4_t *>(&Vt[d][16 * j + 8 * half]) = v;
+                __syncthreads();
             }
+            if (it + NSTAGE - 1 < ntile) issue((it + NSTAGE - 1) % NSTAGE, it + NSTAGE - 1);
         } else {
+            const int tt = it - ntile;
+            __syncthreads();  // everyone is done with stage 0 (and the ring is drained)
+            unsigned char *Kb = ring, *Vb = ring + VOFF;
             for (int c = tid; c < KT * DH / 8; c += NT) {
                 const int key = c >> 4, d8 = (c & 15) * 8;
-                const int tk = kt0 + key;
+                const int tk = tt * KT + key;
                 u32x4_t kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
                 if (tk < p.Tk) {
                     const size_t off = (((size_t)b * p.Tk + tk) * p.Hkv + kvh) * DH + d8;
                     kv = *reinterpret_cast<const u32x4_t *>(p.k_tree + off);
                     vv = *reinterpret_cast<const u32x4_t *>(p.v_tree + off);
                 }
-                *reinterpret_cast<u32x4_t *>(&Ks[key][d8]) = kv;
+                const int krow = row_key(key);  // the row holding this key (the permutation is an involution)
+                *reinterpret_cast<u32x4_t *>(Kb + krow * 256 + (((c & 15) ^ kswz(krow)) << 4)) = kv;
+                const int jb = key >> 4, sl = key & 15;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    Vt[d8 + 2 * e][key] = (uint16_t)(vv[e] & 0xffffu);
-                    Vt[d8 + 2 * e + 1][key] = (uint16_t)(vv[e] >> 16);
+                for (int e = 0; e < 8; ++e) {
+                    const int d = d8 + e;
+                    const uint16_t val = (uint16_t)((e & 1) ? (vv[e >> 1] >> 16) : (vv[e >> 1] & 0xffffu));
+                    reinterpret_cast<uint16_t *>(Vb + jb * 4096 + d * 32)[((sl >> 3) ^ vswz(d)) * 8 + (sl & 7)] = val;
                 }
             }
+            __syncthreads();
+            stage = ring;
+            kind = TILE_TREE;
+            nvalid = p.Tk - tt * KT;
+            mword = tt == 0 ? mw0 : mw1;
         }
-        __syncthreads();
-        if (!wave_active) continue;
-
-        // S^T[key][query] for two 32-key blocks
-        f32x16_t st[2];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) st[kb][r] = 0.f;
-#pragma unroll
-            for (int s = 0; s < 8; ++s) {
-                const u32x4_t a = *reinterpret_cast<const u32x4_t *>(&Ks[kb * 32 + lr][16 * s + 8 * lh]);
-                st[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                                 __builtin_bit_cast(bf16x8_t, qb[s]), st[kb], 0, 0, 0);
-            }
-        }
-        // scale, mask, tile max; key of register r: 32 kb + 8 (r / 4) + 4 lh + r % 4
-        const uint64_t mword = (kt0 / 64 == 0) ? mw0 : mw1;
-        float tmax = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int kk = kb * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-                const bool vis = is_tree ? (((mword >> kk) & 1u) && (kt0 + kk < p.Tk)) : (kt0 + kk < k_end);
-                const float sv = vis ? st[kb][r] * p.scale_log2 : -INFINITY;
-                st[kb][r] = sv;
-                tmax = fmaxf(tmax, sv);
-            }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-        const float m_new = fmaxf(m_run, tmax);
-        const float alpha = (m_new == -INFINITY) ? 1.f : exp2f(m_run - m_new);
-        const float msub = (m_new == -INFINITY) ? 0.f : m_new;
-        float psum = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float pv = exp2f(st[kb][r] - msub);
-                st[kb][r] = pv;
-                psum += pv;
-            }
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) ot[db][r] *= alpha;
-
-        // O^T[d][query] += V^T[d][key] . P^T[key][query], 16 keys per step.
-        // P enters as bf16 hi + lo (two MFMAs on the same V operand): a single
-        // bf16 rounding of P would leave ~2e-3 relative error in the output.
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            const int kb = ks >> 1, r0 = 8 * (ks & 1);
-            u32x4_t ph, pl;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                uint32_t h2, l2;
-                e3_split_bf16x2(st[kb][r0 + 2 * e], st[kb][r0 + 2 * e + 1], h2, l2);
-                ph[e] = h2;
-                pl[e] = l2;
-            }
-#pragma unroll
-            for (int db = 0; db < 4; ++db) {
-                const uint16_t *vrow = &Vt[db * 32 + lr][16 * ks + 4 * lh];
-                const u32x2_t lo = *reinterpret_cast<const u32x2_t *>(vrow);
-                const u32x2_t hi = *reinterpret_cast<const u32x2_t *>(vrow + 8);
-                const bf16x8_t a = __builtin_bit_cast(bf16x8_t, u32x4_t{lo[0], lo[1], hi[0], hi[1]});
-                ot[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, ph), ot[db], 0, 0, 0);
-                ot[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, pl), ot[db], 0, 0, 0);
-            }
-        }
+        if (wave_active) attend_tile(kind, stage, qb, ot, m_run, l_run, lr, lh, nvalid, mword, p.scale_log2);
     }
+
     if (!row_ok) return;
     const float l_tot = l_run + __shfl_xor(l_run, 32);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
@@ -443,7 +534,8 @@ int check_args(const eagle3_tree_attn_args *a) {
     } else {
         return EAGLE3_ERR_UNSUPPORTED;
     }
-    if (a->split_keys < 0 || a->split_keys % KT != 0) return EAGLE3_ERR_UNSUPPORTED;
+    if (a->split_keys < 0 || a->split_keys % KT != 0 || a->split_keys > 16 * MAX_SPLIT_BLOCKS)
+        return EAGLE3_ERR_UNSUPPORTED;
     if (a->mask == nullptr) {
         if (a->parent == nullptr || a->Tq != a->Tk) return EAGLE3_ERR_ARG;
     }
@@ -462,11 +554,14 @@ Plan make_plan(const eagle3_tree_attn_args *a) {
     if (a->split_keys > 0) {
         pl.split_keys = a->split_keys;
     } else {
+        // about one work-group per CU, at least 2 tiles per split (so the
+        // ring has something to overlap), at most 4096 keys per split
         const long base = (long)a->B * a->Hkv * pl.nrb;
         long ns = base > 0 ? (256 + base - 1) / base : 1;
+        if (ns > (ktiles + 1) / 2) ns = (ktiles + 1) / 2;
         if (ns < 1) ns = 1;
-        if (ns > ktiles) ns = ktiles;
-        const long tiles_per = (ktiles + ns - 1) / ns;
+        long tiles_per = (ktiles + ns - 1) / ns;
+        if (tiles_per > MAX_SPLIT_BLOCKS / 4) tiles_per = MAX_SPLIT_BLOCKS / 4;
         pl.split_keys = (int)(tiles_per * KT);
     }
     pl.nsplit = (int)((lmax + pl.split_keys - 1) / pl.split_keys);
