@@ -79,3 +79,18 @@ class VerifyStep:
     def run(self, parent, q, k_tree, v_tree, tokens, stream=None, events=None):
         self.forward(parent, q, k_tree, v_tree, stream, events)
         self.accept(tokens, stream)
+
+    def graph(self, parent, q, k_tree, v_tree, tokens):
+        """Capture one whole step (mask, attention, norm, LM head, accept) in a
+        HIP graph; replaying it re-runs the step on the same buffers. The graph
+        holds no memset nodes (every kernel writes its outputs in full)."""
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            self.run(parent, q, k_tree, v_tree, tokens)   # sizes the workspaces outside the capture
+        torch.cuda.current_stream().wait_stream(side)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.run(parent, q, k_tree, v_tree, tokens)
+        return g
+
