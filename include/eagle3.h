@@ -10,6 +10,8 @@
  *            there is appended), "Tree draft vs chain draft" (the target checks
  *            the whole tree in one forward pass under a mask that lets each
  *            token see only its ancestors).
+ *   [blog]   Spec-Bench blog post on EAGLE-3, section 4.2 (inference table:
+ *            top-k 10, 60 draft tokens); used for workload parameters only.
  *   [news]   News write-up of "EAGLE-3: Scaling up Inference Acceleration of
  *            Large Language Models via Training-Time Test": the draft-stage
  *            paragraphs (low/mid/high features l, m, h fused by an FC from 3k to
@@ -154,8 +156,11 @@ int eagle3_rmsnorm(const void *x, const void *gamma, int M, int K, float eps,
  *   gap [M] fp32 (nullable): top1 - top2, top2 the largest logit over the
  *        other ids (0 on an exact tie)
  *   lse [M] fp32 (nullable): ln sum_v exp(logit_v)
- * Supported: 1 <= topk <= 16; K % 64 == 0; N >= 2. Logits are accumulated in
- * fp32 (bf16 products are exact in fp32).
+ * Supported: 1 <= topk <= 16; K % 64 == 0 (bf16), K % 4 == 0 (fp32); N >= 2.
+ * Logits are accumulated in fp32 (bf16 products are exact in fp32) in a k
+ * order that is fixed per 128-row vocabulary tile, so a row's result never
+ * depends on the other rows; bitwise-equal logits resolve to the lowest id
+ * (duplicate weight rows in different tiles may differ in the last bits).
  */
 size_t eagle3_lmhead_workspace(int M, int N, int K, int topk, int dtype);
 int eagle3_lmhead_argmax(const void *hidden, const void *w, int M, int N, int K, int topk, int dtype,
@@ -178,6 +183,121 @@ int eagle3_lmhead_argmax(const void *hidden, const void *w, int M, int N, int K,
 int eagle3_accept_path(const int32_t *tokens, const int32_t *parent, const uint64_t *mask, int W,
                        const int32_t *target_idx, int B, int T,
                        int32_t *accept_len, int32_t *path, int32_t *out_tokens, void *stream);
+
+
+/*
+ * Dense layers for the EAGLE-3 draft head and small decoders.
+ *
+ * [news] draft stage: an FC reduces the concatenated low/mid/high features
+ * (3k) to k; the result (from step 2 on, the draft's own output) is
+ * concatenated with the embedding of the token one step ahead and an FC takes
+ * 2k to k; a single transformer layer and the target's LM head follow.
+ * reading: the layer is a Llama decoder layer (RMSNorm, GQA with rotate-half
+ * RoPE, SwiGLU MLP, residual adds).
+ *
+ * eagle3_gemm: C[M, N] = A[M, K] . B[N, K]^T (+ residual), where A is the
+ * concatenation along K of nseg (1..3) segments: segment s has k[s] columns
+ * and its row for output row m is a[s][a_rows[s][m]] (a_rows[s] nullable:
+ * row m itself; gathered rows are clamped to [0, a_nrows[s])). So the fusion
+ * FCs read [l; m; h] and [g; E[token]] without building the concatenation.
+ *   a[s]       [rows_s, k[s]] row-major          b  [N, sum k] row-major
+ *   residual   [M, ldc] (nullable; may alias c)   c  [M, ldc] (ldc 0 = N)
+ * bf16: fp32 accumulation, each k[s] % 64 == 0, pointers 16-byte aligned;
+ * fp32: any sizes. Summation order is fixed per output column block, so a
+ * row's result does not depend on the other rows of the call.
+ */
+typedef struct eagle3_gemm_args {
+    int dtype;
+    int M, N;
+    int nseg;
+    const void *a[3];
+    const int32_t *a_rows[3];
+    int a_nrows[3];
+    int k[3];
+    const void *b;
+    const void *residual;
+    void *c;
+    int ldc;
+} eagle3_gemm_args;
+
+int eagle3_gemm(const eagle3_gemm_args *args, void *stream);
+
+/* SwiGLU gating (reading: Llama's MLP): y[m][f] = silu(gu[m][f]) * gu[m][F + f]
+ * with silu(g) = g / (1 + exp(-g)); gu [M, 2F] (gate columns first), y [M, F]. */
+int eagle3_silu_mul(const void *gu, int M, int F, int dtype, void *y, void *stream);
+
+/* Rotary embedding, rotate-half convention (reading): in place on x viewed as
+ * [M][H][D] with row stride ld (elements, >= H * D); row m sits at position
+ * p = pos_offset + pos[m] (e.g. the committed length plus the node's depth)
+ * and pair (i, i + D/2) turns by p * theta^(-2i/D) (angle in double). */
+int eagle3_rope(void *x, int M, int H, int D, int ld, const int32_t *pos, int pos_offset, float theta, int dtype,
+                void *stream);
+
+/* Embedding gather: out[m] = E[ids[m]] (ids clamped to [0, V)); E [V, K],
+ * out [M, K]; K * element size must be a multiple of 16 bytes. */
+int eagle3_embed(const void *E, const int32_t *ids, int M, int K, int V, int dtype, void *out, void *stream);
+
+/*
+ * Append K/V rows to the paged cache after acceptance ([lesson] "Verify-accept
+ * semantics": the accepted tokens become part of the sequence). For sequence
+ * b, rows src[b][0..] of k_rows / v_rows [B, rows_per_seq, Hkv, D] go to
+ * positions start[b] + j of the cache (layouts as in eagle3_tree_attn); the
+ * list ends at the first negative entry or after max_n entries, so the `path`
+ * output of eagle3_accept_path can be passed as is. src [B, max_n] and
+ * start [B] are device int32 arrays; positions past max_blocks * 16 are skipped.
+ */
+int eagle3_commit_kv(const void *k_rows, const void *v_rows, int rows_per_seq, const int32_t *src, int max_n,
+                     int B, int Hkv, int D, int dtype, void *k_cache, void *v_cache, const int32_t *block_table,
+                     int max_blocks, int num_blocks, const int32_t *start, void *stream);
+
+/*
+ * EAGLE-3 draft input fusion ([news] draft stage):
+ *   context mode (a_prev == NULL): g = w_fuse . [l; m; h]; x = w_in . [g; E[tok]]
+ *   step mode    (l = m = h = NULL): x = w_in . [a_prev; E[tok]]
+ * l, m, h, a_prev, g_out, x_out [M, k]; tok [M] int32 (the token one step
+ * ahead of each row); E [V, k]; w_fuse [k, 3k]; w_in [k, 2k] (output-major).
+ * g is stored (g_out, or the workspace when g_out is NULL) in the storage type
+ * before the second FC. bf16 needs k % 64 == 0.
+ */
+size_t eagle3_draft_fuse_workspace(int M, int k, int dtype);
+int eagle3_draft_fuse(const void *l, const void *m, const void *h, const void *a_prev, const int32_t *tok,
+                      const void *E, const void *w_fuse, const void *w_in, int M, int k, int V, int dtype,
+                      void *g_out, void *x_out, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Draft-tree growth, EAGLE-2 style ([news]: the draft's confidence stands in
+ * for the acceptance rate and shapes the tree; [blog] section 4.2: top-k 10,
+ * 60 draft tokens). reading: score(child) = fp32(score(parent) + logp(child)),
+ * every selection ranks by (score desc, creation index asc), and the pool keeps
+ * every candidate ever drafted.
+ *
+ * eagle3_tree_expand: one step for B sequences. The F current frontier nodes
+ * (fr_score, fr_pool = their pool index or -1 for the root, fr_mask = the draft
+ * rows each may attend to, 2 words) each bring C children: child_ids,
+ * child_val [B, F, C] (the LM head's top-C ids and logits) and child_lse
+ * [B, F] (the row's log-sum-exp; nullable when child_val already holds
+ * log-probabilities), logp = fp32(val - lse). The F*C candidates are appended to the pool at
+ * pool_len.. (pool_* [B, pool_cap], creation order frontier-slot major) and the
+ * top NF become the next frontier: next_pool/next_score/next_token [B, NF];
+ * next_mask [B, NF, 2] = parent's mask plus the node's own draft row
+ * row_base + rank; next_arow [B, NF] = b * arow_stride + fr_arow_base + f, the
+ * row (in a per-sequence buffer of draft outputs) holding the parent's output.
+ * Needs F * C <= 256, NF <= F * C, row_base + NF <= 128.
+ *
+ * eagle3_tree_rerank: pool (pool_len entries) -> top N -> creation order ->
+ * parent [B, N + 1] and tokens [B, N + 1] with node 0 = the root
+ * (root_token [B]); parents are remapped (the selection is closed under
+ * parents because a child never outscores its parent). pool_len <= 4096.
+ */
+int eagle3_tree_expand(const float *fr_score, const int32_t *fr_pool, const uint64_t *fr_mask, int fr_arow_base,
+                       int arow_stride, const int32_t *child_ids, const float *child_val, const float *child_lse,
+                       int B, int F, int C, int NF, int pool_len, int pool_cap, int row_base, float *pool_score,
+                       int32_t *pool_token,
+                       int32_t *pool_parent, int32_t *next_pool, float *next_score, int32_t *next_token,
+                       uint64_t *next_mask, int32_t *next_arow, void *stream);
+int eagle3_tree_rerank(const float *pool_score, const int32_t *pool_token, const int32_t *pool_parent, int B,
+                       int pool_len, int pool_cap, int N, const int32_t *root_token, int32_t *parent,
+                       int32_t *tokens, void *stream);
 
 #ifdef __cplusplus
 }

@@ -73,6 +73,8 @@ def _declare(L):
     L.orc_gemm.restype = None
     L.orc_swiglu.argtypes = [I, P, P, I, I, I, P]
     L.orc_swiglu.restype = None
+    L.orc_silu_mul.argtypes = [I, P, I, I, P]
+    L.orc_silu_mul.restype = None
     L.orc_rope.argtypes = [I, P, P, I, I, I, D]
     L.orc_rope.restype = None
     L.orc_embed.argtypes = [I, P, P, I, I, P]
@@ -197,6 +199,14 @@ def swiglu(X, Wgu):
     return Y
 
 
+def silu_mul(GU):
+    GU = _c(GU)
+    M, F = GU.shape[0], GU.shape[1] // 2
+    Y = np.empty((M, F), dtype=GU.dtype)
+    lib().orc_silu_mul(_dt(GU), _p(GU), M, F, _p(Y))
+    return Y
+
+
 def rope(x, pos, theta):
     """x [M, H, D] (copied), pos [M]."""
     x = np.array(x, copy=True, order="C")
@@ -293,7 +303,8 @@ class ToyDecoder:
     reading: pre-norm RMSNorm (gamma = 1) -> fused QKV -> rotate-half RoPE
     at position P + depth(node) -> tree attention over the cached prefix plus
     the node's ancestors -> output projection + residual -> RMSNorm -> SwiGLU
-    MLP + residual; final RMSNorm -> LM head -> argmax.
+    MLP (gate/up product stored, then gated) + residual; final RMSNorm -> LM
+    head -> argmax.
     """
 
     def __init__(self, shape: synth.ToyShape = synth.TOY, seed: int = 0, max_pos: int = 512):
@@ -329,7 +340,7 @@ class ToyDecoder:
             a, _ = tree_attn(q[None], k[None], v[None], self.kv(i), mask, want_lse=False)
             x = gemm(a[0].reshape(T, HD), self.w[f"l{i}.wo"], R=x)
             h2 = rmsnorm(x, eps=s.eps)
-            f = swiglu(h2, self.w[f"l{i}.wgu"])
+            f = silu_mul(gemm(h2, self.w[f"l{i}.wgu"]))
             x = gemm(f, self.w[f"l{i}.wd"], R=x)
             rows.append((k, v))
         hf = rmsnorm(x, eps=s.eps)
@@ -402,3 +413,167 @@ def toy_speculative(shape=synth.TOY, seed=0, n_new=None, parent=None, p_match=No
         m.commit(rows, list(path[0, :a + 1]))
         out.extend(int(t) for t in otok[0, :a + 1])
     return np.asarray(out[:n_new], np.int32), steps
+
+
+# ------------------------------------------------------------------ draft head
+
+def _page(rows_k, rows_v, bs=16):
+    """Contiguous per-sequence K/V rows [B, L, Hkv, D] -> PagedKV (identity tables)."""
+    B, L, Hkv, Dh = rows_k.shape
+    nb = (L + bs - 1) // bs
+    kc = np.zeros((B * nb, Hkv, bs, Dh), rows_k.dtype)
+    vc = np.zeros((B * nb, Hkv, Dh, bs), rows_v.dtype)
+    for b in range(B):
+        for j in range(nb):
+            n = min(bs, L - j * bs)
+            kc[b * nb + j, :, :n, :] = rows_k[b, j * bs:j * bs + n].transpose(1, 0, 2)
+            vc[b * nb + j, :, :, :n] = rows_v[b, j * bs:j * bs + n].transpose(1, 2, 0)
+    table = (np.arange(B)[:, None] * nb + np.arange(nb)[None, :]).astype(np.int32)
+    return synth.PagedKV(kc, vc, table, np.full(B, L, np.int32), bs)
+
+
+def draft_tree(shape, W, l, m, h, ctx_tok, gap=GAP_FLAG):
+    """EAGLE-3 draft head and EAGLE-2 style tree growth, for B sequences.
+
+    News write-up of the EAGLE-3 paper, draft stage: context row t fuses the
+    target's low/mid/high features (g_t = W_fuse [l_t; m_t; h_t]) with the
+    embedding of the token one step ahead (x_t = W_in [g_t; E[tok_{t+1}]]);
+    every row's K/V enters the draft cache (RoPE at position t); the full
+    single layer runs at the last context row, giving a_root. From step 2 on,
+    the target's feature of a drafted token is unavailable and the draft's own
+    output of the parent stands in: x_n = W_in [a_parent; E[tok_n]].
+    readings: the layer is a Llama decoder layer; a node at depth d sits at
+    position ctx + d - 1 and attends to the draft cache plus the draft rows of
+    its ancestors and itself; logp = fp32(logit - lse) of RMSNorm(a) through
+    the target's LM head; score(child) = fp32(score(parent) + logp); each step
+    keeps the top-k candidates as the next frontier and every candidate in the
+    pool; the final tree is the top n_drafts of the pool by (score desc,
+    creation asc), renumbered in creation order under the root.
+    Returns parent, tokens [B, n+1] and per-sequence flags (some membership
+    boundary within `gap`)."""
+    s = shape
+    B, ctx, k = l.shape
+    qd, kvd, C = s.Hq * s.D, s.Hkv * s.D, s.topk
+    wq, wk, wv = W["wqkv"][:qd], W["wqkv"][qd:qd + kvd], W["wqkv"][qd + kvd:]
+    near = np.zeros(B, bool)
+
+    def layer_tail(x, attn):
+        x = gemm(attn, W["wo"], R=x)
+        f = silu_mul(gemm(rmsnorm(x, eps=s.eps), W["wgu"]))
+        return gemm(f, W["wd"], R=x)
+
+    def head(a):
+        idx, val, _, lse = lmhead(rmsnorm(a, eps=s.eps), W["lm_head"], topk=C + 1)
+        logp = (val[:, :C] - lse[:, None]).astype(np.float32)
+        return idx[:, :C], logp, (val[:, C - 1] - val[:, C]) < gap
+
+    # context rows -> draft cache
+    x = draft_fuse(ctx_tok.reshape(-1), W["embed"], W["w_fuse"], W["w_in"],
+                   l=l.reshape(-1, k), m=m.reshape(-1, k), h=h.reshape(-1, k))
+    hn = rmsnorm(x, eps=s.eps)
+    pos = np.tile(np.arange(ctx, dtype=np.int32), B)
+    kr = rope(gemm(hn, wk).reshape(B * ctx, s.Hkv, s.D), pos, s.theta)
+    vr = gemm(hn, wv).reshape(B * ctx, s.Hkv, s.D)
+    cache = _page(kr.reshape(B, ctx, s.Hkv, s.D), vr.reshape(B, ctx, s.Hkv, s.D))
+    # the last context row runs the whole layer: a_root
+    last = np.arange(B) * ctx + ctx - 1
+    qr = rope(gemm(hn[last], wq).reshape(B, s.Hq, s.D), np.full(B, ctx - 1, np.int32), s.theta)
+    empty = np.zeros((B, 0, s.Hkv, s.D), x.dtype)
+    attn, _ = tree_attn(qr[:, None], empty, empty, cache, np.zeros((B, 1, 1), np.uint64), want_lse=False)
+    a_prev = layer_tail(x[last], attn.reshape(B, qd))                      # [B, k]
+    # step 1: the root's top-k children are the first frontier
+    ids, logp, nb_ = head(a_prev)
+    near |= nb_
+    pool_score = [logp.astype(np.float32)]                                 # [B, C] per step
+    pool_tok = [ids]
+    pool_par = [np.full((B, C), -1, np.int32)]
+    order = select_topk(logp, np.tile(np.arange(C, dtype=np.int32), (B, 1)), C)
+    fr_pool = order.astype(np.int32)                                       # pool index of each frontier slot
+    fr_score = np.take_along_axis(logp, order, 1)
+    fr_tok = np.take_along_axis(ids, order, 1)
+    fr_arow = np.zeros((B, C), np.int64)                                   # parent's row in a_prev (the root)
+    fr_rows = [[[] for _ in range(C)] for _ in range(B)]                   # ancestors' draft rows
+    tk = np.zeros((B, (s.steps - 1) * C, s.Hkv, s.D), x.dtype)
+    tv = np.zeros_like(tk)
+    n_pool = C
+    for step in range(2, s.steps + 1):
+        base = (step - 2) * C
+        a_par = a_prev[(np.arange(B)[:, None] * (a_prev.shape[0] // B) + fr_arow).reshape(-1)]
+        xs = draft_fuse(fr_tok.reshape(-1), W["embed"], W["w_fuse"], W["w_in"], a_prev=a_par)
+        hs = rmsnorm(xs, eps=s.eps)
+        ps = np.full(B * C, ctx + step - 2, np.int32)
+        q = rope(gemm(hs, wq).reshape(B * C, s.Hq, s.D), ps, s.theta)
+        tk[:, base:base + C] = rope(gemm(hs, wk).reshape(B * C, s.Hkv, s.D), ps, s.theta).reshape(B, C, s.Hkv, s.D)
+        tv[:, base:base + C] = gemm(hs, wv).reshape(B, C, s.Hkv, s.D)
+        mask = np.zeros((B, C, 2), np.uint64)
+        for b in range(B):
+            for i in range(C):
+                fr_rows[b][i] = fr_rows[b][i] + [base + i]
+                for r in fr_rows[b][i]:
+                    mask[b, i, r // 64] |= np.uint64(1) << np.uint64(r % 64)
+        attn, _ = tree_attn(q.reshape(B, C, s.Hq, s.D), tk, tv, cache, mask, want_lse=False)
+        a_prev = layer_tail(xs, attn.reshape(B * C, qd))                   # [B*C, k]
+        ids, logp, nb_ = head(a_prev)
+        near |= nb_.reshape(B, C).any(axis=1)
+        cand = (fr_score[:, :, None] + logp.reshape(B, C, C)).astype(np.float32).reshape(B, C * C)
+        pool_score.append(cand)
+        pool_tok.append(ids.reshape(B, C * C))
+        pool_par.append(np.repeat(fr_pool, C, axis=1))
+        creation = np.tile(np.arange(n_pool, n_pool + C * C, dtype=np.int32), (B, 1))
+        order = select_topk(cand, creation, C + 1)
+        srt = np.take_along_axis(cand, order, 1)
+        near |= (srt[:, C - 1] - srt[:, C]) < gap
+        order = order[:, :C]
+        new_rows = [[list(fr_rows[b][o // C]) for o in order[b]] for b in range(B)]
+        fr_arow = (order // C).astype(np.int64)                           # parent = frontier slot o // C
+        fr_pool = (n_pool + order).astype(np.int32)
+        fr_score = np.take_along_axis(cand, order, 1)
+        fr_tok = np.take_along_axis(ids.reshape(B, C * C), order, 1)
+        fr_rows = new_rows
+        n_pool += C * C
+    ps_all = np.concatenate(pool_score, 1)
+    tok_all = np.concatenate(pool_tok, 1)
+    par_all = np.concatenate(pool_par, 1)
+    parent, tokens, nb_ = tree_rerank(ps_all, tok_all, par_all, ctx_tok[:, -1], s.n_drafts, gap)
+    near |= nb_
+    return dict(parent=parent, tokens=tokens, flagged=near, pool_score=ps_all, pool_token=tok_all,
+                pool_parent=par_all)
+
+
+def tree_rerank(pool_score, pool_token, pool_parent, root_token, N, gap=GAP_FLAG):
+    """Pool -> top N by (score desc, creation asc) -> creation order under the
+    root (node 0 = root_token): parent, tokens [B, N+1]; `near` flags a gap
+    below `gap` at the N-th / (N+1)-th boundary."""
+    pool_score = np.atleast_2d(pool_score).astype(np.float32)
+    B, P = pool_score.shape
+    k = min(N + 1, P)
+    order = select_topk(pool_score, np.tile(np.arange(P, dtype=np.int32), (B, 1)), k)
+    srt = np.take_along_axis(pool_score, order, 1)
+    near = (srt[:, N - 1] - srt[:, N]) < gap if P > N else np.zeros(B, bool)
+    parent = np.full((B, N + 1), -1, np.int32)
+    tokens = np.zeros((B, N + 1), np.int32)
+    for b in range(B):
+        chosen = np.sort(order[b, :N])                                     # creation order
+        new = {int(c): i + 1 for i, c in enumerate(chosen)}
+        tokens[b, 0] = root_token[b]
+        for c in chosen:
+            pp = int(pool_parent[b, c])
+            parent[b, new[int(c)]] = 0 if pp < 0 else new[pp]
+            tokens[b, new[int(c)]] = pool_token[b, c]
+    return parent, tokens, near
+
+
+def tree_expand(fr_score, fr_pool, child_ids, child_logp, pool_len, NF):
+    """One growth step: F frontier nodes x C children (logp per child) ->
+    candidates with score fp32(score(parent) + logp) (creation order slot
+    major), and the next frontier: the top NF by (score desc, creation asc).
+    Returns cand_score [B, F*C], cand_parent [B, F*C] (pool index of the
+    parent), next_pool / next_score / next_token / next_slot [B, NF]."""
+    fr_score = np.asarray(fr_score, np.float32)
+    B, F, C = child_ids.shape
+    cand = (fr_score[:, :, None] + np.asarray(child_logp, np.float32)).astype(np.float32).reshape(B, F * C)
+    cpar = np.repeat(np.asarray(fr_pool, np.int32), C, axis=1)
+    creation = np.tile(np.arange(pool_len, pool_len + F * C, dtype=np.int32), (B, 1))
+    order = select_topk(cand, creation, NF)
+    return (cand, cpar, (pool_len + order).astype(np.int32), np.take_along_axis(cand, order, 1),
+            np.take_along_axis(child_ids.reshape(B, F * C), order, 1), (order // C).astype(np.int32))

@@ -394,6 +394,17 @@ void orc_swiglu(int dtype, const void *X, const void *Wgu, int M, int F, int K, 
     }
 }
 
+/* SwiGLU gating on a stored gate/up product: gu is [M, 2F] (gate columns
+ * first); y[m][f] = silu(g) * u with silu(g) = g / (1 + exp(-g)). */
+void orc_silu_mul(int dtype, const void *GU, int M, int F, void *Y) {
+#pragma omp parallel for schedule(static)
+    for (long r = 0; r < (long)M * F; ++r) {
+        const int m = (int)(r / F), f = (int)(r % F);
+        const double g = ld(GU, dtype, (size_t)m * 2 * F + f), u = ld(GU, dtype, (size_t)m * 2 * F + F + f);
+        st(Y, dtype, (size_t)r, g / (1.0 + exp(-g)) * u);
+    }
+}
+
 /* Rotary embedding, rotate-half convention (reading: Llama's): for head
  * vector x[0..D) at position p, pair i with i + D/2, angle = p * theta^(-2i/D):
  *   x'[i] = x[i] cos - x[i+D/2] sin;  x'[i+D/2] = x[i+D/2] cos + x[i] sin.

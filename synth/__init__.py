@@ -422,6 +422,9 @@ def toy_plant_stream(shape: ToyShape = TOY, seed: int = 0):
 
 @dataclasses.dataclass
 class DraftShape:
+    """EAGLE-3 draft head + tree growth (news write-up of the EAGLE-3 paper,
+    draft-stage paragraphs; top-k 10 and 60 draft tokens from the Spec-Bench
+    blog post's inference table)."""
     name: str = "draft-b64"
     wid: int = 5
     B: int = 64
@@ -438,9 +441,61 @@ class DraftShape:
     theta: float = 500000.0
     eps: float = 1e-5
     std: float = 0.02
+    lm_std: float = 0.02
+
+    @property
+    def pool_len(self):
+        return self.topk + (self.steps - 1) * self.topk * self.topk
 
 
 DRAFT_B64 = DraftShape()
+# small draft head for element-wise parity; a 15x larger LM-head scale spreads
+# the draft logits so fewer selection boundaries are near-ties
+DRAFT_SMALL = DraftShape("draft-small", 25, B=6, k=256, V=2000, ctx=96, Hq=4, Hkv=2, D=128, F=512, lm_std=0.3)
+
+
+def _blocks_bf16(wid: int, comp: int, shape, std: float, rb: int = 2048, threads: int | None = None) -> np.ndarray:
+    """bf16 N(0, std^2) matrix drawn in row blocks from their own generators
+    default_rng([wid, 0, comp, i]), in parallel threads."""
+    import concurrent.futures
+    import os
+    rows, cols = int(shape[0]), int(np.prod(shape[1:]))
+    out = np.empty((rows, cols), dtype=np.uint16)
+
+    def block(i):
+        r0, r1 = i * rb, min(rows, (i + 1) * rb)
+        out[r0:r1] = normal_bf16(np.random.default_rng([wid, 0, comp, i]), (r1 - r0, cols), std=std)
+
+    with concurrent.futures.ThreadPoolExecutor(threads or min(16, os.cpu_count() or 1)) as ex:
+        list(ex.map(block, range((rows + rb - 1) // rb)))
+    return out.reshape(shape)
+
+
+def draft_weights(shape: DraftShape) -> dict:
+    """bf16 weights of the draft head, output-major ([out, in]); the LM head is
+    the target's. Fixed per workload."""
+    k, V, F = shape.k, shape.V, shape.F
+    qd, kvd = shape.Hq * shape.D, shape.Hkv * shape.D
+    spec = {"embed": ((V, k), shape.std), "w_fuse": ((k, 3 * k), shape.std), "w_in": ((k, 2 * k), shape.std),
+            "wqkv": ((qd + 2 * kvd, k), shape.std), "wo": ((k, qd), shape.std), "wgu": ((2 * F, k), shape.std),
+            "wd": ((k, F), shape.std), "lm_head": ((V, k), shape.lm_std)}
+    return {name: _blocks_bf16(shape.wid, 100 + i, shp, std) for i, (name, (shp, std)) in enumerate(spec.items())}
+
+
+def draft_inputs(shape: DraftShape, seed: int, batch: slice | None = None):
+    """Target features l, m, h [B, ctx, k] ~ N(0, 1) (bf16) and the token one
+    step ahead of every context row, ctx_tok [B, ctx]; the last entry of each
+    row is the root (the token the target just emitted)."""
+    B = shape.B
+    sel = np.arange(B) if batch is None else np.arange(B)[batch]
+    feats = []
+    for c in range(3):
+        # per-sequence draws, so a subset of sequences costs only what it uses
+        rows = [normal_bf16(np.random.default_rng([shape.wid, seed, C_FEAT, c, int(b)]), (shape.ctx, shape.k))
+                for b in sel]
+        feats.append(np.stack(rows))
+    tok = child_rng(shape.wid, seed, C_CTX).integers(0, shape.V, size=(B, shape.ctx)).astype(np.int32)[sel]
+    return feats[0], feats[1], feats[2], tok
 
 
 def ceil_div(a, b):

@@ -1,0 +1,145 @@
+"""GPU parity of the dense layers (GEMM with segmented / gathered A, SiLU
+gating, RoPE, embedding gather, KV commit) and of the EAGLE-3 draft fusion,
+against the oracle on the same inputs. bf16 normwise <= 2e-2, fp32 <= 1e-5;
+copies bit-exact."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from _gpu import dev, host, normwise_rel
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import tree_draft_verification_amd as t
+    return t
+
+
+@pytest.mark.parametrize("M,N,k", [(1, 128, [64]), (200, 300, [128, 64, 192]), (640, 256, [256, 128])])
+def test_gemm_bf16_segments_and_gather(orc, lib, M, N, k):
+    rng = np.random.default_rng(M + N)
+    segs = [synth.normal_bf16(rng, (M if s != 1 else 50, ks)) for s, ks in enumerate(k)]
+    rows = [None] * len(k)
+    if len(k) > 1:
+        rows[1] = rng.integers(0, 50, size=M).astype(np.int32)     # gathered segment (an embedding table)
+    B = synth.normal_bf16(rng, (N, sum(k)), 0.05)
+    R = synth.normal_bf16(rng, (M, N))
+    A = np.concatenate([s if r is None else s[r] for s, r in zip(segs, rows)], axis=1)
+    ref = orc.gemm(A, B, R)
+    sd = [dev(s) for s in segs]
+    rd = [None if r is None else dev(r) for r in rows]
+    c = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    Bd, Rd = dev(B), dev(R)
+    lib.eagle3_gemm(sd, Bd, c, residual=Rd, a_rows=rd)
+    torch.cuda.synchronize()
+    rel, mx = normwise_rel(host(c), ref)
+    assert rel <= 2e-2, (rel, mx)
+
+
+def test_gemm_f32_and_in_place_residual(orc, lib):
+    rng = np.random.default_rng(3)
+    M, N, K = 37, 90, 70
+    A, B, X = synth.normal_f32(rng, (M, K)), synth.normal_f32(rng, (N, K), 0.1), synth.normal_f32(rng, (M, N))
+    ref = orc.gemm(A, B, X)
+    x = dev(X)
+    Ad, Bd = dev(A), dev(B)
+    lib.eagle3_gemm([Ad], Bd, x, residual=x)
+    torch.cuda.synchronize()
+    rel, _ = normwise_rel(host(x), ref)
+    assert rel <= 1e-5
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_silu_mul(orc, lib, dtype):
+    rng = np.random.default_rng(4)
+    GU = synth.normal_f32(rng, (33, 2 * 100), 2.0)
+    if dtype == "bf16":
+        GU = synth.f32_to_bf16(GU)
+    ref = orc.silu_mul(GU)
+    gu = dev(GU)
+    y = torch.empty(33, 100, dtype=gu.dtype, device="cuda")
+    lib.eagle3_silu_mul(gu, y)
+    torch.cuda.synchronize()
+    rel, _ = normwise_rel(host(y), ref)
+    assert rel <= (2e-2 if dtype == "bf16" else 1e-5)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_rope_with_offset_and_stride(orc, lib, dtype):
+    rng = np.random.default_rng(5)
+    M, H, D, theta, off = 9, 4, 64, 500000.0, 1000
+    X = synth.normal_f32(rng, (M, 3 * H * D))          # rows of a fused QKV output
+    if dtype == "bf16":
+        X = synth.f32_to_bf16(X)
+    depth = rng.integers(0, 8, size=M).astype(np.int32)
+    ref = orc.rope(X[:, H * D:2 * H * D].reshape(M, H, D), depth + off, theta)   # the k part
+    x = dev(X)
+    dd = dev(depth)
+    lib.eagle3_rope(x[:, H * D:], M, H, D, 3 * H * D, dd, off, theta)
+    torch.cuda.synchronize()
+    got = host(x)
+    rel, _ = normwise_rel(got[:, H * D:2 * H * D].reshape(M, H, D), ref)
+    assert rel <= (2e-2 if dtype == "bf16" else 1e-5)
+    assert np.array_equal(got[:, :H * D], X[:, :H * D]) and np.array_equal(got[:, 2 * H * D:], X[:, 2 * H * D:])
+
+
+def test_embed_and_commit_are_exact_copies(orc, lib):
+    rng = np.random.default_rng(6)
+    E = synth.normal_bf16(rng, (500, 128))
+    ids = rng.integers(0, 500, size=40).astype(np.int32)
+    Ed, idd = dev(E), dev(ids)
+    out = torch.empty(40, 128, dtype=torch.bfloat16, device="cuda")
+    lib.eagle3_embed(Ed, idd, out)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(out), orc.embed(E, ids))
+    # commit rows 0, 3, 5 (then -1) of sequence 0 and rows 1 of sequence 1 into a paged cache
+    B, T, Hkv, D = 2, 8, 2, 64
+    kr, vr = synth.normal_bf16(rng, (B, T, Hkv, D)), synth.normal_bf16(rng, (B, T, Hkv, D))
+    kv = synth.paged_kv(60, 0, [20, 5], Hkv, D, max_blocks=4)
+    src = np.array([[0, 3, 5, -1, 2, 2, 2, 2], [1, -1, 0, 0, 0, 0, 0, 0]], np.int32)
+    kc, vc, bt = dev(kv.k_cache), dev(kv.v_cache), dev(kv.block_table)
+    lib.eagle3_commit_kv(dev(kr), dev(vr), dev(src), dev(kv.prefix_len), kc, vc, bt)
+    torch.cuda.synchronize()
+    K2, V2 = host(kc), host(vc)
+    for b, rows in ((0, [0, 3, 5]), (1, [1])):
+        for j, r in enumerate(rows):
+            pos = int(kv.prefix_len[b]) + j
+            blk, slot = kv.block_table[b, pos // 16], pos % 16
+            assert np.array_equal(K2[blk, :, slot, :], kr[b, r])
+            assert np.array_equal(V2[blk, :, :, slot], vr[b, r])
+    untouched = np.ones(K2.shape[0], bool)
+    for b, n in ((0, 3), (1, 1)):
+        for j in range(n):
+            untouched[kv.block_table[b, (int(kv.prefix_len[b]) + j) // 16]] = False
+    assert np.array_equal(K2[untouched].view(np.uint16), kv.k_cache[untouched])
+
+
+@pytest.mark.parametrize("mode", ["context", "step"])
+def test_draft_fuse(orc, lib, mode):
+    rng = np.random.default_rng(7)
+    M, k, V = 70, 256, 1000
+    l, m, h, a = (synth.normal_bf16(rng, (M, k)) for _ in range(4))
+    E = synth.normal_bf16(rng, (V, k), 0.02)
+    Wf = synth.normal_bf16(rng, (k, 3 * k), 0.02)
+    Wi = synth.normal_bf16(rng, (k, 2 * k), 0.02)
+    tok = rng.integers(0, V, size=M).astype(np.int32)
+    x = torch.empty(M, k, dtype=torch.bfloat16, device="cuda")
+    Ed, Wfd, Wid, td = dev(E), dev(Wf), dev(Wi), dev(tok)
+    if mode == "context":
+        ref, gref = orc.draft_fuse(tok, E, Wf, Wi, l=l, m=m, h=h, want_g=True)
+        g = torch.empty(M, k, dtype=torch.bfloat16, device="cuda")
+        ld, md, hd = dev(l), dev(m), dev(h)
+        lib.eagle3_draft_fuse(td, Ed, Wid, x, w_fuse=Wfd, l=ld, m=md, h=hd, g_out=g)
+        torch.cuda.synchronize()
+        rel, _ = normwise_rel(host(g), gref)
+        assert rel <= 2e-2
+    else:
+        ref = orc.draft_fuse(tok, E, Wf, Wi, a_prev=a)
+        ad = dev(a)
+        lib.eagle3_draft_fuse(td, Ed, Wid, x, a_prev=ad)
+        torch.cuda.synchronize()
+    rel, mx = normwise_rel(host(x), ref)
+    assert rel <= 2e-2, (rel, mx)

@@ -156,3 +156,15 @@ def test_embed_copies_rows(orc):
     E = synth.f32_to_bf16(synth.normal_f32(rng, (100, 16)))
     ids = np.array([5, 0, 99, 5], np.int32)
     assert np.array_equal(orc.embed(E, ids), E[ids])
+
+
+def test_silu_mul_against_torch(orc):
+    rng = np.random.default_rng(9)
+    GU = synth.normal_f32(rng, (7, 2 * 33), 2.0)
+    Y = orc.silu_mul(GU)
+    t = torch.from_numpy(GU.astype(np.float64))
+    ref = (torch.nn.functional.silu(t[:, :33]) * t[:, 33:]).numpy()
+    np.testing.assert_allclose(Y, ref.astype(np.float32), rtol=1e-6, atol=1e-7)
+    # agrees with the fused form up to the storage rounding of the gate/up product
+    X = synth.normal_f32(rng, (5, 40)); W = synth.normal_f32(rng, (2 * 12, 40), 0.3)
+    np.testing.assert_allclose(orc.silu_mul(orc.gemm(X, W)), orc.swiglu(X, W), rtol=1e-5, atol=1e-6)

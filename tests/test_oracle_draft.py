@@ -1,0 +1,110 @@
+"""Pins for the oracle's EAGLE-3 draft head and tree growth (CPU only).
+
+* The fusion FCs are plain matrix products over the concatenation (numpy fp64
+  matmul on an explicit concatenation); W_in . [a; e] = W_a . a + W_e . e.
+* Step-mode pairing ([news] steps 2-3): a frontier node's draft input uses its
+  parent's draft output with the embedding of its own token.
+* Tree selection: the rerank equals a brute-force full sort of the pool
+  (numpy lexsort); closure under parents; a peaked draft degenerates to a chain
+  of full depth; the drafted tree has n_drafts nodes, parents before children,
+  at most top-k children per node and depth at most the number of steps.
+"""
+import numpy as np
+import pytest
+
+import synth
+
+
+def f64(a):
+    return (synth.bf16_to_f32(a) if a.dtype == np.uint16 else a).astype(np.float64)
+
+
+def test_draft_fuse_is_a_matmul_on_the_concatenation(orc):
+    rng = np.random.default_rng(0)
+    M, k, V = 9, 64, 50
+    l, m, h, a = (synth.normal_bf16(rng, (M, k)) for _ in range(4))
+    E = synth.normal_bf16(rng, (V, k), 0.1)
+    Wf, Wi = synth.normal_bf16(rng, (k, 3 * k), 0.1), synth.normal_bf16(rng, (k, 2 * k), 0.1)
+    tok = rng.integers(0, V, size=M).astype(np.int32)
+    x, g = orc.draft_fuse(tok, E, Wf, Wi, l=l, m=m, h=h, want_g=True)
+    gref = np.concatenate([f64(l), f64(m), f64(h)], 1) @ f64(Wf).T
+    np.testing.assert_allclose(f64(g), gref, rtol=2 ** -8, atol=1e-30)
+    xref = np.concatenate([f64(g), f64(E)[tok]], 1) @ f64(Wi).T
+    np.testing.assert_allclose(f64(x), xref, rtol=2 ** -8, atol=1e-30)
+    xs = orc.draft_fuse(tok, E, Wf, Wi, a_prev=a)
+    split = f64(a) @ f64(Wi)[:, :k].T + f64(E)[tok] @ f64(Wi)[:, k:].T      # W_in [a; e] = W_a a + W_e e
+    np.testing.assert_allclose(f64(xs), split, rtol=2 ** -8, atol=1e-30)
+
+
+def test_rerank_equals_full_sort_and_is_closed(orc):
+    rng = np.random.default_rng(1)
+    B, C, steps, N = 20, 10, 8, 60
+    pool_s, pool_t, pool_p = [], [], []
+    fr_score = np.zeros((B, 1), np.float32)
+    fr_pool = np.full((B, 1), -1, np.int32)
+    n = 0
+    for step in range(1, steps + 1):
+        F = fr_score.shape[1]
+        logp = -np.abs(rng.standard_normal((B, F, C))).astype(np.float32) * 3
+        ids = rng.integers(0, 1000, size=(B, F, C)).astype(np.int32)
+        cand, cpar, npool, nscore, ntok, nslot = orc.tree_expand(fr_score, fr_pool, ids, logp, n, C)
+        pool_s.append(cand); pool_t.append(ids.reshape(B, -1)); pool_p.append(cpar)
+        n += F * C
+        fr_score, fr_pool = nscore, npool
+    S, Tk, Pp = (np.concatenate(x, 1) for x in (pool_s, pool_t, pool_p))
+    parent, tokens, near = orc.tree_rerank(S, Tk, Pp, np.arange(B), N)
+    for b in range(B):
+        brute = np.lexsort((np.arange(S.shape[1]), -S[b].astype(np.float64)))[:N]   # score desc, creation asc
+        chosen = np.sort(brute)
+        assert list(tokens[b, 1:]) == list(Tk[b, chosen])
+        assert orc.tree_check(parent[b])                                  # parents before children
+        sel = set(chosen.tolist())
+        assert all(Pp[b, c] < 0 or int(Pp[b, c]) in sel for c in chosen)  # closed under parents
+        kids = np.bincount(parent[b, 1:], minlength=N + 1)
+        assert kids.max() <= C
+        _, depth = orc.tree_mask(parent[b])
+        assert depth.max() <= steps
+
+
+def test_peaked_draft_is_a_full_depth_chain(orc):
+    """One child per node carries logp 0 and the rest -50: the selected tree
+    contains the full-depth chain of those children."""
+    B, C, steps, N = 1, 10, 8, 60
+    fr_score = np.zeros((B, 1), np.float32); fr_pool = np.full((B, 1), -1, np.int32)
+    pool = []
+    n = 0
+    for step in range(steps):
+        F = fr_score.shape[1]
+        logp = np.full((B, F, C), -50.0, np.float32)
+        logp[:, :, 3] = 0.0
+        ids = (np.arange(F * C).reshape(1, F, C) + 1000 * step).astype(np.int32)
+        cand, cpar, npool, nscore, ntok, _ = orc.tree_expand(fr_score, fr_pool, ids, logp, n, C)
+        pool.append((cand, ids.reshape(B, -1), cpar))
+        n += F * C
+        fr_score, fr_pool = nscore, npool
+    S, Tk, Pp = (np.concatenate([p[i] for p in pool], 1) for i in range(3))
+    parent, tokens, _ = orc.tree_rerank(S, Tk, Pp, [7], N)
+    _, depth = orc.tree_mask(parent[0])
+    assert depth.max() == steps
+    zero = np.flatnonzero(S[0] == 0.0)
+    assert len(zero) == steps and set(Tk[0, zero]).issubset(set(tokens[0]))
+
+
+def test_draft_tree_invariants_and_step_pairing(orc):
+    s = synth.DRAFT_SMALL
+    W = synth.draft_weights(s)
+    l, m, h, tok = synth.draft_inputs(s, 0)
+    r = orc.draft_tree(s, W, l, m, h, tok)
+    N = s.n_drafts
+    for b in range(s.B):
+        par, tk = r["parent"][b], r["tokens"][b]
+        assert orc.tree_check(par) and len(par) == N + 1 and tk[0] == tok[b, -1]
+        _, depth = orc.tree_mask(par)
+        assert 1 <= depth.max() <= s.steps
+        for n in range(N + 1):                   # siblings carry distinct tokens (distinct top-k ids)
+            kids = np.flatnonzero(par == n)
+            assert len(set(tk[kids])) == len(kids) and len(kids) <= s.topk
+    # row-independence: one sequence alone gives the same tree
+    l1, m1, h1, t1 = synth.draft_inputs(s, 0, batch=slice(3, 4))
+    r1 = orc.draft_tree(s, W, l1, m1, h1, t1)
+    assert np.array_equal(r1["parent"][0], r["parent"][3]) and np.array_equal(r1["tokens"][0], r["tokens"][3])

@@ -19,7 +19,7 @@ OK, ERR_ARG, ERR_UNSUPPORTED, ERR_TREE, ERR_RANGE, ERR_HIP, ERR_WORKSPACE = 0, -
 F32, BF16 = 0, 1
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m tree_draft_verification_amd.build` "
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python tree_draft_verification_amd/build.py` "
                       "(there is no fallback path)")
 _lib = ctypes.CDLL(LIB_PATH)
 
@@ -35,6 +35,14 @@ class TreeAttnArgs(ctypes.Structure):
         ("block_table", P), ("max_blocks", I), ("prefix_len", P),
         ("mask", P), ("parent", P), ("out", P), ("lse", P),
         ("split_keys", I),
+    ]
+
+
+class GemmArgs(ctypes.Structure):
+    _fields_ = [
+        ("dtype", I), ("M", I), ("N", I), ("nseg", I),
+        ("a", P * 3), ("a_rows", P * 3), ("a_nrows", I * 3), ("k", I * 3),
+        ("b", P), ("residual", P), ("c", P), ("ldc", I),
     ]
 
 
@@ -54,6 +62,15 @@ _rmsnorm = _sig("eagle3_rmsnorm", I, P, P, I, I, F, I, P, P)
 _lmhead_ws = _sig("eagle3_lmhead_workspace", SZ, I, I, I, I, I)
 _lmhead = _sig("eagle3_lmhead_argmax", I, P, P, I, I, I, I, I, P, P, P, P, P, SZ, P)
 _accept = _sig("eagle3_accept_path", I, P, P, P, I, P, I, I, P, P, P, P)
+_gemm = _sig("eagle3_gemm", I, ctypes.POINTER(GemmArgs), P)
+_silu_mul = _sig("eagle3_silu_mul", I, P, I, I, I, P, P)
+_rope = _sig("eagle3_rope", I, P, I, I, I, I, P, I, F, I, P)
+_embed = _sig("eagle3_embed", I, P, P, I, I, I, I, P, P)
+_commit_kv = _sig("eagle3_commit_kv", I, P, P, I, P, I, I, I, I, I, P, P, P, I, I, P, P)
+_draft_fuse_ws = _sig("eagle3_draft_fuse_workspace", SZ, I, I, I)
+_draft_fuse = _sig("eagle3_draft_fuse", I, P, P, P, P, P, P, P, P, I, I, I, I, P, P, P, SZ, P)
+_tree_expand = _sig("eagle3_tree_expand", I, P, P, P, I, I, P, P, P, I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P)
+_tree_rerank = _sig("eagle3_tree_rerank", I, P, P, P, I, I, I, I, P, P, P, P)
 
 
 class Eagle3Error(RuntimeError):
@@ -157,6 +174,80 @@ def eagle3_accept_path(tokens, target_idx, accept_len, path, out_tokens, parent=
     W = mask.shape[-1] if mask is not None else (T + 63) // 64
     _check(_accept(_ptr(tokens), _ptr(parent), _ptr(mask), W, _ptr(target_idx), B, T, _ptr(accept_len), _ptr(path),
                    _ptr(out_tokens), _stream(stream)), "eagle3_accept_path")
+
+
+def eagle3_gemm(a, b, c, residual=None, a_rows=None, a_nrows=None, ldc=0, M=None, stream=None):
+    """C = [a_0 | a_1 | ...] . b^T (+ residual); a: list of [rows, k_s] tensors
+    (a_rows[s]: optional int32 row gather of segment s)."""
+    a = list(a)
+    g = GemmArgs()
+    g.dtype = _dtype(b)
+    g.M = int(M if M is not None else c.shape[0])
+    g.N = int(b.shape[0])
+    g.nseg = len(a)
+    rows = list(a_rows) if a_rows is not None else [None] * len(a)
+    for i, t in enumerate(a):
+        g.a[i] = _ptr(t)
+        g.k[i] = int(t.shape[-1])
+        g.a_rows[i] = _ptr(rows[i])
+        g.a_nrows[i] = int(t.shape[0]) if rows[i] is not None else 0
+    g.b, g.residual, g.c, g.ldc = _ptr(b), _ptr(residual), _ptr(c), int(ldc)
+    _check(_gemm(ctypes.byref(g), _stream(stream)), "eagle3_gemm")
+
+
+def eagle3_silu_mul(gu, y, stream=None):
+    M, F = y.shape[0], y.shape[-1]
+    _check(_silu_mul(_ptr(gu), M, F, _dtype(gu), _ptr(y), _stream(stream)), "eagle3_silu_mul")
+
+
+def eagle3_rope(x, M, H, D, ld, pos, pos_offset, theta, stream=None):
+    _check(_rope(_ptr(x), M, H, D, ld, _ptr(pos), int(pos_offset), float(theta), _dtype(x), _stream(stream)),
+           "eagle3_rope")
+
+
+def eagle3_embed(E, ids, out, stream=None):
+    M, K, V = ids.shape[0], E.shape[1], E.shape[0]
+    _check(_embed(_ptr(E), _ptr(ids), M, K, V, _dtype(E), _ptr(out), _stream(stream)), "eagle3_embed")
+
+
+def eagle3_commit_kv(k_rows, v_rows, src, start, k_cache, v_cache, block_table, stream=None):
+    """k_rows/v_rows [B, rows, Hkv, D]; src [B, max_n] int32 (-1 ends a list)."""
+    B, rows, Hkv, D = k_rows.shape
+    _check(_commit_kv(_ptr(k_rows), _ptr(v_rows), rows, _ptr(src), src.shape[1], B, Hkv, D, _dtype(k_rows),
+                      _ptr(k_cache), _ptr(v_cache), _ptr(block_table), block_table.shape[1], k_cache.shape[0],
+                      _ptr(start), _stream(stream)), "eagle3_commit_kv")
+
+
+def eagle3_draft_fuse_workspace(M, k, dtype) -> int:
+    return int(_draft_fuse_ws(M, k, dtype))
+
+
+def eagle3_draft_fuse(tok, E, w_in, x_out, w_fuse=None, l=None, m=None, h=None, a_prev=None, g_out=None, ws=None,
+                      stream=None):
+    M, k, V = tok.shape[0], E.shape[1], E.shape[0]
+    ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
+    _check(_draft_fuse(_ptr(l), _ptr(m), _ptr(h), _ptr(a_prev), _ptr(tok), _ptr(E), _ptr(w_fuse), _ptr(w_in), M, k,
+                       V, _dtype(E), _ptr(g_out), _ptr(x_out), _ptr(ws), ws_bytes, _stream(stream)),
+           "eagle3_draft_fuse")
+
+
+def eagle3_tree_expand(fr_score, fr_pool, fr_mask, fr_arow_base, arow_stride, child_ids, child_val, child_lse,
+                       pool_len, row_base, pool_score, pool_token, pool_parent, next_pool, next_score, next_token,
+                       next_mask, next_arow, stream=None):
+    B, F, C = child_ids.shape
+    NF = next_pool.shape[1]
+    _check(_tree_expand(_ptr(fr_score), _ptr(fr_pool), _ptr(fr_mask), int(fr_arow_base), int(arow_stride),
+                        _ptr(child_ids), _ptr(child_val), _ptr(child_lse), B, F, C, NF, int(pool_len),
+                        pool_score.shape[1], int(row_base), _ptr(pool_score), _ptr(pool_token), _ptr(pool_parent),
+                        _ptr(next_pool), _ptr(next_score), _ptr(next_token), _ptr(next_mask), _ptr(next_arow),
+                        _stream(stream)), "eagle3_tree_expand")
+
+
+def eagle3_tree_rerank(pool_score, pool_token, pool_parent, pool_len, root_token, parent, tokens, stream=None):
+    B, cap = pool_score.shape
+    N = parent.shape[1] - 1
+    _check(_tree_rerank(_ptr(pool_score), _ptr(pool_token), _ptr(pool_parent), B, int(pool_len), cap, N,
+                        _ptr(root_token), _ptr(parent), _ptr(tokens), _stream(stream)), "eagle3_tree_rerank")
 
 
 def exported_symbols():

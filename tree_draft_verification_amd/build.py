@@ -1,8 +1,8 @@
 """Compile the HIP sources under csrc/ into libeagle3.so for gfx950.
 
 Each .hip file is compiled to an object in parallel, then linked with hipcc.
-Usage: ``python -m tree_draft_verification_amd.build`` (or build() from
-Python). Always recompiles.
+Usage: ``python tree_draft_verification_amd/build.py`` (by path: importing the
+package needs the library). Always recompiles.
 """
 import concurrent.futures
 import glob

@@ -1,0 +1,383 @@
+// Dense layers around the verify step and the EAGLE-3 draft head: GEMM with a
+// K-segmented, optionally row-gathered A operand (so the draft's fusion FCs
+// read [l; m; h] and [g; E[token]] without building the concatenation), SiLU
+// gating, rotary embedding, embedding gather and KV-cache commit.
+//
+// The draft stage ([news] draft-stage paragraphs of the write-up of "EAGLE-3:
+// Scaling up Inference Acceleration of Large Language Models via Training-Time
+// Test"): an FC takes the concatenated low/mid/high features (3k) to k; the
+// result (or, from step 2 on, the draft's own output) is concatenated with the
+// embedding of the token one step ahead and an FC takes 2k to k; a single
+// transformer layer follows. reading: that layer is a Llama decoder layer
+// (RMSNorm, GQA attention with rotate-half RoPE, SwiGLU MLP, residuals).
+#include "common.h"
+
+namespace {
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+constexpr int GBM = 128, GBN = 128, GBK = 64, GNS = 3;
+constexpr int G_ASTAGE = GBM * 128, G_BSTAGE = GBN * 128;  // bytes: 64 bf16 per row
+constexpr int G_STAGE = G_ASTAGE + G_BSTAGE;
+constexpr int G_LOADS = G_STAGE / 1024 / 4;                 // 1 KB DMA loads per wave per stage
+
+struct GemmParams {
+    const void *a[3];
+    const int32_t *a_rows[3];
+    int k[3];
+    int kofs[3];
+    int nseg;
+    const void *b;
+    const void *res;
+    void *c;
+    int M, N, K, ldc, a_nrows[3];
+};
+
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// C[M, N] = A[M, K] . B[N, K]^T (+ R), bf16 in/out, fp32 accumulate.
+// One 256-thread work-group per 128 x 128 output tile; waves as 2 x 2, each
+// 64 x 64 (2 x 2 MFMA blocks). A and B chunks (64 k) go straight to a 3-stage
+// LDS ring by 16-byte global_load_lds; rows XOR-swizzled at 16 B.
+__global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmParams p) {
+    __shared__ __attribute__((aligned(1024))) unsigned char ring[GNS * G_STAGE];
+    __shared__ int arow[3][GBM];  // gathered A row of each tile row, per segment
+    const int mt = blockIdx.x, nt = blockIdx.y;
+    const int m0 = mt * GBM, n0 = nt * GBN;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int lr = lane & 31, lh = lane >> 5;
+
+    for (int i = tid; i < 3 * GBM; i += 256) {
+        const int s = i / GBM, r = i % GBM;
+        int m = min(m0 + r, p.M - 1);
+        if (s < p.nseg && p.a_rows[s]) m = min(max(p.a_rows[s][m], 0), p.a_nrows[s] - 1);
+        arow[s][r] = m;
+    }
+    __syncthreads();
+
+    // this lane's load j covers stage block blk = wave * G_LOADS + j (8 rows of 128 B);
+    // blocks 0..15 are A rows, 16..31 B rows; lane fills row 8 blk + lane / 8, column lane % 8
+    const int col = lane & 7;
+    auto issue = [&](int stage, int kc) {
+        unsigned char *base = ring + stage * G_STAGE;
+        int seg = 0;
+        while (seg + 1 < p.nseg && kc >= p.kofs[seg + 1]) ++seg;  // chunk kc lies in one segment
+#pragma unroll
+        for (int j = 0; j < G_LOADS; ++j) {
+            const int blk = wave * G_LOADS + j;
+            const void *src;
+            if (blk < G_ASTAGE / 1024) {
+                const int row = blk * 8 + lane / 8;
+                src = (const uint16_t *)p.a[seg] + (size_t)arow[seg][row] * p.k[seg] + (kc - p.kofs[seg]) +
+                      8 * (col ^ swz(row));
+            } else {
+                const int row = (blk - G_ASTAGE / 1024) * 8 + lane / 8;
+                const int n = min(n0 + row, p.N - 1);
+                src = (const uint16_t *)p.b + (size_t)n * p.K + kc + 8 * (col ^ swz(row));
+            }
+            __builtin_amdgcn_global_load_lds(src, (lds_void_t *)(base + blk * 1024), 16, 0, 0);
+        }
+    };
+
+    f32x16_t acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][jj][r] = 0.f;
+
+    const int nch = p.K / GBK;
+#pragma unroll
+    for (int st = 0; st < GNS - 1; ++st)
+        if (st < nch) issue(st, st * GBK);
+    const int wm = wave >> 1, wn = wave & 1;
+    for (int c = 0; c < nch; ++c) {
+        if (c + GNS - 2 < nch) wait_vmcnt<(GNS - 2) * G_LOADS>();
+        else wait_vmcnt<0>();
+        // bare barrier: a fenced one would drain the stages still in flight
+        __builtin_amdgcn_s_barrier();
+        __asm__ volatile("" ::: "memory");
+        if (c + GNS - 1 < nch) issue((c + GNS - 1) % GNS, (c + GNS - 1) * GBK);
+        const unsigned char *ab = ring + (c % GNS) * G_STAGE;
+        const unsigned char *bb = ab + G_ASTAGE;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int cl = 4 * lh + s;  // both operands take k = 32 lh + 8 s .. +7 of the chunk
+            u32x4_t av[2], bv[2];
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb) {
+                const int row = wm * 64 + mb * 32 + lr;
+                av[mb] = *reinterpret_cast<const u32x4_t *>(ab + row * 128 + ((cl ^ swz(row)) << 4));
+            }
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) {
+                const int row = wn * 64 + nb * 32 + lr;
+                bv[nb] = *reinterpret_cast<const u32x4_t *>(bb + row * 128 + ((cl ^ swz(row)) << 4));
+            }
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb)
+                    acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, av[mb]),
+                                                                          __builtin_bit_cast(bf16x8_t, bv[nb]),
+                                                                          acc[mb][nb], 0, 0, 0);
+        }
+    }
+    // D[m][n]: lane holds n = lr of its block, m = 8 (r / 4) + 4 lh + r % 4
+    const uint16_t *res = (const uint16_t *)p.res;
+    uint16_t *cc = (uint16_t *)p.c;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int m = m0 + wm * 64 + mb * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+                const int n = n0 + wn * 64 + nb * 32 + lr;
+                if (m < p.M && n < p.N) {
+                    float v = acc[mb][nb][r];
+                    if (res) v += e3_bf16_to_f32(res[(size_t)m * p.ldc + n]);
+                    cc[(size_t)m * p.ldc + n] = e3_f32_to_bf16(v);
+                }
+            }
+}
+
+// fp32 GEMM for small models: 16 x 16 output tile per 256 threads, 16-wide k
+// chunks through LDS; every output accumulates k in ascending order.
+__global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
+    __shared__ float As[16][17];
+    __shared__ float Bs[16][17];
+    const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+    const int m = blockIdx.x * 16 + ty, n = blockIdx.y * 16 + tx;
+    float acc = 0.f;
+    for (int kc = 0; kc < p.K; kc += 16) {
+        {   // A element (row ty, k tx) and B element (row ty, k tx) of this chunk
+            const int k = kc + tx;
+            const int ma = blockIdx.x * 16 + ty;
+            float av = 0.f;
+            if (ma < p.M && k < p.K) {
+                int seg = 0;
+                while (seg + 1 < p.nseg && k >= p.kofs[seg + 1]) ++seg;
+                int row = ma;
+                if (p.a_rows[seg]) row = min(max(p.a_rows[seg][ma], 0), p.a_nrows[seg] - 1);
+                av = ((const float *)p.a[seg])[(size_t)row * p.k[seg] + (k - p.kofs[seg])];
+            }
+            As[ty][tx] = av;
+            const int nb = blockIdx.y * 16 + ty;
+            Bs[ty][tx] = (nb < p.N && k < p.K) ? ((const float *)p.b)[(size_t)nb * p.K + k] : 0.f;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < 16; ++kk) acc = fmaf(As[ty][kk], Bs[tx][kk], acc);
+        __syncthreads();
+    }
+    if (m < p.M && n < p.N) {
+        float v = acc;
+        if (p.res) v += ((const float *)p.res)[(size_t)m * p.ldc + n];
+        ((float *)p.c)[(size_t)m * p.ldc + n] = v;
+    }
+}
+
+// y[m][f] = silu(gu[m][f]) * gu[m][F + f]
+template <bool BF16>
+__global__ __launch_bounds__(256) void silu_mul_kernel(const void *__restrict__ gu, int M, int F, void *__restrict__ y) {
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (size_t)M * F) return;
+    const size_t m = i / F, f = i % F;
+    float g, u;
+    if (BF16) {
+        g = e3_bf16_to_f32(((const uint16_t *)gu)[m * 2 * F + f]);
+        u = e3_bf16_to_f32(((const uint16_t *)gu)[m * 2 * F + F + f]);
+    } else {
+        g = ((const float *)gu)[m * 2 * F + f];
+        u = ((const float *)gu)[m * 2 * F + F + f];
+    }
+    const float v = g / (1.f + expf(-g)) * u;
+    if (BF16) ((uint16_t *)y)[i] = e3_f32_to_bf16(v);
+    else ((float *)y)[i] = v;
+}
+
+// Rotate-half RoPE in place on x viewed as [M][H][D] with row stride ld
+// (elements): pair (i, i + D/2) at position p = pos_offset + pos[m] turns by
+// p * theta^(-2i/D); the angle is formed in double precision.
+template <bool BF16>
+__global__ __launch_bounds__(256) void rope_kernel(void *__restrict__ x, int M, int H, int D, int ld,
+                                                   const int32_t *__restrict__ pos, int pos_offset, double log_theta) {
+    const int half = D / 2;
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (size_t)M * H * half) return;
+    const int j = (int)(i % half);
+    const size_t mh = i / half;
+    const int h = (int)(mh % H), m = (int)(mh / H);
+    const double ang = (double)(pos_offset + pos[m]) * exp(-2.0 * j / D * log_theta);
+    double sn, cs;
+    sincos(ang, &sn, &cs);
+    const size_t base = (size_t)m * ld + (size_t)h * D;
+    if (BF16) {
+        uint16_t *p = (uint16_t *)x;
+        const double a = e3_bf16_to_f32(p[base + j]), b = e3_bf16_to_f32(p[base + j + half]);
+        p[base + j] = e3_f32_to_bf16((float)(a * cs - b * sn));
+        p[base + j + half] = e3_f32_to_bf16((float)(b * cs + a * sn));
+    } else {
+        float *p = (float *)x;
+        const double a = p[base + j], b = p[base + j + half];
+        p[base + j] = (float)(a * cs - b * sn);
+        p[base + j + half] = (float)(b * cs + a * sn);
+    }
+}
+
+// out[m] = E[clamp(ids[m])], 16 bytes per thread
+__global__ __launch_bounds__(256) void embed_kernel(const uint4 *__restrict__ E, const int32_t *__restrict__ ids,
+                                                    int M, int row_vec, int V, uint4 *__restrict__ out) {
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (size_t)M * row_vec) return;
+    const int m = (int)(i / row_vec), c = (int)(i % row_vec);
+    const int id = min(max(ids[m], 0), V - 1);
+    out[i] = E[(size_t)id * row_vec + c];
+}
+
+// Append rows to the paged cache: for sequence b, rows src[b][0..] (indices
+// into k_rows/v_rows [B, rows_per_seq, Hkv, D]; the list ends at the first
+// negative entry or after max_n) land at positions start[b] + j. Cache
+// layouts: K [blk][Hkv][16][D], V [blk][Hkv][D][16].
+template <bool BF16>
+__global__ __launch_bounds__(256) void commit_kv_kernel(const void *__restrict__ k_rows, const void *__restrict__ v_rows,
+                                                        int rows_per_seq, const int32_t *__restrict__ src, int max_n,
+                                                        int Hkv, int D, void *__restrict__ k_cache,
+                                                        void *__restrict__ v_cache,
+                                                        const int32_t *__restrict__ block_table, int max_blocks,
+                                                        int num_blocks, const int32_t *__restrict__ start) {
+    const int b = blockIdx.y;
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (size_t)max_n * Hkv * D) return;
+    const int d = (int)(i % D), h = (int)((i / D) % Hkv), j = (int)(i / ((size_t)D * Hkv));
+    const int32_t *s = src + (size_t)b * max_n;
+    for (int q = 0; q <= j; ++q)
+        if (s[q] < 0) return;  // the list ended before entry j
+    const int r = min(s[j], rows_per_seq - 1);
+    const int posn = start[b] + j;
+    if (posn < 0 || posn >= max_blocks * 16) return;
+    const int blk = min(max(block_table[(size_t)b * max_blocks + posn / 16], 0), num_blocks - 1);
+    const int slot = posn % 16;
+    const size_t srow = (((size_t)b * rows_per_seq + r) * Hkv + h) * D + d;
+    const size_t kdst = (((size_t)blk * Hkv + h) * 16 + slot) * D + d;
+    const size_t vdst = (((size_t)blk * Hkv + h) * D + d) * 16 + slot;
+    if (BF16) {
+        ((uint16_t *)k_cache)[kdst] = ((const uint16_t *)k_rows)[srow];
+        ((uint16_t *)v_cache)[vdst] = ((const uint16_t *)v_rows)[srow];
+    } else {
+        ((float *)k_cache)[kdst] = ((const float *)k_rows)[srow];
+        ((float *)v_cache)[vdst] = ((const float *)v_rows)[srow];
+    }
+}
+
+unsigned grid1(size_t n) { return (unsigned)((n + 255) / 256); }
+
+}  // namespace
+
+extern "C" int eagle3_gemm(const eagle3_gemm_args *a, void *stream) {
+    if (!a) return EAGLE3_ERR_ARG;
+    if (a->M < 0 || a->N < 1 || a->nseg < 1 || a->nseg > 3) return EAGLE3_ERR_ARG;
+    if (a->dtype != EAGLE3_BF16 && a->dtype != EAGLE3_F32) return EAGLE3_ERR_UNSUPPORTED;
+    if (a->M == 0) return EAGLE3_OK;
+    if (!a->b || !a->c) return EAGLE3_ERR_ARG;
+    const int ldc = a->ldc > 0 ? a->ldc : a->N;
+    if (ldc < a->N) return EAGLE3_ERR_ARG;
+    GemmParams p{};
+    int K = 0;
+    for (int s = 0; s < a->nseg; ++s) {
+        if (!a->a[s] || a->k[s] < 1) return EAGLE3_ERR_ARG;
+        if (a->a_rows[s] && a->a_nrows[s] < 1) return EAGLE3_ERR_ARG;
+        if (a->dtype == EAGLE3_BF16 && (a->k[s] % GBK != 0 || !e3_aligned16(a->a[s]))) return EAGLE3_ERR_UNSUPPORTED;
+        p.a[s] = a->a[s];
+        p.a_rows[s] = a->a_rows[s];
+        p.a_nrows[s] = a->a_rows[s] ? a->a_nrows[s] : a->M;
+        p.k[s] = a->k[s];
+        p.kofs[s] = K;
+        K += a->k[s];
+    }
+    if (a->dtype == EAGLE3_BF16 && !e3_aligned16(a->b)) return EAGLE3_ERR_ARG;
+    p.nseg = a->nseg; p.b = a->b; p.res = a->residual; p.c = a->c;
+    p.M = a->M; p.N = a->N; p.K = K; p.ldc = ldc;
+    const hipStream_t st = e3_stream(stream);
+    if (a->dtype == EAGLE3_BF16) {
+        dim3 grid((a->M + GBM - 1) / GBM, (a->N + GBN - 1) / GBN);
+        gemm_bf16_kernel<<<grid, 256, 0, st>>>(p);
+    } else {
+        dim3 grid((a->M + 15) / 16, (a->N + 15) / 16);
+        gemm_f32_kernel<<<grid, 256, 0, st>>>(p);
+    }
+    E3_LAUNCH_CHECK();
+    return EAGLE3_OK;
+}
+
+extern "C" int eagle3_silu_mul(const void *gu, int M, int F, int dtype, void *y, void *stream) {
+    if (M < 0 || F < 1) return EAGLE3_ERR_ARG;
+    if (dtype != EAGLE3_BF16 && dtype != EAGLE3_F32) return EAGLE3_ERR_UNSUPPORTED;
+    if (M == 0) return EAGLE3_OK;
+    if (!gu || !y) return EAGLE3_ERR_ARG;
+    const size_t n = (size_t)M * F;
+    if (dtype == EAGLE3_BF16) silu_mul_kernel<true><<<grid1(n), 256, 0, e3_stream(stream)>>>(gu, M, F, y);
+    else silu_mul_kernel<false><<<grid1(n), 256, 0, e3_stream(stream)>>>(gu, M, F, y);
+    E3_LAUNCH_CHECK();
+    return EAGLE3_OK;
+}
+
+extern "C" int eagle3_rope(void *x, int M, int H, int D, int ld, const int32_t *pos, int pos_offset, float theta,
+                           int dtype, void *stream) {
+    if (M < 0 || H < 1 || D < 2 || (D & 1) || !(theta > 1.f)) return EAGLE3_ERR_ARG;
+    if (dtype != EAGLE3_BF16 && dtype != EAGLE3_F32) return EAGLE3_ERR_UNSUPPORTED;
+    if (ld < H * D) return EAGLE3_ERR_ARG;
+    if (M == 0) return EAGLE3_OK;
+    if (!x || !pos) return EAGLE3_ERR_ARG;
+    const size_t n = (size_t)M * H * (D / 2);
+    const double lt = log((double)theta);
+    if (dtype == EAGLE3_BF16) rope_kernel<true><<<grid1(n), 256, 0, e3_stream(stream)>>>(x, M, H, D, ld, pos, pos_offset, lt);
+    else rope_kernel<false><<<grid1(n), 256, 0, e3_stream(stream)>>>(x, M, H, D, ld, pos, pos_offset, lt);
+    E3_LAUNCH_CHECK();
+    return EAGLE3_OK;
+}
+
+extern "C" int eagle3_embed(const void *E, const int32_t *ids, int M, int K, int V, int dtype, void *out,
+                            void *stream) {
+    if (M < 0 || K < 1 || V < 1) return EAGLE3_ERR_ARG;
+    if (dtype != EAGLE3_BF16 && dtype != EAGLE3_F32) return EAGLE3_ERR_UNSUPPORTED;
+    const int esz = dtype == EAGLE3_BF16 ? 2 : 4;
+    if (((size_t)K * esz) % 16 != 0) return EAGLE3_ERR_UNSUPPORTED;
+    if (M == 0) return EAGLE3_OK;
+    if (!E || !ids || !out || !e3_aligned16(E) || !e3_aligned16(out)) return EAGLE3_ERR_ARG;
+    const int row_vec = (int)((size_t)K * esz / 16);
+    embed_kernel<<<grid1((size_t)M * row_vec), 256, 0, e3_stream(stream)>>>((const uint4 *)E, ids, M, row_vec, V,
+                                                                           (uint4 *)out);
+    E3_LAUNCH_CHECK();
+    return EAGLE3_OK;
+}
+
+extern "C" int eagle3_commit_kv(const void *k_rows, const void *v_rows, int rows_per_seq, const int32_t *src,
+                                int max_n, int B, int Hkv, int D, int dtype, void *k_cache, void *v_cache,
+                                const int32_t *block_table, int max_blocks, int num_blocks, const int32_t *start,
+                                void *stream) {
+    if (B < 0 || max_n < 0 || rows_per_seq < 1 || Hkv < 1 || D < 1 || max_blocks < 1 || num_blocks < 1)
+        return EAGLE3_ERR_ARG;
+    if (dtype != EAGLE3_BF16 && dtype != EAGLE3_F32) return EAGLE3_ERR_UNSUPPORTED;
+    if (B == 0 || max_n == 0) return EAGLE3_OK;
+    if (!k_rows || !v_rows || !src || !k_cache || !v_cache || !block_table || !start) return EAGLE3_ERR_ARG;
+    dim3 grid(grid1((size_t)max_n * Hkv * D), B);
+    if (dtype == EAGLE3_BF16)
+        commit_kv_kernel<true><<<grid, 256, 0, e3_stream(stream)>>>(k_rows, v_rows, rows_per_seq, src, max_n, Hkv, D,
+                                                                   k_cache, v_cache, block_table, max_blocks,
+                                                                   num_blocks, start);
+    else
+        commit_kv_kernel<false><<<grid, 256, 0, e3_stream(stream)>>>(k_rows, v_rows, rows_per_seq, src, max_n, Hkv, D,
+                                                                    k_cache, v_cache, block_table, max_blocks,
+                                                                    num_blocks, start);
+    E3_LAUNCH_CHECK();
+    return EAGLE3_OK;
+}
