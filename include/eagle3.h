@@ -237,14 +237,25 @@ int eagle3_rope(void *x, int M, int H, int D, int ld, const int32_t *pos, int po
  * out [M, K]; K * element size must be a multiple of 16 bytes. */
 int eagle3_embed(const void *E, const int32_t *ids, int M, int K, int V, int dtype, void *out, void *stream);
 
+/* Row copy: dst[dst_rows[i]] = src[src_rows[i]] for i < n (device int32
+ * tables; NULL = identity); a row index outside [0, src_nrows) or
+ * [0, dst_nrows) skips that row. Rows are row_bytes long (a multiple of 16;
+ * both bases 16-byte aligned). Used to gather the parents' draft outputs and
+ * to place a draft step's K/V rows among the tree keys. Repeated destination
+ * rows race. */
+int eagle3_copy_rows(const void *src, const int32_t *src_rows, int src_nrows, void *dst, const int32_t *dst_rows,
+                     int dst_nrows, int n, size_t row_bytes, void *stream);
+
 /*
  * Append K/V rows to the paged cache after acceptance ([lesson] "Verify-accept
  * semantics": the accepted tokens become part of the sequence). For sequence
  * b, rows src[b][0..] of k_rows / v_rows [B, rows_per_seq, Hkv, D] go to
  * positions start[b] + j of the cache (layouts as in eagle3_tree_attn); the
  * list ends at the first negative entry or after max_n entries, so the `path`
- * output of eagle3_accept_path can be passed as is. src [B, max_n] and
- * start [B] are device int32 arrays; positions past max_blocks * 16 are skipped.
+ * output of eagle3_accept_path can be passed as is; a NULL src means rows
+ * 0..max_n-1 of every sequence (bulk ingest of a context). src [B, max_n] and
+ * start [B] are device int32 arrays; positions past max_blocks * 16 are
+ * skipped; B <= 65535. Entries listing the same cache position race.
  */
 int eagle3_commit_kv(const void *k_rows, const void *v_rows, int rows_per_seq, const int32_t *src, int max_n,
                      int B, int Hkv, int D, int dtype, void *k_cache, void *v_cache, const int32_t *block_table,

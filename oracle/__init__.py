@@ -432,7 +432,7 @@ def _page(rows_k, rows_v, bs=16):
     return synth.PagedKV(kc, vc, table, np.full(B, L, np.int32), bs)
 
 
-def draft_tree(shape, W, l, m, h, ctx_tok, gap=GAP_FLAG):
+def draft_tree(shape, W, l, m, h, ctx_tok, gap=GAP_FLAG, follow=None):
     """EAGLE-3 draft head and EAGLE-2 style tree growth, for B sequences.
 
     News write-up of the EAGLE-3 paper, draft stage: context row t fuses the
@@ -449,23 +449,70 @@ def draft_tree(shape, W, l, m, h, ctx_tok, gap=GAP_FLAG):
     keeps the top-k candidates as the next frontier and every candidate in the
     pool; the final tree is the top n_drafts of the pool by (score desc,
     creation asc), renumbered in creation order under the root.
-    Returns parent, tokens [B, n+1] and per-sequence flags (some membership
-    boundary within `gap`)."""
+    Returns parent, tokens [B, n+1] and per-sequence flags: some selection
+    boundary within `gap` that can reach the final tree (a top-k boundary of a
+    node's children or a frontier boundary whose score at stake lies within
+    `gap` of the n-th pool score, or the final rerank boundary).
+
+    follow: checks the choices of another run instead of making its own. A
+    dict with, per step, "ids" [B, F, C] (the children taken at each frontier
+    node) and "frontier" [B, C] (the candidates taken, as indices into that
+    step's candidates, in frontier order), and "selected" [B, n] (pool indices
+    of the final tree). The arithmetic is unchanged; the result also holds the
+    logits of the taken children ("lm_val", per step) and, per sequence, how
+    far each kind of choice falls below the best alternative in this run's
+    numbers ("margin": 0 when the choices agree; inf when a taken child is
+    not among this run's top 16). Either way "choices" holds the choices made,
+    in the same form."""
     s = shape
     B, ctx, k = l.shape
     qd, kvd, C = s.Hq * s.D, s.Hkv * s.D, s.topk
     wq, wk, wv = W["wqkv"][:qd], W["wqkv"][qd:qd + kvd], W["wqkv"][qd + kvd:]
     near = np.zeros(B, bool)
+    margin = {"lm": np.zeros(B), "frontier": np.zeros(B), "final": np.zeros(B)}
+    lm_vals, a_steps = [], []
+    choices = {"ids": [], "frontier": []}
+    wide = C + 1 if follow is None else 16
 
     def layer_tail(x, attn):
         x = gemm(attn, W["wo"], R=x)
         f = silu_mul(gemm(rmsnorm(x, eps=s.eps), W["wgu"]))
         return gemm(f, W["wd"], R=x)
 
-    def head(a):
-        idx, val, _, lse = lmhead(rmsnorm(a, eps=s.eps), W["lm_head"], topk=C + 1)
-        logp = (val[:, :C] - lse[:, None]).astype(np.float32)
-        return idx[:, :C], logp, (val[:, C - 1] - val[:, C]) < gap
+    def head(a, step):
+        idx, val, _, lse = lmhead(rmsnorm(a, eps=s.eps), W["lm_head"], topk=wide)
+        if follow is None:
+            ids, v = idx[:, :C], val[:, :C]
+        else:
+            ids = np.asarray(follow["ids"][step - 1]).reshape(-1, C).astype(np.int32)
+            v = np.full(ids.shape, -np.inf)
+            for r in range(ids.shape[0]):
+                for j in range(C):
+                    hit = np.flatnonzero(idx[r] == ids[r, j])
+                    if len(hit):
+                        v[r, j] = val[r, hit[0]]
+            worst = np.maximum(val[:, C - 1] - v.min(axis=1), 0.0)
+            margin["lm"] = np.maximum(margin["lm"], worst.reshape(B, -1).max(axis=1))
+            lm_vals.append(v.reshape(B, -1, C))
+        logp = (v - lse[:, None]).astype(np.float32)
+        choices["ids"].append(ids.reshape(B, -1, C))
+        return ids, logp, val[:, C - 1] - val[:, C]
+
+    def take(cand, step, start):
+        """The next frontier: own choice, or the followed one (with its margin)."""
+        creation = np.tile(np.arange(start, start + cand.shape[1], dtype=np.int32), (B, 1))
+        own = select_topk(cand, creation, min(C + 1, cand.shape[1]))
+        if follow is None:
+            choices["frontier"].append(own[:, :C])
+            return own[:, :C]
+        order = np.asarray(follow["frontier"][step - 1]).astype(np.int64)
+        chosen = np.zeros(cand.shape, bool)
+        np.put_along_axis(chosen, order, True, 1)
+        if (~chosen).any():
+            lo = np.where(chosen, cand, np.inf).min(axis=1)
+            hi = np.where(chosen, -np.inf, cand).max(axis=1)
+            margin["frontier"] = np.maximum(margin["frontier"], np.maximum(hi - lo, 0.0))
+        return order
 
     # context rows -> draft cache
     x = draft_fuse(ctx_tok.reshape(-1), W["embed"], W["w_fuse"], W["w_in"],
@@ -481,16 +528,18 @@ def draft_tree(shape, W, l, m, h, ctx_tok, gap=GAP_FLAG):
     empty = np.zeros((B, 0, s.Hkv, s.D), x.dtype)
     attn, _ = tree_attn(qr[:, None], empty, empty, cache, np.zeros((B, 1, 1), np.uint64), want_lse=False)
     a_prev = layer_tail(x[last], attn.reshape(B, qd))                      # [B, k]
+    a_root = a_prev
     # step 1: the root's top-k children are the first frontier
-    ids, logp, nb_ = head(a_prev)
-    near |= nb_
+    ids, logp, lm_gap = head(a_prev, 1)
+    # near-ties seen along the way: (gap [B, n], score at stake [B, n])
+    ties = [(lm_gap[:, None], logp[:, C - 1:C].astype(np.float32))]
     pool_score = [logp.astype(np.float32)]                                 # [B, C] per step
-    pool_tok = [ids]
+    pool_tok = [ids.reshape(B, C)]
     pool_par = [np.full((B, C), -1, np.int32)]
-    order = select_topk(logp, np.tile(np.arange(C, dtype=np.int32), (B, 1)), C)
+    order = take(pool_score[0], 1, 0)
     fr_pool = order.astype(np.int32)                                       # pool index of each frontier slot
-    fr_score = np.take_along_axis(logp, order, 1)
-    fr_tok = np.take_along_axis(ids, order, 1)
+    fr_score = np.take_along_axis(pool_score[0], order, 1)
+    fr_tok = np.take_along_axis(pool_tok[0], order, 1)
     fr_arow = np.zeros((B, C), np.int64)                                   # parent's row in a_prev (the root)
     fr_rows = [[[] for _ in range(C)] for _ in range(B)]                   # ancestors' draft rows
     tk = np.zeros((B, (s.steps - 1) * C, s.Hkv, s.D), x.dtype)
@@ -513,17 +562,17 @@ def draft_tree(shape, W, l, m, h, ctx_tok, gap=GAP_FLAG):
                     mask[b, i, r // 64] |= np.uint64(1) << np.uint64(r % 64)
         attn, _ = tree_attn(q.reshape(B, C, s.Hq, s.D), tk, tv, cache, mask, want_lse=False)
         a_prev = layer_tail(xs, attn.reshape(B * C, qd))                   # [B*C, k]
-        ids, logp, nb_ = head(a_prev)
-        near |= nb_.reshape(B, C).any(axis=1)
+        a_steps.append(a_prev)
+        ids, logp, lm_gap = head(a_prev, step)
         cand = (fr_score[:, :, None] + logp.reshape(B, C, C)).astype(np.float32).reshape(B, C * C)
+        ties.append((lm_gap.reshape(B, C), cand.reshape(B, C, C)[:, :, C - 1]))
         pool_score.append(cand)
         pool_tok.append(ids.reshape(B, C * C))
         pool_par.append(np.repeat(fr_pool, C, axis=1))
         creation = np.tile(np.arange(n_pool, n_pool + C * C, dtype=np.int32), (B, 1))
-        order = select_topk(cand, creation, C + 1)
-        srt = np.take_along_axis(cand, order, 1)
-        near |= (srt[:, C - 1] - srt[:, C]) < gap
-        order = order[:, :C]
+        srt = np.take_along_axis(cand, select_topk(cand, creation, C + 1), 1)
+        ties.append(((srt[:, C - 1] - srt[:, C])[:, None], srt[:, C - 1:C]))
+        order = take(cand, step, n_pool)
         new_rows = [[list(fr_rows[b][o // C]) for o in order[b]] for b in range(B)]
         fr_arow = (order // C).astype(np.int64)                           # parent = frontier slot o // C
         fr_pool = (n_pool + order).astype(np.int32)
@@ -534,10 +583,40 @@ def draft_tree(shape, W, l, m, h, ctx_tok, gap=GAP_FLAG):
     ps_all = np.concatenate(pool_score, 1)
     tok_all = np.concatenate(pool_tok, 1)
     par_all = np.concatenate(pool_par, 1)
-    parent, tokens, nb_ = tree_rerank(ps_all, tok_all, par_all, ctx_tok[:, -1], s.n_drafts, gap)
-    near |= nb_
+    N = s.n_drafts
+    if follow is None:
+        parent, tokens, nb_ = tree_rerank(ps_all, tok_all, par_all, ctx_tok[:, -1], N, gap)
+        near |= nb_
+        # A near-tie (the k-th / (k+1)-th child of one node, or the last / first
+        # candidate outside a frontier) may resolve the other way on another
+        # machine. Scores never grow along a path, so it can change the final
+        # tree only if the score at stake is within `gap` of the N-th pool score.
+        theta = select_topk(ps_all, np.tile(np.arange(ps_all.shape[1], dtype=np.int32), (B, 1)), N)
+        theta = np.take_along_axis(ps_all, theta[:, -1:], 1)
+        for g, sc in ties:
+            near |= ((g < gap) & (sc >= theta - gap)).any(axis=1)
+        own = select_topk(ps_all, np.tile(np.arange(ps_all.shape[1], dtype=np.int32), (B, 1)), N)
+        choices["selected"] = np.sort(own, axis=1)
+    else:
+        sel = np.sort(np.asarray(follow["selected"]).astype(np.int64), axis=1)
+        chosen = np.zeros(ps_all.shape, bool)
+        np.put_along_axis(chosen, sel, True, 1)
+        lo = np.where(chosen, ps_all, np.inf).min(axis=1)
+        hi = np.where(chosen, -np.inf, ps_all).max(axis=1)
+        margin["final"] = np.maximum(hi - lo, 0.0)
+        parent = np.full((B, N + 1), -1, np.int32)
+        tokens = np.zeros((B, N + 1), np.int32)
+        for b in range(B):
+            new = {int(c): i + 1 for i, c in enumerate(sel[b])}
+            tokens[b, 0] = ctx_tok[b, -1]
+            for c in sel[b]:
+                pp = int(par_all[b, c])
+                parent[b, new[int(c)]] = 0 if pp < 0 else new.get(pp, -2)   # -2: parent not in the tree
+                tokens[b, new[int(c)]] = tok_all[b, c]
     return dict(parent=parent, tokens=tokens, flagged=near, pool_score=ps_all, pool_token=tok_all,
-                pool_parent=par_all)
+                pool_parent=par_all, x_ctx=x.reshape(B, ctx, k), k_ctx=kr.reshape(B, ctx, s.Hkv, s.D),
+                v_ctx=vr.reshape(B, ctx, s.Hkv, s.D), a_root=a_root, a_steps=a_steps, lm_val=lm_vals,
+                margin=margin, choices=choices)
 
 
 def tree_rerank(pool_score, pool_token, pool_parent, root_token, N, gap=GAP_FLAG):

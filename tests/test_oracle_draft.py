@@ -8,6 +8,9 @@
   (numpy lexsort); closure under parents; a peaked draft degenerates to a chain
   of full depth; the drafted tree has n_drafts nodes, parents before children,
   at most top-k children per node and depth at most the number of steps.
+* Follow mode (used to check another run's choices): following its own
+  choices reproduces its own tree with zero margins; swapping one taken child
+  for the next one down costs exactly that logit gap.
 """
 import numpy as np
 import pytest
@@ -104,7 +107,65 @@ def test_draft_tree_invariants_and_step_pairing(orc):
         for n in range(N + 1):                   # siblings carry distinct tokens (distinct top-k ids)
             kids = np.flatnonzero(par == n)
             assert len(set(tk[kids])) == len(kids) and len(kids) <= s.topk
+    # scores never grow along a path (the premise of the near-tie flag rule)
+    ps, pp = r["pool_score"], r["pool_parent"]
+    for b in range(s.B):
+        has = pp[b] >= 0
+        assert (ps[b][has] <= ps[b][pp[b][has]]).all()
     # row-independence: one sequence alone gives the same tree
     l1, m1, h1, t1 = synth.draft_inputs(s, 0, batch=slice(3, 4))
     r1 = orc.draft_tree(s, W, l1, m1, h1, t1)
     assert np.array_equal(r1["parent"][0], r["parent"][3]) and np.array_equal(r1["tokens"][0], r["tokens"][3])
+
+
+def test_follow_mode_margins(orc):
+    s = synth.DRAFT_SMALL
+    W = synth.draft_weights(s)
+    l, m, h, tok = synth.draft_inputs(s, 1)
+    r = orc.draft_tree(s, W, l, m, h, tok)
+    f = orc.draft_tree(s, W, l, m, h, tok, follow=r["choices"])
+    assert np.array_equal(f["parent"], r["parent"]) and np.array_equal(f["tokens"], r["tokens"])
+    assert np.array_equal(f["pool_score"], r["pool_score"])
+    assert all((v == 0).all() for v in f["margin"].values())
+    # swap, at the last step, the 10th child of sequence 0's first frontier node for the 11th
+    idx, val, _, _ = orc.lmhead(orc.rmsnorm(r["a_steps"][-1][:1], eps=s.eps), W["lm_head"], topk=s.topk + 1)
+    ids = [a.copy() for a in r["choices"]["ids"]]
+    ids[-1][0, 0, s.topk - 1] = idx[0, s.topk]
+    g = orc.draft_tree(s, W, l, m, h, tok, follow=dict(r["choices"], ids=ids))
+    assert g["margin"]["lm"][0] == val[0, s.topk - 1] - val[0, s.topk] > 0
+    assert (g["margin"]["lm"][1:] == 0).all()
+    # a final selection that drops the best entry for a worse one
+    sel = r["choices"]["selected"].copy()
+    ps = r["pool_score"][2]
+    best = int(np.argmax(ps))
+    out = int(np.flatnonzero(~np.isin(np.arange(len(ps)), sel[2]))[0])
+    sel[2][sel[2] == best] = out
+    sel[2].sort()
+    h2 = orc.draft_tree(s, W, l, m, h, tok, follow=dict(r["choices"], selected=sel))
+    assert h2["margin"]["final"][2] >= ps[best] - ps[out] > 0 and h2["margin"]["final"][0] == 0
+
+
+def test_bf16_draft_logits_move_with_last_bit_noise(orc):
+    """With bf16 storage at every layer boundary, flipping the last bit of 1%
+    of one input tensor moves the oracle's own draft logits along fixed
+    choices by several 1e-2: other correct bf16 arithmetic lands anywhere in
+    that band, so GPU draft trees are compared by replaying their choices, not
+    bit for bit. Last-bit noise in fp32 storage moves them by less than 1e-4."""
+    s = synth.DRAFT_SMALL
+    W = synth.draft_weights(s)
+    l, m, h, tok = synth.draft_inputs(s, 0)
+    r = orc.draft_tree(s, W, l, m, h, tok)
+    noisy = l.copy()
+    noisy[np.random.default_rng(5).random(l.shape) < 0.01] ^= np.uint16(1)
+    f = orc.draft_tree(s, W, noisy, m, h, tok, follow=r["choices"])
+    moved = max(np.abs(a - b).max() for a, b in zip(f["lm_val"], orc.draft_tree(s, W, l, m, h, tok,
+                                                                                  follow=r["choices"])["lm_val"]))
+    assert moved > 0.03
+    cv = lambda a: synth.bf16_to_f32(a)  # noqa: E731
+    W32 = {k: cv(v) for k, v in W.items()}
+    r32 = orc.draft_tree(s, W32, cv(l), cv(m), cv(h), tok)
+    n32 = cv(l).copy()
+    n32.view(np.uint32)[np.random.default_rng(5).random(l.shape) < 0.01] ^= np.uint32(1)
+    f32 = orc.draft_tree(s, W32, n32, cv(m), cv(h), tok, follow=r32["choices"])
+    g32 = orc.draft_tree(s, W32, cv(l), cv(m), cv(h), tok, follow=r32["choices"])
+    assert max(np.abs(a - b).max() for a, b in zip(f32["lm_val"], g32["lm_val"])) < 1e-4

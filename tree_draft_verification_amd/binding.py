@@ -67,6 +67,7 @@ _silu_mul = _sig("eagle3_silu_mul", I, P, I, I, I, P, P)
 _rope = _sig("eagle3_rope", I, P, I, I, I, I, P, I, F, I, P)
 _embed = _sig("eagle3_embed", I, P, P, I, I, I, I, P, P)
 _commit_kv = _sig("eagle3_commit_kv", I, P, P, I, P, I, I, I, I, I, P, P, P, I, I, P, P)
+_copy_rows = _sig("eagle3_copy_rows", I, P, P, I, P, P, I, I, SZ, P)
 _draft_fuse_ws = _sig("eagle3_draft_fuse_workspace", SZ, I, I, I)
 _draft_fuse = _sig("eagle3_draft_fuse", I, P, P, P, P, P, P, P, P, I, I, I, I, P, P, P, SZ, P)
 _tree_expand = _sig("eagle3_tree_expand", I, P, P, P, I, I, P, P, P, I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P)
@@ -210,10 +211,21 @@ def eagle3_embed(E, ids, out, stream=None):
     _check(_embed(_ptr(E), _ptr(ids), M, K, V, _dtype(E), _ptr(out), _stream(stream)), "eagle3_embed")
 
 
-def eagle3_commit_kv(k_rows, v_rows, src, start, k_cache, v_cache, block_table, stream=None):
-    """k_rows/v_rows [B, rows, Hkv, D]; src [B, max_n] int32 (-1 ends a list)."""
+def eagle3_copy_rows(src, dst, n, src_rows=None, dst_rows=None, stream=None):
+    """dst[dst_rows[i]] = src[src_rows[i]] for i < n (rows = first dimension)."""
+    rb = src[0].numel() * src.element_size()
+    if dst[0].numel() * dst.element_size() != rb:
+        raise ValueError("row sizes differ")
+    _check(_copy_rows(_ptr(src), _ptr(src_rows), src.shape[0], _ptr(dst), _ptr(dst_rows), dst.shape[0], int(n), rb,
+                      _stream(stream)), "eagle3_copy_rows")
+
+
+def eagle3_commit_kv(k_rows, v_rows, src, start, k_cache, v_cache, block_table, max_n=None, stream=None):
+    """k_rows/v_rows [B, rows, Hkv, D]; src [B, max_n] int32 (-1 ends a list),
+    or None for rows 0..max_n-1."""
     B, rows, Hkv, D = k_rows.shape
-    _check(_commit_kv(_ptr(k_rows), _ptr(v_rows), rows, _ptr(src), src.shape[1], B, Hkv, D, _dtype(k_rows),
+    max_n = src.shape[1] if src is not None else int(max_n if max_n is not None else rows)
+    _check(_commit_kv(_ptr(k_rows), _ptr(v_rows), rows, _ptr(src), max_n, B, Hkv, D, _dtype(k_rows),
                       _ptr(k_cache), _ptr(v_cache), _ptr(block_table), block_table.shape[1], k_cache.shape[0],
                       _ptr(start), _stream(stream)), "eagle3_commit_kv")
 

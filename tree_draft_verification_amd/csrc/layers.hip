@@ -245,8 +245,9 @@ __global__ __launch_bounds__(256) void embed_kernel(const uint4 *__restrict__ E,
 
 // Append rows to the paged cache: for sequence b, rows src[b][0..] (indices
 // into k_rows/v_rows [B, rows_per_seq, Hkv, D]; the list ends at the first
-// negative entry or after max_n) land at positions start[b] + j. Cache
-// layouts: K [blk][Hkv][16][D], V [blk][Hkv][D][16].
+// negative entry or after max_n; a null list means rows 0..max_n-1) land at
+// positions start[b] + j. Cache layouts: K [blk][Hkv][16][D], V [blk][Hkv][D][16].
+// One work-group per (entry j, sequence b).
 template <bool BF16>
 __global__ __launch_bounds__(256) void commit_kv_kernel(const void *__restrict__ k_rows, const void *__restrict__ v_rows,
                                                         int rows_per_seq, const int32_t *__restrict__ src, int max_n,
@@ -254,28 +255,48 @@ __global__ __launch_bounds__(256) void commit_kv_kernel(const void *__restrict__
                                                         void *__restrict__ v_cache,
                                                         const int32_t *__restrict__ block_table, int max_blocks,
                                                         int num_blocks, const int32_t *__restrict__ start) {
-    const int b = blockIdx.y;
-    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= (size_t)max_n * Hkv * D) return;
-    const int d = (int)(i % D), h = (int)((i / D) % Hkv), j = (int)(i / ((size_t)D * Hkv));
-    const int32_t *s = src + (size_t)b * max_n;
-    for (int q = 0; q <= j; ++q)
-        if (s[q] < 0) return;  // the list ended before entry j
-    const int r = min(s[j], rows_per_seq - 1);
+    const int j = blockIdx.x, b = blockIdx.y;
+    int r = j;
+    if (src) {
+        const int32_t *s = src + (size_t)b * max_n;
+        int ended = 0;
+        for (int q = threadIdx.x; q <= j; q += blockDim.x) ended |= s[q] < 0;
+        if (__syncthreads_or(ended)) return;  // the list ended before entry j
+        r = s[j];
+    }
+    r = min(r, rows_per_seq - 1);
     const int posn = start[b] + j;
     if (posn < 0 || posn >= max_blocks * 16) return;
     const int blk = min(max(block_table[(size_t)b * max_blocks + posn / 16], 0), num_blocks - 1);
     const int slot = posn % 16;
-    const size_t srow = (((size_t)b * rows_per_seq + r) * Hkv + h) * D + d;
-    const size_t kdst = (((size_t)blk * Hkv + h) * 16 + slot) * D + d;
-    const size_t vdst = (((size_t)blk * Hkv + h) * D + d) * 16 + slot;
-    if (BF16) {
-        ((uint16_t *)k_cache)[kdst] = ((const uint16_t *)k_rows)[srow];
-        ((uint16_t *)v_cache)[vdst] = ((const uint16_t *)v_rows)[srow];
-    } else {
-        ((float *)k_cache)[kdst] = ((const float *)k_rows)[srow];
-        ((float *)v_cache)[vdst] = ((const float *)v_rows)[srow];
+    for (int i = threadIdx.x; i < Hkv * D; i += blockDim.x) {
+        const int d = i % D, h = i / D;
+        const size_t srow = (((size_t)b * rows_per_seq + r) * Hkv + h) * D + d;
+        const size_t kdst = (((size_t)blk * Hkv + h) * 16 + slot) * D + d;
+        const size_t vdst = (((size_t)blk * Hkv + h) * D + d) * 16 + slot;
+        if (BF16) {
+            ((uint16_t *)k_cache)[kdst] = ((const uint16_t *)k_rows)[srow];
+            ((uint16_t *)v_cache)[vdst] = ((const uint16_t *)v_rows)[srow];
+        } else {
+            ((float *)k_cache)[kdst] = ((const float *)k_rows)[srow];
+            ((float *)v_cache)[vdst] = ((const float *)v_rows)[srow];
+        }
     }
+}
+
+// dst[dst_rows[i]] = src[src_rows[i]] for i < n, 16 bytes per thread; a null
+// table is the identity; rows outside [0, nrows) are skipped.
+__global__ __launch_bounds__(256) void copy_rows_kernel(const uint4 *__restrict__ src,
+                                                        const int32_t *__restrict__ src_rows, int src_nrows,
+                                                        uint4 *__restrict__ dst, const int32_t *__restrict__ dst_rows,
+                                                        int dst_nrows, int n, int row_vec) {
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (size_t)n * row_vec) return;
+    const int m = (int)(i / row_vec), c = (int)(i % row_vec);
+    const int sr = src_rows ? src_rows[m] : m;
+    const int dr = dst_rows ? dst_rows[m] : m;
+    if (sr < 0 || sr >= src_nrows || dr < 0 || dr >= dst_nrows) return;
+    dst[(size_t)dr * row_vec + c] = src[(size_t)sr * row_vec + c];
 }
 
 unsigned grid1(size_t n) { return (unsigned)((n + 255) / 256); }
@@ -368,8 +389,9 @@ extern "C" int eagle3_commit_kv(const void *k_rows, const void *v_rows, int rows
         return EAGLE3_ERR_ARG;
     if (dtype != EAGLE3_BF16 && dtype != EAGLE3_F32) return EAGLE3_ERR_UNSUPPORTED;
     if (B == 0 || max_n == 0) return EAGLE3_OK;
-    if (!k_rows || !v_rows || !src || !k_cache || !v_cache || !block_table || !start) return EAGLE3_ERR_ARG;
-    dim3 grid(grid1((size_t)max_n * Hkv * D), B);
+    if (!k_rows || !v_rows || !k_cache || !v_cache || !block_table || !start) return EAGLE3_ERR_ARG;
+    if (B > 65535) return EAGLE3_ERR_UNSUPPORTED;
+    dim3 grid(max_n, B);
     if (dtype == EAGLE3_BF16)
         commit_kv_kernel<true><<<grid, 256, 0, e3_stream(stream)>>>(k_rows, v_rows, rows_per_seq, src, max_n, Hkv, D,
                                                                    k_cache, v_cache, block_table, max_blocks,
@@ -378,6 +400,19 @@ extern "C" int eagle3_commit_kv(const void *k_rows, const void *v_rows, int rows
         commit_kv_kernel<false><<<grid, 256, 0, e3_stream(stream)>>>(k_rows, v_rows, rows_per_seq, src, max_n, Hkv, D,
                                                                     k_cache, v_cache, block_table, max_blocks,
                                                                     num_blocks, start);
+    E3_LAUNCH_CHECK();
+    return EAGLE3_OK;
+}
+
+extern "C" int eagle3_copy_rows(const void *src, const int32_t *src_rows, int src_nrows, void *dst,
+                                const int32_t *dst_rows, int dst_nrows, int n, size_t row_bytes, void *stream) {
+    if (n < 0 || src_nrows < 0 || dst_nrows < 0 || row_bytes == 0) return EAGLE3_ERR_ARG;
+    if (row_bytes % 16 != 0 || row_bytes / 16 > 0x7fffffff) return EAGLE3_ERR_UNSUPPORTED;
+    if (n == 0) return EAGLE3_OK;
+    if (!src || !dst || !e3_aligned16(src) || !e3_aligned16(dst)) return EAGLE3_ERR_ARG;
+    const int row_vec = (int)(row_bytes / 16);
+    copy_rows_kernel<<<grid1((size_t)n * row_vec), 256, 0, e3_stream(stream)>>>(
+        (const uint4 *)src, src_rows, src_nrows, (uint4 *)dst, dst_rows, dst_nrows, n, row_vec);
     E3_LAUNCH_CHECK();
     return EAGLE3_OK;
 }
