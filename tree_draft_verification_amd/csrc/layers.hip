@@ -16,10 +16,19 @@ namespace {
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-constexpr int GBM = 128, GBN = 128, GBK = 64, GNS = 3;
-constexpr int G_ASTAGE = GBM * 128, G_BSTAGE = GBN * 128;  // bytes: 64 bf16 per row
-constexpr int G_STAGE = G_ASTAGE + G_BSTAGE;
-constexpr int G_LOADS = G_STAGE / 1024 / 4;                 // 1 KB DMA loads per wave per stage
+// bf16 GEMM tiles: BM x 256 outputs per 256-thread work-group (BM = 256 or
+// 128), waves 2 x 2, each (BM/2) x 128 in 32 x 32 MFMA blocks. K advances in
+// chunks of 32 through a 4-stage LDS ring filled by 16-byte global_load_lds
+// (three chunks in flight while one is multiplied).
+constexpr int GBN = 256, GBK = 32, GNS = 4, GROW = GBK * 2;  // LDS row: 32 bf16 = 64 B
+constexpr int GSEG_ALIGN = 64;                                 // segment widths are multiples of this
+
+template <int BM>
+struct GTile {
+    static constexpr int STAGE = (BM + GBN) * GROW;  // bytes per ring stage
+    static constexpr int LOADS = STAGE / 1024 / 4;   // 1 KB DMA loads per wave per stage
+    static constexpr int MB = BM / 64, NB = GBN / 64;  // 32 x 32 blocks per wave
+};
 
 struct GemmParams {
     const void *a[3];
@@ -31,9 +40,13 @@ struct GemmParams {
     const void *res;
     void *c;
     int M, N, K, ldc, a_nrows[3];
+    int mt, nt;  // tile counts
 };
 
-__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
+// 16-byte column of a 64-byte LDS row, XOR-swizzled so that the 32 rows an
+// MFMA operand read touches spread over all banks (16 consecutive rows land
+// on 16 distinct 16-byte slots of a 256-byte window, 8 rows on 8 slots of 128)
+__device__ __forceinline__ int gswz(int row) { return (row ^ (row >> 2)) & 3; }
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -41,55 +54,103 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-// C[M, N] = A[M, K] . B[N, K]^T (+ R), bf16 in/out, fp32 accumulate.
-// One 256-thread work-group per 128 x 128 output tile; waves as 2 x 2, each
-// 64 x 64 (2 x 2 MFMA blocks). A and B chunks (64 k) go straight to a 3-stage
-// LDS ring by 16-byte global_load_lds; rows XOR-swizzled at 16 B.
+// wait until at most N LDS reads are outstanding; the fragments are tied to
+// the wait so no use of them can be scheduled above it
+template <int N, int MB>
+__device__ __forceinline__ void lgkm_wait(u32x4_t *av, u32x4_t *bv) {
+    static_assert(MB == 2 || MB == 4, "fragment count");
+    if constexpr (MB == 4) {
+        __asm__ volatile("s_waitcnt lgkmcnt(%8)"
+                         : "+v"(av[0]), "+v"(av[1]), "+v"(av[2]), "+v"(av[3]), "+v"(bv[0]), "+v"(bv[1]),
+                           "+v"(bv[2]), "+v"(bv[3])
+                         : "i"(N));
+    } else {
+        __asm__ volatile("s_waitcnt lgkmcnt(%6)"
+                         : "+v"(av[0]), "+v"(av[1]), "+v"(bv[0]), "+v"(bv[1]), "+v"(bv[2]), "+v"(bv[3])
+                         : "i"(N));
+    }
+}
+
+// Work-group id -> output tile. Work-groups are dealt to the 8 XCDs in turn;
+// give each XCD a contiguous run of tiles, ordered N-fastest within groups of
+// 8 M-tiles, so the tiles one XCD runs together share A rows and B rows in its L2.
+__device__ __forceinline__ void tile_of(int L, int nwg, int MT, int NT, int &mt, int &nt) {
+    const int q = nwg >> 3, r = nwg & 7, x = L & 7, j = L >> 3;
+    const int t = (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + j;
+    const int G = 8, gsz_full = G * NT;
+    const int g = t / gsz_full, first = g * G, gs = min(G, MT - first);
+    const int u = t - g * gsz_full;
+    mt = first + u % gs;
+    nt = u / gs;
+}
+
+// C[M, N] = A[M, K] . B[N, K]^T (+ R), bf16 in/out, fp32 accumulate. A is up
+// to three K-segments, each optionally row-gathered.
+template <int BM>
 __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmParams p) {
-    __shared__ __attribute__((aligned(1024))) unsigned char ring[GNS * G_STAGE];
-    __shared__ int arow[3][GBM];  // gathered A row of each tile row, per segment
-    const int mt = blockIdx.x, nt = blockIdx.y;
-    const int m0 = mt * GBM, n0 = nt * GBN;
+    using T = GTile<BM>;
+    __shared__ __attribute__((aligned(1024))) unsigned char ring[GNS * T::STAGE];
+    __shared__ int arow[3][BM];  // source row of each tile row, per segment
+    int mt, nt;
+    tile_of(blockIdx.x, gridDim.x, p.mt, p.nt, mt, nt);
+    const int m0 = mt * BM, n0 = nt * GBN;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int lr = lane & 31, lh = lane >> 5;
 
-    for (int i = tid; i < 3 * GBM; i += 256) {
-        const int s = i / GBM, r = i % GBM;
+    for (int i = tid; i < 3 * BM; i += 256) {
+        const int s = i / BM, r = i % BM;
         int m = min(m0 + r, p.M - 1);
         if (s < p.nseg && p.a_rows[s]) m = min(max(p.a_rows[s][m], 0), p.a_nrows[s] - 1);
         arow[s][r] = m;
     }
     __syncthreads();
 
-    // this lane's load j covers stage block blk = wave * G_LOADS + j (8 rows of 128 B);
-    // blocks 0..15 are A rows, 16..31 B rows; lane fills row 8 blk + lane / 8, column lane % 8
-    const int col = lane & 7;
-    auto issue = [&](int stage, int kc) {
-        unsigned char *base = ring + stage * G_STAGE;
-        int seg = 0;
-        while (seg + 1 < p.nseg && kc >= p.kofs[seg + 1]) ++seg;  // chunk kc lies in one segment
+    // load j of this wave fills stage block blk = wave * LOADS + j (16 rows of
+    // 64 B; A rows first, then B rows); lane -> row 16 blk + lane / 4, slot lane % 4.
+    // Source pointers are formed once per A segment; a chunk only adds its k offset.
+    const int slot = lane & 3;
+    const uint16_t *src_base[T::LOADS];
+    int seg = 0;
+    // segment fields by constant index only (a run-time index would turn
+    // these kernel-argument reads into per-chunk memory loads)
+    const int kofs1 = p.nseg > 1 ? p.kofs[1] : 0x7fffffff, kofs2 = p.nseg > 2 ? p.kofs[2] : 0x7fffffff;
+    auto set_bases = [&](int sg) {
+        const uint16_t *aseg = (const uint16_t *)(sg == 0 ? p.a[0] : sg == 1 ? p.a[1] : p.a[2]);
+        const int kseg = sg == 0 ? p.k[0] : sg == 1 ? p.k[1] : p.k[2];
+        const int oseg = sg == 0 ? 0 : sg == 1 ? kofs1 : kofs2;
 #pragma unroll
-        for (int j = 0; j < G_LOADS; ++j) {
-            const int blk = wave * G_LOADS + j;
-            const void *src;
-            if (blk < G_ASTAGE / 1024) {
-                const int row = blk * 8 + lane / 8;
-                src = (const uint16_t *)p.a[seg] + (size_t)arow[seg][row] * p.k[seg] + (kc - p.kofs[seg]) +
-                      8 * (col ^ swz(row));
+        for (int j = 0; j < T::LOADS; ++j) {
+            const int blk = wave * T::LOADS + j;
+            const int row = blk * 16 + (lane >> 2);
+            if (row < BM) {
+                src_base[j] = aseg + (size_t)arow[sg][row] * kseg - oseg + 8 * (slot ^ gswz(row));
             } else {
-                const int row = (blk - G_ASTAGE / 1024) * 8 + lane / 8;
-                const int n = min(n0 + row, p.N - 1);
-                src = (const uint16_t *)p.b + (size_t)n * p.K + kc + 8 * (col ^ swz(row));
+                const int n = min(n0 + row - BM, p.N - 1);
+                src_base[j] = (const uint16_t *)p.b + (size_t)n * p.K + 8 * (slot ^ gswz(row));
             }
-            __builtin_amdgcn_global_load_lds(src, (lds_void_t *)(base + blk * 1024), 16, 0, 0);
+        }
+    };
+    set_bases(0);
+    // B rows use the full K offset kc; A rows the offset within the segment (kofs folded into the base)
+    auto issue = [&](int stage, int kc) {
+        const int sg = kc >= kofs2 ? 2 : kc >= kofs1 ? 1 : 0;  // chunks arrive in k order
+        if (sg != seg) {
+            seg = sg;
+            set_bases(seg);
+        }
+        unsigned char *base = ring + stage * T::STAGE;
+#pragma unroll
+        for (int j = 0; j < T::LOADS; ++j) {
+            const int blk = wave * T::LOADS + j;
+            __builtin_amdgcn_global_load_lds((const void *)(src_base[j] + kc), (lds_void_t *)(base + blk * 1024), 16, 0, 0);
         }
     };
 
-    f32x16_t acc[2][2];
+    f32x16_t acc[T::MB][T::NB];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < T::MB; ++i)
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj)
+        for (int jj = 0; jj < T::NB; ++jj)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][jj][r] = 0.f;
 
@@ -98,49 +159,90 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmParams p) {
     for (int st = 0; st < GNS - 1; ++st)
         if (st < nch) issue(st, st * GBK);
     const int wm = wave >> 1, wn = wave & 1;
-    for (int c = 0; c < nch; ++c) {
-        if (c + GNS - 2 < nch) wait_vmcnt<(GNS - 2) * G_LOADS>();
+    // per-lane LDS byte offsets of the operand rows (sub-step 0 and 1 differ by the column)
+    int aoff[T::MB][2], boff[T::NB][2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        const int cl = 2 * s + lh;  // both operands take k = 16 s + 8 lh .. +7 of the chunk
+#pragma unroll
+        for (int mb = 0; mb < T::MB; ++mb) {
+            const int row = wm * (BM / 2) + mb * 32 + lr;
+            aoff[mb][s] = row * GROW + ((cl ^ gswz(row)) << 4);
+        }
+#pragma unroll
+        for (int nb = 0; nb < T::NB; ++nb) {
+            const int row = wn * 128 + nb * 32 + lr;
+            boff[nb][s] = BM * GROW + row * GROW + ((cl ^ gswz(row)) << 4);
+        }
+    }
+    auto wait_chunk = [&](int c) {  // chunk c has landed in LDS for every wave
+        const int ahead = min(nch - 1 - c, GNS - 2);
+        if (ahead >= 2) wait_vmcnt<2 * T::LOADS>();
+        else if (ahead == 1) wait_vmcnt<T::LOADS>();
         else wait_vmcnt<0>();
-        // bare barrier: a fenced one would drain the stages still in flight
+        // bare barrier: a fenced one would drain the chunks still in flight
         __builtin_amdgcn_s_barrier();
         __asm__ volatile("" ::: "memory");
-        if (c + GNS - 1 < nch) issue((c + GNS - 1) % GNS, (c + GNS - 1) * GBK);
-        const unsigned char *ab = ring + (c % GNS) * G_STAGE;
-        const unsigned char *bb = ab + G_ASTAGE;
+    };
+    u32x4_t av0[T::MB], bv0[T::NB], av1[T::MB], bv1[T::NB];
+    // Fragment reads are issued as inline ds_read_b128: the compiler cannot
+    // tell ring slots apart and would otherwise wait for every LDS DMA still
+    // in flight before each read. Completion is awaited explicitly (lgkm).
+    const uint32_t ring_lds = (uint32_t)(uintptr_t)(lds_void_t *)ring;
+    auto read = [&](int slotk, int s, u32x4_t *av, u32x4_t *bv) {
+        const uint32_t base = ring_lds + slotk * T::STAGE;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const int cl = 4 * lh + s;  // both operands take k = 32 lh + 8 s .. +7 of the chunk
-            u32x4_t av[2], bv[2];
+        for (int mb = 0; mb < T::MB; ++mb)
+            __asm__ volatile("ds_read_b128 %0, %1" : "=v"(av[mb]) : "v"(base + aoff[mb][s]));
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb) {
-                const int row = wm * 64 + mb * 32 + lr;
-                av[mb] = *reinterpret_cast<const u32x4_t *>(ab + row * 128 + ((cl ^ swz(row)) << 4));
-            }
+        for (int nb = 0; nb < T::NB; ++nb)
+            __asm__ volatile("ds_read_b128 %0, %1" : "=v"(bv[nb]) : "v"(base + boff[nb][s]));
+    };
+    auto mma = [&](const u32x4_t *av, const u32x4_t *bv) {
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb) {
-                const int row = wn * 64 + nb * 32 + lr;
-                bv[nb] = *reinterpret_cast<const u32x4_t *>(bb + row * 128 + ((cl ^ swz(row)) << 4));
-            }
+        for (int mb = 0; mb < T::MB; ++mb)
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-                for (int nb = 0; nb < 2; ++nb)
-                    acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, av[mb]),
-                                                                          __builtin_bit_cast(bf16x8_t, bv[nb]),
-                                                                          acc[mb][nb], 0, 0, 0);
+            for (int nb = 0; nb < T::NB; ++nb)
+                acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, av[mb]),
+                                                                      __builtin_bit_cast(bf16x8_t, bv[nb]),
+                                                                      acc[mb][nb], 0, 0, 0);
+    };
+    // software pipeline: the fragments of the next half-chunk are read while
+    // the MFMAs of the current one run; the barrier that hands a ring slot
+    // back to the loads sits between two MFMA groups
+    constexpr int NRD = T::MB + T::NB;  // LDS reads per half-chunk
+    if (nch > 0) {
+        wait_chunk(0);
+        if (GNS - 1 < nch) issue(GNS - 1, (GNS - 1) * GBK);
+        read(0, 0, av0, bv0);
+    }
+    for (int c = 0; c < nch; ++c) {
+        read(c % GNS, 1, av1, bv1);
+        lgkm_wait<NRD, T::MB>(av0, bv0);
+        mma(av0, bv0);
+        if (c + 1 < nch) {
+            // every wave's reads of chunk c are done before its slot is refilled
+            lgkm_wait<0, T::MB>(av1, bv1);
+            wait_chunk(c + 1);
+            if (c + GNS < nch) issue(c % GNS, (c + GNS) * GBK);
+            read((c + 1) % GNS, 0, av0, bv0);
+            lgkm_wait<NRD, T::MB>(av1, bv1);
+        } else {
+            lgkm_wait<0, T::MB>(av1, bv1);
         }
+        mma(av1, bv1);
     }
     // D[m][n]: lane holds n = lr of its block, m = 8 (r / 4) + 4 lh + r % 4
     const uint16_t *res = (const uint16_t *)p.res;
     uint16_t *cc = (uint16_t *)p.c;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < T::MB; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
+        for (int nb = 0; nb < T::NB; ++nb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int m = m0 + wm * 64 + mb * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-                const int n = n0 + wn * 64 + nb * 32 + lr;
+                const int m = m0 + wm * (BM / 2) + mb * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+                const int n = n0 + wn * 128 + nb * 32 + lr;
                 if (m < p.M && n < p.N) {
                     float v = acc[mb][nb][r];
                     if (res) v += e3_bf16_to_f32(res[(size_t)m * p.ldc + n]);
@@ -316,7 +418,8 @@ extern "C" int eagle3_gemm(const eagle3_gemm_args *a, void *stream) {
     for (int s = 0; s < a->nseg; ++s) {
         if (!a->a[s] || a->k[s] < 1) return EAGLE3_ERR_ARG;
         if (a->a_rows[s] && a->a_nrows[s] < 1) return EAGLE3_ERR_ARG;
-        if (a->dtype == EAGLE3_BF16 && (a->k[s] % GBK != 0 || !e3_aligned16(a->a[s]))) return EAGLE3_ERR_UNSUPPORTED;
+        if (a->dtype == EAGLE3_BF16 && (a->k[s] % GSEG_ALIGN != 0 || !e3_aligned16(a->a[s])))
+            return EAGLE3_ERR_UNSUPPORTED;
         p.a[s] = a->a[s];
         p.a_rows[s] = a->a_rows[s];
         p.a_nrows[s] = a->a_rows[s] ? a->a_nrows[s] : a->M;
@@ -329,8 +432,16 @@ extern "C" int eagle3_gemm(const eagle3_gemm_args *a, void *stream) {
     p.M = a->M; p.N = a->N; p.K = K; p.ldc = ldc;
     const hipStream_t st = e3_stream(stream);
     if (a->dtype == EAGLE3_BF16) {
-        dim3 grid((a->M + GBM - 1) / GBM, (a->N + GBN - 1) / GBN);
-        gemm_bf16_kernel<<<grid, 256, 0, st>>>(p);
+        // 256-row tiles once they fill the chip, 128-row tiles below that
+        const int nt = (a->N + GBN - 1) / GBN;
+        const int mt256 = (a->M + 255) / 256;
+        if ((long)mt256 * nt >= 256) {
+            p.mt = mt256; p.nt = nt;
+            gemm_bf16_kernel<256><<<mt256 * nt, 256, 0, st>>>(p);
+        } else {
+            p.mt = (a->M + 127) / 128; p.nt = nt;
+            gemm_bf16_kernel<128><<<p.mt * nt, 256, 0, st>>>(p);
+        }
     } else {
         dim3 grid((a->M + 15) / 16, (a->N + 15) / 16);
         gemm_f32_kernel<<<grid, 256, 0, st>>>(p);
