@@ -58,7 +58,10 @@ def compare(orc, h, w, topk, got, want_lse, tol=1e-4):
     return int((~clean).sum())
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 5000, 512), (61, 4103, 512), (183, 3001, 1024), (64, 8192, 4096)])
+# M >= 128 runs the head as a GEMM of 256 x 256 tiles: 183, 300 and 640 give
+# ragged hidden tiles, 3001 and 2049 ragged vocabulary tiles
+@pytest.mark.parametrize("M,N,K", [(1, 5000, 512), (61, 4103, 512), (183, 3001, 1024), (64, 8192, 4096),
+                                   (300, 3001, 512), (640, 2049, 256)])
 @pytest.mark.parametrize("topk", [1, 2, 10, 16])
 def test_bf16_parity(orc, lib, M, N, K, topk):
     rng = np.random.default_rng(M * 7 + N + topk)

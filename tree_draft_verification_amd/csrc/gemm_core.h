@@ -1,0 +1,233 @@
+// bf16 GEMM core shared by the dense layers and the large-batch LM head:
+// C = A . B^T over one output tile, A [M, K] (up to three K-segments, each
+// optionally row-gathered) and B [N, K], both k-contiguous; fp32 accumulators
+// stay in registers for the caller's epilogue.
+#pragma once
+#include "common.h"
+
+namespace e3g {
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// bf16 GEMM tiles: BM x 256 outputs per 256-thread work-group (BM = 256 or
+// 128), waves 2 x 2, each (BM/2) x 128 in 32 x 32 MFMA blocks. K advances in
+// chunks of 32 through a 4-stage LDS ring filled by 16-byte global_load_lds
+// (three chunks in flight while one is multiplied).
+constexpr int GBN = 256, GBK = 32, GNS = 4, GROW = GBK * 2;  // LDS row: 32 bf16 = 64 B
+constexpr int GSEG_ALIGN = 64;                                 // segment widths are multiples of this
+
+template <int BM>
+struct GTile {
+    static constexpr int STAGE = (BM + GBN) * GROW;  // bytes per ring stage
+    static constexpr int LOADS = STAGE / 1024 / 4;   // 1 KB DMA loads per wave per stage
+    static constexpr int MB = BM / 64, NB = GBN / 64;  // 32 x 32 blocks per wave
+};
+
+struct GemmParams {
+    const void *a[3];
+    const int32_t *a_rows[3];
+    int k[3];
+    int kofs[3];
+    int nseg;
+    const void *b;
+    const void *res;
+    void *c;
+    int M, N, K, ldc, a_nrows[3];
+    int mt, nt;  // tile counts
+};
+
+// 16-byte column of a 64-byte LDS row, XOR-swizzled so that the 32 rows an
+// MFMA operand read touches spread over all banks (16 consecutive rows land
+// on 16 distinct 16-byte slots of a 256-byte window, 8 rows on 8 slots of 128)
+__device__ __forceinline__ int gswz(int row) { return (row ^ (row >> 2)) & 3; }
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// wait until at most N LDS reads are outstanding; the fragments are tied to
+// the wait so no use of them can be scheduled above it
+template <int N, int MB>
+__device__ __forceinline__ void lgkm_wait(u32x4_t *av, u32x4_t *bv) {
+    static_assert(MB == 2 || MB == 4, "fragment count");
+    if constexpr (MB == 4) {
+        __asm__ volatile("s_waitcnt lgkmcnt(%8)"
+                         : "+v"(av[0]), "+v"(av[1]), "+v"(av[2]), "+v"(av[3]), "+v"(bv[0]), "+v"(bv[1]),
+                           "+v"(bv[2]), "+v"(bv[3])
+                         : "i"(N));
+    } else {
+        __asm__ volatile("s_waitcnt lgkmcnt(%6)"
+                         : "+v"(av[0]), "+v"(av[1]), "+v"(bv[0]), "+v"(bv[1]), "+v"(bv[2]), "+v"(bv[3])
+                         : "i"(N));
+    }
+}
+
+// Work-group id -> output tile. Work-groups are dealt to the 8 XCDs in turn;
+// give each XCD a contiguous run of tiles, ordered N-fastest within groups of
+// 8 M-tiles, so the tiles one XCD runs together share A rows and B rows in its L2.
+__device__ __forceinline__ void tile_of(int L, int nwg, int MT, int NT, int &mt, int &nt) {
+    const int q = nwg >> 3, r = nwg & 7, x = L & 7, j = L >> 3;
+    const int t = (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + j;
+    const int G = 8, gsz_full = G * NT;
+    const int g = t / gsz_full, first = g * G, gs = min(G, MT - first);
+    const int u = t - g * gsz_full;
+    mt = first + u % gs;
+    nt = u / gs;
+}
+
+// Source row of each tile row, per segment (rows past M clamp to M - 1; their
+// results are dropped by the epilogue).
+template <int BM>
+__device__ __forceinline__ void fill_arow(const GemmParams &p, int m0, int (*arow)[BM]) {
+    for (int i = threadIdx.x; i < 3 * BM; i += 256) {
+        const int s = i / BM, r = i % BM;
+        int m = min(m0 + r, p.M - 1);
+        if (s < p.nseg && p.a_rows[s]) m = min(max(p.a_rows[s][m], 0), p.a_nrows[s] - 1);
+        arow[s][r] = m;
+    }
+    __syncthreads();
+}
+
+// The K loop of one BM x 256 tile at (m0, n0). ring: GNS * GTile<BM>::STAGE
+// bytes of LDS (1 KB aligned). On return acc holds the tile: wave (wm, wn) =
+// (wave / 2, wave % 2), block (mb, nb), register r of lane (lr, lh) is
+// C[m0 + wm BM/2 + 32 mb + 8 (r / 4) + 4 lh + r % 4][n0 + 128 wn + 32 nb + lr].
+template <int BM>
+__device__ __forceinline__ void mainloop(const GemmParams &p, int m0, int n0, unsigned char *ring,
+                                         const int (*arow)[BM],
+                                         f32x16_t (&acc)[GTile<BM>::MB][GTile<BM>::NB]) {
+    using T = GTile<BM>;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int lr = lane & 31, lh = lane >> 5;
+    // load j of this wave fills stage block blk = wave * LOADS + j (16 rows of
+    // 64 B; A rows first, then B rows); lane -> row 16 blk + lane / 4, slot lane % 4.
+    // Source pointers are formed once per A segment; a chunk only adds its k offset.
+    const int slot = lane & 3;
+    const uint16_t *src_base[T::LOADS];
+    int seg = 0;
+    // segment fields by constant index only (a run-time index would turn
+    // these kernel-argument reads into per-chunk memory loads)
+    const int kofs1 = p.nseg > 1 ? p.kofs[1] : 0x7fffffff, kofs2 = p.nseg > 2 ? p.kofs[2] : 0x7fffffff;
+    auto set_bases = [&](int sg) {
+        const uint16_t *aseg = (const uint16_t *)(sg == 0 ? p.a[0] : sg == 1 ? p.a[1] : p.a[2]);
+        const int kseg = sg == 0 ? p.k[0] : sg == 1 ? p.k[1] : p.k[2];
+        const int oseg = sg == 0 ? 0 : sg == 1 ? kofs1 : kofs2;
+#pragma unroll
+        for (int j = 0; j < T::LOADS; ++j) {
+            const int blk = wave * T::LOADS + j;
+            const int row = blk * 16 + (lane >> 2);
+            if (row < BM) {
+                src_base[j] = aseg + (size_t)arow[sg][row] * kseg - oseg + 8 * (slot ^ gswz(row));
+            } else {
+                const int n = min(n0 + row - BM, p.N - 1);
+                src_base[j] = (const uint16_t *)p.b + (size_t)n * p.K + 8 * (slot ^ gswz(row));
+            }
+        }
+    };
+    set_bases(0);
+    // B rows use the full K offset kc; A rows the offset within the segment (kofs folded into the base)
+    auto issue = [&](int stage, int kc) {
+        const int sg = kc >= kofs2 ? 2 : kc >= kofs1 ? 1 : 0;  // chunks arrive in k order
+        if (sg != seg) {
+            seg = sg;
+            set_bases(seg);
+        }
+        unsigned char *base = ring + stage * T::STAGE;
+#pragma unroll
+        for (int j = 0; j < T::LOADS; ++j) {
+            const int blk = wave * T::LOADS + j;
+            __builtin_amdgcn_global_load_lds((const void *)(src_base[j] + kc), (lds_void_t *)(base + blk * 1024), 16,
+                                             0, 0);
+        }
+    };
+
+#pragma unroll
+    for (int i = 0; i < T::MB; ++i)
+#pragma unroll
+        for (int jj = 0; jj < T::NB; ++jj)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][jj][r] = 0.f;
+
+    const int nch = p.K / GBK;
+#pragma unroll
+    for (int st = 0; st < GNS - 1; ++st)
+        if (st < nch) issue(st, st * GBK);
+    const int wm = wave >> 1, wn = wave & 1;
+    // per-lane LDS byte offsets of the operand rows (sub-step 0 and 1 differ by the column)
+    int aoff[T::MB][2], boff[T::NB][2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        const int cl = 2 * s + lh;  // both operands take k = 16 s + 8 lh .. +7 of the chunk
+#pragma unroll
+        for (int mb = 0; mb < T::MB; ++mb) {
+            const int row = wm * (BM / 2) + mb * 32 + lr;
+            aoff[mb][s] = row * GROW + ((cl ^ gswz(row)) << 4);
+        }
+#pragma unroll
+        for (int nb = 0; nb < T::NB; ++nb) {
+            const int row = wn * 128 + nb * 32 + lr;
+            boff[nb][s] = BM * GROW + row * GROW + ((cl ^ gswz(row)) << 4);
+        }
+    }
+    auto wait_chunk = [&](int c) {  // chunk c has landed in LDS for every wave
+        const int ahead = min(nch - 1 - c, GNS - 2);
+        if (ahead >= 2) wait_vmcnt<2 * T::LOADS>();
+        else if (ahead == 1) wait_vmcnt<T::LOADS>();
+        else wait_vmcnt<0>();
+        // bare barrier: a fenced one would drain the chunks still in flight
+        __builtin_amdgcn_s_barrier();
+        __asm__ volatile("" ::: "memory");
+    };
+    u32x4_t av0[T::MB], bv0[T::NB], av1[T::MB], bv1[T::NB];
+    // Fragment reads are issued as inline ds_read_b128: the compiler cannot
+    // tell ring slots apart and would otherwise wait for every LDS DMA still
+    // in flight before each read. Completion is awaited explicitly (lgkm).
+    const uint32_t ring_lds = (uint32_t)(uintptr_t)(lds_void_t *)ring;
+    auto read = [&](int slotk, int s, u32x4_t *av, u32x4_t *bv) {
+        const uint32_t base = ring_lds + slotk * T::STAGE;
+#pragma unroll
+        for (int mb = 0; mb < T::MB; ++mb)
+            __asm__ volatile("ds_read_b128 %0, %1" : "=v"(av[mb]) : "v"(base + aoff[mb][s]));
+#pragma unroll
+        for (int nb = 0; nb < T::NB; ++nb)
+            __asm__ volatile("ds_read_b128 %0, %1" : "=v"(bv[nb]) : "v"(base + boff[nb][s]));
+    };
+    auto mma = [&](const u32x4_t *av, const u32x4_t *bv) {
+#pragma unroll
+        for (int mb = 0; mb < T::MB; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < T::NB; ++nb)
+                acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, av[mb]),
+                                                                      __builtin_bit_cast(bf16x8_t, bv[nb]),
+                                                                      acc[mb][nb], 0, 0, 0);
+    };
+    // software pipeline: the fragments of the next half-chunk are read while
+    // the MFMAs of the current one run; the barrier that hands a ring slot
+    // back to the loads sits between two MFMA groups
+    constexpr int NRD = T::MB + T::NB;  // LDS reads per half-chunk
+    if (nch > 0) {
+        wait_chunk(0);
+        if (GNS - 1 < nch) issue(GNS - 1, (GNS - 1) * GBK);
+        read(0, 0, av0, bv0);
+    }
+    for (int c = 0; c < nch; ++c) {
+        read(c % GNS, 1, av1, bv1);
+        lgkm_wait<NRD, T::MB>(av0, bv0);
+        mma(av0, bv0);
+        if (c + 1 < nch) {
+            // every wave's reads of chunk c are done before its slot is refilled
+            lgkm_wait<0, T::MB>(av1, bv1);
+            wait_chunk(c + 1);
+            if (c + GNS < nch) issue(c % GNS, (c + GNS) * GBK);
+            read((c + 1) % GNS, 0, av0, bv0);
+            lgkm_wait<NRD, T::MB>(av1, bv1);
+        } else {
+            lgkm_wait<0, T::MB>(av1, bv1);
+        }
+        mma(av1, bv1);
+    }
+}
+
+}  // namespace e3g

@@ -29,6 +29,7 @@
 // Pass 2 (one work-group per row): merges all tiles' records in a fixed order,
 // so results are deterministic.
 #include "common.h"
+#include "gemm_core.h"
 
 namespace {
 
@@ -190,6 +191,80 @@ __global__ __launch_bounds__(256, 2) void lmhead_bf16_kernel(const uint16_t *__r
     tile_select<BM, BN, KK, LSE>(lg, m0, M, n0, N, tile, ntiles, p);
 }
 
+// Many hidden rows (verify batches of whole trees, draft steps): the head is
+// a dense bf16 GEMM. 256 hidden rows x 256 vocabulary rows per work-group on
+// the shared GEMM core; the logit tile is then staged in LDS a quarter (64
+// hidden rows) at a time for the same per-row selection.
+// Work-group order: hidden tiles fastest, so the work-groups of one
+// vocabulary tile run together and read its weight rows once; each XCD takes
+// a contiguous run.
+__device__ __forceinline__ void lm_tile_of(int L, int nwg, int MT, int &mt, int &nt) {
+    const int q = nwg >> 3, r = nwg & 7, x = L & 7, j = L >> 3;
+    const int t = (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + j;
+    mt = t % MT;
+    nt = t / MT;
+}
+
+constexpr int BIG_BN = e3g::GBN;  // vocabulary rows per tile, many-row path
+
+template <int KK, bool LSE>
+__global__ __launch_bounds__(256, 1) void lmhead_big_kernel(e3g::GemmParams gp, int nrec, Partials p) {
+    using T = e3g::GTile<256>;
+    __shared__ __attribute__((aligned(1024))) unsigned char ring[e3g::GNS * T::STAGE];
+    __shared__ int arow[3][256];
+    static_assert(4 * 64 * 128 * sizeof(float) <= sizeof(ring), "per-wave staging must fit the ring");
+    int mt, nt;
+    lm_tile_of(blockIdx.x, gridDim.x, gp.mt, mt, nt);
+    const int m0 = mt * 256, n0 = nt * BIG_BN;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int lr = lane & 31, lh = lane >> 5, wm = wave >> 1, wn = wave & 1;
+    e3g::fill_arow<256>(gp, m0, arow);
+    f32x16_t acc[T::MB][T::NB];
+    e3g::mainloop<256>(gp, m0, n0, ring, arow, acc);
+    __syncthreads();  // every wave is done with the ring
+    // Each wave selects over its own 128 x 128 sub-tile, 64 hidden rows at a
+    // time, staged in a private 32 KB slice of the ring (row-skewed columns:
+    // conflict-free row scans); one lane owns one row, so there is no merging
+    // inside the tile. Its record is (row, 2 * tile + column half).
+    float *st = reinterpret_cast<float *>(ring) + wave * 64 * 128;
+    const int vbase = n0 + wn * 128;
+    const int rec_tile = 2 * nt + wn;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+#pragma unroll
+        for (int mb = 2 * half; mb < 2 * half + 2; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < T::NB; ++nb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = (mb & 1) * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+                    st[row * 128 + ((nb * 32 + lr + row) & 127)] = acc[mb][nb][r];
+                }
+        // a wave's LDS accesses complete in order: the scan below sees the stores
+        float lv[KK]; int li[KK];
+        e3_topk_init<KK>(lv, li);
+        float mx = -INFINITY, se = 0.f;
+        const int row = lane;
+        const int nvalid = min(128, gp.N - vbase);
+        for (int j = 0; j < nvalid; ++j) {
+            const float x = st[row * 128 + ((j + row) & 127)];
+            const int v = vbase + j;
+            if (e3_better(x, v, lv[KK - 1], li[KK - 1])) e3_topk_insert<KK>(lv, li, x, v);
+            if (LSE) {
+                if (x > mx) { se = se * __expf(mx - x) + 1.f; mx = x; }
+                else se += __expf(x - mx);
+            }
+        }
+        const int m = m0 + wm * 128 + half * 64 + row;
+        if (m < gp.M) {
+            const size_t rec = (size_t)m * nrec + rec_tile;
+#pragma unroll
+            for (int s2 = 0; s2 < KK; ++s2) { p.val[rec * KK + s2] = lv[s2]; p.idx[rec * KK + s2] = li[s2]; }
+            if (LSE) { p.mx[rec] = mx; p.se[rec] = se; }
+        }
+    }
+}
+
 template <int KK, bool LSE>
 __global__ __launch_bounds__(256) void lmhead_f32_kernel(const float *__restrict__ h, const float *__restrict__ w,
                                                          int M, int N, int K, int ntiles, Partials p) {
@@ -275,7 +350,7 @@ __global__ __launch_bounds__(256) void lmhead_merge_kernel(int ntiles, Partials 
 
 int kk_for(int topk) {
     const int need = topk < 2 ? 2 : topk;
-    return need <= 2 ? 2 : need <= 4 ? 4 : need <= 8 ? 8 : 16;
+    return need <= 2 ? 2 : need <= 4 ? 4 : need <= 8 ? 8 : need <= 10 ? 10 : 16;
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -291,12 +366,30 @@ Partials carve(void *ws, int M, int ntiles, int KK) {
     return p;
 }
 
+// from this many hidden rows on, the bf16 head runs as a dense GEMM
+constexpr int BIG_M = 128;
+
+bool use_big(int M, int K, int dtype) { return dtype == EAGLE3_BF16 && M >= BIG_M && K % e3g::GSEG_ALIGN == 0; }
+
+// partial records per row (the many-row path keeps one per 128-column half tile)
+int tiles_for(int M, int N, int K, int dtype) {
+    if (use_big(M, K, dtype)) return 2 * ((N + BIG_BN - 1) / BIG_BN);
+    const int bn = dtype == EAGLE3_BF16 ? BN_B : BN_F;
+    return (N + bn - 1) / bn;
+}
+
 template <int KK, bool LSE>
 void launch(const void *hidden, const void *w, int M, int N, int K, int topk, int dtype, int32_t *idx, float *val,
             float *gap, float *lse, void *ws, hipStream_t st) {
-    const int ntiles = (N + (dtype == EAGLE3_BF16 ? BN_B : BN_F) - 1) / (dtype == EAGLE3_BF16 ? BN_B : BN_F);
+    const int ntiles = tiles_for(M, N, K, dtype);
     const Partials p = carve(ws, M, ntiles, KK);
-    if (dtype == EAGLE3_BF16) {
+    if (use_big(M, K, dtype)) {
+        e3g::GemmParams gp{};
+        gp.a[0] = hidden; gp.k[0] = K; gp.nseg = 1;
+        gp.b = w; gp.M = M; gp.N = N; gp.K = K; gp.ldc = N;
+        gp.mt = (M + 255) / 256; gp.nt = (N + BIG_BN - 1) / BIG_BN;
+        lmhead_big_kernel<KK, LSE><<<gp.mt * gp.nt, 256, 0, st>>>(gp, ntiles, p);
+    } else if (dtype == EAGLE3_BF16) {
         dim3 grid((M + 63) / 64, ntiles);
         lmhead_bf16_kernel<KK, LSE><<<grid, 256, 0, st>>>((const uint16_t *)hidden, (const uint16_t *)w, M, N, K,
                                                           ntiles, p);
@@ -318,8 +411,7 @@ void launch_kk(bool want_lse, const void *hidden, const void *w, int M, int N, i
 
 extern "C" size_t eagle3_lmhead_workspace(int M, int N, int K, int topk, int dtype) {
     if (M <= 0 || N <= 0 || topk < 1) return 0;
-    const int bn = dtype == EAGLE3_BF16 ? BN_B : BN_F;
-    const int ntiles = (N + bn - 1) / bn;
+    const int ntiles = tiles_for(M, N, K, dtype);
     const int KK = kk_for(topk);
     const size_t rec = (size_t)M * ntiles;
     return align256(rec * KK * 4) + align256(rec * KK * 4) + align256(rec * 4) + align256(rec * 4);
@@ -343,6 +435,7 @@ extern "C" int eagle3_lmhead_argmax(const void *hidden, const void *w, int M, in
         case 2: launch_kk<2>(want_lse, hidden, w, M, N, K, topk, dtype, idx, val, gap, lse, ws, st); break;
         case 4: launch_kk<4>(want_lse, hidden, w, M, N, K, topk, dtype, idx, val, gap, lse, ws, st); break;
         case 8: launch_kk<8>(want_lse, hidden, w, M, N, K, topk, dtype, idx, val, gap, lse, ws, st); break;
+        case 10: launch_kk<10>(want_lse, hidden, w, M, N, K, topk, dtype, idx, val, gap, lse, ws, st); break;
         default: launch_kk<16>(want_lse, hidden, w, M, N, K, topk, dtype, idx, val, gap, lse, ws, st); break;
     }
     E3_LAUNCH_CHECK();
