@@ -185,48 +185,108 @@ __device__ __forceinline__ void mainloop(const GemmParams &p, int m0, int n0, un
     // tell ring slots apart and would otherwise wait for every LDS DMA still
     // in flight before each read. Completion is awaited explicitly (lgkm).
     const uint32_t ring_lds = (uint32_t)(uintptr_t)(lds_void_t *)ring;
-    auto read = [&](int slotk, int s, u32x4_t *av, u32x4_t *bv) {
+    constexpr int NMF = T::MB * T::NB;  // MFMAs per half-chunk
+    constexpr int NRD = T::MB + T::NB;  // fragment reads per half-chunk
+    static_assert(NRD <= NMF && T::LOADS <= NMF, "one read and one load per MFMA at most");
+    auto rd = [&](int slotk, int s, int i, u32x4_t *av, u32x4_t *bv) {
         const uint32_t base = ring_lds + slotk * T::STAGE;
-#pragma unroll
-        for (int mb = 0; mb < T::MB; ++mb)
-            __asm__ volatile("ds_read_b128 %0, %1" : "=v"(av[mb]) : "v"(base + aoff[mb][s]));
-#pragma unroll
-        for (int nb = 0; nb < T::NB; ++nb)
-            __asm__ volatile("ds_read_b128 %0, %1" : "=v"(bv[nb]) : "v"(base + boff[nb][s]));
+        if (i < T::MB) __asm__ volatile("ds_read_b128 %0, %1" : "=v"(av[i]) : "v"(base + aoff[i][s]));
+        else __asm__ volatile("ds_read_b128 %0, %1" : "=v"(bv[i - T::MB]) : "v"(base + boff[i - T::MB][s]));
     };
-    auto mma = [&](const u32x4_t *av, const u32x4_t *bv) {
-#pragma unroll
-        for (int mb = 0; mb < T::MB; ++mb)
-#pragma unroll
-            for (int nb = 0; nb < T::NB; ++nb)
-                acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, av[mb]),
-                                                                      __builtin_bit_cast(bf16x8_t, bv[nb]),
-                                                                      acc[mb][nb], 0, 0, 0);
+    auto mf = [&](int j, const u32x4_t *av, const u32x4_t *bv) {
+        const int mb = j / T::NB, nb = j % T::NB;
+        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, av[mb]),
+                                                              __builtin_bit_cast(bf16x8_t, bv[nb]), acc[mb][nb], 0,
+                                                              0, 0);
     };
-    // software pipeline: the fragments of the next half-chunk are read while
-    // the MFMAs of the current one run; the barrier that hands a ring slot
-    // back to the loads sits between two MFMA groups
-    constexpr int NRD = T::MB + T::NB;  // LDS reads per half-chunk
+    auto dma = [&](int stage, int kc, int j) {
+        const int blk = wave * T::LOADS + j;
+        __builtin_amdgcn_global_load_lds((const void *)(src_base[j] + kc),
+                                         (lds_void_t *)(ring + stage * T::STAGE + blk * 1024), 16, 0, 0);
+    };
+    auto select_seg = [&](int kc) {
+        const int sg = kc >= kofs2 ? 2 : kc >= kofs1 ? 1 : 0;  // chunks arrive in k order
+        if (sg != seg) {
+            seg = sg;
+            set_bases(seg);
+        }
+    };
+    // Software pipeline, one wave per SIMD: each instruction between two
+    // MFMA groups would leave the matrix pipe idle, so the fragment reads of
+    // the next half-chunk and the DMA loads of a later chunk sit between the
+    // MFMAs of the current one (scheduling barriers pin that order).
+    // A: MFMAs of (c, first half) with the reads of (c, second half) between them.
+    auto phase_a = [&](int c) {
+        lgkm_wait<0, T::MB>(av0, bv0);
+        const int sl = c % GNS;
+#pragma unroll
+        for (int j = 0; j < NMF; ++j) {
+            mf(j, av0, bv0);
+            __builtin_amdgcn_sched_barrier(0);
+            if (j < NRD) {
+                rd(sl, 1, j, av1, bv1);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        lgkm_wait<0, T::MB>(av1, bv1);
+    };
+    // C: MFMAs of (c, second half) with the reads of (c + 1, first half) and,
+    // when `refill`, the loads of chunk c + GNS into chunk c's slot.
+    auto phase_c = [&](int c, bool next, bool refill) {
+        const int sl = (c + 1) % GNS, kc = (c + GNS) * GBK;
+        if (refill) select_seg(kc);
+        if (next && refill) {
+#pragma unroll
+            for (int j = 0; j < NMF; ++j) {
+                mf(j, av1, bv1);
+                __builtin_amdgcn_sched_barrier(0);
+                if (j < NRD) {
+                    rd(sl, 0, j, av0, bv0);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                if (j >= NMF - T::LOADS) {
+                    dma(c % GNS, kc, j - (NMF - T::LOADS));
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+        } else if (next) {
+#pragma unroll
+            for (int j = 0; j < NMF; ++j) {
+                mf(j, av1, bv1);
+                __builtin_amdgcn_sched_barrier(0);
+                if (j < NRD) {
+                    rd(sl, 0, j, av0, bv0);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < NMF; ++j) mf(j, av1, bv1);
+        }
+    };
     if (nch > 0) {
         wait_chunk(0);
         if (GNS - 1 < nch) issue(GNS - 1, (GNS - 1) * GBK);
-        read(0, 0, av0, bv0);
+#pragma unroll
+        for (int i = 0; i < NRD; ++i) rd(0, 0, i, av0, bv0);
     }
-    for (int c = 0; c < nch; ++c) {
-        read(c % GNS, 1, av1, bv1);
-        lgkm_wait<NRD, T::MB>(av0, bv0);
-        mma(av0, bv0);
+    // steady state: every chunk refills a slot, wait depth is fixed
+    const int steady = nch - GNS;
+    for (int c = 0; c < steady; ++c) {
+        phase_a(c);
+        wait_vmcnt<2 * T::LOADS>();  // chunk c + 1 has landed (c + 2, c + 3 may be in flight)
+        __builtin_amdgcn_s_barrier();
+        __asm__ volatile("" ::: "memory");
+        phase_c(c, true, true);
+    }
+    for (int c = steady < 0 ? 0 : steady; c < nch; ++c) {
+        phase_a(c);
         if (c + 1 < nch) {
-            // every wave's reads of chunk c are done before its slot is refilled
-            lgkm_wait<0, T::MB>(av1, bv1);
             wait_chunk(c + 1);
-            if (c + GNS < nch) issue(c % GNS, (c + GNS) * GBK);
-            read((c + 1) % GNS, 0, av0, bv0);
-            lgkm_wait<NRD, T::MB>(av1, bv1);
+            phase_c(c, true, false);
         } else {
-            lgkm_wait<0, T::MB>(av1, bv1);
+            phase_c(c, false, false);
         }
-        mma(av1, bv1);
     }
 }
 
