@@ -1,11 +1,11 @@
-"""Write the oracle's results for the full-size 8B-shaped batch-1 verify step
-(seeds 0..4) to verify_llama8b-b1.json: the draft tokens planted against the
+"""Write the oracle's results for a full-size verify workload (default: the
+8B-shaped batch-1 step, seeds 0..4) to verify_<workload>.json: the draft tokens planted against the
 oracle's argmax, the oracle's per-node argmax and top-2 gap, and the accepted
 path. The benchmark reads the planted tokens from here (so no planting ever
 uses the GPU's own argmax) and the GPU tests compare against the rest.
 
 Calls only the oracle and the seeded generators. Usage:
-    python tests/golden/make_verify_golden.py
+    python tests/golden/make_verify_golden.py [workload [number of seeds]]
 """
 import json
 import os
@@ -39,4 +39,6 @@ def main(name="llama8b-b1", seeds=range(5)):
 
 
 if __name__ == "__main__":
-    main(*sys.argv[1:2])
+    name = sys.argv[1] if len(sys.argv) > 1 else "llama8b-b1"
+    n = int(sys.argv[2]) if len(sys.argv) > 2 else 5
+    main(name, range(n))

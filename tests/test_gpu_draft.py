@@ -217,16 +217,63 @@ def test_draft_head_small_matches_oracle(orc, seed):
     print(f"seed {seed}: {same}/{s.B} trees identical to the oracle's own; {info}")
 
 
-@pytest.mark.slow
-@pytest.mark.timeout(400)
-def test_draft_head_full_size_sequence0(orc):
+@pytest.fixture(scope="module")
+def full_size_draft():
+    """The full-size draft head (64 sequences, k 4096, context 1024, vocab
+    128256), run once on the GPU for the tests below."""
     s = synth.DRAFT_B64
     W = synth.draft_weights(s)
     l, m, h, tok = synth.draft_inputs(s, 0)
     head, rec = _gpu_draft(s, W, l, m, h, tok)
     del l, m, h
-    par = host(head.parent)
-    assert all(_valid(p) for p in par)
+    out = dict(s=s, W=W, tok=tok, parent=host(head.parent), tokens=host(head.tokens), head=head, rec=rec)
+    yield out
+    del out["head"]
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(400)
+def test_draft_head_full_size_sequence0(orc, full_size_draft):
+    f = full_size_draft
+    s, W = f["s"], f["W"]
+    assert all(_valid(p) for p in f["parent"])
     l0, m0, h0, t0 = synth.draft_inputs(s, 0, batch=slice(0, 1))
-    info = _check_choices(orc, s, W, l0, m0, h0, t0, head, rec, [0])
+    info = _check_choices(orc, s, W, l0, m0, h0, t0, f["head"], f["rec"], [0])
     print(f"full size, sequence 0: {info}")
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(400)
+def test_verify_on_drafted_trees(orc, full_size_draft):
+    """The verify step on the trees the draft head just built (8B shapes, 64
+    sequences, prefix 1024, the target's head = the head the draft used; the
+    draft and target are independent random models, so acceptance is rare).
+    Sequence 0 against the oracle: attention within the bf16 tolerance, the
+    accepted path and emitted tokens exact unless flagged."""
+    import dataclasses
+    import oracle as orc_mod
+    import tree_draft_verification_amd as e3
+    f = full_size_draft
+    shape = synth.VerifyShape("draft-b64-verify", 6, B=64, Hq=32, Hkv=8, D=128, V=128256, n_drafts=60, depth=8)
+    inp = dataclasses.replace(synth.verify_inputs(shape, 0), parent=f["parent"])
+    Wl = f["W"]["lm_head"]
+    kc, vc, bt, pl, w = (dev(x) for x in (inp.kv.k_cache, inp.kv.v_cache, inp.kv.block_table, inp.kv.prefix_len, Wl))
+    step = e3.VerifyStep(shape.B, shape.T, shape.Hq, shape.Hkv, shape.D, shape.V, kc, vc, bt, pl, w)
+    par, q, kt, vt, tk = dev(inp.parent), dev(inp.q), dev(inp.k_tree), dev(inp.v_tree), dev(f["tokens"])
+    step.run(par, q, kt, vt, tk)
+    torch.cuda.synchronize()
+    acc_len = host(step.accept_len)
+    assert ((acc_len >= 0) & (acc_len <= 8)).all()
+    one = dataclasses.replace(synth.verify_inputs(shape, 0, batch=slice(0, 1)), parent=f["parent"][:1])
+    ref = orc_mod.verify_step(one, Wl, tokens=f["tokens"][:1])
+    rel = normwise_rel(host(step.attn).reshape(shape.B, -1)[:1], ref["attn"].reshape(1, -1))[0]
+    assert rel <= 2e-2
+    idx = host(step.idx).reshape(shape.B, shape.T)[0]
+    clean = ref["gap"][0] >= 1e-3
+    assert np.array_equal(idx[clean], ref["idx"][0][clean])
+    if not ref["flagged"][0]:
+        for name in ("accept_len", "path", "out_tokens"):
+            assert np.array_equal(host(getattr(step, name))[:1], ref[name]), name
+    print(f"verify on drafted trees: accept_len mean {acc_len.mean():.3f} (sequence 0: {acc_len[0]}, "
+          f"flagged {bool(ref['flagged'][0])}), attention rel err {rel:.2e}")

@@ -97,6 +97,8 @@ class DraftHead:
         self.parent = torch.empty(B, n_drafts + 1, dtype=i32, device=dv)
         self.tokens = torch.empty(B, n_drafts + 1, dtype=i32, device=dv)
         self._ctx_bufs = None
+        # optional (start, end) event pairs, one taken per LM-head call, in call order
+        self.events = []
 
     # ----------------------------------------------------------- context
     def _ctx_buffers(self):
@@ -152,8 +154,13 @@ class DraftHead:
     def _head(self, a, M):
         hn = self.hn[:M]
         B_.eagle3_rmsnorm(a, hn, eps=self.eps)
+        ev = self.events.pop(0) if self.events else None
+        if ev:
+            ev[0].record()
         B_.eagle3_lmhead_argmax(hn, self.w["lm_head"], self.C, self.ids[:M], self.val[:M], None, self.lse[:M],
                                 self.lm_ws)
+        if ev:
+            ev[1].record()
 
     # ----------------------------------------------------------- growth
     def grow(self, record=None):
