@@ -111,98 +111,152 @@ enum TileKind { TILE_FULL = 0, TILE_PARTIAL = 1, TILE_TREE = 2 };
 // stay below 256, harmless in fp32), which makes O rescaling rare.
 constexpr float kLazyMax = 8.f;
 
-// One 64-key tile for one wave: S^T = K.Q^T, online softmax, O^T += V^T.P^T.
-// kind is wave-uniform (one copy of the code serves every tile kind).
-__device__ __forceinline__ void attend_tile(int kind, const unsigned char *stage, const u32x4_t (&qb)[8],
-                                            f32x16_t (&ot)[4], float &m_run, float &l_run, int lr, int lh,
-                                            int nvalid, uint64_t mword, float scale_log2) {
-    const unsigned char *Kb = stage, *Vb = stage + VOFF;
-    f32x16_t st[2];
+// LDS fragment reads are inline ds_read_b128: the compiler cannot tell ring
+// stages apart and would otherwise wait for every K/V DMA still in flight
+// (the whole ring) before the first read of a tile. Each read is awaited
+// explicitly (lgkmcnt), with the wait tied to its destination register.
+__device__ __forceinline__ void lds_read16(u32x4_t &r, uint32_t addr) {
+    __asm__ volatile("ds_read_b128 %0, %1" : "=v"(r) : "v"(addr));
+}
+template <int N>
+__device__ __forceinline__ void lgkm_wait1(u32x4_t &r) {
+    __asm__ volatile("s_waitcnt lgkmcnt(%1)" : "+v"(r) : "i"(N));
+}
+// wait until at most n (0..2) LDS reads are outstanding
+__device__ __forceinline__ void lgkm_upto(int n, u32x4_t &r) {
+    if (n >= 2) lgkm_wait1<2>(r);
+    else if (n == 1) lgkm_wait1<1>(r);
+    else lgkm_wait1<0>(r);
+}
+
+// One 64-key tile for one wave and its RB blocks of 32 query rows: S^T =
+// K.Q^T, online softmax, O^T += V^T.P^T. Every K / V fragment read from LDS
+// feeds the MFMAs of all RB row blocks, and the row blocks' independent
+// softmax work interleaves with the MFMAs of the others. kind is wave-uniform.
+// Operand fragments are read two steps ahead through a 4-slot buffer.
+template <int RB>
+__device__ __forceinline__ void attend_tile(int kind, const unsigned char *stage, const u32x4_t (&qb)[RB][8],
+                                            f32x16_t (&ot)[RB][4], float (&m_run)[RB], float (&l_run)[RB], int lr,
+                                            int lh, int nvalid, const uint64_t (&mword)[RB], float scale_log2) {
+    const uint32_t kb_lds = (uint32_t)(uintptr_t)(lds_void_t *)stage;
+    const uint32_t vb_lds = kb_lds + VOFF;
+    u32x4_t fr[4];
+    // QK step j: key block kb = j & 1 (alternating accumulators), d-step s = j >> 1
+    auto kaddr = [&](int j) {
+        const int kb = j & 1, s = j >> 1, row = kb * 32 + lr;
+        // lane half lh holds d = 16 s + 8 lh .. +7, i.e. 16-byte column 2 s + lh
+        return kb_lds + row * 256 + (((2 * s + lh) ^ kswz(row)) << 4);
+    };
+    f32x16_t st[RB][2];
+    lds_read16(fr[0], kaddr(0));
+    lds_read16(fr[1], kaddr(1));
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-        const int row = kb * 32 + lr;
+    for (int j = 0; j < 16; ++j) {
+        if (j + 2 < 16) lds_read16(fr[(j + 2) & 3], kaddr(j + 2));
+        lgkm_upto(15 - j < 2 ? 15 - j : 2, fr[j & 3]);
+        const int kb = j & 1, s = j >> 1;
 #pragma unroll
-        for (int s = 0; s < 8; ++s) {
-            // lane half lh holds d = 16 s + 8 lh .. +7, i.e. 16-byte column 2 s + lh
-            const u32x4_t a = *reinterpret_cast<const u32x4_t *>(Kb + row * 256 + (((2 * s + lh) ^ kswz(row)) << 4));
+        for (int rb = 0; rb < RB; ++rb) {
             if (s == 0) {
                 const f32x16_t z = {};
-                st[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                                 __builtin_bit_cast(bf16x8_t, qb[s]), z, 0, 0, 0);
+                st[rb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, fr[j & 3]),
+                                                                     __builtin_bit_cast(bf16x8_t, qb[rb][s]), z, 0,
+                                                                     0, 0);
             } else {
-                st[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                                 __builtin_bit_cast(bf16x8_t, qb[s]), st[kb], 0, 0, 0);
+                st[rb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, fr[j & 3]),
+                                                                     __builtin_bit_cast(bf16x8_t, qb[rb][s]),
+                                                                     st[rb][kb], 0, 0, 0);
             }
         }
     }
-    // register r of block kb holds key 32 kb + 16 (r / 8) + 8 lh + (r % 8)
-    if (kind != TILE_FULL) {
+    // PV step j: 16-key step ks = j >> 2, d block db = j & 3; the first two V
+    // fragments are read now and land during the softmax
+    auto vaddr = [&](int j) {
+        const int ks = j >> 2, db = j & 3, d = db * 32 + lr;
+        return vb_lds + ks * 4096 + d * 32 + ((lh ^ vswz(d)) << 4);
+    };
+    lds_read16(fr[0], vaddr(0));
+    lds_read16(fr[1], vaddr(1));
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+        // register r of block kb holds key 32 kb + 16 (r / 8) + 8 lh + (r % 8)
+        if (kind != TILE_FULL) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int kk = kb * 32 + 16 * (r >> 3) + 8 * lh + (r & 7);
+                    const bool vis = kk < nvalid && (kind != TILE_TREE || ((mword[rb] >> kk) & 1u));
+                    st[rb][kb][r] = vis ? st[rb][kb][r] : -INFINITY;
+                }
+        }
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, st[rb][kb][r]);
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * scale_log2;
+        // refresh the running max only when it is exceeded by more than 2^kLazyMax
+        const bool grow = tmax > m_run[rb] + kLazyMax;
+        if (__ballot(grow)) {
+            const float m_new = grow ? tmax : m_run[rb];
+            const float alpha = (m_run[rb] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run[rb] - m_new);
+            l_run[rb] *= alpha;
+#pragma unroll
+            for (int db = 0; db < 4; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) ot[rb][db][r] *= alpha;
+            m_run[rb] = m_new;
+        }
+        const float msub = (m_run[rb] == -INFINITY) ? 0.f : m_run[rb];
+        float psum = 0.f;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int kk = kb * 32 + 16 * (r >> 3) + 8 * lh + (r & 7);
-                const bool vis = kk < nvalid && (kind != TILE_TREE || ((mword >> kk) & 1u));
-                st[kb][r] = vis ? st[kb][r] : -INFINITY;
+                const float pv = __builtin_amdgcn_exp2f(fmaf(st[rb][kb][r], scale_log2, -msub));
+                st[rb][kb][r] = pv;
+                psum += pv;
             }
+        l_run[rb] += psum;
     }
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, st[kb][r]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * scale_log2;
-    // refresh the running max only when it is exceeded by more than 2^kLazyMax
-    const bool grow = tmax > m_run + kLazyMax;
-    if (__ballot(grow)) {
-        const float m_new = grow ? tmax : m_run;
-        const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) ot[db][r] *= alpha;
-        m_run = m_new;
-    }
-    const float msub = (m_run == -INFINITY) ? 0.f : m_run;
-    float psum = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const float pv = __builtin_amdgcn_exp2f(fmaf(st[kb][r], scale_log2, -msub));
-            st[kb][r] = pv;
-            psum += pv;
-        }
-    l_run += psum;
     // 16 keys per step = one cache block of the tile; this lane's 8 P values
     // are keys 8 lh .. 8 lh + 7 of the block. P enters as bf16 hi + lo (two
     // MFMAs on the same V operand): a single bf16 rounding of P would leave
     // ~2e-3 relative error in the output.
+    u32x4_t ph[RB], pl[RB];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-        const int kb = ks >> 1, r0 = 8 * (ks & 1);
-        u32x4_t ph, pl;
+    for (int j = 0; j < 16; ++j) {
+        const int ks = j >> 2, db = j & 3;
+        if (db == 0) {
+            const int kb = ks >> 1, r0 = 8 * (ks & 1);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            uint32_t h2, l2;
-            e3_split_bf16x2(st[kb][r0 + 2 * e], st[kb][r0 + 2 * e + 1], h2, l2);
-            ph[e] = h2;
-            pl[e] = l2;
+            for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    uint32_t h2, l2;
+                    e3_split_bf16x2(st[rb][kb][r0 + 2 * e], st[rb][kb][r0 + 2 * e + 1], h2, l2);
+                    ph[rb][e] = h2;
+                    pl[rb][e] = l2;
+                }
         }
+        if (j + 2 < 16) lds_read16(fr[(j + 2) & 3], vaddr(j + 2));
+        lgkm_upto(15 - j < 2 ? 15 - j : 2, fr[j & 3]);
+        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, fr[j & 3]);
 #pragma unroll
-        for (int db = 0; db < 4; ++db) {
-            const int d = db * 32 + lr;
-            const u32x4_t v = *reinterpret_cast<const u32x4_t *>(Vb + ks * 4096 + d * 32 + ((lh ^ vswz(d)) << 4));
-            const bf16x8_t a = __builtin_bit_cast(bf16x8_t, v);
-            ot[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, ph), ot[db], 0, 0, 0);
-            ot[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, pl), ot[db], 0, 0, 0);
+        for (int rb = 0; rb < RB; ++rb) {
+            ot[rb][db] =
+                __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, ph[rb]), ot[rb][db], 0, 0, 0);
+            ot[rb][db] =
+                __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, pl[rb]), ot[rb][db], 0, 0, 0);
         }
     }
 }
 
-template <int NW>
+// NW waves of RB x 32 query rows each (NW * RB * 32 = ROWS_PER_WG).
+template <int NW, int RB>
 __global__ __launch_bounds__(NW * 64) void tree_attn_bf16_kernel(AttnParams p) {
+    static_assert(NW * RB * 32 == ROWS_PER_WG, "a work-group covers one block of query rows");
     __shared__ __attribute__((aligned(1024))) unsigned char ring[NSTAGE * STAGE];
     __shared__ int bids[MAX_SPLIT_BLOCKS];
     constexpr int NT = NW * 64;
@@ -220,11 +274,17 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_bf16_kernel(AttnParams p) {
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int lr = lane & 31, lh = lane >> 5;
-    const int row = rb * ROWS_PER_WG + wave * 32 + lr;  // this lane's query row
-    const bool row_ok = row < p.R;
-    const int t = row_ok ? row / p.G : 0;
-    const int hq = kvh * p.G + (row_ok ? row % p.G : 0);
-    const bool wave_active = rb * ROWS_PER_WG + wave * 32 < p.R;
+    // this lane's query rows, one per row block
+    int row[RB], t[RB], hq[RB];
+    bool row_ok[RB];
+#pragma unroll
+    for (int k = 0; k < RB; ++k) {
+        row[k] = rb * ROWS_PER_WG + (wave * RB + k) * 32 + lr;
+        row_ok[k] = row[k] < p.R;
+        t[k] = row_ok[k] ? row[k] / p.G : 0;
+        hq[k] = kvh * p.G + (row_ok[k] ? row[k] % p.G : 0);
+    }
+    const bool wave_active = rb * ROWS_PER_WG + wave * RB * 32 < p.R;
 
     // physical ids of the cache blocks this split reads
     const int blk0 = k_begin / 16;
@@ -261,25 +321,35 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_bf16_kernel(AttnParams p) {
     };
 
     // Q^T operand: d = 16 s + 8 lh + i
-    u32x4_t qb[8];
-    {
-        const uint16_t *qrow = p.q + (((size_t)b * p.Tq + t) * p.Hq + hq) * DH + 8 * lh;
+    u32x4_t qb[RB][8];
+    uint64_t mw0[RB], mw1[RB];
+#pragma unroll
+    for (int k = 0; k < RB; ++k) {
+        const uint16_t *qrow = p.q + (((size_t)b * p.Tq + t[k]) * p.Hq + hq[k]) * DH + 8 * lh;
 #pragma unroll
         for (int s = 0; s < 8; ++s)
-            qb[s] = row_ok ? *reinterpret_cast<const u32x4_t *>(qrow + 16 * s) : u32x4_t{0u, 0u, 0u, 0u};
+            qb[k][s] = row_ok[k] ? *reinterpret_cast<const u32x4_t *>(qrow + 16 * s) : u32x4_t{0u, 0u, 0u, 0u};
+        mw0[k] = 0; mw1[k] = 0;
+        if (last && row_ok[k]) query_mask(p, b, t[k], mw0[k], mw1[k]);
     }
-    uint64_t mw0 = 0, mw1 = 0;
-    if (last && row_ok) query_mask(p, b, t, mw0, mw1);
 
-    f32x16_t ot[4];
+    f32x16_t ot[RB][4];
+    float m_run[RB], l_run[RB];
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+    for (int k = 0; k < RB; ++k) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) ot[db][r] = 0.f;
-    float m_run = -INFINITY, l_run = 0.f;
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) ot[k][db][r] = 0.f;
+        m_run[k] = -INFINITY;
+        l_run[k] = 0.f;
+    }
 
     const int ntile = (k_end - k_begin + KT - 1) / KT;
-    __syncthreads();  // block ids (and the q / mask loads) are in
+    // q and mask words have landed before any K/V DMA is queued behind them
+    // (otherwise the first use of q inside the tile loop waits for the ring)
+    wait_vmcnt<0>();
+    __syncthreads();  // block ids are in
 #pragma unroll
     for (int st = 0; st < NSTAGE - 1; ++st)
         if (st < ntile) issue(st, st);
@@ -291,7 +361,9 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_bf16_kernel(AttnParams p) {
     for (int it = 0; it < ntile + ntree; ++it) {
         const unsigned char *stage;
         int kind, nvalid;
-        uint64_t mword = 0;
+        uint64_t mword[RB];
+#pragma unroll
+        for (int k = 0; k < RB; ++k) mword[k] = 0;
         if (it < ntile) {
             if (it + NSTAGE - 2 < ntile) wait_vmcnt<(NSTAGE - 2) * LOADS>();
             else wait_vmcnt<0>();
@@ -342,44 +414,49 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_bf16_kernel(AttnParams p) {
             stage = ring;
             kind = TILE_TREE;
             nvalid = p.Tk - tt * KT;
-            mword = tt == 0 ? mw0 : mw1;
+#pragma unroll
+            for (int k = 0; k < RB; ++k) mword[k] = tt == 0 ? mw0[k] : mw1[k];
         }
-        if (wave_active) attend_tile(kind, stage, qb, ot, m_run, l_run, lr, lh, nvalid, mword, p.scale_log2);
+        if (wave_active) attend_tile<RB>(kind, stage, qb, ot, m_run, l_run, lr, lh, nvalid, mword, p.scale_log2);
     }
 
-    if (!row_ok) return;
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    // lane holds d = 32 db + 8 (r / 4) + 4 lh + r % 4 for its query
-    if (nsplit_b == 1) {
-        uint16_t *orow = p.out + (((size_t)b * p.Tq + t) * p.Hq + hq) * DH;
 #pragma unroll
-        for (int db = 0; db < 4; ++db)
+    for (int k = 0; k < RB; ++k) {
+        if (!row_ok[k]) continue;
+        const float l_tot = l_run[k] + __shfl_xor(l_run[k], 32);
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        // lane holds d = 32 db + 8 (r / 4) + 4 lh + r % 4 for its query
+        if (nsplit_b == 1) {
+            uint16_t *orow = p.out + (((size_t)b * p.Tq + t[k]) * p.Hq + hq[k]) * DH;
 #pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-                const int d = db * 32 + 8 * g4 + 4 * lh;
-                u32x2_t o;
-                o[0] = e3_pack_bf16x2(ot[db][4 * g4] * inv, ot[db][4 * g4 + 1] * inv);
-                o[1] = e3_pack_bf16x2(ot[db][4 * g4 + 2] * inv, ot[db][4 * g4 + 3] * inv);
-                *reinterpret_cast<u32x2_t *>(orow + d) = o;
+            for (int db = 0; db < 4; ++db)
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const int d = db * 32 + 8 * g4 + 4 * lh;
+                    u32x2_t o;
+                    o[0] = e3_pack_bf16x2(ot[k][db][4 * g4] * inv, ot[k][db][4 * g4 + 1] * inv);
+                    o[1] = e3_pack_bf16x2(ot[k][db][4 * g4 + 2] * inv, ot[k][db][4 * g4 + 3] * inv);
+                    *reinterpret_cast<u32x2_t *>(orow + d) = o;
+                }
+            if (p.lse && lh == 0)
+                p.lse[((size_t)b * p.Tq + t[k]) * p.Hq + hq[k]] =
+                    l_tot > 0.f ? (m_run[k] + log2f(l_tot)) * kLn2 : -INFINITY;
+        } else {
+            const size_t prow = (((size_t)b * p.Hkv + kvh) * p.nsplit + split) * p.Rpad + row[k];
+            float *orow = p.ws_o + prow * DH;
+#pragma unroll
+            for (int db = 0; db < 4; ++db)
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const int d = db * 32 + 8 * g4 + 4 * lh;
+                    f32x4_t o = {ot[k][db][4 * g4] * inv, ot[k][db][4 * g4 + 1] * inv, ot[k][db][4 * g4 + 2] * inv,
+                                 ot[k][db][4 * g4 + 3] * inv};
+                    *reinterpret_cast<f32x4_t *>(orow + d) = o;
+                }
+            if (lh == 0) {
+                p.ws_ml[prow * 2] = m_run[k];
+                p.ws_ml[prow * 2 + 1] = l_tot;
             }
-        if (p.lse && lh == 0)
-            p.lse[((size_t)b * p.Tq + t) * p.Hq + hq] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
-    } else {
-        const size_t prow = (((size_t)b * p.Hkv + kvh) * p.nsplit + split) * p.Rpad + row;
-        float *orow = p.ws_o + prow * DH;
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-                const int d = db * 32 + 8 * g4 + 4 * lh;
-                f32x4_t o = {ot[db][4 * g4] * inv, ot[db][4 * g4 + 1] * inv, ot[db][4 * g4 + 2] * inv,
-                             ot[db][4 * g4 + 3] * inv};
-                *reinterpret_cast<f32x4_t *>(orow + d) = o;
-            }
-        if (lh == 0) {
-            p.ws_ml[prow * 2] = m_run;
-            p.ws_ml[prow * 2 + 1] = l_tot;
         }
     }
 }
@@ -515,7 +592,7 @@ __global__ __launch_bounds__(64) void tree_attn_f32_kernel(AttnF32 p) {
 // ---------------------------------------------------------------- host side
 
 struct Plan {
-    int nrb, nsplit, split_keys, nw;
+    int nrb, nsplit, split_keys;
     size_t ws_bytes;
 };
 
@@ -547,8 +624,6 @@ Plan make_plan(const eagle3_tree_attn_args *a) {
     const int G = a->Hq / a->Hkv;
     const int R = a->Tq * G;
     pl.nrb = (R + ROWS_PER_WG - 1) / ROWS_PER_WG;
-    const int rows0 = R < ROWS_PER_WG ? R : ROWS_PER_WG;
-    pl.nw = rows0 <= 64 ? 2 : rows0 <= 128 ? 4 : 8;
     const long lmax = (long)a->max_blocks * a->block_size;
     const long ktiles = lmax > 0 ? (lmax + KT - 1) / KT : 1;
     if (a->split_keys > 0) {
@@ -612,11 +687,10 @@ extern "C" int eagle3_tree_attn(const eagle3_tree_attn_args *a, void *ws, size_t
             p.ws_ml = (float *)((char *)ws + ((rows * DH * 4 + 255) & ~(size_t)255));
         }
         dim3 grid(pl.nsplit * pl.nrb, a->Hkv, a->B);
-        switch (pl.nw) {
-            case 2: tree_attn_bf16_kernel<2><<<grid, 128, 0, st>>>(p); break;
-            case 4: tree_attn_bf16_kernel<4><<<grid, 256, 0, st>>>(p); break;
-            default: tree_attn_bf16_kernel<8><<<grid, 512, 0, st>>>(p); break;
-        }
+        // 8 waves of 32 rows cover the 256-row block (two row blocks per wave
+        // would share every fragment read, but 64 rows of Q, scores and output
+        // accumulators do not fit the register file)
+        tree_attn_bf16_kernel<8, 1><<<grid, 512, 0, st>>>(p);
         if (pl.nsplit > 1) tree_attn_combine_kernel<<<a->B * a->Tq * a->Hq, DH, 0, st>>>(p);
     } else {
         AttnF32 p;

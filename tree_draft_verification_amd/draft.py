@@ -97,6 +97,7 @@ class DraftHead:
         self.parent = torch.empty(B, n_drafts + 1, dtype=i32, device=dv)
         self.tokens = torch.empty(B, n_drafts + 1, dtype=i32, device=dv)
         self._ctx_bufs = None
+        self._ws = None
         # optional (start, end) event pairs, one taken per LM-head call, in call order
         self.events = []
 
@@ -139,8 +140,14 @@ class DraftHead:
         attn = self.attn[:B]
         a = B_.tree_attn_args(q.view(B, 1, self.Hq, self.D), none, none, self.k_cache, self.v_cache, self.table,
                               self.plen, attn.view(B, 1, self.Hq, self.D), mask=self.root_mask)
-        B_.eagle3_tree_attn(a, None, 0)
+        B_.eagle3_tree_attn(a, self._attn_ws(a))
         self._layer_tail(self.x1, attn, self.a_root, B)
+
+    def _attn_ws(self, a):
+        need = max(256, B_.eagle3_tree_attn_workspace(a))
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = torch.empty(need, dtype=torch.uint8, device=self.dev)
+        return self._ws
 
     def _layer_tail(self, x, attn, out, M):
         w = self.w
@@ -198,7 +205,7 @@ class DraftHead:
             B_.eagle3_copy_rows(self.vt, tv2, M, dst_rows=rows)
             a = B_.tree_attn_args(self.q.view(B, C, self.Hq, D), self.tk, self.tv, self.k_cache, self.v_cache,
                                   self.table, self.plen, self.attn.view(B, C, self.Hq, D), mask=fr["mask"])
-            B_.eagle3_tree_attn(a, None, 0)
+            B_.eagle3_tree_attn(a, self._attn_ws(a))
             self._layer_tail(self.xs, self.attn, a_out, M)
             self._head(a_out, M)
             B_.eagle3_tree_expand(fr["score"], fr["pool"], fr["mask"], 0, C, self.ids.view(B, C, C),
