@@ -112,6 +112,9 @@ int eagle3_tree_mask(const int32_t *parent, int B, int T, int W,
  * split_keys: prefix keys per work-group split (multiple of 64), 0 = chosen by
  * the library from B, Hkv and max_blocks. Results do not depend on the call's
  * batch composition, but may differ in the last bits between split choices.
+ * norm_out (nullable): the RMSNorm (gamma = 1, eps = norm_eps) of each output
+ * row [Hq * D], as eagle3_rmsnorm on out would give; fused into the split merge
+ * when the prefix is split.
  */
 typedef struct eagle3_tree_attn_args {
     int dtype;
@@ -131,6 +134,8 @@ typedef struct eagle3_tree_attn_args {
     void *out;
     float *lse;
     int split_keys;
+    void *norm_out;  /* nullable: [B, Tq, Hq * D], RMSNorm (gamma = 1, norm_eps) of each output row */
+    float norm_eps;
 } eagle3_tree_attn_args;
 
 size_t eagle3_tree_attn_workspace(const eagle3_tree_attn_args *a);

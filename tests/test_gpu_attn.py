@@ -10,7 +10,7 @@ import pytest
 import torch
 
 import synth
-from _gpu import dev, host, normwise_rel
+from _gpu import as_f64, dev, host, normwise_rel
 
 pytestmark = pytest.mark.gpu
 
@@ -57,6 +57,7 @@ CASES = [
     (1, 16, 4, 4, [129], 0),             # MHA, small tree
     (2, 1, 8, 2, [17, 0], 0),            # root only
     (2, 100, 4, 1, [40, 90], 0),         # W = 2
+    (4, 61, 32, 8, [700, 1100, 64, 0], 64),  # split, too many work-groups for a tree split
 ]
 
 
@@ -145,3 +146,42 @@ def test_deterministic(orc, lib):
     a, la = gpu_attn(lib, inp, mask=mask)
     b, lb = gpu_attn(lib, inp, mask=mask)
     assert np.array_equal(a, b) and np.array_equal(la, lb)
+
+
+@pytest.mark.parametrize("split", [0, 4096])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_norm_out(orc, lib, split, dtype):
+    """The optional RMS-normalised copy of the output (the hidden row the LM
+    head reads): with the prefix split (combine pass writes it) and unsplit
+    (separate RMSNorm launch). It must equal RMSNorm of the attention output
+    the same call wrote, and the oracle's RMSNorm of the oracle attention."""
+    B, T, Hq, Hkv = 1, 61, 32, 8
+    parent, inp = make(130, B, T, Hq, Hkv, [1100], dtype=dtype)
+    W = (T + 63) // 64
+    mask, _ = orc.tree_mask(parent, W)
+    q, kt, vt = dev(inp.q), dev(inp.k_tree), dev(inp.v_tree)
+    kc, vc = dev(inp.kv.k_cache), dev(inp.kv.v_cache)
+    bt, pl, mk = dev(inp.kv.block_table), dev(inp.kv.prefix_len), dev(mask)
+    out = torch.empty_like(q)
+    nrm = torch.empty_like(q)
+    eps = 1e-5
+    args = lib.tree_attn_args(q, kt, vt, kc, vc, bt, pl, out, mask=mk, split_keys=split, norm_out=nrm, norm_eps=eps)
+    ws_n = lib.eagle3_tree_attn_workspace(args)
+    ws = torch.empty(max(ws_n, 256), dtype=torch.uint8, device="cuda")
+    lib.eagle3_tree_attn(args, ws)
+    ref_n = torch.empty_like(q)
+    lib.eagle3_rmsnorm(out.view(B * T, -1), ref_n.view(B * T, -1), eps=eps)
+    torch.cuda.synchronize()
+    got, got_n, own_n = host(out), host(nrm), host(ref_n)
+    ref, _ = orc.tree_attn(inp.q, inp.k_tree, inp.v_tree, inp.kv, mask)
+    rel, mx = normwise_rel(got, ref)
+    tol = 2e-2 if dtype == "bf16" else 1e-5
+    assert rel <= tol, (rel, mx)
+    K = Hq * q.shape[-1]
+    oref = orc.rmsnorm(ref.reshape(B * T, K), eps=eps).reshape(got_n.shape)
+    rel, mx = normwise_rel(got_n, oref)
+    assert rel <= tol, (rel, mx)
+    # against the GPU's own RMSNorm of the same output: one storage rounding
+    a, b = as_f64(got_n), as_f64(own_n)
+    ulp = 2.0 ** -7 if dtype == "bf16" else 2.0 ** -22
+    assert np.all(np.abs(a - b) <= ulp * np.maximum(np.abs(b), 1e-30) + 1e-30), np.abs(a - b).max()

@@ -35,6 +35,7 @@ class TreeAttnArgs(ctypes.Structure):
         ("block_table", P), ("max_blocks", I), ("prefix_len", P),
         ("mask", P), ("parent", P), ("out", P), ("lse", P),
         ("split_keys", I),
+        ("norm_out", P), ("norm_eps", F),
     ]
 
 
@@ -124,7 +125,7 @@ def eagle3_tree_mask(parent, W, mask, depth=None, status=None, stream=None):
 
 
 def tree_attn_args(q, k_tree, v_tree, k_cache, v_cache, block_table, prefix_len, out, mask=None, parent=None,
-                   lse=None, scale=None, split_keys=0) -> TreeAttnArgs:
+                   lse=None, scale=None, split_keys=0, norm_out=None, norm_eps=1e-5) -> TreeAttnArgs:
     B, Tq, Hq, D = q.shape
     Tk, Hkv = k_tree.shape[1], k_tree.shape[2]
     W = mask.shape[-1] if mask is not None else (Tq + 63) // 64
@@ -138,6 +139,7 @@ def tree_attn_args(q, k_tree, v_tree, k_cache, v_cache, block_table, prefix_len,
     a.block_table, a.max_blocks, a.prefix_len = _ptr(block_table), block_table.shape[1], _ptr(prefix_len)
     a.mask, a.parent, a.out, a.lse = _ptr(mask), _ptr(parent), _ptr(out), _ptr(lse)
     a.split_keys = int(split_keys)
+    a.norm_out, a.norm_eps = _ptr(norm_out), float(norm_eps)
     return a
 
 

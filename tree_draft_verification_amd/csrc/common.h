@@ -90,3 +90,15 @@ __device__ __forceinline__ void e3_lse_combine(float &m, float &s, float m2, flo
     s = s * __expf(m - mn) + s2 * __expf(m2 - mn);
     m = mn;
 }
+
+// sum over a 256-thread work-group (red: 4 floats of LDS); every thread gets the total
+__device__ __forceinline__ float e3_block_sum_256(float v, float *red) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    if (lane == 0) red[wave] = v;
+    __syncthreads();
+    const float s = red[0] + red[1] + red[2] + red[3];
+    __syncthreads();
+    return s;
+}

@@ -8,17 +8,6 @@
 
 namespace {
 
-__device__ __forceinline__ float block_sum_256(float v, float *red) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    if (lane == 0) red[wave] = v;
-    __syncthreads();
-    const float s = red[0] + red[1] + red[2] + red[3];
-    __syncthreads();
-    return s;
-}
-
 template <bool BF16>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const void *__restrict__ x, const void *__restrict__ gamma,
                                                       int K, float eps, void *__restrict__ y) {
@@ -43,7 +32,7 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const void *__restrict__ x
 #pragma unroll
         for (int i = 0; i < 8; ++i) ss += v[i] * v[i];
     }
-    const float total = block_sum_256(ss, red);
+    const float total = e3_block_sum_256(ss, red);
     const float r = 1.0f / sqrtf(total / (float)K + eps);
     for (int c = threadIdx.x * 8; c < K; c += 256 * 8) {
         float v[8], g[8];

@@ -47,6 +47,7 @@ struct AttnParams {
     float *ws_o;   // [B, Hkv, nsplit, Rpad, D]
     float *ws_ml;  // [B, Hkv, nsplit, Rpad, 2]
     int B, Tq, Tk, Hq, Hkv, W, G, R, Rpad, nrb, nsplit, split_keys, max_blocks, num_blocks;
+    int tree_split;  // 1: the tree keys are a split of their own (after the prefix splits)
     float scale_log2;
 };
 
@@ -56,6 +57,14 @@ __device__ __forceinline__ int clamped_len(const int32_t *prefix_len, int b, int
     const int L = prefix_len[b];
     if (num_blocks <= 0) return 0;
     return max(0, min(L, max_blocks * bs));
+}
+
+// Splits of one sequence: prefix splits of split_keys keys, plus (tree_split)
+// one more for the tree keys; without tree_split the last prefix split also
+// takes the tree keys (an empty prefix still makes one split).
+__device__ __forceinline__ int splits_of(int L, int split_keys, int tree_split) {
+    const int npre = L > 0 ? (L + split_keys - 1) / split_keys : 0;
+    return tree_split ? npre + 1 : (npre > 0 ? npre : 1);
 }
 
 __device__ __forceinline__ int clamped_block(const int32_t *btab, int j, int num_blocks) {
@@ -266,11 +275,12 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_bf16_kernel(AttnParams p) {
     const int kvh = blockIdx.y, b = blockIdx.z;
     const int L = clamped_len(p.prefix_len, b, p.max_blocks, 16, p.num_blocks);
     const int C = p.split_keys;
-    const int nsplit_b = L > 0 ? (L + C - 1) / C : 1;
+    const int nsplit_b = splits_of(L, C, p.tree_split);
     if (split >= nsplit_b) return;
-    const int k_begin = split * C;
-    const int k_end = min(L, k_begin + C);
-    const bool last = split == nsplit_b - 1;
+    const bool last = split == nsplit_b - 1;           // this split takes the tree keys
+    const bool tree_only = p.tree_split && last;       // ... and no prefix keys
+    const int k_begin = tree_only ? 0 : split * C;
+    const int k_end = tree_only ? 0 : min(L, k_begin + C);
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int lr = lane & 31, lh = lane >> 5;
@@ -466,7 +476,7 @@ __global__ __launch_bounds__(128) void tree_attn_combine_kernel(AttnParams p) {
     const int idx = blockIdx.x;  // (b, t, hq)
     const int hq = idx % p.Hq, t = (idx / p.Hq) % p.Tq, b = idx / (p.Hq * p.Tq);
     const int L = clamped_len(p.prefix_len, b, p.max_blocks, 16, p.num_blocks);
-    const int nsplit_b = L > 0 ? (L + p.split_keys - 1) / p.split_keys : 1;
+    const int nsplit_b = splits_of(L, p.split_keys, p.tree_split);
     if (nsplit_b <= 1) return;
     const int kvh = hq / p.G, row = t * p.G + hq % p.G;
     const size_t base = ((size_t)b * p.Hkv + kvh) * p.nsplit;
@@ -485,6 +495,83 @@ __global__ __launch_bounds__(128) void tree_attn_combine_kernel(AttnParams p) {
     p.out[(((size_t)b * p.Tq + t) * p.Hq + hq) * DH + d] = e3_f32_to_bf16(o);
     if (p.lse && d == 0)
         p.lse[((size_t)b * p.Tq + t) * p.Hq + hq] = den > 0.f ? (M + log2f(den)) * kLn2 : -INFINITY;
+}
+
+// Combine and RMSNorm in one pass: one work-group per (sequence, node) row
+// merges the split partials of all Hq heads (split weights per head in LDS),
+// writes the attention output row and its RMSNorm (gamma = 1) computed from
+// the stored bf16 values, as the separate norm would.
+constexpr int CN_MAXS = 32;  // splits per sequence the fused pass handles
+constexpr int CN_MAXH = 64;  // query heads the fused pass handles
+
+__global__ __launch_bounds__(256) void tree_attn_combine_norm_kernel(AttnParams p, uint16_t *__restrict__ norm_out,
+                                                                     float eps) {
+    __shared__ float wgt[CN_MAXH][CN_MAXS];
+    __shared__ float red[4];
+    const int t = blockIdx.x % p.Tq, b = blockIdx.x / p.Tq;
+    const int L = clamped_len(p.prefix_len, b, p.max_blocks, 16, p.num_blocks);
+    const int nsplit_b = splits_of(L, p.split_keys, p.tree_split);
+    for (int hq = threadIdx.x; hq < p.Hq; hq += blockDim.x) {
+        const int kvh = hq / p.G, row = t * p.G + hq % p.G;
+        const size_t base = ((size_t)b * p.Hkv + kvh) * p.nsplit;
+        float M = -INFINITY;
+        for (int s = 0; s < nsplit_b; ++s) M = fmaxf(M, p.ws_ml[((base + s) * p.Rpad + row) * 2]);
+        float den = 0.f;
+        for (int s = 0; s < nsplit_b; ++s) {
+            const size_t prow = (base + s) * p.Rpad + row;
+            const float ms = p.ws_ml[prow * 2], ls = p.ws_ml[prow * 2 + 1];
+            const float w = (ms == -INFINITY) ? 0.f : ls * exp2f(ms - M);
+            wgt[hq][s] = w;
+            den += w;
+        }
+        const float inv = den > 0.f ? 1.f / den : 0.f;
+        for (int s = 0; s < nsplit_b; ++s) wgt[hq][s] *= inv;
+        if (p.lse) p.lse[((size_t)b * p.Tq + t) * p.Hq + hq] = den > 0.f ? (M + log2f(den)) * kLn2 : -INFINITY;
+    }
+    __syncthreads();
+    const int K = p.Hq * DH;
+    float v[4][8];  // this thread's 8 consecutive elements of each pass (K <= 8192)
+    float ss = 0.f;
+    uint16_t *orow = p.out + ((size_t)b * p.Tq + t) * K;
+#pragma unroll
+    for (int ps = 0; ps < 4; ++ps) {
+        const int c = (ps * 256 + threadIdx.x) * 8;
+        if (c >= K) break;
+        const int hq = c / DH, d = c % DH;
+        const int kvh = hq / p.G, row = t * p.G + hq % p.G;
+        const size_t base = ((size_t)b * p.Hkv + kvh) * p.nsplit;
+        float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int s = 0; s < nsplit_b; ++s) {
+            const float w = wgt[hq][s];
+            const float *src = p.ws_o + ((base + s) * p.Rpad + row) * DH + d;
+            const f32x4_t a = *reinterpret_cast<const f32x4_t *>(src);
+            const f32x4_t c4 = *reinterpret_cast<const f32x4_t *>(src + 4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) { o[i] += w * a[i]; o[4 + i] += w * c4[i]; }
+        }
+        u32x4_t packed;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            packed[i] = e3_pack_bf16x2(o[2 * i], o[2 * i + 1]);
+            v[ps][2 * i] = __uint_as_float(packed[i] << 16);
+            v[ps][2 * i + 1] = __uint_as_float(packed[i] & 0xffff0000u);
+        }
+        *reinterpret_cast<u32x4_t *>(orow + c) = packed;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ss += v[ps][i] * v[ps][i];
+    }
+    const float total = e3_block_sum_256(ss, red);
+    const float r = 1.0f / sqrtf(total / (float)K + eps);
+    uint16_t *nrow = norm_out + ((size_t)b * p.Tq + t) * K;
+#pragma unroll
+    for (int ps = 0; ps < 4; ++ps) {
+        const int c = (ps * 256 + threadIdx.x) * 8;
+        if (c >= K) break;
+        u32x4_t packed;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) packed[i] = e3_pack_bf16x2(v[ps][2 * i] * r, v[ps][2 * i + 1] * r);
+        *reinterpret_cast<u32x4_t *>(nrow + c) = packed;
+    }
 }
 
 // ---------------------------------------------------------------- fp32 path
@@ -592,7 +679,7 @@ __global__ __launch_bounds__(64) void tree_attn_f32_kernel(AttnF32 p) {
 // ---------------------------------------------------------------- host side
 
 struct Plan {
-    int nrb, nsplit, split_keys;
+    int nrb, nsplit, split_keys, tree_split;
     size_t ws_bytes;
 };
 
@@ -641,6 +728,13 @@ Plan make_plan(const eagle3_tree_attn_args *a) {
     }
     pl.nsplit = (int)((lmax + pl.split_keys - 1) / pl.split_keys);
     if (pl.nsplit < 1) pl.nsplit = 1;
+    // when the prefix is split anyway and one more split still fits in one
+    // pass over the CUs (one 512-thread work-group per CU), the tree keys
+    // become a split of their own, so no split does a prefix share plus the
+    // tree; past one pass the extra work-groups would form a second wave
+    const long wgs = (long)a->B * a->Hkv * pl.nrb * (pl.nsplit + 1);
+    pl.tree_split = (a->dtype == EAGLE3_BF16 && pl.nsplit > 1 && a->Tk > 0 && wgs <= 256) ? 1 : 0;
+    pl.nsplit += pl.tree_split;
     pl.ws_bytes = 0;
     if (a->dtype == EAGLE3_BF16 && pl.nsplit > 1) {
         const size_t rows = (size_t)a->B * a->Hkv * pl.nsplit * (size_t)pl.nrb * ROWS_PER_WG;
@@ -663,7 +757,8 @@ extern "C" int eagle3_tree_attn(const eagle3_tree_attn_args *a, void *ws, size_t
     if (!a->q || !a->out || !a->block_table || !a->prefix_len) return EAGLE3_ERR_ARG;
     if (a->Tk > 0 && (!a->k_tree || !a->v_tree)) return EAGLE3_ERR_ARG;
     if (a->num_blocks > 0 && (!a->k_cache || !a->v_cache)) return EAGLE3_ERR_ARG;
-    for (const void *ptr : {a->q, a->k_tree, a->v_tree, a->k_cache, a->v_cache, (const void *)a->out})
+    for (const void *ptr : {a->q, a->k_tree, a->v_tree, a->k_cache, a->v_cache, (const void *)a->out,
+                            (const void *)a->norm_out})
         if (ptr && !e3_aligned16(ptr)) return EAGLE3_ERR_ARG;
     const Plan pl = make_plan(a);
     if (ws_bytes < pl.ws_bytes || (pl.ws_bytes > 0 && !ws)) return EAGLE3_ERR_WORKSPACE;
@@ -679,6 +774,7 @@ extern "C" int eagle3_tree_attn(const eagle3_tree_attn_args *a, void *ws, size_t
         p.B = a->B; p.Tq = a->Tq; p.Tk = a->Tk; p.Hq = a->Hq; p.Hkv = a->Hkv; p.W = a->W; p.G = G;
         p.R = a->Tq * G; p.nrb = pl.nrb; p.Rpad = pl.nrb * ROWS_PER_WG; p.nsplit = pl.nsplit;
         p.split_keys = pl.split_keys; p.max_blocks = a->max_blocks; p.num_blocks = a->num_blocks;
+        p.tree_split = pl.tree_split;
         p.scale_log2 = a->scale * kLog2e;
         p.ws_o = nullptr; p.ws_ml = nullptr;
         if (pl.ws_bytes > 0) {
@@ -691,7 +787,16 @@ extern "C" int eagle3_tree_attn(const eagle3_tree_attn_args *a, void *ws, size_t
         // would share every fragment read, but 64 rows of Q, scores and output
         // accumulators do not fit the register file)
         tree_attn_bf16_kernel<8, 1><<<grid, 512, 0, st>>>(p);
-        if (pl.nsplit > 1) tree_attn_combine_kernel<<<a->B * a->Tq * a->Hq, DH, 0, st>>>(p);
+        const bool fused_norm = a->norm_out && pl.nsplit > 1 && pl.nsplit <= CN_MAXS && a->Hq <= CN_MAXH;
+        if (fused_norm)
+            tree_attn_combine_norm_kernel<<<a->B * a->Tq, 256, 0, st>>>(p, (uint16_t *)a->norm_out, a->norm_eps);
+        else if (pl.nsplit > 1)
+            tree_attn_combine_kernel<<<a->B * a->Tq * a->Hq, DH, 0, st>>>(p);
+        if (a->norm_out && !fused_norm) {
+            const int rc2 = eagle3_rmsnorm(a->out, nullptr, a->B * a->Tq, a->Hq * DH, a->norm_eps, EAGLE3_BF16,
+                                           a->norm_out, stream);
+            if (rc2 != EAGLE3_OK) return rc2;
+        }
     } else {
         AttnF32 p;
         p.q = (const float *)a->q; p.k_tree = (const float *)a->k_tree; p.v_tree = (const float *)a->v_tree;
@@ -702,6 +807,11 @@ extern "C" int eagle3_tree_attn(const eagle3_tree_attn_args *a, void *ws, size_t
         p.max_blocks = a->max_blocks; p.block_size = a->block_size; p.num_blocks = a->num_blocks;
         p.scale = a->scale;
         tree_attn_f32_kernel<<<a->B * a->Tq * a->Hq, 64, 0, st>>>(p);
+        if (a->norm_out) {
+            const int rc2 = eagle3_rmsnorm(a->out, nullptr, a->B * a->Tq, a->Hq * a->D, a->norm_eps, EAGLE3_F32,
+                                           a->norm_out, stream);
+            if (rc2 != EAGLE3_OK) return rc2;
+        }
     }
     E3_LAUNCH_CHECK();
     return EAGLE3_OK;

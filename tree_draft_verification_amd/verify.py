@@ -44,14 +44,16 @@ class VerifyStep:
 
     def _args(self, q, k_tree, v_tree):
         a = B_.tree_attn_args(q, k_tree, v_tree, self.k_cache, self.v_cache, self.block_table, self.prefix_len,
-                              self.attn, mask=self.mask, split_keys=self.split_keys)
+                              self.attn, mask=self.mask, split_keys=self.split_keys, norm_out=self.hidden,
+                              norm_eps=self.eps)
         need = B_.eagle3_tree_attn_workspace(a)
         if self._attn_ws is None or self._attn_ws.numel() < need:
             self._attn_ws = torch.empty(max(256, need), dtype=torch.uint8, device=q.device)
         return a
 
     def forward(self, parent, q, k_tree, v_tree, stream=None, events=None):
-        """Enqueue a0-a3 (mask, attention, norm, LM-head argmax). ``events``:
+        """Enqueue a0-a3 (mask, attention with the RMSNorm of its output rows,
+        LM-head argmax). ``events``:
         optional {"attn": (start, end), "lmhead": (start, end)} HIP events
         recorded around those calls on the same stream."""
         ev = events or {}
@@ -60,7 +62,6 @@ class VerifyStep:
         self._record(ev, "attn", 0, stream)
         B_.eagle3_tree_attn(a, self._attn_ws, stream=stream)
         self._record(ev, "attn", 1, stream)
-        B_.eagle3_rmsnorm(self.attn.view(self.B * self.T, self.K), self.hidden, eps=self.eps, stream=stream)
         self._record(ev, "lmhead", 0, stream)
         B_.eagle3_lmhead_argmax(self.hidden, self.w_lm, 1, self.idx, self.val, self.gap, None, self.lm_ws,
                                 stream=stream)
