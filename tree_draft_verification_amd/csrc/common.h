@@ -18,8 +18,24 @@ typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2_t;
         if (hipGetLastError() != hipSuccess) return EAGLE3_ERR_HIP; \
     } while (0)
 
+// cache-policy operand of a global load: non-temporal (streamed once)
+#define E3_CPOL_NT 2
+
 static inline bool e3_aligned16(const void *p) { return (((uintptr_t)p) & 15u) == 0; }
 static inline hipStream_t e3_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
+
+// compute units of the current device (queried once per device)
+static inline int e3_cu_count() {
+    static int cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cache[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cache[dev] = n;
+    }
+    return cache[dev];
+}
 
 __device__ __forceinline__ float e3_bf16_to_f32(uint16_t u) { return __uint_as_float(((uint32_t)u) << 16); }
 

@@ -97,7 +97,7 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-template <int KK, bool LSE>
+template <int KK, bool LSE, bool NTW>
 __global__ __launch_bounds__(256, 2) void lmhead_bf16_kernel(const uint16_t *__restrict__ h,
                                                              const uint16_t *__restrict__ w, int M, int N, int K,
                                                              int ntiles, Partials p) {
@@ -137,8 +137,17 @@ __global__ __launch_bounds__(256, 2) void lmhead_bf16_kernel(const uint16_t *__r
     auto issue = [&](int stage, int kc) {
         unsigned char *base = smem + stage * (WST + HST);
 #pragma unroll
-        for (int j = 0; j < LOADS; ++j)
-            __builtin_amdgcn_global_load_lds((const void *)(src[j] + kc), (lds_void_t *)(base + dst[j]), 16, 0, 0);
+        for (int j = 0; j < LOADS; ++j) {
+            // with one hidden tile the weight is read once per call: then
+            // non-temporal, so the stream does not evict the hidden rows
+            // every tile re-reads
+            if (NTW && wave * LOADS + j < WBLK)
+                __builtin_amdgcn_global_load_lds((const void *)(src[j] + kc), (lds_void_t *)(base + dst[j]), 16, 0,
+                                                 E3_CPOL_NT);
+            else
+                __builtin_amdgcn_global_load_lds((const void *)(src[j] + kc), (lds_void_t *)(base + dst[j]), 16, 0,
+                                                 0);
+        }
     };
 
     f32x16_t acc[2];
@@ -391,8 +400,12 @@ void launch(const void *hidden, const void *w, int M, int N, int K, int topk, in
         lmhead_big_kernel<KK, LSE><<<gp.mt * gp.nt, 256, 0, st>>>(gp, ntiles, p);
     } else if (dtype == EAGLE3_BF16) {
         dim3 grid((M + 63) / 64, ntiles);
-        lmhead_bf16_kernel<KK, LSE><<<grid, 256, 0, st>>>((const uint16_t *)hidden, (const uint16_t *)w, M, N, K,
-                                                          ntiles, p);
+        if (grid.x == 1)
+            lmhead_bf16_kernel<KK, LSE, true><<<grid, 256, 0, st>>>((const uint16_t *)hidden, (const uint16_t *)w, M,
+                                                                    N, K, ntiles, p);
+        else
+            lmhead_bf16_kernel<KK, LSE, false><<<grid, 256, 0, st>>>((const uint16_t *)hidden, (const uint16_t *)w, M,
+                                                                     N, K, ntiles, p);
     } else {
         dim3 grid((M + 15) / 16, ntiles);
         lmhead_f32_kernel<KK, LSE><<<grid, 256, 0, st>>>((const float *)hidden, (const float *)w, M, N, K, ntiles, p);
