@@ -95,8 +95,12 @@ __device__ __forceinline__ void e3_topk_merge_xor(float (&lv)[KK], int (&li)[KK]
     float ov[KK]; int oi[KK];
 #pragma unroll
     for (int s = 0; s < KK; ++s) { ov[s] = __shfl_xor(lv[s], mask); oi[s] = __shfl_xor(li[s], mask); }
+    // the other list is sorted too: once an entry cannot enter, none after it can
 #pragma unroll
-    for (int s = 0; s < KK; ++s) e3_topk_insert<KK>(lv, li, ov[s], oi[s]);
+    for (int s = 0; s < KK; ++s) {
+        if (!e3_better(ov[s], oi[s], lv[KK - 1], li[KK - 1])) break;
+        e3_topk_insert<KK>(lv, li, ov[s], oi[s]);
+    }
 }
 
 // log-sum-exp pair (max, sum of exp(x - max)) combination

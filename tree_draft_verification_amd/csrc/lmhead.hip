@@ -53,15 +53,24 @@ __device__ __forceinline__ void tile_select(const float (*lg)[BNt + 4], int m0, 
     constexpr int TPR = 256 / BMt;
     constexpr int PER = BNt / TPR;
     const int row = threadIdx.x / TPR, part = threadIdx.x % TPR;
+    static_assert(PER % 4 == 0, "16-byte reads of a thread's run");
     float lv[KK]; int li[KK];
     e3_topk_init<KK>(lv, li);
     float mx = -INFINITY, se = 0.f;
     const int vbeg = part * PER;
+    // the thread's whole run in a few wide reads first: one LDS round trip
+    // per element would serialise the scan on LDS latency
+    float xs[PER];
+#pragma unroll
+    for (int i = 0; i < PER; i += 4) {
+        const f32x4_t q = *reinterpret_cast<const f32x4_t *>(&lg[row][vbeg + i]);
+        xs[i] = q[0]; xs[i + 1] = q[1]; xs[i + 2] = q[2]; xs[i + 3] = q[3];
+    }
+#pragma unroll
     for (int i = 0; i < PER; ++i) {
-        const int vl = vbeg + i;
-        const int v = n0 + vl;
+        const int v = n0 + vbeg + i;
         if (v >= N) break;
-        const float x = lg[row][vl];
+        const float x = xs[i];
         if (e3_better(x, v, lv[KK - 1], li[KK - 1])) e3_topk_insert<KK>(lv, li, x, v);
         if (LSE) {
             if (x > mx) { se = se * __expf(mx - x) + 1.f; mx = x; }
@@ -232,9 +241,10 @@ __global__ __launch_bounds__(256, 1) void lmhead_big_kernel(e3g::GemmParams gp, 
     e3g::mainloop<256>(gp, m0, n0, ring, arow, acc);
     __syncthreads();  // every wave is done with the ring
     // Each wave selects over its own 128 x 128 sub-tile, 64 hidden rows at a
-    // time, staged in a private 32 KB slice of the ring (row-skewed columns:
-    // conflict-free row scans); one lane owns one row, so there is no merging
-    // inside the tile. Its record is (row, 2 * tile + column half).
+    // time, staged in a private 32 KB slice of the ring (columns rotated by 4
+    // per row, so 16-byte row reads of 16 lanes cover all banks); one lane
+    // owns one row, so there is no merging inside the tile. Its record is
+    // (row, 2 * tile + column half).
     float *st = reinterpret_cast<float *>(ring) + wave * 64 * 128;
     const int vbase = n0 + wn * 128;
     const int rec_tile = 2 * nt + wn;
@@ -247,7 +257,7 @@ __global__ __launch_bounds__(256, 1) void lmhead_big_kernel(e3g::GemmParams gp, 
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int row = (mb & 1) * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-                    st[row * 128 + ((nb * 32 + lr + row) & 127)] = acc[mb][nb][r];
+                    st[row * 128 + ((nb * 32 + lr + 4 * row) & 127)] = acc[mb][nb][r];
                 }
         // a wave's LDS accesses complete in order: the scan below sees the stores
         float lv[KK]; int li[KK];
@@ -255,13 +265,52 @@ __global__ __launch_bounds__(256, 1) void lmhead_big_kernel(e3g::GemmParams gp, 
         float mx = -INFINITY, se = 0.f;
         const int row = lane;
         const int nvalid = min(128, gp.N - vbase);
-        for (int j = 0; j < nvalid; ++j) {
-            const float x = st[row * 128 + ((j + row) & 127)];
-            const int v = vbase + j;
-            if (e3_better(x, v, lv[KK - 1], li[KK - 1])) e3_topk_insert<KK>(lv, li, x, v);
+        // short lists: 32 columns at a time, eight 16-byte reads, then the
+        // batch maximum rescales the running sum once, and a batch whose
+        // maximum is below a full list's last entry is skipped (ties cannot
+        // enter either: the list's ids are all smaller). Long lists: one
+        // column at a time (an unrolled batch of long inserts is slower)
+        if constexpr (KK > 4) {
+            for (int j = 0; j < nvalid; ++j) {
+                const float x = st[row * 128 + ((j + 4 * row) & 127)];
+                const int v = vbase + j;
+                if (e3_better(x, v, lv[KK - 1], li[KK - 1])) e3_topk_insert<KK>(lv, li, x, v);
+                if (LSE) {
+                    if (x > mx) { se = se * __expf(mx - x) + 1.f; mx = x; }
+                    else se += __expf(x - mx);
+                }
+            }
+        } else for (int b = 0; b < 4; ++b) {
+            const int jv = nvalid - b * 32;   // valid columns in this batch
+            if (jv <= 0) break;
+            float xs[32];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const f32x4_t t = *reinterpret_cast<const f32x4_t *>(st + row * 128 + ((b * 32 + 4 * q + 4 * row) & 127));
+                xs[4 * q] = t[0]; xs[4 * q + 1] = t[1]; xs[4 * q + 2] = t[2]; xs[4 * q + 3] = t[3];
+            }
+#pragma unroll
+            for (int i = 0; i < 32; ++i)
+                if (i >= jv) xs[i] = -INFINITY;
+            float bm = xs[0];
+#pragma unroll
+            for (int i = 1; i < 32; ++i) bm = fmaxf(bm, xs[i]);
             if (LSE) {
-                if (x > mx) { se = se * __expf(mx - x) + 1.f; mx = x; }
-                else se += __expf(x - mx);
+                const float nm = fmaxf(mx, bm);
+                if (nm != -INFINITY) {
+                    float sb = 0.f;
+#pragma unroll
+                    for (int i = 0; i < 32; ++i) sb += __expf(xs[i] - nm);
+                    se = se * __expf(mx - nm) + sb;
+                    mx = nm;
+                }
+            }
+            if (bm > lv[KK - 1] || li[KK - 1] == 0x7fffffff) {
+#pragma unroll
+                for (int i = 0; i < 32; ++i) {
+                    const int v = vbase + b * 32 + i;
+                    if (i < jv && e3_better(xs[i], v, lv[KK - 1], li[KK - 1])) e3_topk_insert<KK>(lv, li, xs[i], v);
+                }
             }
         }
         const int m = m0 + wm * 128 + half * 64 + row;
@@ -324,8 +373,15 @@ __global__ __launch_bounds__(256) void lmhead_merge_kernel(int ntiles, Partials 
     float mx = -INFINITY, se = 0.f;
     for (int t = threadIdx.x; t < ntiles; t += 256) {
         const size_t rec = (size_t)m * ntiles + t;
+        float rv[KK]; int ri[KK];
 #pragma unroll
-        for (int s = 0; s < KK; ++s) e3_topk_insert<KK>(lv, li, p.val[rec * KK + s], p.idx[rec * KK + s]);
+        for (int s = 0; s < KK; ++s) { rv[s] = p.val[rec * KK + s]; ri[s] = p.idx[rec * KK + s]; }
+        // a record is sorted: once an entry cannot enter, none after it can
+#pragma unroll
+        for (int s = 0; s < KK; ++s) {
+            if (!e3_better(rv[s], ri[s], lv[KK - 1], li[KK - 1])) break;
+            e3_topk_insert<KK>(lv, li, rv[s], ri[s]);
+        }
         if (LSE) e3_lse_combine(mx, se, p.mx[rec], p.se[rec]);
     }
 #pragma unroll
