@@ -109,6 +109,34 @@ def test_exact_ties_pick_lowest_index(lib):
         assert gg[m] <= 1e-5 * max(1.0, abs(gv[m, 0]))
 
 
+def test_exact_ties_many_rows(lib):
+    """Many-row path (M >= 128, GEMM tiles): every logit of a row is summed in
+    the same k order, so duplicate weight rows give bitwise equal logits
+    wherever they sit (same 256-column tile, other tiles, the ragged last
+    tile). A boosted row and its copies take the top places in ascending id
+    order, with gap exactly 0."""
+    rng = np.random.default_rng(7)
+    M, N, K = 200, 3000, 256
+    h = synth.normal_bf16(rng, (M, K))
+    wf = synth.bf16_to_f32(synth.normal_bf16(rng, (N, K), 0.02))
+    src = 1234
+    wf[src] *= 6.0
+    w = synth.f32_to_bf16(wf)
+    dups = [5, 1200, 1300, 2999]       # first tile, same tile as src, next tile, ragged last tile
+    for d in dups:
+        w[d] = w[src]
+    ties = sorted(dups + [src])
+    ref = synth.bf16_to_f32(h).astype(np.float64) @ synth.bf16_to_f32(w).astype(np.float64).T
+    others = np.delete(ref, ties, axis=1).max(axis=1)
+    wins = ref[:, src] > others + 1e-3
+    assert wins.sum() >= 20
+    gi, gv, gg, _ = gpu_lmhead(lib, h, w, 8, False)
+    for m in np.nonzero(wins)[0]:
+        assert list(gi[m, :5]) == ties, (m, gi[m])
+        assert np.all(gv[m, :5] == gv[m, 0])
+        assert gg[m] == 0.0
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_rmsnorm_parity(orc, lib, dtype):
     rng = np.random.default_rng(7)

@@ -65,41 +65,56 @@ __device__ __forceinline__ void e3_split_bf16x2(float a, float b, uint32_t &hi, 
     lo = e3_pack_bf16x2(a - ha, b - hb);
 }
 
-// (value, index) order used by every selection: larger value first, then lower index.
-__device__ __forceinline__ bool e3_better(float va, int ia, float vb, int ib) {
-    return va > vb || (va == vb && ia < ib);
+// Selection keys. Every selection orders (value, index) pairs by larger
+// value first, then lower index. The pair is packed into one 64-bit key whose
+// unsigned order is that order: the high word is the float's bits made
+// order-preserving (sign bit flipped for positives, all bits for negatives;
+// -0 is read as +0), the low word the complemented index. NaN maps to 0, the
+// key of an empty slot, so it is never selected.
+__device__ __forceinline__ uint64_t e3_key(float v, int i) {
+    const uint32_t u = __float_as_uint(v == 0.f ? 0.f : v);
+    const bool nan = v != v;
+    const uint32_t hi = nan ? 0u : ((u & 0x80000000u) ? ~u : (u | 0x80000000u));
+    const uint32_t lo = nan ? 0u : ~(uint32_t)i;
+    return ((uint64_t)hi << 32) | lo;
 }
 
-// insert (v, i) into the sorted list (L[0] best); drops the worst entry.
-template <int KK>
-__device__ __forceinline__ void e3_topk_insert(float (&lv)[KK], int (&li)[KK], float v, int i) {
-#pragma unroll
-    for (int s = 0; s < KK; ++s) {
-        if (e3_better(v, i, lv[s], li[s])) {
-            float tv = lv[s]; int ti = li[s];
-            lv[s] = v; li[s] = i;
-            v = tv; i = ti;
-        }
-    }
+// value and index of a key; an empty slot reads as (-inf, INT_MAX)
+__device__ __forceinline__ float e3_key_val(uint64_t k) {
+    const uint32_t hi = (uint32_t)(k >> 32);
+    return k == 0 ? -INFINITY : __uint_as_float((hi & 0x80000000u) ? (hi & 0x7fffffffu) : ~hi);
 }
+__device__ __forceinline__ int e3_key_idx(uint64_t k) { return k == 0 ? 0x7fffffff : (int)~(uint32_t)k; }
 
 template <int KK>
-__device__ __forceinline__ void e3_topk_init(float (&lv)[KK], int (&li)[KK]) {
+__device__ __forceinline__ void e3_kinit(uint64_t (&L)[KK]) {
 #pragma unroll
-    for (int s = 0; s < KK; ++s) { lv[s] = -INFINITY; li[s] = 0x7fffffff; }
+    for (int s = 0; s < KK; ++s) L[s] = 0;
+}
+
+// insert key k into the descending list L (L[0] best), dropping the last
+// entry; branch-free: every slot takes its upper neighbour, k or itself
+template <int KK>
+__device__ __forceinline__ void e3_kinsert(uint64_t (&L)[KK], uint64_t k) {
+    bool g[KK];
+#pragma unroll
+    for (int s = 0; s < KK; ++s) g[s] = k > L[s];
+#pragma unroll
+    for (int s = KK - 1; s > 0; --s) L[s] = g[s - 1] ? L[s - 1] : (g[s] ? k : L[s]);
+    L[0] = g[0] ? k : L[0];
 }
 
 // merge the list held by lane (lane ^ mask) into this lane's list
 template <int KK>
-__device__ __forceinline__ void e3_topk_merge_xor(float (&lv)[KK], int (&li)[KK], int mask) {
-    float ov[KK]; int oi[KK];
+__device__ __forceinline__ void e3_kmerge_xor(uint64_t (&L)[KK], int mask) {
+    uint64_t o[KK];
 #pragma unroll
-    for (int s = 0; s < KK; ++s) { ov[s] = __shfl_xor(lv[s], mask); oi[s] = __shfl_xor(li[s], mask); }
+    for (int s = 0; s < KK; ++s) o[s] = __shfl_xor(L[s], mask);
     // the other list is sorted too: once an entry cannot enter, none after it can
 #pragma unroll
     for (int s = 0; s < KK; ++s) {
-        if (!e3_better(ov[s], oi[s], lv[KK - 1], li[KK - 1])) break;
-        e3_topk_insert<KK>(lv, li, ov[s], oi[s]);
+        if (!(o[s] > L[KK - 1])) break;
+        e3_kinsert<KK>(L, o[s]);
     }
 }
 

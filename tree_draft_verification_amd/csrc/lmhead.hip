@@ -23,8 +23,11 @@
 //     "column" operand, so each accumulator register of a lane belongs to one
 //     hidden row.
 // Pass 1, fp32: plain FMA loop over a 256-row vocabulary tile (small models).
+//   - With one hidden tile the weight rows are loaded non-temporal: the
+//     head is streamed once per call and should not evict the hidden rows.
 // Epilogue (both): the logit tile is staged in LDS; a few threads per row keep
-// a sorted top-KK list (value desc, id asc) and an online (max, sum exp) pair,
+// a sorted top-KK list of 64-bit selection keys (value desc, id asc; one
+// unsigned compare per step, branch-free inserts) and a (max, sum exp) pair,
 // merged by lane shuffles; one record per (row, tile) goes to the workspace.
 // Pass 2 (one work-group per row): merges all tiles' records in a fixed order,
 // so results are deterministic.
@@ -40,11 +43,24 @@ constexpr int NSTAGE = 3;  // LDS ring depth, bf16 path
 constexpr int ROT = 7;     // chunk rotation per tile
 
 struct Partials {
-    float *val;  // [M, ntiles, KK]
-    int *idx;    // [M, ntiles, KK]
-    float *mx;   // [M, ntiles]
-    float *se;   // [M, ntiles]
+    uint64_t *key;  // [M, ntiles, KK] selection keys, descending
+    float *mx;      // [M, ntiles]
+    float *se;      // [M, ntiles]
 };
+
+// one record: a row's sorted list over one tile (KK even: 16-byte stores)
+template <int KK>
+__device__ __forceinline__ void store_record(const Partials &p, size_t rec, const uint64_t (&L)[KK]) {
+    static_assert(KK % 2 == 0, "records are written 16 bytes at a time");
+    u32x4_t *dst = reinterpret_cast<u32x4_t *>(p.key + rec * KK);
+#pragma unroll
+    for (int s = 0; s < KK; s += 2) {
+        u32x4_t q;
+        q[0] = (uint32_t)L[s]; q[1] = (uint32_t)(L[s] >> 32);
+        q[2] = (uint32_t)L[s + 1]; q[3] = (uint32_t)(L[s + 1] >> 32);
+        dst[s / 2] = q;
+    }
+}
 
 // Per-row selection over an LDS tile lg[BMt][BNt + 4]; 256 / BMt threads per row.
 template <int BMt, int BNt, int KK, bool LSE>
@@ -54,9 +70,8 @@ __device__ __forceinline__ void tile_select(const float (*lg)[BNt + 4], int m0, 
     constexpr int PER = BNt / TPR;
     const int row = threadIdx.x / TPR, part = threadIdx.x % TPR;
     static_assert(PER % 4 == 0, "16-byte reads of a thread's run");
-    float lv[KK]; int li[KK];
-    e3_topk_init<KK>(lv, li);
-    float mx = -INFINITY, se = 0.f;
+    uint64_t L[KK];
+    e3_kinit<KK>(L);
     const int vbeg = part * PER;
     // the thread's whole run in a few wide reads first: one LDS round trip
     // per element would serialise the scan on LDS latency
@@ -66,20 +81,25 @@ __device__ __forceinline__ void tile_select(const float (*lg)[BNt + 4], int m0, 
         const f32x4_t q = *reinterpret_cast<const f32x4_t *>(&lg[row][vbeg + i]);
         xs[i] = q[0]; xs[i + 1] = q[1]; xs[i + 2] = q[2]; xs[i + 3] = q[3];
     }
+    const int nv = N - (n0 + vbeg);   // valid entries of the run (may exceed PER)
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-        const int v = n0 + vbeg + i;
-        if (v >= N) break;
-        const float x = xs[i];
-        if (e3_better(x, v, lv[KK - 1], li[KK - 1])) e3_topk_insert<KK>(lv, li, x, v);
-        if (LSE) {
-            if (x > mx) { se = se * __expf(mx - x) + 1.f; mx = x; }
-            else se += __expf(x - mx);
+        if (i >= nv) xs[i] = -INFINITY;
+        const uint64_t k = i < nv ? e3_key(xs[i], n0 + vbeg + i) : 0;
+        if (k > L[KK - 1]) e3_kinsert<KK>(L, k);
+    }
+    float mx = -INFINITY, se = 0.f;
+    if (LSE) {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) mx = fmaxf(mx, xs[i]);
+        if (mx != -INFINITY) {
+#pragma unroll
+            for (int i = 0; i < PER; ++i) se += __expf(xs[i] - mx);
         }
     }
 #pragma unroll
     for (int off = 1; off < TPR; off <<= 1) {
-        e3_topk_merge_xor<KK>(lv, li, off);
+        e3_kmerge_xor<KK>(L, off);
         if (LSE) {
             const float m2 = __shfl_xor(mx, off), s2 = __shfl_xor(se, off);
             e3_lse_combine(mx, se, m2, s2);
@@ -88,8 +108,7 @@ __device__ __forceinline__ void tile_select(const float (*lg)[BNt + 4], int m0, 
     const int m = m0 + row;
     if (part == 0 && m < M) {
         const size_t rec = (size_t)m * ntiles + tile;
-#pragma unroll
-        for (int s = 0; s < KK; ++s) { p.val[rec * KK + s] = lv[s]; p.idx[rec * KK + s] = li[s]; }
+        store_record<KK>(p, rec, L);
         if (LSE) { p.mx[rec] = mx; p.se[rec] = se; }
     }
 }
@@ -260,64 +279,47 @@ __global__ __launch_bounds__(256, 1) void lmhead_big_kernel(e3g::GemmParams gp, 
                     st[row * 128 + ((nb * 32 + lr + 4 * row) & 127)] = acc[mb][nb][r];
                 }
         // a wave's LDS accesses complete in order: the scan below sees the stores
-        float lv[KK]; int li[KK];
-        e3_topk_init<KK>(lv, li);
+        uint64_t L[KK];
+        e3_kinit<KK>(L);
         float mx = -INFINITY, se = 0.f;
         const int row = lane;
         const int nvalid = min(128, gp.N - vbase);
-        // short lists: 32 columns at a time, eight 16-byte reads, then the
-        // batch maximum rescales the running sum once, and a batch whose
-        // maximum is below a full list's last entry is skipped (ties cannot
-        // enter either: the list's ids are all smaller). Long lists: one
-        // column at a time (an unrolled batch of long inserts is slower)
-        if constexpr (KK > 4) {
-            for (int j = 0; j < nvalid; ++j) {
-                const float x = st[row * 128 + ((j + 4 * row) & 127)];
-                const int v = vbase + j;
-                if (e3_better(x, v, lv[KK - 1], li[KK - 1])) e3_topk_insert<KK>(lv, li, x, v);
-                if (LSE) {
-                    if (x > mx) { se = se * __expf(mx - x) + 1.f; mx = x; }
-                    else se += __expf(x - mx);
-                }
-            }
-        } else for (int b = 0; b < 4; ++b) {
-            const int jv = nvalid - b * 32;   // valid columns in this batch
+        // 8 columns at a time: two 16-byte reads, the batch maximum rescales
+        // the running sum once, then branch-free inserts of the keys that
+        // beat the list's last entry
+        for (int b = 0; b < 16; ++b) {
+            const int jv = nvalid - b * 8;   // valid columns in this batch
             if (jv <= 0) break;
-            float xs[32];
+            float xs[8];
 #pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const f32x4_t t = *reinterpret_cast<const f32x4_t *>(st + row * 128 + ((b * 32 + 4 * q + 4 * row) & 127));
+            for (int q = 0; q < 2; ++q) {
+                const f32x4_t t = *reinterpret_cast<const f32x4_t *>(st + row * 128 + ((b * 8 + 4 * q + 4 * row) & 127));
                 xs[4 * q] = t[0]; xs[4 * q + 1] = t[1]; xs[4 * q + 2] = t[2]; xs[4 * q + 3] = t[3];
             }
 #pragma unroll
-            for (int i = 0; i < 32; ++i)
+            for (int i = 0; i < 8; ++i) {
                 if (i >= jv) xs[i] = -INFINITY;
-            float bm = xs[0];
-#pragma unroll
-            for (int i = 1; i < 32; ++i) bm = fmaxf(bm, xs[i]);
+                const uint64_t k = i < jv ? e3_key(xs[i], vbase + b * 8 + i) : 0;
+                if (k > L[KK - 1]) e3_kinsert<KK>(L, k);
+            }
             if (LSE) {
+                float bm = xs[0];
+#pragma unroll
+                for (int i = 1; i < 8; ++i) bm = fmaxf(bm, xs[i]);
                 const float nm = fmaxf(mx, bm);
                 if (nm != -INFINITY) {
                     float sb = 0.f;
 #pragma unroll
-                    for (int i = 0; i < 32; ++i) sb += __expf(xs[i] - nm);
+                    for (int i = 0; i < 8; ++i) sb += __expf(xs[i] - nm);
                     se = se * __expf(mx - nm) + sb;
                     mx = nm;
-                }
-            }
-            if (bm > lv[KK - 1] || li[KK - 1] == 0x7fffffff) {
-#pragma unroll
-                for (int i = 0; i < 32; ++i) {
-                    const int v = vbase + b * 32 + i;
-                    if (i < jv && e3_better(xs[i], v, lv[KK - 1], li[KK - 1])) e3_topk_insert<KK>(lv, li, xs[i], v);
                 }
             }
         }
         const int m = m0 + wm * 128 + half * 64 + row;
         if (m < gp.M) {
             const size_t rec = (size_t)m * nrec + rec_tile;
-#pragma unroll
-            for (int s2 = 0; s2 < KK; ++s2) { p.val[rec * KK + s2] = lv[s2]; p.idx[rec * KK + s2] = li[s2]; }
+            store_record<KK>(p, rec, L);
             if (LSE) { p.mx[rec] = mx; p.se[rec] = se; }
         }
     }
@@ -363,30 +365,34 @@ template <int KK, bool LSE>
 __global__ __launch_bounds__(256) void lmhead_merge_kernel(int ntiles, Partials p, int topk, int32_t *__restrict__ idx,
                                                            float *__restrict__ val, float *__restrict__ gap,
                                                            float *__restrict__ lse) {
-    __shared__ float sv[4][KK];
-    __shared__ int si[4][KK];
+    __shared__ uint64_t sk[4][KK];
     __shared__ float smx[4], sse[4];
     const int m = blockIdx.x;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    float lv[KK]; int li[KK];
-    e3_topk_init<KK>(lv, li);
+    uint64_t L[KK];
+    e3_kinit<KK>(L);
     float mx = -INFINITY, se = 0.f;
     for (int t = threadIdx.x; t < ntiles; t += 256) {
         const size_t rec = (size_t)m * ntiles + t;
-        float rv[KK]; int ri[KK];
+        uint64_t rk[KK];
+        const u32x4_t *src = reinterpret_cast<const u32x4_t *>(p.key + rec * KK);
 #pragma unroll
-        for (int s = 0; s < KK; ++s) { rv[s] = p.val[rec * KK + s]; ri[s] = p.idx[rec * KK + s]; }
+        for (int s = 0; s < KK; s += 2) {
+            const u32x4_t q = src[s / 2];
+            rk[s] = ((uint64_t)q[1] << 32) | q[0];
+            rk[s + 1] = ((uint64_t)q[3] << 32) | q[2];
+        }
         // a record is sorted: once an entry cannot enter, none after it can
 #pragma unroll
         for (int s = 0; s < KK; ++s) {
-            if (!e3_better(rv[s], ri[s], lv[KK - 1], li[KK - 1])) break;
-            e3_topk_insert<KK>(lv, li, rv[s], ri[s]);
+            if (!(rk[s] > L[KK - 1])) break;
+            e3_kinsert<KK>(L, rk[s]);
         }
         if (LSE) e3_lse_combine(mx, se, p.mx[rec], p.se[rec]);
     }
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
-        e3_topk_merge_xor<KK>(lv, li, off);
+        e3_kmerge_xor<KK>(L, off);
         if (LSE) {
             const float m2 = __shfl_xor(mx, off), s2 = __shfl_xor(se, off);
             e3_lse_combine(mx, se, m2, s2);
@@ -394,21 +400,28 @@ __global__ __launch_bounds__(256) void lmhead_merge_kernel(int ntiles, Partials 
     }
     if (lane == 0) {
 #pragma unroll
-        for (int s = 0; s < KK; ++s) { sv[wave][s] = lv[s]; si[wave][s] = li[s]; }
+        for (int s = 0; s < KK; ++s) sk[wave][s] = L[s];
         smx[wave] = mx; sse[wave] = se;
     }
     __syncthreads();
     if (threadIdx.x == 0) {
         for (int wv = 1; wv < 4; ++wv) {
 #pragma unroll
-            for (int s = 0; s < KK; ++s) e3_topk_insert<KK>(lv, li, sv[wv][s], si[wv][s]);
+            for (int s = 0; s < KK; ++s) {
+                const uint64_t k = sk[wv][s];
+                if (!(k > L[KK - 1])) break;
+                e3_kinsert<KK>(L, k);
+            }
             if (LSE) e3_lse_combine(mx, se, smx[wv], sse[wv]);
         }
-        for (int s = 0; s < topk; ++s) {
-            idx[(size_t)m * topk + s] = li[s];
-            if (val) val[(size_t)m * topk + s] = lv[s];
+#pragma unroll
+        for (int s = 0; s < KK; ++s) {
+            if (s < topk) {
+                idx[(size_t)m * topk + s] = e3_key_idx(L[s]);
+                if (val) val[(size_t)m * topk + s] = e3_key_val(L[s]);
+            }
         }
-        if (gap) gap[m] = lv[0] - lv[1];
+        if (gap) gap[m] = e3_key_val(L[0]) - e3_key_val(L[1]);
         if (LSE) lse[m] = mx + __logf(se);
     }
 }
@@ -424,9 +437,8 @@ Partials carve(void *ws, int M, int ntiles, int KK) {
     char *b = (char *)ws;
     const size_t rec = (size_t)M * ntiles;
     Partials p;
-    p.val = (float *)b; b += align256(rec * KK * sizeof(float));
-    p.idx = (int *)b;   b += align256(rec * KK * sizeof(int));
-    p.mx = (float *)b;  b += align256(rec * sizeof(float));
+    p.key = (uint64_t *)b; b += align256(rec * KK * sizeof(uint64_t));
+    p.mx = (float *)b;     b += align256(rec * sizeof(float));
     p.se = (float *)b;
     return p;
 }
@@ -483,7 +495,7 @@ extern "C" size_t eagle3_lmhead_workspace(int M, int N, int K, int topk, int dty
     const int ntiles = tiles_for(M, N, K, dtype);
     const int KK = kk_for(topk);
     const size_t rec = (size_t)M * ntiles;
-    return align256(rec * KK * 4) + align256(rec * KK * 4) + align256(rec * 4) + align256(rec * 4);
+    return align256(rec * KK * 8) + align256(rec * 4) + align256(rec * 4);
 }
 
 extern "C" int eagle3_lmhead_argmax(const void *hidden, const void *w, int M, int N, int K, int topk, int dtype,
