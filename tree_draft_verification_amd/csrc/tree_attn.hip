@@ -506,27 +506,46 @@ constexpr int CN_MAXH = 64;  // query heads the fused pass handles
 
 __global__ __launch_bounds__(256) void tree_attn_combine_norm_kernel(AttnParams p, uint16_t *__restrict__ norm_out,
                                                                      float eps) {
+    static_assert(CN_MAXS == 32 && CN_MAXH % 32 == 0, "8 lanes x 4 splits per head, 32 heads per pass");
     __shared__ float wgt[CN_MAXH][CN_MAXS];
     __shared__ float red[4];
     const int t = blockIdx.x % p.Tq, b = blockIdx.x / p.Tq;
     const int L = clamped_len(p.prefix_len, b, p.max_blocks, 16, p.num_blocks);
     const int nsplit_b = splits_of(L, p.split_keys, p.tree_split);
-    for (int hq = threadIdx.x; hq < p.Hq; hq += blockDim.x) {
-        const int kvh = hq / p.G, row = t * p.G + hq % p.G;
-        const size_t base = ((size_t)b * p.Hkv + kvh) * p.nsplit;
-        float M = -INFINITY;
-        for (int s = 0; s < nsplit_b; ++s) M = fmaxf(M, p.ws_ml[((base + s) * p.Rpad + row) * 2]);
-        float den = 0.f;
-        for (int s = 0; s < nsplit_b; ++s) {
-            const size_t prow = (base + s) * p.Rpad + row;
-            const float ms = p.ws_ml[prow * 2], ls = p.ws_ml[prow * 2 + 1];
-            const float w = (ms == -INFINITY) ? 0.f : ls * exp2f(ms - M);
-            wgt[hq][s] = w;
-            den += w;
+    // split weights: 8 lanes per head, lane j takes splits j, j+8, j+16, j+24
+    // (all loads issued together), max and sum over the 8 lanes by shuffles
+    {
+        const int j = threadIdx.x & 7;
+        for (int hq = threadIdx.x >> 3; hq < p.Hq; hq += 32) {
+            const int kvh = hq / p.G, row = t * p.G + hq % p.G;
+            const size_t base = ((size_t)b * p.Hkv + kvh) * p.nsplit;
+            float ms[4], ls[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int sp = j + 8 * u;
+                ms[u] = -INFINITY; ls[u] = 0.f;
+                if (sp < nsplit_b) {
+                    const f32x2_t ml = *reinterpret_cast<const f32x2_t *>(p.ws_ml + ((base + sp) * p.Rpad + row) * 2);
+                    ms[u] = ml[0]; ls[u] = ml[1];
+                }
+            }
+            float M = fmaxf(fmaxf(ms[0], ms[1]), fmaxf(ms[2], ms[3]));
+#pragma unroll
+            for (int off = 1; off < 8; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
+            float w[4], den = 0.f;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                w[u] = (ms[u] == -INFINITY) ? 0.f : ls[u] * exp2f(ms[u] - M);
+                den += w[u];
+            }
+#pragma unroll
+            for (int off = 1; off < 8; off <<= 1) den += __shfl_xor(den, off);
+            const float inv = den > 0.f ? 1.f / den : 0.f;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) wgt[hq][j + 8 * u] = w[u] * inv;   // zero past nsplit_b
+            if (p.lse && j == 0)
+                p.lse[((size_t)b * p.Tq + t) * p.Hq + hq] = den > 0.f ? (M + log2f(den)) * kLn2 : -INFINITY;
         }
-        const float inv = den > 0.f ? 1.f / den : 0.f;
-        for (int s = 0; s < nsplit_b; ++s) wgt[hq][s] *= inv;
-        if (p.lse) p.lse[((size_t)b * p.Tq + t) * p.Hq + hq] = den > 0.f ? (M + log2f(den)) * kLn2 : -INFINITY;
     }
     __syncthreads();
     const int K = p.Hq * DH;
@@ -541,13 +560,22 @@ __global__ __launch_bounds__(256) void tree_attn_combine_norm_kernel(AttnParams 
         const int kvh = hq / p.G, row = t * p.G + hq % p.G;
         const size_t base = ((size_t)b * p.Hkv + kvh) * p.nsplit;
         float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        for (int s = 0; s < nsplit_b; ++s) {
-            const float w = wgt[hq][s];
-            const float *src = p.ws_o + ((base + s) * p.Rpad + row) * DH + d;
-            const f32x4_t a = *reinterpret_cast<const f32x4_t *>(src);
-            const f32x4_t c4 = *reinterpret_cast<const f32x4_t *>(src + 4);
+        // splits 8 at a time, their loads in flight together
+        for (int s0 = 0; s0 < nsplit_b; s0 += 8) {
+            f32x4_t a[8], c4[8];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) { o[i] += w * a[i]; o[4 + i] += w * c4[i]; }
+            for (int u = 0; u < 8; ++u) {
+                const int sp = min(s0 + u, nsplit_b - 1);   // weight 0 past the end
+                const float *src = p.ws_o + ((base + sp) * p.Rpad + row) * DH + d;
+                a[u] = *reinterpret_cast<const f32x4_t *>(src);
+                c4[u] = *reinterpret_cast<const f32x4_t *>(src + 4);
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const float w = (s0 + u < nsplit_b) ? wgt[hq][s0 + u] : 0.f;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) { o[i] += w * a[u][i]; o[4 + i] += w * c4[u][i]; }
+            }
         }
         u32x4_t packed;
 #pragma unroll
