@@ -11,9 +11,11 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 
 // bf16 GEMM tiles: BM x 256 outputs per 256-thread work-group (BM = 256 or
 // 128), waves 2 x 2, each (BM/2) x 128 in 32 x 32 MFMA blocks. K advances in
-// chunks of 32 through a 4-stage LDS ring filled by 16-byte global_load_lds
-// (three chunks in flight while one is multiplied).
-constexpr int GBN = 256, GBK = 32, GNS = 4, GROW = GBK * 2;  // LDS row: 32 bf16 = 64 B
+// chunks of 32 through an LDS ring filled by 16-byte global_load_lds: 4
+// stages for BM = 256 (three chunks in flight while one is multiplied, one
+// work-group per CU), 3 stages for BM = 128 (72 KB, so two work-groups share
+// a CU and one's waits are covered by the other's MFMAs).
+constexpr int GBN = 256, GBK = 32, GROW = GBK * 2;  // LDS row: 32 bf16 = 64 B
 constexpr int GSEG_ALIGN = 64;                                 // segment widths are multiples of this
 
 template <int BM>
@@ -21,6 +23,8 @@ struct GTile {
     static constexpr int STAGE = (BM + GBN) * GROW;  // bytes per ring stage
     static constexpr int LOADS = STAGE / 1024 / 4;   // 1 KB DMA loads per wave per stage
     static constexpr int MB = BM / 64, NB = GBN / 64;  // 32 x 32 blocks per wave
+    static constexpr int NS = BM == 256 ? 4 : 3;       // ring stages
+    static constexpr int RING = NS * STAGE;             // ring bytes
 };
 
 struct GemmParams {
@@ -90,7 +94,7 @@ __device__ __forceinline__ void fill_arow(const GemmParams &p, int m0, int (*aro
     __syncthreads();
 }
 
-// The K loop of one BM x 256 tile at (m0, n0). ring: GNS * GTile<BM>::STAGE
+// The K loop of one BM x 256 tile at (m0, n0). ring: GTile<BM>::RING
 // bytes of LDS (1 KB aligned). On return acc holds the tile: wave (wm, wn) =
 // (wave / 2, wave % 2), block (mb, nb), register r of lane (lr, lh) is
 // C[m0 + wm BM/2 + 32 mb + 8 (r / 4) + 4 lh + r % 4][n0 + 128 wn + 32 nb + lr].
@@ -152,7 +156,7 @@ __device__ __forceinline__ void mainloop(const GemmParams &p, int m0, int n0, un
 
     const int nch = p.K / GBK;
 #pragma unroll
-    for (int st = 0; st < GNS - 1; ++st)
+    for (int st = 0; st < T::NS - 1; ++st)
         if (st < nch) issue(st, st * GBK);
     const int wm = wave >> 1, wn = wave & 1;
     // per-lane LDS byte offsets of the operand rows (sub-step 0 and 1 differ by the column)
@@ -172,7 +176,7 @@ __device__ __forceinline__ void mainloop(const GemmParams &p, int m0, int n0, un
         }
     }
     auto wait_chunk = [&](int c) {  // chunk c has landed in LDS for every wave
-        const int ahead = min(nch - 1 - c, GNS - 2);
+        const int ahead = min(nch - 1 - c, T::NS - 2);
         if (ahead >= 2) wait_vmcnt<2 * T::LOADS>();
         else if (ahead == 1) wait_vmcnt<T::LOADS>();
         else wait_vmcnt<0>();
@@ -218,7 +222,7 @@ __device__ __forceinline__ void mainloop(const GemmParams &p, int m0, int n0, un
     // A: MFMAs of (c, first half) with the reads of (c, second half) between them.
     auto phase_a = [&](int c) {
         lgkm_wait<0, T::MB>(av0, bv0);
-        const int sl = c % GNS;
+        const int sl = c % T::NS;
 #pragma unroll
         for (int j = 0; j < NMF; ++j) {
             mf(j, av0, bv0);
@@ -231,9 +235,9 @@ __device__ __forceinline__ void mainloop(const GemmParams &p, int m0, int n0, un
         lgkm_wait<0, T::MB>(av1, bv1);
     };
     // C: MFMAs of (c, second half) with the reads of (c + 1, first half) and,
-    // when `refill`, the loads of chunk c + GNS into chunk c's slot.
+    // when `refill`, the loads of chunk c + NS into chunk c's slot.
     auto phase_c = [&](int c, bool next, bool refill) {
-        const int sl = (c + 1) % GNS, kc = (c + GNS) * GBK;
+        const int sl = (c + 1) % T::NS, kc = (c + T::NS) * GBK;
         if (refill) select_seg(kc);
         if (next && refill) {
 #pragma unroll
@@ -245,7 +249,7 @@ __device__ __forceinline__ void mainloop(const GemmParams &p, int m0, int n0, un
                     __builtin_amdgcn_sched_barrier(0);
                 }
                 if (j >= NMF - T::LOADS) {
-                    dma(c % GNS, kc, j - (NMF - T::LOADS));
+                    dma(c % T::NS, kc, j - (NMF - T::LOADS));
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
@@ -266,15 +270,15 @@ __device__ __forceinline__ void mainloop(const GemmParams &p, int m0, int n0, un
     };
     if (nch > 0) {
         wait_chunk(0);
-        if (GNS - 1 < nch) issue(GNS - 1, (GNS - 1) * GBK);
+        if (T::NS - 1 < nch) issue(T::NS - 1, (T::NS - 1) * GBK);
 #pragma unroll
         for (int i = 0; i < NRD; ++i) rd(0, 0, i, av0, bv0);
     }
     // steady state: every chunk refills a slot, wait depth is fixed
-    const int steady = nch - GNS;
+    const int steady = nch - T::NS;
     for (int c = 0; c < steady; ++c) {
         phase_a(c);
-        wait_vmcnt<2 * T::LOADS>();  // chunk c + 1 has landed (c + 2, c + 3 may be in flight)
+        wait_vmcnt<(T::NS - 2) * T::LOADS>();  // chunk c + 1 has landed (later ones may be in flight)
         __builtin_amdgcn_s_barrier();
         __asm__ volatile("" ::: "memory");
         phase_c(c, true, true);

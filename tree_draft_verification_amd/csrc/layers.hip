@@ -20,9 +20,9 @@ using namespace e3g;
 // C[M, N] = A[M, K] . B[N, K]^T (+ R), bf16 in/out, fp32 accumulate. A is up
 // to three K-segments, each optionally row-gathered.
 template <int BM>
-__global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmParams p) {
+__global__ __launch_bounds__(256, BM == 128 ? 2 : 1) void gemm_bf16_kernel(GemmParams p) {
     using T = GTile<BM>;
-    __shared__ __attribute__((aligned(1024))) unsigned char ring[GNS * T::STAGE];
+    __shared__ __attribute__((aligned(1024))) unsigned char ring[T::RING];
     __shared__ int arow[3][BM];  // source row of each tile row, per segment
     int mt, nt;
     tile_of(blockIdx.x, gridDim.x, p.mt, p.nt, mt, nt);
@@ -232,16 +232,11 @@ extern "C" int eagle3_gemm(const eagle3_gemm_args *a, void *stream) {
     p.M = a->M; p.N = a->N; p.K = K; p.ldc = ldc;
     const hipStream_t st = e3_stream(stream);
     if (a->dtype == EAGLE3_BF16) {
-        // 256-row tiles once they fill the chip, 128-row tiles below that
+        // 128-row tiles, two work-groups per CU: measured at least as fast as
+        // 256-row tiles (one per CU) from 640 x 28672 x 4096 to 8192^3
         const int nt = (a->N + GBN - 1) / GBN;
-        const int mt256 = (a->M + 255) / 256;
-        if ((long)mt256 * nt >= 256) {
-            p.mt = mt256; p.nt = nt;
-            gemm_bf16_kernel<256><<<mt256 * nt, 256, 0, st>>>(p);
-        } else {
-            p.mt = (a->M + 127) / 128; p.nt = nt;
-            gemm_bf16_kernel<128><<<p.mt * nt, 256, 0, st>>>(p);
-        }
+        p.mt = (a->M + 127) / 128; p.nt = nt;
+        gemm_bf16_kernel<128><<<p.mt * nt, 256, 0, st>>>(p);
     } else {
         dim3 grid((a->M + 15) / 16, (a->N + 15) / 16);
         gemm_f32_kernel<<<grid, 256, 0, st>>>(p);

@@ -229,9 +229,12 @@ __global__ __launch_bounds__(256, 2) void lmhead_bf16_kernel(const uint16_t *__r
 }
 
 // Many hidden rows (verify batches of whole trees, draft steps): the head is
-// a dense bf16 GEMM. 256 hidden rows x 256 vocabulary rows per work-group on
-// the shared GEMM core; the logit tile is then staged in LDS a quarter (64
-// hidden rows) at a time for the same per-row selection.
+// a dense bf16 GEMM on the shared GEMM core, BM hidden rows x 256 vocabulary
+// rows per work-group. BM = 256 (one work-group per CU, the most reuse) for
+// short lists; BM = 128 (two per CU, so one's long selection epilogue
+// overlaps the other's MFMAs) for lists of 8 and more. Each wave's logit
+// block is then staged in LDS 64 (BM = 256) or 32 (BM = 128) hidden rows at a
+// time for the per-row selection.
 // Work-group order: hidden tiles fastest, so the work-groups of one
 // vocabulary tile run together and read its weight rows once; each XCD takes
 // a contiguous run.
@@ -243,63 +246,70 @@ __device__ __forceinline__ void lm_tile_of(int L, int nwg, int MT, int &mt, int 
 }
 
 constexpr int BIG_BN = e3g::GBN;  // vocabulary rows per tile, many-row path
+constexpr int big_bm(int KK) { return KK >= 8 ? 128 : 256; }
 
-template <int KK, bool LSE>
-__global__ __launch_bounds__(256, 1) void lmhead_big_kernel(e3g::GemmParams gp, int nrec, Partials p) {
-    using T = e3g::GTile<256>;
-    __shared__ __attribute__((aligned(1024))) unsigned char ring[e3g::GNS * T::STAGE];
-    __shared__ int arow[3][256];
-    static_assert(4 * 64 * 128 * sizeof(float) <= sizeof(ring), "per-wave staging must fit the ring");
+template <int BM, int KK, bool LSE>
+__global__ __launch_bounds__(256, BM == 128 ? 2 : 1) void lmhead_big_kernel(e3g::GemmParams gp, int nrec,
+                                                                             Partials p) {
+    using T = e3g::GTile<BM>;
+    constexpr int LPR = BM == 256 ? 1 : 2;  // lanes per hidden row in the selection
+    constexpr int RP = 64 / LPR;            // hidden rows staged per pass
+    constexpr int CPL = 128 / LPR;          // columns one lane scans
+    constexpr int MBP = RP / 32;            // 32-row accumulator blocks per pass
+    __shared__ __attribute__((aligned(1024))) unsigned char ring[T::RING];
+    __shared__ int arow[3][BM];
+    static_assert(4 * RP * 128 * sizeof(float) <= sizeof(ring), "per-wave staging must fit the ring");
     int mt, nt;
     lm_tile_of(blockIdx.x, gridDim.x, gp.mt, mt, nt);
-    const int m0 = mt * 256, n0 = nt * BIG_BN;
+    const int m0 = mt * BM, n0 = nt * BIG_BN;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int lr = lane & 31, lh = lane >> 5, wm = wave >> 1, wn = wave & 1;
-    e3g::fill_arow<256>(gp, m0, arow);
+    e3g::fill_arow<BM>(gp, m0, arow);
     f32x16_t acc[T::MB][T::NB];
-    e3g::mainloop<256>(gp, m0, n0, ring, arow, acc);
+    e3g::mainloop<BM>(gp, m0, n0, ring, arow, acc);
     __syncthreads();  // every wave is done with the ring
-    // Each wave selects over its own 128 x 128 sub-tile, 64 hidden rows at a
-    // time, staged in a private 32 KB slice of the ring (columns rotated by 4
-    // per row, so 16-byte row reads of 16 lanes cover all banks); one lane
-    // owns one row, so there is no merging inside the tile. Its record is
-    // (row, 2 * tile + column half).
-    float *st = reinterpret_cast<float *>(ring) + wave * 64 * 128;
+    // Each wave selects over its own (BM/2) x 128 block, RP hidden rows at a
+    // time, staged in a private slice of the ring (columns rotated by 4 per
+    // row). Lane (row, ch) scans CPL columns of its row; with two lanes per
+    // row the halves merge by one shuffle. The record is (row, 2 * tile + wn).
+    float *st = reinterpret_cast<float *>(ring) + wave * RP * 128;
     const int vbase = n0 + wn * 128;
     const int rec_tile = 2 * nt + wn;
+    const int row = lane % RP, ch = lane / RP;
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
+    for (int pass = 0; pass < T::MB / MBP; ++pass) {
 #pragma unroll
-        for (int mb = 2 * half; mb < 2 * half + 2; ++mb)
+        for (int mbi = 0; mbi < MBP; ++mbi)
 #pragma unroll
             for (int nb = 0; nb < T::NB; ++nb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int row = (mb & 1) * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-                    st[row * 128 + ((nb * 32 + lr + 4 * row) & 127)] = acc[mb][nb][r];
+                    const int sr = mbi * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+                    st[sr * 128 + ((nb * 32 + lr + 4 * sr) & 127)] = acc[pass * MBP + mbi][nb][r];
                 }
         // a wave's LDS accesses complete in order: the scan below sees the stores
         uint64_t L[KK];
         e3_kinit<KK>(L);
         float mx = -INFINITY, se = 0.f;
-        const int row = lane;
-        const int nvalid = min(128, gp.N - vbase);
+        const int c0 = CPL * ch;
+        const int nvalid = min(CPL, gp.N - vbase - c0);
         // 8 columns at a time: two 16-byte reads, the batch maximum rescales
         // the running sum once, then branch-free inserts of the keys that
         // beat the list's last entry
-        for (int b = 0; b < 16; ++b) {
+        for (int b = 0; b < CPL / 8; ++b) {
             const int jv = nvalid - b * 8;   // valid columns in this batch
             if (jv <= 0) break;
             float xs[8];
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
-                const f32x4_t t = *reinterpret_cast<const f32x4_t *>(st + row * 128 + ((b * 8 + 4 * q + 4 * row) & 127));
+                const f32x4_t t =
+                    *reinterpret_cast<const f32x4_t *>(st + row * 128 + ((c0 + b * 8 + 4 * q + 4 * row) & 127));
                 xs[4 * q] = t[0]; xs[4 * q + 1] = t[1]; xs[4 * q + 2] = t[2]; xs[4 * q + 3] = t[3];
             }
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 if (i >= jv) xs[i] = -INFINITY;
-                const uint64_t k = i < jv ? e3_key(xs[i], vbase + b * 8 + i) : 0;
+                const uint64_t k = i < jv ? e3_key(xs[i], vbase + c0 + b * 8 + i) : 0;
                 if (k > L[KK - 1]) e3_kinsert<KK>(L, k);
             }
             if (LSE) {
@@ -316,8 +326,15 @@ __global__ __launch_bounds__(256, 1) void lmhead_big_kernel(e3g::GemmParams gp, 
                 }
             }
         }
-        const int m = m0 + wm * 128 + half * 64 + row;
-        if (m < gp.M) {
+        if constexpr (LPR == 2) {
+            e3_kmerge_xor<KK>(L, 32);
+            if (LSE) {
+                const float m2 = __shfl_xor(mx, 32), s2 = __shfl_xor(se, 32);
+                e3_lse_combine(mx, se, m2, s2);
+            }
+        }
+        const int m = m0 + wm * (BM / 2) + pass * RP + row;
+        if (ch == 0 && m < gp.M) {
             const size_t rec = (size_t)m * nrec + rec_tile;
             store_record<KK>(p, rec, L);
             if (LSE) { p.mx[rec] = mx; p.se[rec] = se; }
@@ -464,8 +481,9 @@ void launch(const void *hidden, const void *w, int M, int N, int K, int topk, in
         e3g::GemmParams gp{};
         gp.a[0] = hidden; gp.k[0] = K; gp.nseg = 1;
         gp.b = w; gp.M = M; gp.N = N; gp.K = K; gp.ldc = N;
-        gp.mt = (M + 255) / 256; gp.nt = (N + BIG_BN - 1) / BIG_BN;
-        lmhead_big_kernel<KK, LSE><<<gp.mt * gp.nt, 256, 0, st>>>(gp, ntiles, p);
+        constexpr int BM = big_bm(KK);
+        gp.mt = (M + BM - 1) / BM; gp.nt = (N + BIG_BN - 1) / BIG_BN;
+        lmhead_big_kernel<BM, KK, LSE><<<gp.mt * gp.nt, 256, 0, st>>>(gp, ntiles, p);
     } else if (dtype == EAGLE3_BF16) {
         dim3 grid((M + 63) / 64, ntiles);
         if (grid.x == 1)
