@@ -11,19 +11,19 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 
 // bf16 GEMM tiles: BM x 256 outputs per 256-thread work-group (BM = 256 or
 // 128), waves 2 x 2, each (BM/2) x 128 in 32 x 32 MFMA blocks. K advances in
-// chunks of 32 through an LDS ring filled by 16-byte global_load_lds: 4
-// stages for BM = 256 (three chunks in flight while one is multiplied, one
-// work-group per CU), 3 stages for BM = 128 (72 KB, so two work-groups share
-// a CU and one's waits are covered by the other's MFMAs).
+// chunks of 32 through an NS-stage LDS ring filled by 16-byte
+// global_load_lds: NS = 4 keeps three chunks in flight while one is
+// multiplied (one work-group per CU); BM = 128 with NS = 3 takes 72 KB, so
+// two work-groups share a CU and one's waits are covered by the other's MFMAs.
 constexpr int GBN = 256, GBK = 32, GROW = GBK * 2;  // LDS row: 32 bf16 = 64 B
 constexpr int GSEG_ALIGN = 64;                                 // segment widths are multiples of this
 
-template <int BM>
+template <int BM, int NS_ = 4>
 struct GTile {
     static constexpr int STAGE = (BM + GBN) * GROW;  // bytes per ring stage
     static constexpr int LOADS = STAGE / 1024 / 4;   // 1 KB DMA loads per wave per stage
     static constexpr int MB = BM / 64, NB = GBN / 64;  // 32 x 32 blocks per wave
-    static constexpr int NS = BM == 256 ? 4 : 3;       // ring stages
+    static constexpr int NS = NS_;                      // ring stages
     static constexpr int RING = NS * STAGE;             // ring bytes
 };
 
@@ -94,15 +94,15 @@ __device__ __forceinline__ void fill_arow(const GemmParams &p, int m0, int (*aro
     __syncthreads();
 }
 
-// The K loop of one BM x 256 tile at (m0, n0). ring: GTile<BM>::RING
+// The K loop of one BM x 256 tile at (m0, n0). ring: GTile<BM, NS>::RING
 // bytes of LDS (1 KB aligned). On return acc holds the tile: wave (wm, wn) =
 // (wave / 2, wave % 2), block (mb, nb), register r of lane (lr, lh) is
 // C[m0 + wm BM/2 + 32 mb + 8 (r / 4) + 4 lh + r % 4][n0 + 128 wn + 32 nb + lr].
-template <int BM>
+template <int BM, int NS>
 __device__ __forceinline__ void mainloop(const GemmParams &p, int m0, int n0, unsigned char *ring,
                                          const int (*arow)[BM],
-                                         f32x16_t (&acc)[GTile<BM>::MB][GTile<BM>::NB]) {
-    using T = GTile<BM>;
+                                         f32x16_t (&acc)[GTile<BM, NS>::MB][GTile<BM, NS>::NB]) {
+    using T = GTile<BM, NS>;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int lr = lane & 31, lh = lane >> 5;
     // load j of this wave fills stage block blk = wave * LOADS + j (16 rows of

@@ -19,9 +19,9 @@ using namespace e3g;
 
 // C[M, N] = A[M, K] . B[N, K]^T (+ R), bf16 in/out, fp32 accumulate. A is up
 // to three K-segments, each optionally row-gathered.
-template <int BM>
-__global__ __launch_bounds__(256, BM == 128 ? 2 : 1) void gemm_bf16_kernel(GemmParams p) {
-    using T = GTile<BM>;
+template <int BM, int NS>
+__global__ __launch_bounds__(256, NS == 3 ? 2 : 1) void gemm_bf16_kernel(GemmParams p) {
+    using T = GTile<BM, NS>;
     __shared__ __attribute__((aligned(1024))) unsigned char ring[T::RING];
     __shared__ int arow[3][BM];  // source row of each tile row, per segment
     int mt, nt;
@@ -31,7 +31,7 @@ __global__ __launch_bounds__(256, BM == 128 ? 2 : 1) void gemm_bf16_kernel(GemmP
     const int lr = lane & 31, lh = lane >> 5, wm = wave >> 1, wn = wave & 1;
     fill_arow<BM>(p, m0, arow);
     f32x16_t acc[T::MB][T::NB];
-    mainloop<BM>(p, m0, n0, ring, arow, acc);
+    mainloop<BM, NS>(p, m0, n0, ring, arow, acc);
     // D[m][n]: lane holds n = lr of its block, m = 8 (r / 4) + 4 lh + r % 4
     const uint16_t *res = (const uint16_t *)p.res;
     uint16_t *cc = (uint16_t *)p.c;
@@ -232,11 +232,27 @@ extern "C" int eagle3_gemm(const eagle3_gemm_args *a, void *stream) {
     p.M = a->M; p.N = a->N; p.K = K; p.ldc = ldc;
     const hipStream_t st = e3_stream(stream);
     if (a->dtype == EAGLE3_BF16) {
-        // 128-row tiles, two work-groups per CU: measured at least as fast as
-        // 256-row tiles (one per CU) from 640 x 28672 x 4096 to 8192^3
+        // Tile shape by the amount of work (measured): 256-row tiles once
+        // they make four passes over the CUs (most reuse, 65536 x 4096 x
+        // 12288: 1.01 vs 0.90 PFLOP/s); else 128-row tiles two per CU while
+        // those fill both slots of every CU (640 x 28672 x 4096: 0.59 vs
+        // 0.50); else 256-row tiles if they fill the CUs once (3904 x 4096 x
+        // 4096: 0.82 vs 0.72); below that 128-row tiles one per CU with the
+        // deeper ring (640 x 4096 x 14336: 0.39 vs 0.33).
         const int nt = (a->N + GBN - 1) / GBN;
-        p.mt = (a->M + 127) / 128; p.nt = nt;
-        gemm_bf16_kernel<128><<<p.mt * nt, 256, 0, st>>>(p);
+        const long t256 = (long)((a->M + 255) / 256) * nt, t128 = (long)((a->M + 127) / 128) * nt;
+        const long cus = e3_cu_count();
+        p.nt = nt;
+        if (t256 >= 4 * cus || (t128 < 2 * cus && t256 >= cus)) {
+            p.mt = (a->M + 255) / 256;
+            gemm_bf16_kernel<256, 4><<<p.mt * nt, 256, 0, st>>>(p);
+        } else if (t128 >= 2 * cus) {
+            p.mt = (a->M + 127) / 128;
+            gemm_bf16_kernel<128, 3><<<p.mt * nt, 256, 0, st>>>(p);
+        } else {
+            p.mt = (a->M + 127) / 128;
+            gemm_bf16_kernel<128, 4><<<p.mt * nt, 256, 0, st>>>(p);
+        }
     } else {
         dim3 grid((a->M + 15) / 16, (a->N + 15) / 16);
         gemm_f32_kernel<<<grid, 256, 0, st>>>(p);

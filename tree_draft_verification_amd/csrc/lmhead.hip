@@ -251,7 +251,7 @@ constexpr int big_bm(int KK) { return KK >= 8 ? 128 : 256; }
 template <int BM, int KK, bool LSE>
 __global__ __launch_bounds__(256, BM == 128 ? 2 : 1) void lmhead_big_kernel(e3g::GemmParams gp, int nrec,
                                                                              Partials p) {
-    using T = e3g::GTile<BM>;
+    using T = e3g::GTile<BM, BM == 128 ? 3 : 4>;
     constexpr int LPR = BM == 256 ? 1 : 2;  // lanes per hidden row in the selection
     constexpr int RP = 64 / LPR;            // hidden rows staged per pass
     constexpr int CPL = 128 / LPR;          // columns one lane scans
@@ -266,7 +266,7 @@ __global__ __launch_bounds__(256, BM == 128 ? 2 : 1) void lmhead_big_kernel(e3g:
     const int lr = lane & 31, lh = lane >> 5, wm = wave >> 1, wn = wave & 1;
     e3g::fill_arow<BM>(gp, m0, arow);
     f32x16_t acc[T::MB][T::NB];
-    e3g::mainloop<BM>(gp, m0, n0, ring, arow, acc);
+    e3g::mainloop<BM, T::NS>(gp, m0, n0, ring, arow, acc);
     __syncthreads();  // every wave is done with the ring
     // Each wave selects over its own (BM/2) x 128 block, RP hidden rows at a
     // time, staged in a private slice of the ring (columns rotated by 4 per
