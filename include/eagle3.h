@@ -208,8 +208,17 @@ int eagle3_accept_path(const int32_t *tokens, const int32_t *parent, const uint6
  *   a[s]       [rows_s, k[s]] row-major          b  [N, sum k] row-major
  *   residual   [M, ldc] (nullable; may alias c)   c  [M, ldc] (ldc 0 = N)
  * bf16: fp32 accumulation, each k[s] % 64 == 0, pointers 16-byte aligned;
- * fp32: any sizes. Summation order is fixed per output column block, so a
- * row's result does not depend on the other rows of the call.
+ * fp32: any sizes. Without a workspace the summation order is fixed per
+ * output column block, so a row's result does not depend on the other rows
+ * of the call.
+ * ws / ws_bytes (optional, device, caller-owned, 16-byte aligned): when the
+ * output tiles would leave more than half of the CUs idle, a bf16 call given
+ * at least eagle3_gemm_workspace(args) bytes splits K over up to 8
+ * work-groups per tile and adds the fp32 partials in split order (plus the
+ * residual) before the one rounding to bf16. The split count depends on M,
+ * so with a workspace a row's rounding can depend on the batch (results stay
+ * within the same accuracy). NULL or too small: no split, same results as
+ * without.
  */
 typedef struct eagle3_gemm_args {
     int dtype;
@@ -223,7 +232,12 @@ typedef struct eagle3_gemm_args {
     const void *residual;
     void *c;
     int ldc;
+    void *ws;
+    size_t ws_bytes;
 } eagle3_gemm_args;
+
+/* bytes of workspace the call would use to split K (0: it would not split) */
+size_t eagle3_gemm_workspace(const eagle3_gemm_args *args);
 
 int eagle3_gemm(const eagle3_gemm_args *args, void *stream);
 
@@ -273,7 +287,9 @@ int eagle3_commit_kv(const void *k_rows, const void *v_rows, int rows_per_seq, c
  * l, m, h, a_prev, g_out, x_out [M, k]; tok [M] int32 (the token one step
  * ahead of each row); E [V, k]; w_fuse [k, 3k]; w_in [k, 2k] (output-major).
  * g is stored (g_out, or the workspace when g_out is NULL) in the storage type
- * before the second FC. bf16 needs k % 64 == 0.
+ * before the second FC. bf16 needs k % 64 == 0. The workspace query also
+ * covers the K splits of the two GEMMs (see eagle3_gemm); a smaller
+ * workspace that still holds g (or none, with g_out) runs them unsplit.
  */
 size_t eagle3_draft_fuse_workspace(int M, int k, int dtype);
 int eagle3_draft_fuse(const void *l, const void *m, const void *h, const void *a_prev, const int32_t *tok,

@@ -47,7 +47,7 @@ def test_status_strings(lib):
     for code in (0, -1, -2, -3, -4, -5, -6):
         s = lib.eagle3_status_string(code).decode()
         assert s.startswith("EAGLE3_")
-    assert lib.eagle3_abi_version() == 1
+    assert lib.eagle3_abi_version() == 2
 
 
 FAKE = 0x10000          # 16-byte aligned, never dereferenced on the host

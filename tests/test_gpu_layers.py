@@ -24,10 +24,13 @@ def _bf16_ulp(x16):
     return np.ldexp(1.0, np.maximum(e, 1) - 127 - 7)
 
 
-# (4000, 4100, ...) fills the chip with 256-row tiles and leaves ragged M and N tails
-@pytest.mark.parametrize("M,N,k", [(1, 128, [64]), (200, 300, [128, 64, 192]), (640, 256, [256, 128]),
-                                   (4000, 4100, [128, 64, 64])])
-def test_gemm_bf16_segments_and_gather(orc, lib, M, N, k):
+# (4000, 4100, ...) fills the chip with 256-row tiles and leaves ragged M and N tails;
+# with a workspace, (640, 4096, ...) splits K in 3 across segment boundaries and
+# (64, 1000, ...) in 8 with a ragged N tile
+@pytest.mark.parametrize("M,N,k,split", [(1, 128, [64], False), (200, 300, [128, 64, 192], False),
+                                         (640, 256, [256, 128], False), (4000, 4100, [128, 64, 64], False),
+                                         (640, 4096, [1024, 512, 512], True), (64, 1000, [4096, 4096], True)])
+def test_gemm_bf16_segments_and_gather(orc, lib, M, N, k, split):
     rng = np.random.default_rng(M + N)
     segs = [synth.normal_bf16(rng, (M if s != 1 else 50, ks)) for s, ks in enumerate(k)]
     rows = [None] * len(k)
@@ -41,7 +44,12 @@ def test_gemm_bf16_segments_and_gather(orc, lib, M, N, k):
     rd = [None if r is None else dev(r) for r in rows]
     c = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
     Bd, Rd = dev(B), dev(R)
-    lib.eagle3_gemm(sd, Bd, c, residual=Rd, a_rows=rd)
+    ws = None
+    if split:
+        need = lib.eagle3_gemm_workspace(sd, Bd, c)
+        assert need > 0
+        ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    lib.eagle3_gemm(sd, Bd, c, residual=Rd, a_rows=rd, ws=ws)
     torch.cuda.synchronize()
     got = host(c)
     rel, mx = normwise_rel(got, ref)
@@ -56,6 +64,33 @@ def test_gemm_bf16_segments_and_gather(orc, lib, M, N, k):
     bad = d > ulp * 1.0001 + 4e-6 * S
     assert not bad.any(), (int(bad.sum()), d[bad][:5], as_f64(ref)[bad][:5], np.argwhere(bad)[:5])
     assert (got == ref).mean() >= 0.98, (got == ref).mean()
+
+
+def test_gemm_split_k_in_place_residual(orc, lib):
+    """Split-K path with the residual aliasing the output (x += A . B^T), as
+    the draft layer's O and down projections do; the split result stays within
+    the unsplit path's bound of it."""
+    rng = np.random.default_rng(9)
+    M, N, K = 640, 4096, 4096
+    A, B, X = synth.normal_bf16(rng, (M, K)), synth.normal_bf16(rng, (N, K), 0.02), synth.normal_bf16(rng, (M, N))
+    ref = orc.gemm(A, B, X)
+    Ad, Bd = dev(A), dev(B)
+    x = dev(X)
+    x0 = dev(X)
+    need = lib.eagle3_gemm_workspace([Ad], Bd, x)
+    assert need > 0
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    lib.eagle3_gemm([Ad], Bd, x, residual=x, ws=ws)
+    lib.eagle3_gemm([Ad], Bd, x0, residual=x0)
+    torch.cuda.synchronize()
+    got, unsplit = host(x), host(x0)
+    rel, mx = normwise_rel(got, ref)
+    assert rel <= 2e-2, (rel, mx)
+    d = np.abs(as_f64(got) - as_f64(ref))
+    S = np.abs(as_f64(A)) @ np.abs(as_f64(B)).T + np.abs(as_f64(X))
+    bad = d > np.maximum(_bf16_ulp(ref), _bf16_ulp(got)) * 1.0001 + 4e-6 * S
+    assert not bad.any(), int(bad.sum())
+    assert (got == unsplit).mean() >= 0.98
 
 
 def test_gemm_f32_and_in_place_residual(orc, lib):

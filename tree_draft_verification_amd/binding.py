@@ -43,7 +43,7 @@ class GemmArgs(ctypes.Structure):
     _fields_ = [
         ("dtype", I), ("M", I), ("N", I), ("nseg", I),
         ("a", P * 3), ("a_rows", P * 3), ("a_nrows", I * 3), ("k", I * 3),
-        ("b", P), ("residual", P), ("c", P), ("ldc", I),
+        ("b", P), ("residual", P), ("c", P), ("ldc", I), ("ws", P), ("ws_bytes", SZ),
     ]
 
 
@@ -64,6 +64,7 @@ _lmhead_ws = _sig("eagle3_lmhead_workspace", SZ, I, I, I, I, I)
 _lmhead = _sig("eagle3_lmhead_argmax", I, P, P, I, I, I, I, I, P, P, P, P, P, SZ, P)
 _accept = _sig("eagle3_accept_path", I, P, P, P, I, P, I, I, P, P, P, P)
 _gemm = _sig("eagle3_gemm", I, ctypes.POINTER(GemmArgs), P)
+_gemm_ws = _sig("eagle3_gemm_workspace", SZ, ctypes.POINTER(GemmArgs))
 _silu_mul = _sig("eagle3_silu_mul", I, P, I, I, I, P, P)
 _rope = _sig("eagle3_rope", I, P, I, I, I, I, P, I, F, I, P)
 _embed = _sig("eagle3_embed", I, P, P, I, I, I, I, P, P)
@@ -179,9 +180,7 @@ def eagle3_accept_path(tokens, target_idx, accept_len, path, out_tokens, parent=
                    _ptr(out_tokens), _stream(stream)), "eagle3_accept_path")
 
 
-def eagle3_gemm(a, b, c, residual=None, a_rows=None, a_nrows=None, ldc=0, M=None, stream=None):
-    """C = [a_0 | a_1 | ...] . b^T (+ residual); a: list of [rows, k_s] tensors
-    (a_rows[s]: optional int32 row gather of segment s)."""
+def _gemm_args(a, b, c, residual, a_rows, ldc, M, ws):
     a = list(a)
     g = GemmArgs()
     g.dtype = _dtype(b)
@@ -195,6 +194,21 @@ def eagle3_gemm(a, b, c, residual=None, a_rows=None, a_nrows=None, ldc=0, M=None
         g.a_rows[i] = _ptr(rows[i])
         g.a_nrows[i] = int(t.shape[0]) if rows[i] is not None else 0
     g.b, g.residual, g.c, g.ldc = _ptr(b), _ptr(residual), _ptr(c), int(ldc)
+    g.ws = _ptr(ws)
+    g.ws_bytes = ws.numel() * ws.element_size() if isinstance(ws, torch.Tensor) else 0
+    return g
+
+
+def eagle3_gemm_workspace(a, b, c, M=None) -> int:
+    """Bytes of workspace eagle3_gemm would use for this call to split K."""
+    return int(_gemm_ws(ctypes.byref(_gemm_args(a, b, c, None, None, 0, M, None))))
+
+
+def eagle3_gemm(a, b, c, residual=None, a_rows=None, a_nrows=None, ldc=0, M=None, stream=None, ws=None):
+    """C = [a_0 | a_1 | ...] . b^T (+ residual); a: list of [rows, k_s] tensors
+    (a_rows[s]: optional int32 row gather of segment s; ws: optional workspace
+    that lets a call with few output tiles split K)."""
+    g = _gemm_args(a, b, c, residual, a_rows, ldc, M, ws)
     _check(_gemm(ctypes.byref(g), _stream(stream)), "eagle3_gemm")
 
 

@@ -7,10 +7,29 @@
 // embedding rows are gathered inside the GEMM's A operand.
 #include "common.h"
 
-extern "C" size_t eagle3_draft_fuse_workspace(int M, int k, int dtype) {
-    if (M <= 0 || k <= 0) return 0;
+namespace {
+
+size_t g_bytes(int M, int k, int dtype) {
     const size_t esz = dtype == EAGLE3_BF16 ? 2 : 4;
     return ((size_t)M * k * esz + 255) & ~(size_t)255;
+}
+
+// K-split workspace of the two FCs (the larger of the two)
+size_t split_bytes(int M, int k, int dtype) {
+    eagle3_gemm_args a{};
+    a.dtype = dtype; a.M = M; a.N = k;
+    a.nseg = 3; a.k[0] = a.k[1] = a.k[2] = k;
+    const size_t s3 = eagle3_gemm_workspace(&a);
+    a.nseg = 2; a.k[2] = 0;
+    const size_t s2 = eagle3_gemm_workspace(&a);
+    return s3 > s2 ? s3 : s2;
+}
+
+}  // namespace
+
+extern "C" size_t eagle3_draft_fuse_workspace(int M, int k, int dtype) {
+    if (M <= 0 || k <= 0) return 0;
+    return g_bytes(M, k, dtype) + split_bytes(M, k, dtype);
 }
 
 extern "C" int eagle3_draft_fuse(const void *l, const void *m, const void *h, const void *a_prev, const int32_t *tok,
@@ -25,10 +44,18 @@ extern "C" int eagle3_draft_fuse(const void *l, const void *m, const void *h, co
     if (context && (!l || !m || !h || !w_fuse)) return EAGLE3_ERR_ARG;
     if (!context && (l || m || h)) return EAGLE3_ERR_ARG;
     const void *first = a_prev;
+    // K-split space after the g region, when the caller gave enough
+    const size_t gb = g_bytes(M, k, dtype);
+    void *split_ws = nullptr;
+    size_t split_ws_bytes = 0;
+    if (ws && ws_bytes > gb) {
+        split_ws = (char *)ws + gb;
+        split_ws_bytes = ws_bytes - gb;
+    }
     if (context) {
         void *g = g_out;
         if (!g) {
-            if (ws_bytes < eagle3_draft_fuse_workspace(M, k, dtype) || !ws) return EAGLE3_ERR_WORKSPACE;
+            if (ws_bytes < gb || !ws) return EAGLE3_ERR_WORKSPACE;
             g = ws;
         }
         eagle3_gemm_args fa{};
@@ -36,6 +63,7 @@ extern "C" int eagle3_draft_fuse(const void *l, const void *m, const void *h, co
         fa.a[0] = l; fa.a[1] = m; fa.a[2] = h;
         fa.k[0] = fa.k[1] = fa.k[2] = k;
         fa.b = w_fuse; fa.c = g; fa.ldc = k;
+        fa.ws = split_ws; fa.ws_bytes = split_ws_bytes;
         const int rc = eagle3_gemm(&fa, stream);
         if (rc != EAGLE3_OK) return rc;
         first = g;
@@ -45,5 +73,6 @@ extern "C" int eagle3_draft_fuse(const void *l, const void *m, const void *h, co
     xa.a[0] = first; xa.k[0] = k;
     xa.a[1] = E; xa.a_rows[1] = tok; xa.a_nrows[1] = V; xa.k[1] = k;
     xa.b = w_in; xa.c = x_out; xa.ldc = k;
+    xa.ws = split_ws; xa.ws_bytes = split_ws_bytes;
     return eagle3_gemm(&xa, stream);
 }

@@ -94,13 +94,15 @@ __device__ __forceinline__ void fill_arow(const GemmParams &p, int m0, int (*aro
     __syncthreads();
 }
 
-// The K loop of one BM x 256 tile at (m0, n0). ring: GTile<BM, NS>::RING
+// The K loop of one BM x 256 tile at (m0, n0) over the k chunks c_begin ..
+// c_begin + nch - 1 (32 columns each; a split of K, or all of it). ring:
+// GTile<BM, NS>::RING
 // bytes of LDS (1 KB aligned). On return acc holds the tile: wave (wm, wn) =
 // (wave / 2, wave % 2), block (mb, nb), register r of lane (lr, lh) is
 // C[m0 + wm BM/2 + 32 mb + 8 (r / 4) + 4 lh + r % 4][n0 + 128 wn + 32 nb + lr].
 template <int BM, int NS>
-__device__ __forceinline__ void mainloop(const GemmParams &p, int m0, int n0, unsigned char *ring,
-                                         const int (*arow)[BM],
+__device__ __forceinline__ void mainloop(const GemmParams &p, int m0, int n0, int c_begin, int nch,
+                                         unsigned char *ring, const int (*arow)[BM],
                                          f32x16_t (&acc)[GTile<BM, NS>::MB][GTile<BM, NS>::NB]) {
     using T = GTile<BM, NS>;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -154,10 +156,9 @@ __device__ __forceinline__ void mainloop(const GemmParams &p, int m0, int n0, un
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][jj][r] = 0.f;
 
-    const int nch = p.K / GBK;
 #pragma unroll
     for (int st = 0; st < T::NS - 1; ++st)
-        if (st < nch) issue(st, st * GBK);
+        if (st < nch) issue(st, (c_begin + st) * GBK);
     const int wm = wave >> 1, wn = wave & 1;
     // per-lane LDS byte offsets of the operand rows (sub-step 0 and 1 differ by the column)
     int aoff[T::MB][2], boff[T::NB][2];
@@ -237,7 +238,7 @@ __device__ __forceinline__ void mainloop(const GemmParams &p, int m0, int n0, un
     // C: MFMAs of (c, second half) with the reads of (c + 1, first half) and,
     // when `refill`, the loads of chunk c + NS into chunk c's slot.
     auto phase_c = [&](int c, bool next, bool refill) {
-        const int sl = (c + 1) % T::NS, kc = (c + T::NS) * GBK;
+        const int sl = (c + 1) % T::NS, kc = (c_begin + c + T::NS) * GBK;
         if (refill) select_seg(kc);
         if (next && refill) {
 #pragma unroll
@@ -270,7 +271,7 @@ __device__ __forceinline__ void mainloop(const GemmParams &p, int m0, int n0, un
     };
     if (nch > 0) {
         wait_chunk(0);
-        if (T::NS - 1 < nch) issue(T::NS - 1, (T::NS - 1) * GBK);
+        if (T::NS - 1 < nch) issue(T::NS - 1, (c_begin + T::NS - 1) * GBK);
 #pragma unroll
         for (int i = 0; i < NRD; ++i) rd(0, 0, i, av0, bv0);
     }

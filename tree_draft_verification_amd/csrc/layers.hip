@@ -10,6 +10,8 @@
 // embedding of the token one step ahead and an FC takes 2k to k; a single
 // transformer layer follows. reading: that layer is a Llama decoder layer
 // (RMSNorm, GQA attention with rotate-half RoPE, SwiGLU MLP, residuals).
+#include <algorithm>
+
 #include "common.h"
 #include "gemm_core.h"
 
@@ -19,19 +21,43 @@ using namespace e3g;
 
 // C[M, N] = A[M, K] . B[N, K]^T (+ R), bf16 in/out, fp32 accumulate. A is up
 // to three K-segments, each optionally row-gathered.
-template <int BM, int NS>
-__global__ __launch_bounds__(256, NS == 3 ? 2 : 1) void gemm_bf16_kernel(GemmParams p) {
+//
+// Split K (SPLIT): work-group w takes tile w % tiles and k chunks
+// [s nch / S, (s + 1) nch / S) of split s = w / tiles, and stores its fp32
+// partial tile to part[s][M][N]; gemm_reduce_kernel adds the splits in
+// order (plus the residual) and rounds once.
+template <int BM, int NS, bool SPLIT>
+__global__ __launch_bounds__(256, NS == 3 ? 2 : 1) void gemm_bf16_kernel(GemmParams p, int nsplit, float *part) {
     using T = GTile<BM, NS>;
     __shared__ __attribute__((aligned(1024))) unsigned char ring[T::RING];
     __shared__ int arow[3][BM];  // source row of each tile row, per segment
+    const int tiles = p.mt * p.nt;
+    const int split = SPLIT ? (int)blockIdx.x / tiles : 0;
     int mt, nt;
-    tile_of(blockIdx.x, gridDim.x, p.mt, p.nt, mt, nt);
+    tile_of(SPLIT ? (int)blockIdx.x % tiles : (int)blockIdx.x, tiles, p.mt, p.nt, mt, nt);
     const int m0 = mt * BM, n0 = nt * GBN;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int lr = lane & 31, lh = lane >> 5, wm = wave >> 1, wn = wave & 1;
     fill_arow<BM>(p, m0, arow);
     f32x16_t acc[T::MB][T::NB];
-    mainloop<BM, NS>(p, m0, n0, ring, arow, acc);
+    const int nch_all = p.K / GBK;
+    const int c_begin = SPLIT ? (int)((long)split * nch_all / nsplit) : 0;
+    const int c_end = SPLIT ? (int)((long)(split + 1) * nch_all / nsplit) : nch_all;
+    mainloop<BM, NS>(p, m0, n0, c_begin, c_end - c_begin, ring, arow, acc);
+    if constexpr (SPLIT) {
+        float *dst = part + (size_t)split * p.M * p.N;
+#pragma unroll
+        for (int mb = 0; mb < T::MB; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < T::NB; ++nb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int m = m0 + wm * (BM / 2) + mb * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+                    const int n = n0 + wn * 128 + nb * 32 + lr;
+                    if (m < p.M && n < p.N) dst[(size_t)m * p.N + n] = acc[mb][nb][r];
+                }
+        return;
+    }
     // D[m][n]: lane holds n = lr of its block, m = 8 (r / 4) + 4 lh + r % 4
     const uint16_t *res = (const uint16_t *)p.res;
     uint16_t *cc = (uint16_t *)p.c;
@@ -49,6 +75,18 @@ __global__ __launch_bounds__(256, NS == 3 ? 2 : 1) void gemm_bf16_kernel(GemmPar
                     cc[(size_t)m * p.ldc + n] = e3_f32_to_bf16(v);
                 }
             }
+}
+
+// Sum of the split partials in split order (+ residual), rounded once to bf16.
+__global__ __launch_bounds__(256) void gemm_reduce_kernel(const float *__restrict__ part, int nsplit, int M, int N,
+                                                          const uint16_t *res, uint16_t *c, int ldc) {
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (size_t)M * N) return;
+    const int m = (int)(i / N), n = (int)(i % N);
+    float v = 0.f;
+    for (int s = 0; s < nsplit; ++s) v += part[(size_t)s * M * N + i];
+    if (res) v += e3_bf16_to_f32(res[(size_t)m * ldc + n]);
+    c[(size_t)m * ldc + n] = e3_f32_to_bf16(v);
 }
 
 // fp32 GEMM for small models: 16 x 16 output tile per 256 threads, 16-wide k
@@ -203,7 +241,33 @@ __global__ __launch_bounds__(256) void copy_rows_kernel(const uint4 *__restrict_
 
 unsigned grid1(size_t n) { return (unsigned)((n + 255) / 256); }
 
+// Splits of K for a bf16 call whose 128-row tiles would leave more than half
+// of the CUs idle: enough splits to give every CU a work-group, at least 16
+// chunks (512 columns) each, at most 8.
+int gemm_splits(const eagle3_gemm_args *a, int K) {
+    if (a->dtype != EAGLE3_BF16 || a->M < 1 || a->N < 1) return 1;
+    const long tiles = (long)((a->M + 127) / 128) * ((a->N + GBN - 1) / GBN);
+    const long cus = e3_cu_count();
+    if (2 * tiles > cus) return 1;
+    long s = cus / tiles;
+    s = std::min(s, (long)(K / GBK / 16));
+    s = std::min(s, 8L);
+    return s < 2 ? 1 : (int)s;
+}
+
+int gemm_k(const eagle3_gemm_args *a) {
+    int K = 0;
+    for (int s = 0; s < a->nseg && s < 3; ++s) K += a->k[s] > 0 ? a->k[s] : 0;
+    return K;
+}
+
 }  // namespace
+
+extern "C" size_t eagle3_gemm_workspace(const eagle3_gemm_args *a) {
+    if (!a || a->nseg < 1 || a->nseg > 3 || a->M < 1 || a->N < 1) return 0;
+    const int S = gemm_splits(a, gemm_k(a));
+    return S > 1 ? (size_t)S * a->M * a->N * sizeof(float) : 0;
+}
 
 extern "C" int eagle3_gemm(const eagle3_gemm_args *a, void *stream) {
     if (!a) return EAGLE3_ERR_ARG;
@@ -231,7 +295,17 @@ extern "C" int eagle3_gemm(const eagle3_gemm_args *a, void *stream) {
     p.nseg = a->nseg; p.b = a->b; p.res = a->residual; p.c = a->c;
     p.M = a->M; p.N = a->N; p.K = K; p.ldc = ldc;
     const hipStream_t st = e3_stream(stream);
-    if (a->dtype == EAGLE3_BF16) {
+    const int S = a->dtype == EAGLE3_BF16 ? gemm_splits(a, K) : 1;
+    if (S > 1 && a->ws && a->ws_bytes >= (size_t)S * a->M * a->N * sizeof(float) && e3_aligned16(a->ws)) {
+        // few tiles: split K so every CU gets a work-group, then reduce
+        p.nt = (a->N + GBN - 1) / GBN;
+        p.mt = (a->M + 127) / 128;
+        float *part = (float *)a->ws;
+        gemm_bf16_kernel<128, 4, true><<<p.mt * p.nt * S, 256, 0, st>>>(p, S, part);
+        gemm_reduce_kernel<<<grid1((size_t)a->M * a->N), 256, 0, st>>>(part, S, a->M, a->N,
+                                                                       (const uint16_t *)a->residual,
+                                                                       (uint16_t *)a->c, ldc);
+    } else if (a->dtype == EAGLE3_BF16) {
         // Tile shape by the amount of work (measured): 256-row tiles once
         // they make four passes over the CUs (most reuse, 65536 x 4096 x
         // 12288: 1.01 vs 0.90 PFLOP/s); else 128-row tiles two per CU while
@@ -245,13 +319,13 @@ extern "C" int eagle3_gemm(const eagle3_gemm_args *a, void *stream) {
         p.nt = nt;
         if (t256 >= 4 * cus || (t128 < 2 * cus && t256 >= cus)) {
             p.mt = (a->M + 255) / 256;
-            gemm_bf16_kernel<256, 4><<<p.mt * nt, 256, 0, st>>>(p);
+            gemm_bf16_kernel<256, 4, false><<<p.mt * nt, 256, 0, st>>>(p, 1, nullptr);
         } else if (t128 >= 2 * cus) {
             p.mt = (a->M + 127) / 128;
-            gemm_bf16_kernel<128, 3><<<p.mt * nt, 256, 0, st>>>(p);
+            gemm_bf16_kernel<128, 3, false><<<p.mt * nt, 256, 0, st>>>(p, 1, nullptr);
         } else {
             p.mt = (a->M + 127) / 128;
-            gemm_bf16_kernel<128, 4><<<p.mt * nt, 256, 0, st>>>(p);
+            gemm_bf16_kernel<128, 4, false><<<p.mt * nt, 256, 0, st>>>(p, 1, nullptr);
         }
     } else {
         dim3 grid((a->M + 15) / 16, (a->N + 15) / 16);

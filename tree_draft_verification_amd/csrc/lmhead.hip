@@ -266,7 +266,7 @@ __global__ __launch_bounds__(256, BM == 128 ? 2 : 1) void lmhead_big_kernel(e3g:
     const int lr = lane & 31, lh = lane >> 5, wm = wave >> 1, wn = wave & 1;
     e3g::fill_arow<BM>(gp, m0, arow);
     f32x16_t acc[T::MB][T::NB];
-    e3g::mainloop<BM, T::NS>(gp, m0, n0, ring, arow, acc);
+    e3g::mainloop<BM, T::NS>(gp, m0, n0, 0, gp.K / e3g::GBK, ring, arow, acc);
     __syncthreads();  // every wave is done with the ring
     // Each wave selects over its own (BM/2) x 128 block, RP hidden rows at a
     // time, staged in a private slice of the ring (columns rotated by 4 per

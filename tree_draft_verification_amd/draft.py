@@ -98,6 +98,9 @@ class DraftHead:
         self.tokens = torch.empty(B, n_drafts + 1, dtype=i32, device=dv)
         self._ctx_bufs = None
         self._ws = None
+        self._gws = None   # K-split workspace of the few-tile GEMMs (shared: one stream)
+        self._fws = torch.empty(max(256, B_.eagle3_draft_fuse_workspace(M, self.k, B_._dtype(E))),
+                                dtype=torch.uint8, device=dv)
         # optional (start, end) event pairs, one taken per LM-head call, in call order
         self.events = []
 
@@ -123,8 +126,8 @@ class DraftHead:
         B_.eagle3_draft_fuse(ctx_tok.reshape(R), w["embed"], w["w_in"], cb["x"], w_fuse=w["w_fuse"],
                              l=l.reshape(R, k), m=m.reshape(R, k), h=h.reshape(R, k), g_out=cb["g"])
         B_.eagle3_rmsnorm(cb["x"], cb["hn"], eps=self.eps)
-        B_.eagle3_gemm([cb["hn"]], self.wk, cb["k"])
-        B_.eagle3_gemm([cb["hn"]], self.wv, cb["v"])
+        self._gemm([cb["hn"]], self.wk, cb["k"])
+        self._gemm([cb["hn"]], self.wv, cb["v"])
         B_.eagle3_rope(cb["k"], R, self.Hkv, self.D, self.kvd, self.ctx_pos, 0, self.theta)
         kr = cb["k"].view(B, ctx, self.Hkv, self.D)
         vr = cb["v"].view(B, ctx, self.Hkv, self.D)
@@ -134,7 +137,7 @@ class DraftHead:
         h1 = self.hs[:B]
         B_.eagle3_rmsnorm(self.x1, h1, eps=self.eps)
         q = self.q[:B]
-        B_.eagle3_gemm([h1], self.wq, q)
+        self._gemm([h1], self.wq, q)
         B_.eagle3_rope(q, B, self.Hq, self.D, self.qd, self.zero_pos, ctx - 1, self.theta)
         none = self.tk[:, :0]
         attn = self.attn[:B]
@@ -142,6 +145,15 @@ class DraftHead:
                               self.plen, attn.view(B, 1, self.Hq, self.D), mask=self.root_mask)
         B_.eagle3_tree_attn(a, self._attn_ws(a))
         self._layer_tail(self.x1, attn, self.a_root, B)
+
+    def _gemm(self, a, b, c, residual=None):
+        need = B_.eagle3_gemm_workspace(a, b, c)
+        ws = None
+        if need:
+            if self._gws is None or self._gws.numel() < need:
+                self._gws = torch.empty(need, dtype=torch.uint8, device=self.dev)
+            ws = self._gws
+        B_.eagle3_gemm(a, b, c, residual=residual, ws=ws)
 
     def _attn_ws(self, a):
         need = max(256, B_.eagle3_tree_attn_workspace(a))
@@ -152,11 +164,11 @@ class DraftHead:
     def _layer_tail(self, x, attn, out, M):
         w = self.w
         x2, h2, gu, f = self.x2[:M], self.h2[:M], self.gu[:M], self.f[:M]
-        B_.eagle3_gemm([attn], w["wo"], x2, residual=x)
+        self._gemm([attn], w["wo"], x2, residual=x)
         B_.eagle3_rmsnorm(x2, h2, eps=self.eps)
-        B_.eagle3_gemm([h2], w["wgu"], gu)
+        self._gemm([h2], w["wgu"], gu)
         B_.eagle3_silu_mul(gu, f)
-        B_.eagle3_gemm([f], w["wd"], out, residual=x2)
+        self._gemm([f], w["wd"], out, residual=x2)
 
     def _head(self, a, M):
         hn = self.hn[:M]
@@ -191,11 +203,12 @@ class DraftHead:
             fr, nx = self.fr[s % 2], self.fr[(s + 1) % 2]
             a_out = self.a[s % 2]
             B_.eagle3_copy_rows(a_src, self.a_par, M, src_rows=fr["arow"].view(-1))
-            B_.eagle3_draft_fuse(fr["token"].view(-1), self.w["embed"], self.w["w_in"], self.xs, a_prev=self.a_par)
+            B_.eagle3_draft_fuse(fr["token"].view(-1), self.w["embed"], self.w["w_in"], self.xs, a_prev=self.a_par,
+                                 ws=self._fws)
             B_.eagle3_rmsnorm(self.xs, self.hs, eps=self.eps)
-            B_.eagle3_gemm([self.hs], self.wq, self.q)
-            B_.eagle3_gemm([self.hs], self.wk, self.kt)
-            B_.eagle3_gemm([self.hs], self.wv, self.vt)
+            self._gemm([self.hs], self.wq, self.q)
+            self._gemm([self.hs], self.wk, self.kt)
+            self._gemm([self.hs], self.wv, self.vt)
             pos = self.ctx + s - 2
             B_.eagle3_rope(self.q, M, self.Hq, D, self.qd, self.zero_pos, pos, self.theta)
             B_.eagle3_rope(self.kt, M, self.Hkv, D, self.kvd, self.zero_pos, pos, self.theta)
