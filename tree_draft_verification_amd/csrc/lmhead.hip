@@ -7,7 +7,8 @@
 // each forward reads all parameters), so for few rows this is an HBM stream.
 //
 // Pass 1, bf16 (one work-group per 128-row vocabulary tile x 64-row hidden
-// tile, 4 waves, 2 work-groups per CU):
+// tile, 4 waves, 2 work-groups per CU; for argmax-only calls with one hidden
+// tile, 8 waves over a 256-row vocabulary tile, 1 work-group per CU):
 //   - 64-wide k chunks of the weight tile (128 rows x 128 B) and of the hidden
 //     tile (64 rows x 128 B) go straight from global memory into a 3-stage LDS
 //     ring with 16-byte global_load_lds (no VGPR round trip); each 1 KB load
@@ -36,7 +37,7 @@
 
 namespace {
 
-constexpr int BN_B = 128;  // vocabulary rows per tile, bf16 path
+constexpr int BN_B = 128;  // vocabulary rows per tile of the 4-wave few-row kernel (32 per wave)
 constexpr int BN_F = 256;  // vocabulary rows per tile, fp32 path
 constexpr int BK = 64;     // k per chunk, bf16 path
 constexpr int NSTAGE = 3;  // LDS ring depth, bf16 path
@@ -62,11 +63,11 @@ __device__ __forceinline__ void store_record(const Partials &p, size_t rec, cons
     }
 }
 
-// Per-row selection over an LDS tile lg[BMt][BNt + 4]; 256 / BMt threads per row.
-template <int BMt, int BNt, int KK, bool LSE>
+// Per-row selection over an LDS tile lg[BMt][BNt + 4]; NT / BMt threads per row.
+template <int BMt, int BNt, int KK, bool LSE, int NT = 256>
 __device__ __forceinline__ void tile_select(const float (*lg)[BNt + 4], int m0, int M, int n0, int N, int tile,
                                             int ntiles, const Partials &p) {
-    constexpr int TPR = 256 / BMt;
+    constexpr int TPR = NT / BMt;
     constexpr int PER = BNt / TPR;
     const int row = threadIdx.x / TPR, part = threadIdx.x % TPR;
     static_assert(PER % 4 == 0, "16-byte reads of a thread's run");
@@ -125,15 +126,15 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-template <int KK, bool LSE, bool NTW>
-__global__ __launch_bounds__(256, 2) void lmhead_bf16_kernel(const uint16_t *__restrict__ h,
+template <int KK, bool LSE, bool NTW, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void lmhead_bf16_kernel(const uint16_t *__restrict__ h,
                                                              const uint16_t *__restrict__ w, int M, int N, int K,
                                                              int ntiles, Partials p) {
-    constexpr int BM = 64, BN = BN_B, NS = NSTAGE;
+    constexpr int BM = 64, BN = 32 * NW, NS = NSTAGE;
     constexpr int WST = BN * 128, HST = BM * 128;   // bytes of one stage (128 B = 64 bf16 per row)
     constexpr int WBLK = WST / 1024;                 // 1 KB load blocks of the weight part
-    constexpr int LOADS = (WST + HST) / 1024 / 4;    // 1 KB loads per wave per stage
-    static_assert((WST + HST) % 4096 == 0, "stage must split evenly over 4 waves");
+    constexpr int LOADS = (WST + HST) / 1024 / NW;  // 1 KB loads per wave per stage
+    static_assert((WST + HST) % (1024 * NW) == 0, "stage must split evenly over the waves");
     __shared__ __attribute__((aligned(1024))) unsigned char smem[NS * (WST + HST)];
     static_assert(sizeof(float) * BM * (BN + 4) <= sizeof(smem), "logit tile must fit the ring");
 
@@ -225,7 +226,7 @@ __global__ __launch_bounds__(256, 2) void lmhead_bf16_kernel(const uint16_t *__r
         for (int r = 0; r < 16; ++r)
             lg[mb * 32 + lr][wave * 32 + 8 * (r >> 2) + 4 * lh + (r & 3)] = acc[mb][r];
     __syncthreads();
-    tile_select<BM, BN, KK, LSE>(lg, m0, M, n0, N, tile, ntiles, p);
+    tile_select<BM, BN, KK, LSE, 64 * NW>(lg, m0, M, n0, N, tile, ntiles, p);
 }
 
 // Many hidden rows (verify batches of whole trees, draft steps): the head is
@@ -466,16 +467,22 @@ constexpr int BIG_M = 128;
 bool use_big(int M, int K, int dtype) { return dtype == EAGLE3_BF16 && M >= BIG_M && K % e3g::GSEG_ALIGN == 0; }
 
 // partial records per row (the many-row path keeps one per 128-column half tile)
-int tiles_for(int M, int N, int K, int dtype) {
+// few rows, shortest lists (argmax and gap), one hidden tile: 8 waves over a
+// 256-row vocabulary tile, one work-group per CU, halve the hidden-row
+// traffic per weight byte (8B batch-1 tile pass 179 -> 171 us); longer
+// lists keep 4 waves over 128 rows, whose selection is cheaper per tile
+bool wide_tiles(int M, int KK, int dtype) { return dtype == EAGLE3_BF16 && KK == 2 && M <= 64; }
+
+int tiles_for(int M, int N, int K, int dtype, int KK) {
     if (use_big(M, K, dtype)) return 2 * ((N + BIG_BN - 1) / BIG_BN);
-    const int bn = dtype == EAGLE3_BF16 ? BN_B : BN_F;
+    const int bn = dtype == EAGLE3_BF16 ? (wide_tiles(M, KK, dtype) ? 2 * BN_B : BN_B) : BN_F;
     return (N + bn - 1) / bn;
 }
 
 template <int KK, bool LSE>
 void launch(const void *hidden, const void *w, int M, int N, int K, int topk, int dtype, int32_t *idx, float *val,
             float *gap, float *lse, void *ws, hipStream_t st) {
-    const int ntiles = tiles_for(M, N, K, dtype);
+    const int ntiles = tiles_for(M, N, K, dtype, KK);
     const Partials p = carve(ws, M, ntiles, KK);
     if (use_big(M, K, dtype)) {
         e3g::GemmParams gp{};
@@ -486,12 +493,13 @@ void launch(const void *hidden, const void *w, int M, int N, int K, int topk, in
         lmhead_big_kernel<BM, KK, LSE><<<gp.mt * gp.nt, 256, 0, st>>>(gp, ntiles, p);
     } else if (dtype == EAGLE3_BF16) {
         dim3 grid((M + 63) / 64, ntiles);
-        if (grid.x == 1)
-            lmhead_bf16_kernel<KK, LSE, true><<<grid, 256, 0, st>>>((const uint16_t *)hidden, (const uint16_t *)w, M,
-                                                                    N, K, ntiles, p);
+        const uint16_t *hp = (const uint16_t *)hidden, *wp = (const uint16_t *)w;
+        if (wide_tiles(M, KK, dtype))
+            lmhead_bf16_kernel<KK, LSE, true, 8><<<grid, 512, 0, st>>>(hp, wp, M, N, K, ntiles, p);
+        else if (grid.x == 1)
+            lmhead_bf16_kernel<KK, LSE, true, 4><<<grid, 256, 0, st>>>(hp, wp, M, N, K, ntiles, p);
         else
-            lmhead_bf16_kernel<KK, LSE, false><<<grid, 256, 0, st>>>((const uint16_t *)hidden, (const uint16_t *)w, M,
-                                                                     N, K, ntiles, p);
+            lmhead_bf16_kernel<KK, LSE, false, 4><<<grid, 256, 0, st>>>(hp, wp, M, N, K, ntiles, p);
     } else {
         dim3 grid((M + 15) / 16, ntiles);
         lmhead_f32_kernel<KK, LSE><<<grid, 256, 0, st>>>((const float *)hidden, (const float *)w, M, N, K, ntiles, p);
@@ -510,8 +518,8 @@ void launch_kk(bool want_lse, const void *hidden, const void *w, int M, int N, i
 
 extern "C" size_t eagle3_lmhead_workspace(int M, int N, int K, int topk, int dtype) {
     if (M <= 0 || N <= 0 || topk < 1) return 0;
-    const int ntiles = tiles_for(M, N, K, dtype);
     const int KK = kk_for(topk);
+    const int ntiles = tiles_for(M, N, K, dtype, KK);
     const size_t rec = (size_t)M * ntiles;
     return align256(rec * KK * 8) + align256(rec * 4) + align256(rec * 4);
 }
