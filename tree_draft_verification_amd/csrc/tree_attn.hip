@@ -29,6 +29,8 @@
 // the scores and over dimensions for P.V; for small models.
 #include "common.h"
 
+#include <type_traits>
+
 namespace {
 
 constexpr int KT = 64;       // keys per tile
@@ -65,6 +67,33 @@ __device__ __forceinline__ int clamped_len(const int32_t *prefix_len, int b, int
 __device__ __forceinline__ int splits_of(int L, int split_keys, int tree_split) {
     const int npre = L > 0 ? (L + split_keys - 1) / split_keys : 0;
     return tree_split ? npre + 1 : (npre > 0 ? npre : 1);
+}
+
+// Sequences are dealt to work-group slots longest (clamped) prefix first,
+// ties by lower index: the long sequences start in the first pass over the
+// CUs and the short ones fill in behind them (longest-processing-time-first
+// list order), instead of the batch order, which can leave a CU with two
+// long sequences. Every wave ranks the sequences by counting; slot r takes
+// the sequence of rank r. Past LPT_MAX_B sequences the batch order is kept.
+constexpr int LPT_MAX_B = 256;
+__device__ __forceinline__ int seq_of_slot(const int32_t *prefix_len, int B, int r, int max_blocks, int num_blocks) {
+    if (B > LPT_MAX_B) return r;
+    const int lane = threadIdx.x & 63;
+    for (int j0 = 0; j0 < B; j0 += 64) {
+        const int j = j0 + lane;
+        int rank = -1;
+        if (j < B) {
+            const int Lj = clamped_len(prefix_len, j, max_blocks, 16, num_blocks);
+            rank = 0;
+            for (int k = 0; k < B; ++k) {
+                const int Lk = clamped_len(prefix_len, k, max_blocks, 16, num_blocks);
+                rank += (Lk > Lj || (Lk == Lj && k < j)) ? 1 : 0;
+            }
+        }
+        const uint64_t hit = __ballot(rank == r);
+        if (hit) return j0 + __ffsll((unsigned long long)hit) - 1;
+    }
+    return r;  // not reached: the ranks are a permutation of 0..B-1
 }
 
 __device__ __forceinline__ int clamped_block(const int32_t *btab, int j, int num_blocks) {
@@ -138,6 +167,46 @@ __device__ __forceinline__ void lgkm_upto(int n, u32x4_t &r) {
     else lgkm_wait1<0>(r);
 }
 
+// compile-time unrolled loop: f(std::integral_constant<int, i>) for i in [I, N)
+template <int I, int N, typename F>
+__device__ __forceinline__ void sfor(F &&f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        sfor<I + 1, N>(f);
+    }
+}
+
+// LDS fragment read at a per-lane address plus a constant byte offset (the
+// instruction's offset field), so the constant parts take no registers
+template <int OFF>
+__device__ __forceinline__ void lds_read16_at(u32x4_t &r, uint32_t addr) {
+    static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
+    __asm__ volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+}
+
+// Per-lane parts of the fragment addresses inside a ring stage. QK step j
+// (key block kb = j & 1, d-step s = j >> 1) reads koff[s] + 8192 kb: row
+// 32 kb + lr, 16-byte column (2 s + lh) ^ kswz(lr) (kswz of the row only sees
+// lr); lane half lh holds d = 16 s + 8 lh .. +7. PV step j (16-key step
+// ks = j >> 2, d block db = j & 3) reads voff + 4096 ks + 1024 db: row
+// (ks, d = 32 db + lr), half lh ^ vswz(lr).
+struct FragOffsets {
+    uint32_t k[8];
+    uint32_t v;
+};
+__device__ __forceinline__ FragOffsets frag_offsets(int lr, int lh) {
+    FragOffsets f;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) f.k[s] = lr * 256 + (((2 * s + lh) ^ kswz(lr)) << 4);
+    f.v = VOFF + lr * 32 + ((lh ^ vswz(lr)) << 4);
+    return f;
+}
+
+// Fragment reads run RA steps ahead through an NF-slot buffer: with one
+// 32 x 32 x 16 MFMA (QK) or two (PV) per read, two reads ahead left the
+// LDS latency exposed at every step.
+constexpr int RA = 4, NF = RA + 2;
+
 // One 64-key tile for one wave and its RB blocks of 32 query rows: S^T =
 // K.Q^T, online softmax, O^T += V^T.P^T. Every K / V fragment read from LDS
 // feeds the MFMAs of all RB row blocks, and the row blocks' independent
@@ -145,47 +214,37 @@ __device__ __forceinline__ void lgkm_upto(int n, u32x4_t &r) {
 // Operand fragments are read two steps ahead through a 4-slot buffer.
 template <int RB>
 __device__ __forceinline__ void attend_tile(int kind, const unsigned char *stage, const u32x4_t (&qb)[RB][8],
-                                            f32x16_t (&ot)[RB][4], float (&m_run)[RB], float (&l_run)[RB], int lr,
-                                            int lh, int nvalid, const uint64_t (&mword)[RB], float scale_log2) {
-    const uint32_t kb_lds = (uint32_t)(uintptr_t)(lds_void_t *)stage;
-    const uint32_t vb_lds = kb_lds + VOFF;
-    u32x4_t fr[4];
+                                            f32x16_t (&ot)[RB][4], float (&m_run)[RB], float (&l_run)[RB],
+                                            const FragOffsets &fo, int lh, int nvalid, const uint64_t (&mword)[RB],
+                                            float scale_log2) {
+    const uint32_t sb = (uint32_t)(uintptr_t)(lds_void_t *)stage;
+    u32x4_t fr[NF];
     // QK step j: key block kb = j & 1 (alternating accumulators), d-step s = j >> 1
-    auto kaddr = [&](int j) {
-        const int kb = j & 1, s = j >> 1, row = kb * 32 + lr;
-        // lane half lh holds d = 16 s + 8 lh .. +7, i.e. 16-byte column 2 s + lh
-        return kb_lds + row * 256 + (((2 * s + lh) ^ kswz(row)) << 4);
+    auto kread = [&](auto J) {
+        constexpr int j = J;
+        lds_read16_at<(j & 1) * 8192>(fr[j % NF], sb + fo.k[j >> 1]);
     };
     f32x16_t st[RB][2];
-    lds_read16(fr[0], kaddr(0));
-    lds_read16(fr[1], kaddr(1));
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-        if (j + 2 < 16) lds_read16(fr[(j + 2) & 3], kaddr(j + 2));
-        lgkm_upto(15 - j < 2 ? 15 - j : 2, fr[j & 3]);
-        const int kb = j & 1, s = j >> 1;
+    sfor<0, RA>(kread);
+    sfor<0, 16>([&](auto J) {
+        constexpr int j = J, kb = j & 1, s = j >> 1;
+        if constexpr (j + RA < 16) kread(std::integral_constant<int, j + RA>{});
+        lgkm_wait1<(15 - j < RA ? 15 - j : RA)>(fr[j % NF]);
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
-            if (s == 0) {
-                const f32x16_t z = {};
-                st[rb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, fr[j & 3]),
-                                                                     __builtin_bit_cast(bf16x8_t, qb[rb][s]), z, 0,
-                                                                     0, 0);
-            } else {
-                st[rb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, fr[j & 3]),
-                                                                     __builtin_bit_cast(bf16x8_t, qb[rb][s]),
-                                                                     st[rb][kb], 0, 0, 0);
-            }
+            const f32x16_t z = {};
+            st[rb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, fr[j % NF]),
+                                                                 __builtin_bit_cast(bf16x8_t, qb[rb][s]),
+                                                                 s == 0 ? z : st[rb][kb], 0, 0, 0);
         }
-    }
-    // PV step j: 16-key step ks = j >> 2, d block db = j & 3; the first two V
+    });
+    // PV step j: 16-key step ks = j >> 2, d block db = j & 3; the first RA V
     // fragments are read now and land during the softmax
-    auto vaddr = [&](int j) {
-        const int ks = j >> 2, db = j & 3, d = db * 32 + lr;
-        return vb_lds + ks * 4096 + d * 32 + ((lh ^ vswz(d)) << 4);
+    auto vread = [&](auto J) {
+        constexpr int j = J;
+        lds_read16_at<(j >> 2) * 4096 + (j & 3) * 1024>(fr[j % NF], sb + fo.v);
     };
-    lds_read16(fr[0], vaddr(0));
-    lds_read16(fr[1], vaddr(1));
+    sfor<0, RA>(vread);
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
         // register r of block kb holds key 32 kb + 16 (r / 8) + 8 lh + (r % 8)
@@ -234,11 +293,10 @@ __device__ __forceinline__ void attend_tile(int kind, const unsigned char *stage
     // MFMAs on the same V operand): a single bf16 rounding of P would leave
     // ~2e-3 relative error in the output.
     u32x4_t ph[RB], pl[RB];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-        const int ks = j >> 2, db = j & 3;
-        if (db == 0) {
-            const int kb = ks >> 1, r0 = 8 * (ks & 1);
+    sfor<0, 16>([&](auto J) {
+        constexpr int j = J, ks = j >> 2, db = j & 3;
+        if constexpr (db == 0) {
+            constexpr int kb = ks >> 1, r0 = 8 * (ks & 1);
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
@@ -249,9 +307,9 @@ __device__ __forceinline__ void attend_tile(int kind, const unsigned char *stage
                     pl[rb][e] = l2;
                 }
         }
-        if (j + 2 < 16) lds_read16(fr[(j + 2) & 3], vaddr(j + 2));
-        lgkm_upto(15 - j < 2 ? 15 - j : 2, fr[j & 3]);
-        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, fr[j & 3]);
+        if constexpr (j + RA < 16) vread(std::integral_constant<int, j + RA>{});
+        lgkm_wait1<(15 - j < RA ? 15 - j : RA)>(fr[j % NF]);
+        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, fr[j % NF]);
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
             ot[rb][db] =
@@ -259,7 +317,7 @@ __device__ __forceinline__ void attend_tile(int kind, const unsigned char *stage
             ot[rb][db] =
                 __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, pl[rb]), ot[rb][db], 0, 0, 0);
         }
-    }
+    });
 }
 
 // NW waves of RB x 32 query rows each (NW * RB * 32 = ROWS_PER_WG).
@@ -272,7 +330,8 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_bf16_kernel(AttnParams p) {
     constexpr int LOADS = 32 / NW;  // 1 KB DMA loads per wave per stage (16 for K, 16 for V)
 
     const int split = blockIdx.x / p.nrb, rb = blockIdx.x % p.nrb;
-    const int kvh = blockIdx.y, b = blockIdx.z;
+    const int kvh = blockIdx.y;
+    const int b = __builtin_amdgcn_readfirstlane(seq_of_slot(p.prefix_len, p.B, blockIdx.z, p.max_blocks, p.num_blocks));
     const int L = clamped_len(p.prefix_len, b, p.max_blocks, 16, p.num_blocks);
     const int C = p.split_keys;
     const int nsplit_b = splits_of(L, C, p.tree_split);
@@ -282,7 +341,8 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_bf16_kernel(AttnParams p) {
     const int k_begin = tree_only ? 0 : split * C;
     const int k_end = tree_only ? 0 : min(L, k_begin + C);
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    // the wave index is wave-uniform; saying so keeps the branches on it scalar
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int lr = lane & 31, lh = lane >> 5;
     // this lane's query rows, one per row block
     int row[RB], t[RB], hq[RB];
@@ -318,15 +378,20 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_bf16_kernel(AttnParams p) {
     }
     const size_t head_off = (size_t)kvh * 16 * DH;
     const size_t blk_stride = (size_t)p.Hkv * 16 * DH;
+    // a wave's LOADS = 4 loads of a stage all come from one cache block (K
+    // for waves 0-3, V for waves 4-7): its address is a scalar base plus a
+    // 32-bit per-lane offset
+    static_assert(LOADS == 4, "one cache block per wave and stage");
     auto issue = [&](int stage, int tile) {
         unsigned char *base = ring + stage * STAGE;
+        const int lb = min(4 * tile + (wave & 3), nblk - 1);  // blocks past the prefix re-read the last
+        const int bid = __builtin_amdgcn_readfirstlane(bids[lb]);
+        const uint16_t *blk = (wave < 4 ? p.k_cache : p.v_cache) + (size_t)bid * blk_stride + head_off;
 #pragma unroll
         for (int j = 0; j < LOADS; ++j) {
             const int q = wave * LOADS + j;
-            const int lb = min(4 * tile + ((q & 15) >> 2), nblk - 1);  // blocks past the prefix re-read the last
-            const uint16_t *src = (q < 16 ? p.k_cache : p.v_cache) + (size_t)bids[lb] * blk_stride + head_off +
-                                  dma_off[j];
-            __builtin_amdgcn_global_load_lds((const void *)src, (lds_void_t *)(base + q * 1024), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const void *)(blk + dma_off[j]), (lds_void_t *)(base + q * 1024), 16,
+                                             0, 0);
         }
     };
 
@@ -355,6 +420,7 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_bf16_kernel(AttnParams p) {
         l_run[k] = 0.f;
     }
 
+    const FragOffsets fo = frag_offsets(lr, lh);
     const int ntile = (k_end - k_begin + KT - 1) / KT;
     // q and mask words have landed before any K/V DMA is queued behind them
     // (otherwise the first use of q inside the tile loop waits for the ring)
@@ -427,7 +493,7 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_bf16_kernel(AttnParams p) {
 #pragma unroll
             for (int k = 0; k < RB; ++k) mword[k] = tt == 0 ? mw0[k] : mw1[k];
         }
-        if (wave_active) attend_tile<RB>(kind, stage, qb, ot, m_run, l_run, lr, lh, nvalid, mword, p.scale_log2);
+        if (wave_active) attend_tile<RB>(kind, stage, qb, ot, m_run, l_run, fo, lh, nvalid, mword, p.scale_log2);
     }
 
 #pragma unroll
