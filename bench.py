@@ -348,7 +348,10 @@ def bench_draft(args):
         "tau_note": "independent random draft and target: acceptance is rare by construction",
         "phase_ms": {"context_ingest": round(ing, 3), "tree_growth": round(grow, 3), "verify": round(ver, 3)},
         "launch": "eager",
-        "sequence0_tree_equals_oracle": tree_same,
+        "sequence0_free_running_tree_equals_oracle": tree_same,
+        "draft_tree_note": ("bf16 draft trees of free-running GPU and oracle runs may differ where rounding "
+                            "reorders near-tie candidates; draft-tree parity is checked by replaying the GPU's "
+                            "choices through the oracle (draft parity tests)"),
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

@@ -58,6 +58,11 @@ CASES = [
     (2, 1, 8, 2, [17, 0], 0),            # root only
     (2, 100, 4, 1, [40, 90], 0),         # W = 2
     (4, 61, 32, 8, [700, 1100, 64, 0], 64),  # split, too many work-groups for a tree split
+    # sequences are dealt to work-groups longest prefix first: more than 64
+    # sequences (two ranking passes) with tied lengths, and more than 256
+    # (batch order kept)
+    (70, 8, 4, 1, [(37 * i) % 5 * 16 + (i % 3) for i in range(70)], 0),
+    (260, 2, 4, 1, [(11 * i) % 7 * 9 for i in range(260)], 0),
 ]
 
 
