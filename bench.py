@@ -96,7 +96,13 @@ def to_dev(a):
     return torch.from_numpy(a).to("cuda")
 
 
-def lm_roofline(M, K, V, us, workload):
+def pcts(us_list):
+    """p10 / p50 / p90 of per-launch times (us)."""
+    import numpy as np
+    return [round(float(x), 2) for x in np.percentile(np.asarray(us_list, dtype=float), [10, 50, 90])]
+
+
+def lm_roofline(M, K, V, us, workload, us_list=None):
     """The LM head against the roofline that binds at this many rows: the
     weight stream (HBM) for a few rows, the bf16 MFMA peak for many."""
     if M <= 64:
@@ -105,13 +111,13 @@ def lm_roofline(M, K, V, us, workload):
         return {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": traffic_from_profile(workload),
                 "kernel": "eagle3_lmhead_argmax (tile pass + merge pass)", "bytes_per_launch": by,
-                "avg_launch_us": round(us, 2)}
+                "avg_launch_us": round(us, 2), "launch_us_p10_p50_p90": pcts(us_list or [us])}
     fl = 2.0 * M * V * K
     ach = fl / (us * 1e-6) / 1e12
     return {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": traffic_from_profile(workload),
             "kernel": "eagle3_lmhead_argmax (GEMM tiles + merge pass)", "flops_per_launch": fl,
-            "avg_launch_us": round(us, 2)}
+            "avg_launch_us": round(us, 2), "launch_us_p10_p50_p90": pcts(us_list or [us])}
 
 
 def bench_verify(args, name):
@@ -201,13 +207,14 @@ def bench_verify(args, name):
             run(i, ev[i])
         torch.cuda.synchronize()
         eager_ms = (time.perf_counter() - t0) * 1e3 / args.steps
-    lm_us = float(np.mean([e["lmhead"][0].elapsed_time(e["lmhead"][1]) for e in ev])) * 1e3
-    at_us = float(np.mean([e["attn"][0].elapsed_time(e["attn"][1]) for e in ev])) * 1e3
+    lm_list = [e["lmhead"][0].elapsed_time(e["lmhead"][1]) * 1e3 for e in ev]
+    at_list = [e["attn"][0].elapsed_time(e["attn"][1]) * 1e3 for e in ev]
+    lm_us, at_us = float(np.mean(lm_list)), float(np.mean(at_list))
     nodes = shape.B * shape.n_drafts
     value = nodes / (ms_per_step * 1e-3)
 
     M, K, V = shape.B * shape.T, shape.K, shape.V
-    roofline = lm_roofline(M, K, V, lm_us, name)
+    roofline = lm_roofline(M, K, V, lm_us, name, lm_list)
     attn_bytes = (shape.B * shape.T * shape.Hq * shape.D * 2 * 2             # q + out
                   + int(plen.sum()) * shape.Hkv * shape.D * 2 * 2            # prefix K + V
                   + shape.B * shape.T * shape.Hkv * shape.D * 2 * 2 + shape.B * shape.T * 8)
@@ -246,7 +253,8 @@ def bench_verify(args, name):
         "launch": "hip_graph_replay" if graphs is not None else "eager",
         "eager_ms_per_step": round(eager_ms, 4) if eager_ms is not None else round(ms_per_step, 4),
         "roofline": roofline,
-        "tree_attn": {"avg_launch_us": round(at_us, 2), "bytes_per_launch": attn_bytes,
+        "tree_attn": {"avg_launch_us": round(at_us, 2), "launch_us_p10_p50_p90": pcts(at_list),
+                      "bytes_per_launch": attn_bytes,
                       "achieved_GBps": round(attn_bytes / (at_us * 1e-6) / 1e9, 1),
                       "hbm_frac": round(attn_bytes / (at_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
                       "flops_per_launch": attn_flops},
@@ -315,8 +323,9 @@ def bench_draft(args):
     grow = float(np.mean([e["t1"].elapsed_time(e["t2"]) for e in evs]))
     ver = float(np.mean([e["t2"].elapsed_time(e["t3"]) for e in evs]))
     # LM-head launches of growth steps 2..8 (640 rows each)
-    lm_us = float(np.mean([a.elapsed_time(b) for pairs in lm_ev for (a, b) in pairs[1:]])) * 1e3
-    roofline = lm_roofline(s.B * s.topk, s.k, s.V, lm_us, "draft-b64")
+    lm_list = [a.elapsed_time(b) * 1e3 for pairs in lm_ev for (a, b) in pairs[1:]]
+    lm_us = float(np.mean(lm_list))
+    roofline = lm_roofline(s.B * s.topk, s.k, s.V, lm_us, "draft-b64", lm_list)
     al = vstep.accept_len.cpu().numpy()
     parent, tokens = head.parent.cpu().numpy(), head.tokens.cpu().numpy()
     nodes = s.B * s.n_drafts
