@@ -96,6 +96,19 @@ def to_dev(a):
     return torch.from_numpy(a).to("cuda")
 
 
+def gpu_sclk_mhz():
+    """Shader clock (MHz) as rocm-smi reports it right now, or None; run in a
+    child process, after a timed region (it takes a fraction of a second)."""
+    import re
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
+        m = re.search(r'"sclk clock speed:": "\((\d+)Mhz\)"', r.stdout)
+        return int(m.group(1)) if m else None
+    except Exception:
+        return None
+
+
 def pcts(us_list):
     """p10 / p50 / p90 of per-launch times (us)."""
     import numpy as np
@@ -197,6 +210,7 @@ def bench_verify(args, name):
             graphs[i % len(graphs)].replay()
     torch.cuda.synchronize()
     t_end = time.perf_counter()
+    sclk = gpu_sclk_mhz()
     ms_per_step = (t_end - t_start) * 1e3 / args.steps
     eager_ms = None
     if graphs is not None:
@@ -248,7 +262,9 @@ def bench_verify(args, name):
         "config": {"workload": name, "batch": shape.B, "draft_nodes": shape.n_drafts, "tree_depth": shape.depth,
                    "prefix": list(shape.prefix), "heads_q_kv": [shape.Hq, shape.Hkv], "head_dim": shape.D,
                    "hidden": shape.K, "vocab": shape.V},
-        "accepted_tok_per_step": round(float(np.mean(taus)), 3), "tau_samples": len(taus),
+        "accepted_tok_per_step": round(float(np.mean(taus)), 3),
+        "accepted_tok_per_step_std": round(float(np.std(taus)), 3), "tau_samples": len(taus),
+        "sclk_mhz_after_timed_region": sclk,
         "parity_vs_oracle": "pass" if parity_ok else "FAIL", "flagged_sequences": flagged,
         "launch": "hip_graph_replay" if graphs is not None else "eager",
         "eager_ms_per_step": round(eager_ms, 4) if eager_ms is not None else round(ms_per_step, 4),
@@ -319,6 +335,7 @@ def bench_draft(args):
         step(evs[i])
     torch.cuda.synchronize()
     ms_per_step = (time.perf_counter() - t_start) * 1e3 / args.steps
+    sclk = gpu_sclk_mhz()
     ing = float(np.mean([e["t0"].elapsed_time(e["t1"]) for e in evs]))
     grow = float(np.mean([e["t1"].elapsed_time(e["t2"]) for e in evs]))
     ver = float(np.mean([e["t2"].elapsed_time(e["t3"]) for e in evs]))
@@ -356,6 +373,7 @@ def bench_draft(args):
         "accepted_tok_per_step": round(float(np.mean(al + 1)), 3), "tau_samples": int(len(al)),
         "tau_note": "independent random draft and target: acceptance is rare by construction",
         "phase_ms": {"context_ingest": round(ing, 3), "tree_growth": round(grow, 3), "verify": round(ver, 3)},
+        "sclk_mhz_after_timed_region": sclk,
         "launch": "eager",
         "sequence0_free_running_tree_equals_oracle": tree_same,
         "draft_tree_note": ("bf16 draft trees of free-running GPU and oracle runs may differ where rounding "
