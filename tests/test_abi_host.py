@@ -126,3 +126,31 @@ def test_tree_attn_errors(lib):
     assert need > 0                                                   # B=1: the prefix is split
     assert f(ctypes.byref(a), FAKE, need - 1, None) == -6
     assert wsq(ctypes.byref(args(B=64))) == 0                         # enough pairs: no split
+
+
+def test_empty_batches_are_no_ops(lib):
+    """A call over zero rows / sequences returns OK before any pointer check or
+    launch (null pointers everywhere, no GPU needed)."""
+    from tree_draft_verification_amd.binding import GemmArgs, TreeAttnArgs
+    f = lib.eagle3_lmhead_argmax
+    f.argtypes = [ctypes.c_void_p, ctypes.c_void_p] + [ctypes.c_int] * 5 + [ctypes.c_void_p] * 5 + [ctypes.c_size_t, ctypes.c_void_p]
+    assert f(None, None, 0, 128256, 4096, 1, 1, None, None, None, None, None, 0, None) == 0
+    f = lib.eagle3_accept_path
+    f.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int] + [ctypes.c_void_p] * 4
+    assert f(None, None, None, 1, None, 0, 61, None, None, None, None) == 0
+    f = lib.eagle3_rmsnorm
+    f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_int,
+                  ctypes.c_void_p, ctypes.c_void_p]
+    assert f(None, None, 0, 4096, 1e-5, 1, None, None) == 0
+    f = lib.eagle3_tree_attn
+    f.argtypes = [ctypes.POINTER(TreeAttnArgs), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    a = TreeAttnArgs(dtype=1, B=0, Tq=61, Tk=61, Hq=32, Hkv=8, D=128, W=1, scale=128 ** -0.5, num_blocks=0,
+                     block_size=16, max_blocks=1, split_keys=0, parent=FAKE)
+    assert f(ctypes.byref(a), None, 0, None) == 0
+    f = lib.eagle3_gemm
+    f.argtypes = [ctypes.POINTER(GemmArgs), ctypes.c_void_p]
+    g = GemmArgs(dtype=1, M=0, N=4096, nseg=1)
+    assert f(ctypes.byref(g), None) == 0
+    f = lib.eagle3_draft_fuse
+    f.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_void_p] * 3 + [ctypes.c_int] * 4 + [ctypes.c_void_p] * 3 + [ctypes.c_size_t, ctypes.c_void_p]
+    assert f(None, None, None, None, None, None, None, None, 0, 4096, 128256, 1, None, None, None, 0, None) == 0
