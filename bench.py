@@ -273,7 +273,12 @@ def bench_verify(args, name):
                       "bytes_per_launch": attn_bytes,
                       "achieved_GBps": round(attn_bytes / (at_us * 1e-6) / 1e9, 1),
                       "hbm_frac": round(attn_bytes / (at_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
-                      "flops_per_launch": attn_flops},
+                      "flops_per_launch": attn_flops,
+                      "mfma_frac": round(attn_flops / (at_us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                      # flops per algorithmic byte against the bf16 ridge point (peak flops / peak bytes):
+                      # above it no kernel can reach the HBM peak at this shape
+                      "flop_per_byte": round(attn_flops / attn_bytes, 1),
+                      "ridge_flop_per_byte": round(PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9), 1)},
         "cpu_baseline": cpu,
     }
 
