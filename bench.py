@@ -393,8 +393,8 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}, "
-              f"WORLD_SIZE {world}); the data-parallel sharding over sequences is described in DESIGN.md",
+        print(f"bench.py measures one GPU only: there is no multi-GPU path (asked for --gpus {args.gpus}, "
+              f"WORLD_SIZE {world}); sharding the batch's sequences over GPUs is a design note, not built",
               file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:

@@ -31,7 +31,7 @@
  *     the call returns without synchronising.
  *   - Errors found on the host are returned before anything is launched:
  *       EAGLE3_ERR_ARG          null pointer, negative size, misalignment
- *       EAGLE3_ERR_UNSUPPORTED  a shape or option this build does not handle
+ *       EAGLE3_ERR_UNSUPPORTED  a shape or option this library does not handle
  *       EAGLE3_ERR_WORKSPACE    ws smaller than the *_workspace() query
  *     A launch failure returns EAGLE3_ERR_HIP. Data errors (a parent[] that is
  *     not a tree in topological order, an id out of range) are reported

@@ -153,15 +153,32 @@ def test_deterministic(orc, lib):
     assert np.array_equal(a, b) and np.array_equal(la, lb)
 
 
-@pytest.mark.parametrize("split", [0, 4096])
+NORM_CASES = [
+    # B, Hkv, prefix lengths, split_keys
+    (1, 8, [1100], 0),
+    (1, 8, [1100], 4096),
+    # one launch with several splits for some sequences and a single split for
+    # others (prefix within one split, or empty): the merge-and-norm pass must
+    # keep the rows the attention pass wrote itself. 8 sequences x 8 KV heads
+    # x 6 splits exceed one work-group per CU, so the tree keys are not a split
+    # of their own there; with 4 sequences they are.
+    (8, 8, [1100, 60, 0, 700, 256, 257, 5, 900], 256),
+    (4, 8, [1100, 60, 0, 700], 256),
+    # the automatic plan at 16 sequences: two prefix splits of 576 keys, no
+    # tree split; every prefix up to 576 keys is a single split
+    (16, 8, [1100, 60, 0, 700, 256, 257, 5, 900, 1000, 30, 512, 577, 800, 1, 1024, 576], 0),
+]
+
+
+@pytest.mark.parametrize("B,Hkv,plen,split", NORM_CASES)
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_norm_out(orc, lib, split, dtype):
+def test_norm_out(orc, lib, B, Hkv, plen, split, dtype):
     """The optional RMS-normalised copy of the output (the hidden row the LM
     head reads): with the prefix split (combine pass writes it) and unsplit
     (separate RMSNorm launch). It must equal RMSNorm of the attention output
     the same call wrote, and the oracle's RMSNorm of the oracle attention."""
-    B, T, Hq, Hkv = 1, 61, 32, 8
-    parent, inp = make(130, B, T, Hq, Hkv, [1100], dtype=dtype)
+    T, Hq = 61, 32
+    parent, inp = make(130, B, T, Hq, Hkv, plen, dtype=dtype)
     W = (T + 63) // 64
     mask, _ = orc.tree_mask(parent, W)
     q, kt, vt = dev(inp.q), dev(inp.k_tree), dev(inp.v_tree)
@@ -179,14 +196,16 @@ def test_norm_out(orc, lib, split, dtype):
     torch.cuda.synchronize()
     got, got_n, own_n = host(out), host(nrm), host(ref_n)
     ref, _ = orc.tree_attn(inp.q, inp.k_tree, inp.v_tree, inp.kv, mask)
-    rel, mx = normwise_rel(got, ref)
     tol = 2e-2 if dtype == "bf16" else 1e-5
-    assert rel <= tol, (rel, mx)
+    for b in range(B):
+        rel, mx = normwise_rel(got[b], ref[b])
+        assert rel <= tol, (b, rel, mx)
     K = Hq * q.shape[-1]
     oref = orc.rmsnorm(ref.reshape(B * T, K), eps=eps).reshape(got_n.shape)
-    rel, mx = normwise_rel(got_n, oref)
-    assert rel <= tol, (rel, mx)
+    for b in range(B):
+        rel, mx = normwise_rel(got_n[b], oref[b])
+        assert rel <= tol, (b, rel, mx)
     # against the GPU's own RMSNorm of the same output: one storage rounding
-    a, b = as_f64(got_n), as_f64(own_n)
+    x, y = as_f64(got_n), as_f64(own_n)
     ulp = 2.0 ** -7 if dtype == "bf16" else 2.0 ** -22
-    assert np.all(np.abs(a - b) <= ulp * np.maximum(np.abs(b), 1e-30) + 1e-30), np.abs(a - b).max()
+    assert np.all(np.abs(x - y) <= ulp * np.maximum(np.abs(y), 1e-30) + 1e-30), np.abs(x - y).max()

@@ -566,7 +566,9 @@ __global__ __launch_bounds__(128) void tree_attn_combine_kernel(AttnParams p) {
 // Combine and RMSNorm in one pass: one work-group per (sequence, node) row
 // merges the split partials of all Hq heads (split weights per head in LDS),
 // writes the attention output row and its RMSNorm (gamma = 1) computed from
-// the stored bf16 values, as the separate norm would.
+// the stored bf16 values, as the separate norm would. A sequence with a
+// single split has no partials: the attention pass wrote its row and lse
+// itself, and this pass only reads the row back for the norm.
 constexpr int CN_MAXS = 32;  // splits per sequence the fused pass handles
 constexpr int CN_MAXH = 64;  // query heads the fused pass handles
 
@@ -578,9 +580,10 @@ __global__ __launch_bounds__(256) void tree_attn_combine_norm_kernel(AttnParams 
     const int t = blockIdx.x % p.Tq, b = blockIdx.x / p.Tq;
     const int L = clamped_len(p.prefix_len, b, p.max_blocks, 16, p.num_blocks);
     const int nsplit_b = splits_of(L, p.split_keys, p.tree_split);
+    const bool direct = nsplit_b == 1;  // uniform over the work-group
     // split weights: 8 lanes per head, lane j takes splits j, j+8, j+16, j+24
     // (all loads issued together), max and sum over the 8 lanes by shuffles
-    {
+    if (!direct) {
         const int j = threadIdx.x & 7;
         for (int hq = threadIdx.x >> 3; hq < p.Hq; hq += 32) {
             const int kvh = hq / p.G, row = t * p.G + hq % p.G;
@@ -622,35 +625,40 @@ __global__ __launch_bounds__(256) void tree_attn_combine_norm_kernel(AttnParams 
     for (int ps = 0; ps < 4; ++ps) {
         const int c = (ps * 256 + threadIdx.x) * 8;
         if (c >= K) break;
-        const int hq = c / DH, d = c % DH;
-        const int kvh = hq / p.G, row = t * p.G + hq % p.G;
-        const size_t base = ((size_t)b * p.Hkv + kvh) * p.nsplit;
-        float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        // splits 8 at a time, their loads in flight together
-        for (int s0 = 0; s0 < nsplit_b; s0 += 8) {
-            f32x4_t a[8], c4[8];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int sp = min(s0 + u, nsplit_b - 1);   // weight 0 past the end
-                const float *src = p.ws_o + ((base + sp) * p.Rpad + row) * DH + d;
-                a[u] = *reinterpret_cast<const f32x4_t *>(src);
-                c4[u] = *reinterpret_cast<const f32x4_t *>(src + 4);
-            }
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const float w = (s0 + u < nsplit_b) ? wgt[hq][s0 + u] : 0.f;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) { o[i] += w * a[u][i]; o[4 + i] += w * c4[u][i]; }
-            }
-        }
         u32x4_t packed;
+        if (direct) {
+            packed = *reinterpret_cast<const u32x4_t *>(orow + c);
+        } else {
+            const int hq = c / DH, d = c % DH;
+            const int kvh = hq / p.G, row = t * p.G + hq % p.G;
+            const size_t base = ((size_t)b * p.Hkv + kvh) * p.nsplit;
+            float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            // splits 8 at a time, their loads in flight together
+            for (int s0 = 0; s0 < nsplit_b; s0 += 8) {
+                f32x4_t a[8], c4[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int sp = min(s0 + u, nsplit_b - 1);   // weight 0 past the end
+                    const float *src = p.ws_o + ((base + sp) * p.Rpad + row) * DH + d;
+                    a[u] = *reinterpret_cast<const f32x4_t *>(src);
+                    c4[u] = *reinterpret_cast<const f32x4_t *>(src + 4);
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const float w = (s0 + u < nsplit_b) ? wgt[hq][s0 + u] : 0.f;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) { o[i] += w * a[u][i]; o[4 + i] += w * c4[u][i]; }
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) packed[i] = e3_pack_bf16x2(o[2 * i], o[2 * i + 1]);
+            *reinterpret_cast<u32x4_t *>(orow + c) = packed;
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            packed[i] = e3_pack_bf16x2(o[2 * i], o[2 * i + 1]);
             v[ps][2 * i] = __uint_as_float(packed[i] << 16);
             v[ps][2 * i + 1] = __uint_as_float(packed[i] & 0xffff0000u);
         }
-        *reinterpret_cast<u32x4_t *>(orow + c) = packed;
 #pragma unroll
         for (int i = 0; i < 8; ++i) ss += v[ps][i] * v[ps][i];
     }
