@@ -569,61 +569,66 @@ __global__ __launch_bounds__(128) void tree_attn_combine_kernel(AttnParams p) {
 // the stored bf16 values, as the separate norm would. A sequence with a
 // single split has no partials: the attention pass wrote its row and lse
 // itself, and this pass only reads the row back for the norm.
-constexpr int CN_MAXS = 32;  // splits per sequence the fused pass handles
-constexpr int CN_MAXH = 64;  // query heads the fused pass handles
+// 512 threads, 8 elements each per pass (one pass for a 4096-wide row), and
+// the partial loads of up to 16 splits in flight together: a row costs about
+// two dependent memory round trips (weights, then partials), which is what
+// bounds this pass at the few-row shapes where it runs.
+constexpr int CN_MAXS = 32;   // splits per sequence the fused pass handles
+constexpr int CN_MAXH = 64;   // query heads the fused pass handles
+constexpr int CN_NT = 512;    // threads per work-group
+constexpr int CN_BATCH = 16;  // splits whose partial loads are in flight together
 
-__global__ __launch_bounds__(256) void tree_attn_combine_norm_kernel(AttnParams p, uint16_t *__restrict__ norm_out,
-                                                                     float eps) {
-    static_assert(CN_MAXS == 32 && CN_MAXH % 32 == 0, "8 lanes x 4 splits per head, 32 heads per pass");
+__global__ __launch_bounds__(CN_NT) void tree_attn_combine_norm_kernel(AttnParams p, uint16_t *__restrict__ norm_out,
+                                                                       float eps) {
+    static_assert(CN_MAXS == 32 && CN_MAXH == CN_NT / 8, "8 lanes x 4 splits per head, all heads in one pass");
     __shared__ float wgt[CN_MAXH][CN_MAXS];
-    __shared__ float red[4];
+    __shared__ float red[CN_NT / 64];
     const int t = blockIdx.x % p.Tq, b = blockIdx.x / p.Tq;
     const int L = clamped_len(p.prefix_len, b, p.max_blocks, 16, p.num_blocks);
     const int nsplit_b = splits_of(L, p.split_keys, p.tree_split);
     const bool direct = nsplit_b == 1;  // uniform over the work-group
     // split weights: 8 lanes per head, lane j takes splits j, j+8, j+16, j+24
     // (all loads issued together), max and sum over the 8 lanes by shuffles
-    if (!direct) {
-        const int j = threadIdx.x & 7;
-        for (int hq = threadIdx.x >> 3; hq < p.Hq; hq += 32) {
-            const int kvh = hq / p.G, row = t * p.G + hq % p.G;
-            const size_t base = ((size_t)b * p.Hkv + kvh) * p.nsplit;
-            float ms[4], ls[4];
+    const int hq_w = threadIdx.x >> 3;
+    if (!direct && hq_w < p.Hq) {
+        const int j = threadIdx.x & 7, hq = hq_w;
+        const int kvh = hq / p.G, row = t * p.G + hq % p.G;
+        const size_t base = ((size_t)b * p.Hkv + kvh) * p.nsplit;
+        float ms[4], ls[4];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int sp = j + 8 * u;
-                ms[u] = -INFINITY; ls[u] = 0.f;
-                if (sp < nsplit_b) {
-                    const f32x2_t ml = *reinterpret_cast<const f32x2_t *>(p.ws_ml + ((base + sp) * p.Rpad + row) * 2);
-                    ms[u] = ml[0]; ls[u] = ml[1];
-                }
+        for (int u = 0; u < 4; ++u) {
+            const int sp = j + 8 * u;
+            ms[u] = -INFINITY; ls[u] = 0.f;
+            if (sp < nsplit_b) {
+                const f32x2_t ml = *reinterpret_cast<const f32x2_t *>(p.ws_ml + ((base + sp) * p.Rpad + row) * 2);
+                ms[u] = ml[0]; ls[u] = ml[1];
             }
-            float M = fmaxf(fmaxf(ms[0], ms[1]), fmaxf(ms[2], ms[3]));
-#pragma unroll
-            for (int off = 1; off < 8; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
-            float w[4], den = 0.f;
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                w[u] = (ms[u] == -INFINITY) ? 0.f : ls[u] * exp2f(ms[u] - M);
-                den += w[u];
-            }
-#pragma unroll
-            for (int off = 1; off < 8; off <<= 1) den += __shfl_xor(den, off);
-            const float inv = den > 0.f ? 1.f / den : 0.f;
-#pragma unroll
-            for (int u = 0; u < 4; ++u) wgt[hq][j + 8 * u] = w[u] * inv;   // zero past nsplit_b
-            if (p.lse && j == 0)
-                p.lse[((size_t)b * p.Tq + t) * p.Hq + hq] = den > 0.f ? (M + log2f(den)) * kLn2 : -INFINITY;
         }
+        float M = fmaxf(fmaxf(ms[0], ms[1]), fmaxf(ms[2], ms[3]));
+#pragma unroll
+        for (int off = 1; off < 8; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
+        float w[4], den = 0.f;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            w[u] = (ms[u] == -INFINITY) ? 0.f : ls[u] * exp2f(ms[u] - M);
+            den += w[u];
+        }
+#pragma unroll
+        for (int off = 1; off < 8; off <<= 1) den += __shfl_xor(den, off);
+        const float inv = den > 0.f ? 1.f / den : 0.f;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) wgt[hq][j + 8 * u] = w[u] * inv;   // zero past nsplit_b
+        if (p.lse && j == 0)
+            p.lse[((size_t)b * p.Tq + t) * p.Hq + hq] = den > 0.f ? (M + log2f(den)) * kLn2 : -INFINITY;
     }
     __syncthreads();
     const int K = p.Hq * DH;
-    float v[4][8];  // this thread's 8 consecutive elements of each pass (K <= 8192)
+    float v[2][8];  // this thread's 8 consecutive elements of each pass (K <= 8192)
     float ss = 0.f;
     uint16_t *orow = p.out + ((size_t)b * p.Tq + t) * K;
 #pragma unroll
-    for (int ps = 0; ps < 4; ++ps) {
-        const int c = (ps * 256 + threadIdx.x) * 8;
+    for (int ps = 0; ps < 2; ++ps) {
+        const int c = (ps * CN_NT + threadIdx.x) * 8;
         if (c >= K) break;
         u32x4_t packed;
         if (direct) {
@@ -633,21 +638,23 @@ __global__ __launch_bounds__(256) void tree_attn_combine_norm_kernel(AttnParams 
             const int kvh = hq / p.G, row = t * p.G + hq % p.G;
             const size_t base = ((size_t)b * p.Hkv + kvh) * p.nsplit;
             float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-            // splits 8 at a time, their loads in flight together
-            for (int s0 = 0; s0 < nsplit_b; s0 += 8) {
-                f32x4_t a[8], c4[8];
+            for (int s0 = 0; s0 < nsplit_b; s0 += CN_BATCH) {
+                f32x4_t a[CN_BATCH], c4[CN_BATCH];
 #pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const int sp = min(s0 + u, nsplit_b - 1);   // weight 0 past the end
-                    const float *src = p.ws_o + ((base + sp) * p.Rpad + row) * DH + d;
-                    a[u] = *reinterpret_cast<const f32x4_t *>(src);
-                    c4[u] = *reinterpret_cast<const f32x4_t *>(src + 4);
+                for (int u = 0; u < CN_BATCH; ++u) {
+                    if (s0 + u < nsplit_b) {  // uniform
+                        const float *src = p.ws_o + ((base + s0 + u) * p.Rpad + row) * DH + d;
+                        a[u] = *reinterpret_cast<const f32x4_t *>(src);
+                        c4[u] = *reinterpret_cast<const f32x4_t *>(src + 4);
+                    }
                 }
 #pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const float w = (s0 + u < nsplit_b) ? wgt[hq][s0 + u] : 0.f;
+                for (int u = 0; u < CN_BATCH; ++u) {
+                    if (s0 + u < nsplit_b) {
+                        const float w = wgt[hq][s0 + u];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) { o[i] += w * a[u][i]; o[4 + i] += w * c4[u][i]; }
+                        for (int i = 0; i < 4; ++i) { o[i] += w * a[u][i]; o[4 + i] += w * c4[u][i]; }
+                    }
                 }
             }
 #pragma unroll
@@ -662,12 +669,19 @@ __global__ __launch_bounds__(256) void tree_attn_combine_norm_kernel(AttnParams 
 #pragma unroll
         for (int i = 0; i < 8; ++i) ss += v[ps][i] * v[ps][i];
     }
-    const float total = e3_block_sum_256(ss, red);
+    // row sum of squares: waves, then the 8 wave sums
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    float total = 0.f;
+#pragma unroll
+    for (int w = 0; w < CN_NT / 64; ++w) total += red[w];
     const float r = 1.0f / sqrtf(total / (float)K + eps);
     uint16_t *nrow = norm_out + ((size_t)b * p.Tq + t) * K;
 #pragma unroll
-    for (int ps = 0; ps < 4; ++ps) {
-        const int c = (ps * 256 + threadIdx.x) * 8;
+    for (int ps = 0; ps < 2; ++ps) {
+        const int c = (ps * CN_NT + threadIdx.x) * 8;
         if (c >= K) break;
         u32x4_t packed;
 #pragma unroll
@@ -891,7 +905,7 @@ extern "C" int eagle3_tree_attn(const eagle3_tree_attn_args *a, void *ws, size_t
         tree_attn_bf16_kernel<8, 1><<<grid, 512, 0, st>>>(p);
         const bool fused_norm = a->norm_out && pl.nsplit > 1 && pl.nsplit <= CN_MAXS && a->Hq <= CN_MAXH;
         if (fused_norm)
-            tree_attn_combine_norm_kernel<<<a->B * a->Tq, 256, 0, st>>>(p, (uint16_t *)a->norm_out, a->norm_eps);
+            tree_attn_combine_norm_kernel<<<a->B * a->Tq, CN_NT, 0, st>>>(p, (uint16_t *)a->norm_out, a->norm_eps);
         else if (pl.nsplit > 1)
             tree_attn_combine_kernel<<<a->B * a->Tq * a->Hq, DH, 0, st>>>(p);
         if (a->norm_out && !fused_norm) {
