@@ -385,23 +385,39 @@ __global__ __launch_bounds__(256) void lmhead_merge_kernel(int ntiles, Partials 
     uint64_t L[KK];
     e3_kinit<KK>(L);
     float mx = -INFINITY, se = 0.f;
-    for (int t = threadIdx.x; t < ntiles; t += 256) {
-        const size_t rec = (size_t)m * ntiles + t;
-        uint64_t rk[KK];
-        const u32x4_t *src = reinterpret_cast<const u32x4_t *>(p.key + rec * KK);
+    // two records per thread and step, both loaded before either is merged
+    // (a 128256-row head at 256 rows per tile has 501 records per row: one
+    // memory round trip instead of two)
+    for (int t0 = threadIdx.x; t0 < ntiles; t0 += 512) {
+        uint64_t rk[2][KK];
+        float rmx[2] = {-INFINITY, -INFINITY}, rse[2] = {0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < KK; s += 2) {
-            const u32x4_t q = src[s / 2];
-            rk[s] = ((uint64_t)q[1] << 32) | q[0];
-            rk[s + 1] = ((uint64_t)q[3] << 32) | q[2];
-        }
-        // a record is sorted: once an entry cannot enter, none after it can
+        for (int u = 0; u < 2; ++u) {
+            const int t = t0 + 256 * u;
 #pragma unroll
-        for (int s = 0; s < KK; ++s) {
-            if (!(rk[s] > L[KK - 1])) break;
-            e3_kinsert<KK>(L, rk[s]);
+            for (int s = 0; s < KK; ++s) rk[u][s] = 0;  // below every key: never enters
+            if (t < ntiles) {
+                const size_t rec = (size_t)m * ntiles + t;
+                const u32x4_t *src = reinterpret_cast<const u32x4_t *>(p.key + rec * KK);
+#pragma unroll
+                for (int s = 0; s < KK; s += 2) {
+                    const u32x4_t q = src[s / 2];
+                    rk[u][s] = ((uint64_t)q[1] << 32) | q[0];
+                    rk[u][s + 1] = ((uint64_t)q[3] << 32) | q[2];
+                }
+                if (LSE) { rmx[u] = p.mx[rec]; rse[u] = p.se[rec]; }
+            }
         }
-        if (LSE) e3_lse_combine(mx, se, p.mx[rec], p.se[rec]);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            // a record is sorted: once an entry cannot enter, none after it can
+#pragma unroll
+            for (int s = 0; s < KK; ++s) {
+                if (!(rk[u][s] > L[KK - 1])) break;
+                e3_kinsert<KK>(L, rk[u][s]);
+            }
+            if (LSE) e3_lse_combine(mx, se, rmx[u], rse[u]);
+        }
     }
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {

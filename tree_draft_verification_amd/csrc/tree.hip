@@ -139,15 +139,19 @@ __global__ __launch_bounds__(64) void accept_kernel(const int32_t *__restrict__ 
     for (int off = 32; off >= 1; off >>= 1) best = max(best, __shfl_xor(best, off));
     const int a = best >> 8;
     const int end = 255 - (best & 255);
-    // path = ancestors of end, ascending index (= root first: parent < child)
+    // path = ancestors of end, ascending index (= root first: parent < child),
+    // taken from the lane that holds node end (end is wave-uniform)
     uint64_t aend[W];
 #pragma unroll
-    for (int w = 0; w < W; ++w) aend[w] = 0;
-    if (mask) {
+    for (int w = 0; w < W; ++w) {
+        aend[w] = 0;
 #pragma unroll
-        for (int w = 0; w < W; ++w) aend[w] = mask[(row + end) * W + w];
-    } else {
-        walk_ancestors<W>(par, T, end, aend);
+        for (int j = 0; j < NPL; ++j)
+            if (j == (end >> 6)) {
+                const uint32_t lo = __shfl((uint32_t)anc[j][w], end & 63);
+                const uint32_t hi = __shfl((uint32_t)(anc[j][w] >> 32), end & 63);
+                aend[w] = ((uint64_t)hi << 32) | lo;
+            }
     }
 #pragma unroll
     for (int j = 0; j < NPL; ++j) {
