@@ -154,32 +154,35 @@ def test_deterministic(orc, lib):
 
 
 NORM_CASES = [
-    # B, Hkv, prefix lengths, split_keys
-    (1, 8, [1100], 0),
-    (1, 8, [1100], 4096),
+    # B, Hq, Hkv, prefix lengths, split_keys
+    (1, 32, 8, [1100], 0),
+    (1, 32, 8, [1100], 4096),
     # one launch with several splits for some sequences and a single split for
     # others (prefix within one split, or empty): the merge-and-norm pass must
     # keep the rows the attention pass wrote itself. 8 sequences x 8 KV heads
     # x 6 splits exceed one work-group per CU, so the tree keys are not a split
     # of their own there; with 4 sequences they are.
-    (8, 8, [1100, 60, 0, 700, 256, 257, 5, 900], 256),
-    (4, 8, [1100, 60, 0, 700], 256),
+    (8, 32, 8, [1100, 60, 0, 700, 256, 257, 5, 900], 256),
+    (4, 32, 8, [1100, 60, 0, 700], 256),
     # the automatic plan at 16 sequences: two prefix splits of 576 keys, no
     # tree split; every prefix up to 576 keys is a single split
-    (16, 8, [1100, 60, 0, 700, 256, 257, 5, 900, 1000, 30, 512, 577, 800, 1, 1024, 576], 0),
+    (16, 32, 8, [1100, 60, 0, 700, 256, 257, 5, 900, 1000, 30, 512, 577, 800, 1, 1024, 576], 0),
     # more than 32 splits: the merge and the norm run as two launches
-    (2, 8, [2200, 40], 64),
+    (2, 32, 8, [2200, 40], 64),
+    # 128 query heads (16 per KV head: four 256-row blocks per head), wider
+    # than the fused pass handles: merge, then the separate norm
+    (2, 128, 8, [900, 0], 256),
 ]
 
 
-@pytest.mark.parametrize("B,Hkv,plen,split", NORM_CASES)
+@pytest.mark.parametrize("B,Hq,Hkv,plen,split", NORM_CASES)
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_norm_out(orc, lib, B, Hkv, plen, split, dtype):
+def test_norm_out(orc, lib, B, Hq, Hkv, plen, split, dtype):
     """The optional RMS-normalised copy of the output (the hidden row the LM
     head reads): with the prefix split (combine pass writes it) and unsplit
     (separate RMSNorm launch). It must equal RMSNorm of the attention output
     the same call wrote, and the oracle's RMSNorm of the oracle attention."""
-    T, Hq = 61, 32
+    T = 61
     parent, inp = make(130, B, T, Hq, Hkv, plen, dtype=dtype)
     W = (T + 63) // 64
     mask, _ = orc.tree_mask(parent, W)

@@ -441,10 +441,14 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_bf16_kernel(AttnParams p) {
 #pragma unroll
         for (int k = 0; k < RB; ++k) mword[k] = 0;
         if (it < ntile) {
-            if (it + NSTAGE - 2 < ntile) wait_vmcnt<(NSTAGE - 2) * LOADS>();
-            else wait_vmcnt<0>();
+            // all of this wave's ring loads, not just those of tile it: the
+            // wait then holds whatever order the DMA completions take (tile
+            // it + 1 was issued a tile earlier and has landed by now; measured
+            // at no cost against waiting for tile it alone)
+            wait_vmcnt<0>();
             // tile it has landed for every wave and every wave is done with the
-            // buffer refilled below; a fenced barrier would drain the whole ring
+            // buffer refilled below; a fenced barrier would also wait for the
+            // compiler's own outstanding operations
             __builtin_amdgcn_s_barrier();
             __asm__ volatile("" ::: "memory");
             stage = ring + (it % NSTAGE) * STAGE;
