@@ -36,7 +36,16 @@ def gpu_attn(lib, inp, mask=None, parent=None, split_keys=0, want_lse=True):
     ws = torch.empty(max(ws_n, 256), dtype=torch.uint8, device="cuda")
     lib.eagle3_tree_attn(args, ws)
     torch.cuda.synchronize()
-    return host(out), (host(lse) if want_lse else None)
+    got = host(out), (host(lse) if want_lse else None)
+    # a second call on the same device inputs must give the same bits; when a
+    # parity check fails, this tells a race in the kernels (the calls differ)
+    # from a wrong result that the inputs determine (they agree)
+    out.fill_(0)
+    lib.eagle3_tree_attn(args, ws)
+    torch.cuda.synchronize()
+    gpu_attn.repeat_identical = bool(np.array_equal(host(out), got[0]) and
+                                     (lse is None or np.array_equal(host(lse), got[1])))
+    return got
 
 
 def make(wid, B, T, Hq, Hkv, plen, dtype="bf16", D=128, seed=0, depth=7, Tq=None):
@@ -79,9 +88,10 @@ def test_bf16_parity(orc, lib, case, mode):
     else:
         got, lse = gpu_attn(lib, inp, parent=parent, split_keys=split)
     rel, mx = normwise_rel(got, ref)
-    assert rel <= 2e-2, (rel, mx, where_wrong(got, ref))
+    same = gpu_attn.repeat_identical
+    assert rel <= 2e-2, (rel, mx, where_wrong(got, ref), "second call identical", same)
     assert np.all(np.isfinite(lse))
-    assert np.abs(lse - ref_lse).max() <= 2e-3
+    assert np.abs(lse - ref_lse).max() <= 2e-3, ("second call identical", same)
 
 
 def where_wrong(got, ref, tol=2e-2):
@@ -210,12 +220,21 @@ def test_norm_out(orc, lib, B, Hq, Hkv, plen, split, dtype):
     lib.eagle3_rmsnorm(out.view(B * T, -1), ref_n.view(B * T, -1), eps=eps)
     torch.cuda.synchronize()
     got, got_n, own_n, got_lse = host(out), host(nrm), host(ref_n), host(lse)
+    # the same call again on the same buffers: bit-identical results
+    out.fill_(0)
+    nrm.fill_(0)
+    lib.eagle3_tree_attn(args, ws)
+    torch.cuda.synchronize()
+    same = (np.array_equal(host(out), got) and np.array_equal(host(nrm), got_n) and
+            np.array_equal(host(lse), got_lse))
     ref, ref_lse = orc.tree_attn(inp.q, inp.k_tree, inp.v_tree, inp.kv, mask)
     tol = 2e-2 if dtype == "bf16" else 1e-5
     for b in range(B):
         rel, mx = normwise_rel(got[b], ref[b])
-        assert rel <= tol, (b, rel, mx)
-        assert np.abs(got_lse[b] - ref_lse[b]).max() <= (2e-3 if dtype == "bf16" else 1e-5), b
+        assert rel <= tol, (b, rel, mx, "second call identical", same)
+        lerr = np.abs(got_lse[b] - ref_lse[b])
+        assert lerr.max() <= (2e-3 if dtype == "bf16" else 1e-5), (
+            b, [tuple(int(x) for x in r) for r in np.argwhere(lerr > 1e-3)[:8]], "second call identical", same)
     K = Hq * q.shape[-1]
     oref = orc.rmsnorm(ref.reshape(B * T, K), eps=eps).reshape(got_n.shape)
     for b in range(B):
