@@ -91,6 +91,28 @@ def functions(asm_text):
             yield m.group(1), lines[st:end + 1]
 
 
+def mfma_overlaps(lines):
+    """MFMAs whose destination overlaps their A or B operand, or partly
+    overlaps C: (line, instruction)."""
+    found = []
+    for i, raw in enumerate(lines):
+        s = raw.split(";")[0].strip()
+        if not s.startswith("v_mfma"):
+            continue
+        ops = s.replace(",", " ").split()[1:]
+        d, a, b, c = (_regs(t) for t in ops[:4])
+        if (d & a) or (d & b) or (c and d & c and c != d):
+            found.append((i + 1, s))
+    return found
+
+
+def test_overlap_scanner_flags_a_planted_case():
+    lines = ["v_mfma_f32_32x32x16_bf16 v[68:83], v[72:75], v[136:139], 0",
+             "v_mfma_f32_32x32x16_bf16 v[84:99], v[68:71], v[136:139], v[84:99]",
+             "v_mfma_f32_32x32x16_bf16 v[0:15], v[16:19], v[20:23], v[4:19]"]
+    assert [f[0] for f in mfma_overlaps(lines)] == [1, 3]
+
+
 def test_scanner_flags_a_planted_early_read():
     """The scanner itself: an early copy and an early MFMA operand are found,
     a read after its wait and a read after an unconditional branch are not."""
@@ -137,4 +159,9 @@ def test_no_read_of_in_flight_lds_fragments(tmp_path):
                 problems.append(f"{os.path.basename(src)} {name} line {line}: {ins} reads v{regs}")
     assert nfun > 20
     assert not problems, "\n".join(problems[:20])
+    # no MFMA may write over its own A or B operand (for the 32x32 forms the
+    # compiler ties the destination only to C; an inline-zero C left it free)
+    overlaps = [f"{os.path.basename(src)} line {ln}: {ins}" for src, text in results
+                for (ln, ins) in mfma_overlaps(text.splitlines())]
+    assert not overlaps, "\n".join(overlaps[:20])
     shutil.rmtree(tmp_path, ignore_errors=True)

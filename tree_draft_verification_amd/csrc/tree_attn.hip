@@ -225,18 +225,27 @@ __device__ __forceinline__ void attend_tile(int kind, const unsigned char *stage
         lds_read16_at<(j & 1) * 8192>(fr[j % NF], sb + fo.k[j >> 1]);
     };
     f32x16_t st[RB][2];
+    // the score accumulators start as registers holding zero, not the MFMA's
+    // inline-zero operand: with the inline zero the destination is not tied
+    // to an input and the compiler placed it over the A operand's registers
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) st[rb][kb][r] = 0.f;
+            __asm__ volatile("" : "+v"(st[rb][kb]));
+        }
     sfor<0, RA>(kread);
     sfor<0, 16>([&](auto J) {
         constexpr int j = J, kb = j & 1, s = j >> 1;
         if constexpr (j + RA < 16) kread(std::integral_constant<int, j + RA>{});
         lgkm_wait1<(15 - j < RA ? 15 - j : RA)>(fr[j % NF]);
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-            const f32x16_t z = {};
+        for (int rb = 0; rb < RB; ++rb)
             st[rb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, fr[j % NF]),
-                                                                 __builtin_bit_cast(bf16x8_t, qb[rb][s]),
-                                                                 s == 0 ? z : st[rb][kb], 0, 0, 0);
-        }
+                                                                 __builtin_bit_cast(bf16x8_t, qb[rb][s]), st[rb][kb],
+                                                                 0, 0, 0);
     });
     // PV step j: 16-key step ks = j >> 2, d block db = j & 3; the first RA V
     // fragments are read now and land during the softmax
