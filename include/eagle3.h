@@ -109,12 +109,12 @@ int eagle3_tree_mask(const int32_t *parent, int B, int T, int W,
  * Supported: bf16 with D = 128; fp32 with D = 64 or 128; block_size 16;
  * Tk <= 64 * W, W in {1, 2}; Hq % Hkv == 0. A query row that sees no key gets
  * out = 0 and lse = -inf. Slots of the cache past prefix_len are never read.
- * split_keys: prefix keys per work-group split (multiple of 64), 0 = chosen by
- * the library from B, Hkv and max_blocks. Results do not depend on the call's
- * batch composition, but may differ in the last bits between split choices.
+ * split_keys: must be 0 (any other value gives EAGLE3_ERR_UNSUPPORTED): one
+ * work-group walks the whole prefix of its (sequence, KV head, block of 256
+ * query rows); bf16 calls need max_blocks * block_size <= 16384. Results do
+ * not depend on the call's batch composition.
  * norm_out (nullable): the RMSNorm (gamma = 1, eps = norm_eps) of each output
- * row [Hq * D], as eagle3_rmsnorm on out would give; fused into the split merge
- * when the prefix is split.
+ * row [Hq * D], as eagle3_rmsnorm on out would give (a second launch).
  */
 typedef struct eagle3_tree_attn_args {
     int dtype;

@@ -121,11 +121,10 @@ def test_tree_attn_errors(lib):
     assert f(ctypes.byref(args(scale=0.0)), None, 0, None) == -1
     assert f(ctypes.byref(args(mask=None)), None, 0, None) == -1      # neither mask nor parent
     assert f(ctypes.byref(args(q=MISALIGNED)), None, 0, None) == -1
-    a = args()
-    need = wsq(ctypes.byref(a))
-    assert need > 0                                                   # B=1: the prefix is split
-    assert f(ctypes.byref(a), FAKE, need - 1, None) == -6
-    assert wsq(ctypes.byref(args(B=64))) == 0                         # enough pairs: no split
+    assert f(ctypes.byref(args(split_keys=128)), None, 0, None) == -2  # prefix splits are switched off
+    assert f(ctypes.byref(args(max_blocks=1025)), None, 0, None) == -2  # > 16384 keys for one work-group
+    assert wsq(ctypes.byref(args())) == 0                              # one work-group per prefix: no scratch
+    assert wsq(ctypes.byref(args(B=64))) == 0
 
 
 def test_empty_batches_are_no_ops(lib):

@@ -75,10 +75,16 @@ CASES = [
 ]
 
 
+SPLIT_OFF = ("prefix splits over work-groups are switched off (EAGLE3_ERR_UNSUPPORTED): the split path "
+             "gave sporadic wrong rows whose cause was not found")
+
+
 @pytest.mark.parametrize("case", range(len(CASES)))
 @pytest.mark.parametrize("mode", ["mask", "parent"])
 def test_bf16_parity(orc, lib, case, mode):
     B, T, Hq, Hkv, plen, split = CASES[case]
+    if split:
+        pytest.skip(SPLIT_OFF)
     parent, inp = make(100 + case, B, T, Hq, Hkv, plen)
     W = (T + 63) // 64
     mask, _ = orc.tree_mask(parent, W)
@@ -197,9 +203,10 @@ NORM_CASES = [
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_norm_out(orc, lib, B, Hq, Hkv, plen, split, dtype):
     """The optional RMS-normalised copy of the output (the hidden row the LM
-    head reads): with the prefix split (combine pass writes it) and unsplit
-    (separate RMSNorm launch). It must equal RMSNorm of the attention output
-    the same call wrote, and the oracle's RMSNorm of the oracle attention."""
+    head reads). It must equal RMSNorm of the attention output the same call
+    wrote, and the oracle's RMSNorm of the oracle attention."""
+    if split:
+        pytest.skip(SPLIT_OFF)
     T = 61
     parent, inp = make(130, B, T, Hq, Hkv, plen, dtype=dtype)
     W = (T + 63) // 64

@@ -18,7 +18,7 @@ def test_graph_replays_match_eager():
     kc, vc, bt, pl = dev(inp.kv.k_cache), dev(inp.kv.v_cache), dev(inp.kv.block_table), dev(inp.kv.prefix_len)
     parent, q, kt, vt = dev(inp.parent), dev(inp.q), dev(inp.k_tree), dev(inp.v_tree)
     tok = dev(inp.plant_id)
-    step = e3.VerifyStep(shape.B, shape.T, shape.Hq, shape.Hkv, shape.D, shape.V, kc, vc, bt, pl, W, split_keys=128)
+    step = e3.VerifyStep(shape.B, shape.T, shape.Hq, shape.Hkv, shape.D, shape.V, kc, vc, bt, pl, W)
     step.run(parent, q, kt, vt, tok)
     torch.cuda.synchronize()
     names = ("attn", "hidden", "idx", "gap", "accept_len", "path", "out_tokens")

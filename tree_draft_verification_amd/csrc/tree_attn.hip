@@ -122,7 +122,7 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 constexpr int NSTAGE = 3;                  // depth of the K/V ring
 constexpr int STAGE = 2 * KT * DH * 2;     // bytes per stage: K tile + V tile (16 KB each)
 constexpr int VOFF = KT * DH * 2;          // V tile offset inside a stage
-constexpr int MAX_SPLIT_BLOCKS = 256;      // cache blocks one split may cover (split_keys <= 4096)
+constexpr int MAX_SPLIT_BLOCKS = 1024;     // cache blocks one work-group may cover (prefixes up to 16384 keys)
 
 // 16-byte column swizzle of K rows (a tile row is one key, 256 B): K reads of
 // 16 consecutive rows then hit 16 distinct bank groups.
@@ -827,7 +827,12 @@ int check_args(const eagle3_tree_attn_args *a) {
     } else {
         return EAGLE3_ERR_UNSUPPORTED;
     }
-    if (a->split_keys < 0 || a->split_keys % KT != 0 || a->split_keys > 16 * MAX_SPLIT_BLOCKS)
+    // one work-group per (sequence, KV head, row block) walks the whole prefix:
+    // splitting a prefix over work-groups is switched off (split_keys must be
+    // 0), because the split path gave sporadic wrong rows whose cause was not
+    // found; block ids of one work-group must fit its LDS table
+    if (a->split_keys != 0) return EAGLE3_ERR_UNSUPPORTED;
+    if (a->dtype == EAGLE3_BF16 && (long)a->max_blocks * a->block_size > 16L * MAX_SPLIT_BLOCKS)
         return EAGLE3_ERR_UNSUPPORTED;
     if (a->mask == nullptr) {
         if (a->parent == nullptr || a->Tq != a->Tk) return EAGLE3_ERR_ARG;
@@ -840,35 +845,13 @@ Plan make_plan(const eagle3_tree_attn_args *a) {
     const int G = a->Hq / a->Hkv;
     const int R = a->Tq * G;
     pl.nrb = (R + ROWS_PER_WG - 1) / ROWS_PER_WG;
+    // a single split covering the largest prefix the block table can address
     const long lmax = (long)a->max_blocks * a->block_size;
-    const long ktiles = lmax > 0 ? (lmax + KT - 1) / KT : 1;
-    if (a->split_keys > 0) {
-        pl.split_keys = a->split_keys;
-    } else {
-        // about one work-group per CU, at least 2 tiles per split (so the
-        // ring has something to overlap), at most 4096 keys per split
-        const long base = (long)a->B * a->Hkv * pl.nrb;
-        long ns = base > 0 ? (256 + base - 1) / base : 1;
-        if (ns > (ktiles + 1) / 2) ns = (ktiles + 1) / 2;
-        if (ns < 1) ns = 1;
-        long tiles_per = (ktiles + ns - 1) / ns;
-        if (tiles_per > MAX_SPLIT_BLOCKS / 4) tiles_per = MAX_SPLIT_BLOCKS / 4;
-        pl.split_keys = (int)(tiles_per * KT);
-    }
-    pl.nsplit = (int)((lmax + pl.split_keys - 1) / pl.split_keys);
-    if (pl.nsplit < 1) pl.nsplit = 1;
-    // when the prefix is split anyway and one more split still fits in one
-    // pass over the CUs (one 512-thread work-group per CU), the tree keys
-    // become a split of their own, so no split does a prefix share plus the
-    // tree; past one pass the extra work-groups would form a second wave
-    const long wgs = (long)a->B * a->Hkv * pl.nrb * (pl.nsplit + 1);
-    pl.tree_split = (a->dtype == EAGLE3_BF16 && pl.nsplit > 1 && a->Tk > 0 && wgs <= 256) ? 1 : 0;
-    pl.nsplit += pl.tree_split;
+    const long keys = lmax > 0 ? (lmax + KT - 1) / KT * KT : KT;
+    pl.split_keys = (int)keys;
+    pl.nsplit = 1;
+    pl.tree_split = 0;
     pl.ws_bytes = 0;
-    if (a->dtype == EAGLE3_BF16 && pl.nsplit > 1) {
-        const size_t rows = (size_t)a->B * a->Hkv * pl.nsplit * (size_t)pl.nrb * ROWS_PER_WG;
-        pl.ws_bytes = ((rows * DH * 4 + 255) & ~(size_t)255) + rows * 2 * 4;
-    }
     return pl;
 }
 
