@@ -432,7 +432,36 @@ def _page(rows_k, rows_v, bs=16):
     return synth.PagedKV(kc, vc, table, np.full(B, L, np.int32), bs)
 
 
-def draft_tree(shape, W, l, m, h, ctx_tok, gap=GAP_FLAG, follow=None):
+class OwnChoice:
+    """The selections of draft_tree itself: a node's children are its top-k
+    logits by (value desc, id asc); the next frontier and the final tree are
+    the top candidates by (score desc, creation asc).
+
+    draft_tree asks a chooser for every selection it makes, so a caller can
+    evaluate this arithmetic along other selections (the tests replay another
+    run's choices that way); `wide` is how many of each row's top logits the
+    chooser is shown."""
+
+    def __init__(self, C):
+        self.C = C
+        self.wide = C + 1
+
+    def children(self, step, idx, val):
+        """-> ids [M, C], their logits [M, C]."""
+        return idx[:, :self.C], val[:, :self.C]
+
+    def frontier(self, step, cand, start):
+        """-> the next frontier as indices into this step's candidates [B, C]."""
+        creation = np.tile(np.arange(start, start + cand.shape[1], dtype=np.int32), (cand.shape[0], 1))
+        return select_topk(cand, creation, self.C)
+
+    def final(self, pool_score, N):
+        """-> pool indices of the final tree [B, N] (any order)."""
+        P = pool_score.shape[1]
+        return select_topk(pool_score, np.tile(np.arange(P, dtype=np.int32), (pool_score.shape[0], 1)), N)
+
+
+def draft_tree(shape, W, l, m, h, ctx_tok, gap=GAP_FLAG, chooser=None):
     """EAGLE-3 draft head and EAGLE-2 style tree growth, for B sequences.
 
     News write-up of the EAGLE-3 paper, draft stage: context row t fuses the
@@ -449,30 +478,24 @@ def draft_tree(shape, W, l, m, h, ctx_tok, gap=GAP_FLAG, follow=None):
     keeps the top-k candidates as the next frontier and every candidate in the
     pool; the final tree is the top n_drafts of the pool by (score desc,
     creation asc), renumbered in creation order under the root.
-    Returns parent, tokens [B, n+1] and per-sequence flags: some selection
+
+    chooser: who makes the selections (default OwnChoice). Returns parent,
+    tokens [B, n+1]; "flagged" per sequence (own choices only): some selection
     boundary within `gap` that can reach the final tree (a top-k boundary of a
     node's children or a frontier boundary whose score at stake lies within
-    `gap` of the n-th pool score, or the final rerank boundary).
-
-    follow: checks the choices of another run instead of making its own. A
-    dict with, per step, "ids" [B, F, C] (the children taken at each frontier
-    node) and "frontier" [B, C] (the candidates taken, as indices into that
-    step's candidates, in frontier order), and "selected" [B, n] (pool indices
-    of the final tree). The arithmetic is unchanged; the result also holds the
-    logits of the taken children ("lm_val", per step) and, per sequence, how
-    far each kind of choice falls below the best alternative in this run's
-    numbers ("margin": 0 when the choices agree; inf when a taken child is
-    not among this run's top 16). Either way "choices" holds the choices made,
-    in the same form."""
+    `gap` of the n-th pool score, or the final rerank boundary); "choices"
+    (the selections made); "rows": per growth step s >= 2 the frontier's
+    tokens, the row of each frontier node's parent in the previous step's
+    outputs (a_root for step 2), the position and the fused inputs x."""
     s = shape
     B, ctx, k = l.shape
     qd, kvd, C = s.Hq * s.D, s.Hkv * s.D, s.topk
     wq, wk, wv = W["wqkv"][:qd], W["wqkv"][qd:qd + kvd], W["wqkv"][qd + kvd:]
+    own = chooser is None
+    ch = OwnChoice(C) if own else chooser
     near = np.zeros(B, bool)
-    margin = {"lm": np.zeros(B), "frontier": np.zeros(B), "final": np.zeros(B)}
-    lm_vals, a_steps = [], []
+    lm_vals, a_steps, rows = [], [], []
     choices = {"ids": [], "frontier": []}
-    wide = C + 1 if follow is None else 16
 
     def layer_tail(x, attn):
         x = gemm(attn, W["wo"], R=x)
@@ -480,38 +503,18 @@ def draft_tree(shape, W, l, m, h, ctx_tok, gap=GAP_FLAG, follow=None):
         return gemm(f, W["wd"], R=x)
 
     def head(a, step):
-        idx, val, _, lse = lmhead(rmsnorm(a, eps=s.eps), W["lm_head"], topk=wide)
-        if follow is None:
-            ids, v = idx[:, :C], val[:, :C]
-        else:
-            ids = np.asarray(follow["ids"][step - 1]).reshape(-1, C).astype(np.int32)
-            v = np.full(ids.shape, -np.inf)
-            for r in range(ids.shape[0]):
-                for j in range(C):
-                    hit = np.flatnonzero(idx[r] == ids[r, j])
-                    if len(hit):
-                        v[r, j] = val[r, hit[0]]
-            worst = np.maximum(val[:, C - 1] - v.min(axis=1), 0.0)
-            margin["lm"] = np.maximum(margin["lm"], worst.reshape(B, -1).max(axis=1))
-            lm_vals.append(v.reshape(B, -1, C))
+        idx, val, _, lse = lmhead(rmsnorm(a, eps=s.eps), W["lm_head"], topk=ch.wide)
+        ids, v = ch.children(step, idx, val)
+        ids = np.asarray(ids).reshape(-1, C).astype(np.int32)
+        v = np.asarray(v).reshape(-1, C)
+        lm_vals.append(v.reshape(B, -1, C))
         logp = (v - lse[:, None]).astype(np.float32)
         choices["ids"].append(ids.reshape(B, -1, C))
         return ids, logp, val[:, C - 1] - val[:, C]
 
     def take(cand, step, start):
-        """The next frontier: own choice, or the followed one (with its margin)."""
-        creation = np.tile(np.arange(start, start + cand.shape[1], dtype=np.int32), (B, 1))
-        own = select_topk(cand, creation, min(C + 1, cand.shape[1]))
-        if follow is None:
-            choices["frontier"].append(own[:, :C])
-            return own[:, :C]
-        order = np.asarray(follow["frontier"][step - 1]).astype(np.int64)
-        chosen = np.zeros(cand.shape, bool)
-        np.put_along_axis(chosen, order, True, 1)
-        if (~chosen).any():
-            lo = np.where(chosen, cand, np.inf).min(axis=1)
-            hi = np.where(chosen, -np.inf, cand).max(axis=1)
-            margin["frontier"] = np.maximum(margin["frontier"], np.maximum(hi - lo, 0.0))
+        order = np.asarray(ch.frontier(step, cand, start)).astype(np.int64)
+        choices["frontier"].append(order)
         return order
 
     # context rows -> draft cache
@@ -547,10 +550,14 @@ def draft_tree(shape, W, l, m, h, ctx_tok, gap=GAP_FLAG, follow=None):
     n_pool = C
     for step in range(2, s.steps + 1):
         base = (step - 2) * C
-        a_par = a_prev[(np.arange(B)[:, None] * (a_prev.shape[0] // B) + fr_arow).reshape(-1)]
+        per_seq = a_prev.shape[0] // B
+        a_par = a_prev[(np.arange(B)[:, None] * per_seq + fr_arow).reshape(-1)]
         xs = draft_fuse(fr_tok.reshape(-1), W["embed"], W["w_fuse"], W["w_in"], a_prev=a_par)
         hs = rmsnorm(xs, eps=s.eps)
+        # the frontier of step s holds nodes of depth s - 1: position ctx + depth - 1
         ps = np.full(B * C, ctx + step - 2, np.int32)
+        rows.append(dict(step=step, tokens=fr_tok.copy(), parent_row=fr_arow.copy(), pos=ps.reshape(B, C).copy(),
+                         x=xs.reshape(B, C, k).copy()))
         q = rope(gemm(hs, wq).reshape(B * C, s.Hq, s.D), ps, s.theta)
         tk[:, base:base + C] = rope(gemm(hs, wk).reshape(B * C, s.Hkv, s.D), ps, s.theta).reshape(B, C, s.Hkv, s.D)
         tv[:, base:base + C] = gemm(hs, wv).reshape(B, C, s.Hkv, s.D)
@@ -569,9 +576,10 @@ def draft_tree(shape, W, l, m, h, ctx_tok, gap=GAP_FLAG, follow=None):
         pool_score.append(cand)
         pool_tok.append(ids.reshape(B, C * C))
         pool_par.append(np.repeat(fr_pool, C, axis=1))
-        creation = np.tile(np.arange(n_pool, n_pool + C * C, dtype=np.int32), (B, 1))
-        srt = np.take_along_axis(cand, select_topk(cand, creation, C + 1), 1)
-        ties.append(((srt[:, C - 1] - srt[:, C])[:, None], srt[:, C - 1:C]))
+        if own:
+            creation = np.tile(np.arange(n_pool, n_pool + C * C, dtype=np.int32), (B, 1))
+            srt = np.take_along_axis(cand, select_topk(cand, creation, C + 1), 1)
+            ties.append(((srt[:, C - 1] - srt[:, C])[:, None], srt[:, C - 1:C]))
         order = take(cand, step, n_pool)
         new_rows = [[list(fr_rows[b][o // C]) for o in order[b]] for b in range(B)]
         fr_arow = (order // C).astype(np.int64)                           # parent = frontier slot o // C
@@ -584,39 +592,31 @@ def draft_tree(shape, W, l, m, h, ctx_tok, gap=GAP_FLAG, follow=None):
     tok_all = np.concatenate(pool_tok, 1)
     par_all = np.concatenate(pool_par, 1)
     N = s.n_drafts
-    if follow is None:
-        parent, tokens, nb_ = tree_rerank(ps_all, tok_all, par_all, ctx_tok[:, -1], N, gap)
+    sel = np.sort(np.asarray(ch.final(ps_all, N)).astype(np.int64), axis=1)
+    choices["selected"] = sel
+    if own:
+        _, _, nb_ = tree_rerank(ps_all, tok_all, par_all, ctx_tok[:, -1], N, gap)
         near |= nb_
         # A near-tie (the k-th / (k+1)-th child of one node, or the last / first
         # candidate outside a frontier) may resolve the other way on another
         # machine. Scores never grow along a path, so it can change the final
         # tree only if the score at stake is within `gap` of the N-th pool score.
-        theta = select_topk(ps_all, np.tile(np.arange(ps_all.shape[1], dtype=np.int32), (B, 1)), N)
-        theta = np.take_along_axis(ps_all, theta[:, -1:], 1)
+        theta = np.take_along_axis(ps_all, sel, 1).min(axis=1, keepdims=True)
         for g, sc in ties:
             near |= ((g < gap) & (sc >= theta - gap)).any(axis=1)
-        own = select_topk(ps_all, np.tile(np.arange(ps_all.shape[1], dtype=np.int32), (B, 1)), N)
-        choices["selected"] = np.sort(own, axis=1)
-    else:
-        sel = np.sort(np.asarray(follow["selected"]).astype(np.int64), axis=1)
-        chosen = np.zeros(ps_all.shape, bool)
-        np.put_along_axis(chosen, sel, True, 1)
-        lo = np.where(chosen, ps_all, np.inf).min(axis=1)
-        hi = np.where(chosen, -np.inf, ps_all).max(axis=1)
-        margin["final"] = np.maximum(hi - lo, 0.0)
-        parent = np.full((B, N + 1), -1, np.int32)
-        tokens = np.zeros((B, N + 1), np.int32)
-        for b in range(B):
-            new = {int(c): i + 1 for i, c in enumerate(sel[b])}
-            tokens[b, 0] = ctx_tok[b, -1]
-            for c in sel[b]:
-                pp = int(par_all[b, c])
-                parent[b, new[int(c)]] = 0 if pp < 0 else new.get(pp, -2)   # -2: parent not in the tree
-                tokens[b, new[int(c)]] = tok_all[b, c]
+    parent = np.full((B, N + 1), -1, np.int32)
+    tokens = np.zeros((B, N + 1), np.int32)
+    for b in range(B):
+        new = {int(c): i + 1 for i, c in enumerate(sel[b])}
+        tokens[b, 0] = ctx_tok[b, -1]
+        for c in sel[b]:
+            pp = int(par_all[b, c])
+            parent[b, new[int(c)]] = 0 if pp < 0 else new.get(pp, -2)   # -2: parent not in the tree
+            tokens[b, new[int(c)]] = tok_all[b, c]
     return dict(parent=parent, tokens=tokens, flagged=near, pool_score=ps_all, pool_token=tok_all,
                 pool_parent=par_all, x_ctx=x.reshape(B, ctx, k), k_ctx=kr.reshape(B, ctx, s.Hkv, s.D),
                 v_ctx=vr.reshape(B, ctx, s.Hkv, s.D), a_root=a_root, a_steps=a_steps, lm_val=lm_vals,
-                margin=margin, choices=choices)
+                choices=choices, rows=rows, tree_k=tk, tree_v=tv)
 
 
 def tree_rerank(pool_score, pool_token, pool_parent, root_token, N, gap=GAP_FLAG):

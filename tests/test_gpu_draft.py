@@ -11,10 +11,12 @@ section 4.2 for top-k 10 / 60 drafts).
   storage at every layer boundary moves the logits by up to ~1e-2, while
   random weights leave neighbouring top logits only a few 1e-2 apart, so
   several trees are correct. The GPU's choices are replayed through the
-  oracle's arithmetic: context K/V, hidden states and logits along them meet
-  the bf16 tolerance; no choice falls below the best alternative by more than
-  3x the largest observed error; the tree equals the renumbered selection
-  exactly.
+  oracle's arithmetic (tests/draft_replay.py): context K/V, hidden states,
+  logits and pool scores along them meet the bf16 tolerance (normwise 2e-2);
+  no choice falls below the best alternative in the oracle's numbers by more
+  than twice that tolerance (2 x 2e-2 x the largest |logit| or |score|: a
+  selection that is best for some values within the tolerance of the
+  oracle's); the tree equals the renumbered selection exactly.
 """
 import numpy as np
 import pytest
@@ -22,6 +24,7 @@ import torch
 
 import synth
 from tests._gpu import dev, host, normwise_rel
+from tests.draft_replay import replay
 
 pytestmark = pytest.mark.gpu
 
@@ -139,11 +142,12 @@ def _gpu_draft(shape, W, l, m, h, tok):
     return head, rec
 
 
-def _check_choices(orc, s, W, l, m, h, tok, head, rec, seqs):
+def _check_choices(orc, s, W, l, m, h, tok, head, rec, seqs, tol=2e-2):
     """The GPU's choices, replayed through the oracle's arithmetic: every
-    number the GPU produced along them within tolerance, and no choice worse
-    than the best alternative by more than 3x the largest score / logit
-    error observed. The tree structure must then equal the renumbering of the
+    number the GPU produced along them within `tol` (normwise), and no choice
+    worse than the best alternative in the oracle's numbers by more than
+    2 x tol x the largest |logit| (children) or |pool score| (frontiers, the
+    final tree). The tree structure must then equal the renumbering of the
     GPU's selection exactly."""
     seqs = np.asarray(seqs)
     C, N = s.topk, s.n_drafts
@@ -153,25 +157,29 @@ def _check_choices(orc, s, W, l, m, h, tok, head, rec, seqs):
     follow = dict(ids=[r["ids"][seqs] for r in rec],
                   frontier=[r["next_pool"][seqs] - (r["pool_len"] if i else 0) for i, r in enumerate(rec)],
                   selected=selected)
-    f = orc.draft_tree(s, W, l, m, h, tok, follow=follow)
+    f = replay(orc, s, W, l, m, h, tok, follow)
     assert np.array_equal(host(head.parent)[seqs], f["parent"]), "tree structure differs"
     assert np.array_equal(host(head.tokens)[seqs], f["tokens"])
-    assert normwise_rel(host(head.a_root)[seqs], f["a_root"])[0] <= 2e-2
-    d_logit = 0.0
+    assert normwise_rel(host(head.a_root)[seqs], f["a_root"])[0] <= tol
+    d_logit, max_logit = 0.0, 0.0
     for i, r in enumerate(rec):
         ref = f["lm_val"][i]
         assert np.isfinite(ref).all(), f"step {i + 1}: a taken child is not among the oracle's top 16"
         rel, err = normwise_rel(r["val"][seqs], ref)
-        assert rel <= 2e-2, f"step {i + 1}: logits off by {rel}"
+        assert rel <= tol, f"step {i + 1}: logits off by {rel}"
         d_logit = max(d_logit, err)
+        max_logit = max(max_logit, float(np.abs(ref).max()))
         if i:
-            assert normwise_rel(r["a"].reshape(-1, C, s.k)[seqs], f["a_steps"][i - 1].reshape(-1, C, s.k))[0] <= 2e-2
-    d_score = float(np.abs(gscore.astype(np.float64) - f["pool_score"]).max())
+            assert normwise_rel(r["a"].reshape(-1, C, s.k)[seqs], f["a_steps"][i - 1].reshape(-1, C, s.k))[0] <= tol
+    rel_s, d_score = normwise_rel(gscore, f["pool_score"])
+    assert rel_s <= tol, f"pool scores off by {rel_s}"
+    max_score = float(np.abs(f["pool_score"]).max())
     mg = f["margin"]
-    assert (mg["lm"] <= 3 * d_logit).all(), (mg["lm"], d_logit)
-    assert (mg["frontier"] <= 3 * d_score).all(), (mg["frontier"], d_score)
-    assert (mg["final"] <= 3 * d_score).all(), (mg["final"], d_score)
-    return dict(d_logit=d_logit, d_score=d_score, n_off=int(sum((v > 0).sum() for v in mg.values())))
+    assert (mg["lm"] <= 2 * tol * max_logit).all(), (mg["lm"], max_logit)
+    assert (mg["frontier"] <= 2 * tol * max_score).all(), (mg["frontier"], max_score)
+    assert (mg["final"] <= 2 * tol * max_score).all(), (mg["final"], max_score)
+    return dict(d_logit=d_logit, d_score=d_score, max_margin={k: float(v.max()) for k, v in mg.items()},
+                n_off=int(sum((v > 0).sum() for v in mg.values())))
 
 
 def test_draft_head_small_f32_matches_oracle(orc):
@@ -190,8 +198,7 @@ def test_draft_head_small_f32_matches_oracle(orc):
             clean += 1
             assert _paths(par[b], tk[b]) == _paths(ref["parent"][b], ref["tokens"][b]), f"sequence {b}"
     assert clean >= s.B // 2
-    info = _check_choices(orc, s, W, l, m, h, tok, head, rec, range(s.B))
-    assert info["d_logit"] < 1e-4
+    info = _check_choices(orc, s, W, l, m, h, tok, head, rec, range(s.B), tol=1e-5)
     print(f"fp32: {clean}/{s.B} unflagged trees identical; {info}")
 
 

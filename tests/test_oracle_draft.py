@@ -2,20 +2,28 @@
 
 * The fusion FCs are plain matrix products over the concatenation (numpy fp64
   matmul on an explicit concatenation); W_in . [a; e] = W_a . a + W_e . e.
-* Step-mode pairing ([news] steps 2-3): a frontier node's draft input uses its
-  parent's draft output with the embedding of its own token.
+* Step-mode pairing and positions ([news] draft stage, steps 2-3): the input
+  row of every frontier node is rebuilt by hand from the explicit
+  concatenation [output of its tree parent; embedding of its own token], with
+  the parent found through the candidate pool's own parent links, and its
+  key row by a hand-written RMSNorm, projection and complex-rotation RoPE at
+  position context + depth - 1.
 * Tree selection: the rerank equals a brute-force full sort of the pool
   (numpy lexsort); closure under parents; a peaked draft degenerates to a chain
   of full depth; the drafted tree has n_drafts nodes, parents before children,
   at most top-k children per node and depth at most the number of steps.
-* Follow mode (used to check another run's choices): following its own
-  choices reproduces its own tree with zero margins; swapping one taken child
-  for the next one down costs exactly that logit gap.
+* Replay of recorded choices (tests/draft_replay.py, used to check another
+  run's choices): replaying its own choices reproduces its own tree with zero
+  margins; swapping one taken child for the next one down costs exactly that
+  logit gap.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 
 import synth
+from tests.draft_replay import replay
 
 
 def f64(a):
@@ -93,7 +101,7 @@ def test_peaked_draft_is_a_full_depth_chain(orc):
     assert len(zero) == steps and set(Tk[0, zero]).issubset(set(tokens[0]))
 
 
-def test_draft_tree_invariants_and_step_pairing(orc):
+def test_draft_tree_invariants(orc):
     s = synth.DRAFT_SMALL
     W = synth.draft_weights(s)
     l, m, h, tok = synth.draft_inputs(s, 0)
@@ -118,12 +126,75 @@ def test_draft_tree_invariants_and_step_pairing(orc):
     assert np.array_equal(r1["parent"][0], r["parent"][3]) and np.array_equal(r1["tokens"][0], r["tokens"][3])
 
 
-def test_follow_mode_margins(orc):
+def _bf16(x):
+    return synth.f32_to_bf16(np.asarray(x, np.float64).astype(np.float32))
+
+
+def _hand_rope(x, pos, theta):
+    """Rotate-half RoPE written as a complex rotation of the pairs
+    (j, j + D/2) by pos * theta^(-2j/D), in fp64."""
+    D = x.shape[-1]
+    j = np.arange(D // 2)
+    ang = pos * theta ** (-2.0 * j / D)
+    z = (x[..., :D // 2] + 1j * x[..., D // 2:]) * np.exp(1j * ang)
+    return np.concatenate([z.real, z.imag], -1)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_draft_step_rows_pair_parent_output_with_own_token(orc, seed):
+    """Every frontier node's input row is W_in [a_parent; E[token]] with the
+    parent taken from the pool's parent links (step 2: the root, whose output
+    is a_root), and its key row sits at position ctx + depth - 1 (depth =
+    step - 1). Two sequences, three growth steps, rebuilt by hand."""
+    s = dataclasses.replace(synth.DRAFT_SMALL, B=2, steps=3, n_drafts=30)
+    W = synth.draft_weights(s)
+    l, m, h, tok = synth.draft_inputs(s, seed)
+    l, m, h, tok = l[:2], m[:2], h[:2], tok[:2]
+    r = orc.draft_tree(s, W, l, m, h, tok)
+    C, k, qd, kvd = s.topk, s.k, s.Hq * s.D, s.Hkv * s.D
+    E, Wi = f64(W["embed"]), f64(W["w_in"])
+    Wk = f64(W["wqkv"])[qd:qd + kvd]
+    starts = [0] + [C + (st - 2) * C * C for st in range(2, s.steps + 1)]     # pool offset of each step
+    # frontier pool indices per step, from the recorded choices
+    fr_pool = [starts[st - 1] + np.asarray(r["choices"]["frontier"][st - 1]) for st in range(1, s.steps)]
+    assert len(r["rows"]) == s.steps - 1
+    n_checked = 0
+    for rr in r["rows"]:
+        st = rr["step"]
+        assert (rr["pos"] == s.ctx + (st - 1) - 1).all()            # depth st - 1 -> ctx + depth - 1
+        for b in range(s.B):
+            for i in range(C):
+                node = fr_pool[st - 2][b, i]                         # this frontier node's pool index
+                assert rr["tokens"][b, i] == r["pool_token"][b, node]
+                par = r["pool_parent"][b, node]
+                if st == 2:
+                    assert par == -1
+                    a_par = f64(r["a_root"][b])
+                else:
+                    slot = np.flatnonzero(fr_pool[st - 3][b] == par)
+                    assert len(slot) == 1                            # the parent is in the previous frontier
+                    a_par = f64(r["a_steps"][st - 3][b * C + slot[0]])
+                x_hand = np.concatenate([a_par, E[r["pool_token"][b, node]]]) @ Wi.T
+                got = f64(rr["x"][b, i])
+                ulp = 2.0 ** -7 * np.abs(x_hand)
+                assert np.all(np.abs(got - x_hand) <= ulp + 1e-30), (st, b, i)
+                # key row: RMSNorm -> K projection -> RoPE at ctx + depth - 1
+                xr = f64(rr["x"][b, i])
+                hn = f64(_bf16(xr / np.sqrt(np.mean(xr * xr) + s.eps)))
+                kl = f64(_bf16(hn @ Wk.T)).reshape(s.Hkv, s.D)
+                k_hand = _hand_rope(kl, s.ctx + st - 2, s.theta)
+                kg = f64(r["tree_k"][b, (st - 2) * C + i])
+                assert np.all(np.abs(kg - k_hand) <= 2.0 ** -7 * np.abs(k_hand) + 1e-6), (st, b, i)
+                n_checked += 1
+    assert n_checked == (s.steps - 1) * s.B * C
+
+
+def test_replay_margins(orc):
     s = synth.DRAFT_SMALL
     W = synth.draft_weights(s)
     l, m, h, tok = synth.draft_inputs(s, 1)
     r = orc.draft_tree(s, W, l, m, h, tok)
-    f = orc.draft_tree(s, W, l, m, h, tok, follow=r["choices"])
+    f = replay(orc, s, W, l, m, h, tok, r["choices"])
     assert np.array_equal(f["parent"], r["parent"]) and np.array_equal(f["tokens"], r["tokens"])
     assert np.array_equal(f["pool_score"], r["pool_score"])
     assert all((v == 0).all() for v in f["margin"].values())
@@ -131,7 +202,7 @@ def test_follow_mode_margins(orc):
     idx, val, _, _ = orc.lmhead(orc.rmsnorm(r["a_steps"][-1][:1], eps=s.eps), W["lm_head"], topk=s.topk + 1)
     ids = [a.copy() for a in r["choices"]["ids"]]
     ids[-1][0, 0, s.topk - 1] = idx[0, s.topk]
-    g = orc.draft_tree(s, W, l, m, h, tok, follow=dict(r["choices"], ids=ids))
+    g = replay(orc, s, W, l, m, h, tok, dict(r["choices"], ids=ids))
     assert g["margin"]["lm"][0] == val[0, s.topk - 1] - val[0, s.topk] > 0
     assert (g["margin"]["lm"][1:] == 0).all()
     # a final selection that drops the best entry for a worse one
@@ -141,7 +212,7 @@ def test_follow_mode_margins(orc):
     out = int(np.flatnonzero(~np.isin(np.arange(len(ps)), sel[2]))[0])
     sel[2][sel[2] == best] = out
     sel[2].sort()
-    h2 = orc.draft_tree(s, W, l, m, h, tok, follow=dict(r["choices"], selected=sel))
+    h2 = replay(orc, s, W, l, m, h, tok, dict(r["choices"], selected=sel))
     assert h2["margin"]["final"][2] >= ps[best] - ps[out] > 0 and h2["margin"]["final"][0] == 0
 
 
@@ -157,15 +228,15 @@ def test_bf16_draft_logits_move_with_last_bit_noise(orc):
     r = orc.draft_tree(s, W, l, m, h, tok)
     noisy = l.copy()
     noisy[np.random.default_rng(5).random(l.shape) < 0.01] ^= np.uint16(1)
-    f = orc.draft_tree(s, W, noisy, m, h, tok, follow=r["choices"])
-    moved = max(np.abs(a - b).max() for a, b in zip(f["lm_val"], orc.draft_tree(s, W, l, m, h, tok,
-                                                                                  follow=r["choices"])["lm_val"]))
+    f = replay(orc, s, W, noisy, m, h, tok, r["choices"])
+    moved = max(np.abs(a - b).max() for a, b in zip(f["lm_val"], replay(orc, s, W, l, m, h, tok,
+                                                                         r["choices"])["lm_val"]))
     assert moved > 0.03
     cv = lambda a: synth.bf16_to_f32(a)  # noqa: E731
     W32 = {k: cv(v) for k, v in W.items()}
     r32 = orc.draft_tree(s, W32, cv(l), cv(m), cv(h), tok)
     n32 = cv(l).copy()
     n32.view(np.uint32)[np.random.default_rng(5).random(l.shape) < 0.01] ^= np.uint32(1)
-    f32 = orc.draft_tree(s, W32, n32, cv(m), cv(h), tok, follow=r32["choices"])
-    g32 = orc.draft_tree(s, W32, cv(l), cv(m), cv(h), tok, follow=r32["choices"])
+    f32 = replay(orc, s, W32, n32, cv(m), cv(h), tok, r32["choices"])
+    g32 = replay(orc, s, W32, cv(l), cv(m), cv(h), tok, r32["choices"])
     assert max(np.abs(a - b).max() for a, b in zip(f32["lm_val"], g32["lm_val"])) < 1e-4
