@@ -239,6 +239,44 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void lmhead_bf16_kernel(const uint
 constexpr int BIG_BN = e3g::GBN;  // vocabulary rows per tile, many-row path
 constexpr int big_bm(int KK) { return KK >= 8 ? 128 : 256; }
 
+// Top-2 of one row over the 128 vocabulary columns a wave holds in the
+// transposed accumulator layout (lane lr: the row; lane half lh: every other
+// group of 4 columns). The scan runs in increasing column order, so the strict
+// comparison keeps the lowest column among equal values; NaN and -inf never
+// enter the list. The two lane halves then merge by (value desc, column asc).
+constexpr int NO_COL = 0x7fffffff;
+__device__ __forceinline__ bool e3_before(float a, int ia, float b, int ib) { return a > b || (a == b && ia < ib); }
+
+template <int NB>
+__device__ __forceinline__ void top2_row(const f32x16_t (&blk)[NB], int lh, int nvalid, float &b0, int &i0, float &b1,
+                                         int &i1) {
+    b0 = -INFINITY; b1 = -INFINITY; i0 = NO_COL; i1 = NO_COL;
+    const bool full = nvalid >= NB * 32;  // uniform
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int col = 32 * nb + 8 * (r >> 2) + 4 * lh + (r & 3);
+            float v = blk[nb][r];
+            if (!full && col >= nvalid) v = -INFINITY;
+            const bool g0 = v > b0, g1 = v > b1;
+            b1 = g0 ? b0 : (g1 ? v : b1);
+            i1 = g0 ? i0 : (g1 ? col : i1);
+            b0 = g0 ? v : b0;
+            i0 = g0 ? col : i0;
+        }
+    const float ob0 = __shfl_xor(b0, 32), ob1 = __shfl_xor(b1, 32);
+    const int oi0 = __shfl_xor(i0, 32), oi1 = __shfl_xor(i1, 32);
+    if (e3_before(ob0, oi0, b0, i0)) {
+        const bool keep = e3_before(b0, i0, ob1, oi1);
+        b1 = keep ? b0 : ob1; i1 = keep ? i0 : oi1;
+        b0 = ob0; i0 = oi0;
+    } else {
+        const bool take = e3_before(ob0, oi0, b1, i1);
+        b1 = take ? ob0 : b1; i1 = take ? oi0 : i1;
+    }
+}
+
 template <int BM, int KK, bool LSE>
 __global__ __launch_bounds__(256, BM == 128 ? 2 : 1) void lmhead_big_kernel(e3g::GemmParams gp, int nrec,
                                                                              Partials p) {
@@ -255,14 +293,39 @@ __global__ __launch_bounds__(256, BM == 128 ? 2 : 1) void lmhead_big_kernel(e3g:
     // XCD runs together share 8 hidden and 4 vocabulary tiles in its L2
     // (hidden tiles fastest over all of them left each hidden tile shared by
     // 2: 13.4 GB of L2 misses per 3904-row launch against 8.1 GB here)
+    // (4 hidden tiles per group: measured 3.75 -> 3.47 ms together with the
+    // loop's issue priority on the 3904-row shape, against groups of 8)
     int mt, nt;
-    e3g::tile_of(blockIdx.x, gridDim.x, gp.mt, gp.nt, mt, nt);
+    e3g::tile_of<4>(blockIdx.x, gridDim.x, gp.mt, gp.nt, mt, nt);
     const int m0 = mt * BM, n0 = nt * BIG_BN;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int lr = lane & 31, lh = lane >> 5, wm = wave >> 1, wn = wave & 1;
     e3g::fill_arow<BM>(gp, m0, arow);
     f32x16_t acc[T::MB][T::NB];
-    e3g::mainloop<BM, T::NS>(gp, m0, n0, 0, gp.K / e3g::GBK, ring, arow, acc);
+    // Top-2 lists without a log-sum-exp (the verify step's argmax and gap):
+    // the transposed tile puts one hidden row in each lane, so the selection
+    // runs on the accumulators directly, with no LDS staging.
+    constexpr bool REG_TOP2 = KK == 2 && !LSE && BM == 256;
+    e3g::mainloop<BM, T::NS, REG_TOP2>(gp, m0, n0, 0, gp.K / e3g::GBK, ring, arow, acc);
+    if constexpr (REG_TOP2) {
+        const int vbase = n0 + wn * 128;
+        const int nvalid = gp.N - vbase;
+        const int rec_tile = 2 * nt + wn;
+#pragma unroll
+        for (int mb = 0; mb < T::MB; ++mb) {
+            float b0, b1;
+            int i0, i1;
+            top2_row<T::NB>(acc[mb], lh, nvalid, b0, i0, b1, i1);
+            const int m = m0 + wm * (BM / 2) + 32 * mb + lr;
+            if (lh == 0 && m < gp.M) {
+                uint64_t L[KK];
+                L[0] = i0 == NO_COL ? 0 : e3_key(b0, vbase + i0);
+                L[1] = i1 == NO_COL ? 0 : e3_key(b1, vbase + i1);
+                store_record<KK>(p, (size_t)m * nrec + rec_tile, L);
+            }
+        }
+        return;
+    }
     __syncthreads();  // every wave is done with the ring
     // Each wave selects over its own (BM/2) x 128 block, RP hidden rows at a
     // time, staged in a private slice of the ring (columns rotated by 4 per
