@@ -115,6 +115,13 @@ int eagle3_tree_mask(const int32_t *parent, int B, int T, int W,
  * not depend on the call's batch composition.
  * norm_out (nullable): the RMSNorm (gamma = 1, eps = norm_eps) of each output
  * row [Hq * D], as eagle3_rmsnorm on out would give (a second launch).
+ * Validate mode: with status [B] int32 non-NULL, each sequence's status is
+ * written before the attention runs: EAGLE3_ERR_RANGE when prefix_len[b] lies
+ * outside [0, max_blocks * block_size] or a block id the prefix uses
+ * (block_table[b][j], j < ceil(prefix_len[b] / block_size)) lies outside
+ * [0, num_blocks); else EAGLE3_ERR_TREE when parent[] is given and is not a
+ * tree in topological order; else EAGLE3_OK. Without it, bad ids are clamped
+ * (wrong values, never an out-of-bounds access).
  */
 typedef struct eagle3_tree_attn_args {
     int dtype;
@@ -136,6 +143,7 @@ typedef struct eagle3_tree_attn_args {
     int split_keys;
     void *norm_out;  /* nullable: [B, Tq, Hq * D], RMSNorm (gamma = 1, norm_eps) of each output row */
     float norm_eps;
+    int32_t *status; /* nullable: [B] validate mode (see above) */
 } eagle3_tree_attn_args;
 
 size_t eagle3_tree_attn_workspace(const eagle3_tree_attn_args *a);
@@ -184,10 +192,17 @@ int eagle3_lmhead_argmax(const void *hidden, const void *w, int M, int N, int K,
  *              target_idx[end] (the target's own token); -1 after
  * Inputs: tokens, target_idx [B, T] int32; exactly one of parent [B, T] or
  * mask [B, T, W] (from eagle3_tree_mask) non-NULL. T <= 64 * W, W in {1, 2}.
+ * Validate mode: with status [B] int32 non-NULL, each sequence's status is
+ * written: EAGLE3_ERR_TREE when a given parent[] is not a tree in topological
+ * order (parent[0] != -1 or parent[n] outside [0, n)), else EAGLE3_ERR_RANGE
+ * when a token or target id lies outside [0, V), else EAGLE3_OK. V >= 1 is
+ * required with status (EAGLE3_ERR_ARG otherwise) and ignored without it. The
+ * outputs are written either way; for a flagged sequence they are unspecified.
  */
 int eagle3_accept_path(const int32_t *tokens, const int32_t *parent, const uint64_t *mask, int W,
                        const int32_t *target_idx, int B, int T,
-                       int32_t *accept_len, int32_t *path, int32_t *out_tokens, void *stream);
+                       int32_t *accept_len, int32_t *path, int32_t *out_tokens,
+                       int V, int32_t *status, void *stream);
 
 
 /*

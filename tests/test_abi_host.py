@@ -47,7 +47,7 @@ def test_status_strings(lib):
     for code in (0, -1, -2, -3, -4, -5, -6):
         s = lib.eagle3_status_string(code).decode()
         assert s.startswith("EAGLE3_")
-    assert lib.eagle3_abi_version() == 2
+    assert lib.eagle3_abi_version() == 3
 
 
 FAKE = 0x10000          # 16-byte aligned, never dereferenced on the host
@@ -65,12 +65,19 @@ def test_tree_mask_errors(lib):
     assert f(None, 0, 10, 1, None, None, None, None) == 0          # empty batch is a no-op
 
 
+ACCEPT_ARGTYPES = ([ctypes.c_void_p] * 3 + [ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int]
+                   + [ctypes.c_void_p] * 3 + [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p])
+
+
 def test_accept_errors(lib):
     f = lib.eagle3_accept_path
-    f.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int] + [ctypes.c_void_p] * 4
-    assert f(FAKE, FAKE, FAKE, 1, FAKE, 2, 8, FAKE, FAKE, FAKE, None) == -1   # both parent and mask
-    assert f(FAKE, None, None, 1, FAKE, 2, 8, FAKE, FAKE, FAKE, None) == -1   # neither
-    assert f(FAKE, FAKE, None, 1, FAKE, 2, 70, FAKE, FAKE, FAKE, None) == -2  # T > 64 W
+    f.argtypes = ACCEPT_ARGTYPES
+    assert f(FAKE, FAKE, FAKE, 1, FAKE, 2, 8, FAKE, FAKE, FAKE, 0, None, None) == -1   # both parent and mask
+    assert f(FAKE, None, None, 1, FAKE, 2, 8, FAKE, FAKE, FAKE, 0, None, None) == -1   # neither
+    assert f(FAKE, FAKE, None, 1, FAKE, 2, 70, FAKE, FAKE, FAKE, 0, None, None) == -2  # T > 64 W
+    # validate mode needs the vocabulary size
+    assert f(FAKE, FAKE, None, 1, FAKE, 2, 8, FAKE, FAKE, FAKE, 0, FAKE, None) == -1
+    assert f(FAKE, FAKE, None, 1, FAKE, 0, 8, FAKE, FAKE, FAKE, 0, FAKE, None) == -1
 
 
 def test_rmsnorm_errors(lib):
@@ -135,8 +142,8 @@ def test_empty_batches_are_no_ops(lib):
     f.argtypes = [ctypes.c_void_p, ctypes.c_void_p] + [ctypes.c_int] * 5 + [ctypes.c_void_p] * 5 + [ctypes.c_size_t, ctypes.c_void_p]
     assert f(None, None, 0, 128256, 4096, 1, 1, None, None, None, None, None, 0, None) == 0
     f = lib.eagle3_accept_path
-    f.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int] + [ctypes.c_void_p] * 4
-    assert f(None, None, None, 1, None, 0, 61, None, None, None, None) == 0
+    f.argtypes = ACCEPT_ARGTYPES
+    assert f(None, None, None, 1, None, 0, 61, None, None, None, 0, None, None) == 0
     f = lib.eagle3_rmsnorm
     f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_int,
                   ctypes.c_void_p, ctypes.c_void_p]

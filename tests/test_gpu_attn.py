@@ -251,3 +251,42 @@ def test_norm_out(orc, lib, B, Hq, Hkv, plen, split, dtype):
     x, y = as_f64(got_n), as_f64(own_n)
     ulp = 2.0 ** -7 if dtype == "bf16" else 2.0 ** -22
     assert np.all(np.abs(x - y) <= ulp * np.maximum(np.abs(y), 1e-30) + 1e-30), np.abs(x - y).max()
+
+
+def test_validate_mode_flags_bad_block_ids_and_lengths(orc, lib):
+    """Validate mode (status non-NULL): a block id outside the pool in the
+    part of the table a prefix uses, or a prefix longer than the table, gives
+    EAGLE3_ERR_RANGE for that sequence only; a bad id past the prefix's blocks
+    is never read and is not flagged. The clean sequences' outputs still meet
+    the parity tolerance (the kernels clamp the bad ids, so no access leaves
+    the buffers)."""
+    B, T, Hq, Hkv = 4, 61, 8, 2
+    parent, inp = make(170, B, T, Hq, Hkv, [300, 100, 64, 50])
+    mask, _ = orc.tree_mask(parent, 1)
+    ref, _ = orc.tree_attn(inp.q, inp.k_tree, inp.v_tree, inp.kv, mask)
+    bt = inp.kv.block_table.copy()
+    nb = inp.kv.k_cache.shape[0]
+    bt[1, 3] = nb                        # used by the 100-key prefix (blocks 0..6)
+    bt[3, 5] = nb + 7                    # past the 50-key prefix's 4 blocks: never read
+    plen = inp.kv.prefix_len.copy()
+    plen[2] = bt.shape[1] * 16 + 1       # longer than the table can address
+    q, kt, vt = dev(inp.q), dev(inp.k_tree), dev(inp.v_tree)
+    kc, vc, dbt, dpl, mk = dev(inp.kv.k_cache), dev(inp.kv.v_cache), dev(bt), dev(plen), dev(mask)
+    out = torch.empty_like(q)
+    status = torch.full((B,), 99, dtype=torch.int32, device="cuda")
+    args = lib.tree_attn_args(q, kt, vt, kc, vc, dbt, dpl, out, mask=mk, status=status)
+    lib.eagle3_tree_attn(args, None)
+    torch.cuda.synchronize()
+    assert list(host(status)) == [0, -4, -4, 0]
+    got = host(out)
+    for b in (0, 3):
+        assert normwise_rel(got[b], ref[b])[0] <= 2e-2
+    # parent[] mode also checks the tree order
+    bad_parent = parent.copy()
+    bad_parent[0, 10] = 20
+    status.fill_(99)
+    args = lib.tree_attn_args(q, kt, vt, kc, vc, dev(inp.kv.block_table), dev(inp.kv.prefix_len), out,
+                              parent=dev(bad_parent), status=status)
+    lib.eagle3_tree_attn(args, None)
+    torch.cuda.synchronize()
+    assert list(host(status)) == [-3, 0, 0, 0]

@@ -104,3 +104,35 @@ def test_accept_lesson_cases(orc, lib):
     al, path, out = run_accept(lib, tok.astype(np.int32), parent, idx, False, orc)
     assert list(al) == [4, 1, 0]
     assert [int((o >= 0).sum()) for o in out] == [5, 2, 1]
+
+
+def test_accept_validate_mode_flags_bad_ids(orc, lib):
+    """Validate mode (status non-NULL): one bad id planted per sequence. A
+    token outside [0, V) and a target id below 0 give EAGLE3_ERR_RANGE, a
+    parent[] out of topological order EAGLE3_ERR_TREE; clean sequences get
+    EAGLE3_OK and their outputs still equal the oracle's."""
+    rng = np.random.default_rng(5)
+    B, T, V = 5, 61, 3001
+    parent = np.stack([synth.random_tree(rng, T, max_children=10) for _ in range(B)])
+    idx = rng.integers(0, V, size=(B, T)).astype(np.int32)
+    tok = synth.plant_tokens(parent, idx, np.full(B, 0.9), rng.random((B, T)), rng.integers(0, V, size=(B, T)))
+    tok = tok.astype(np.int32)
+    want = orc.accept(tok, parent, idx)
+    tok[1, 17] = V                       # token past the vocabulary
+    idx[2, 40] = -1                      # negative target id
+    parent[3, 30] = 45                   # a parent after its child
+    al = torch.empty((B,), dtype=torch.int32, device="cuda")
+    path = torch.empty((B, T), dtype=torch.int32, device="cuda")
+    out = torch.empty((B, T), dtype=torch.int32, device="cuda")
+    status = torch.full((B,), 99, dtype=torch.int32, device="cuda")
+    lib.eagle3_accept_path(dev(tok), dev(idx), al, path, out, parent=dev(parent), V=V, status=status)
+    torch.cuda.synchronize()
+    assert list(host(status)) == [0, -4, -4, -3, 0]
+    for b in (0, 4):
+        assert host(al)[b] == want[0][b] and np.array_equal(host(path)[b], want[1][b])
+    # the same call in mask mode: the range checks still apply, the tree check needs parent[]
+    m, _ = orc.tree_mask(np.where(np.arange(B)[:, None] == 3, np.stack([synth.chain_tree(T - 1)] * B), parent), 1)
+    status.fill_(99)
+    lib.eagle3_accept_path(dev(tok), dev(idx), al, path, out, mask=dev(m), V=V, status=status)
+    torch.cuda.synchronize()
+    assert list(host(status)) == [0, -4, -4, 0, 0]

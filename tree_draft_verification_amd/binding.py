@@ -36,6 +36,7 @@ class TreeAttnArgs(ctypes.Structure):
         ("mask", P), ("parent", P), ("out", P), ("lse", P),
         ("split_keys", I),
         ("norm_out", P), ("norm_eps", F),
+        ("status", P),
     ]
 
 
@@ -62,7 +63,7 @@ _tree_attn = _sig("eagle3_tree_attn", I, ctypes.POINTER(TreeAttnArgs), P, SZ, P)
 _rmsnorm = _sig("eagle3_rmsnorm", I, P, P, I, I, F, I, P, P)
 _lmhead_ws = _sig("eagle3_lmhead_workspace", SZ, I, I, I, I, I)
 _lmhead = _sig("eagle3_lmhead_argmax", I, P, P, I, I, I, I, I, P, P, P, P, P, SZ, P)
-_accept = _sig("eagle3_accept_path", I, P, P, P, I, P, I, I, P, P, P, P)
+_accept = _sig("eagle3_accept_path", I, P, P, P, I, P, I, I, P, P, P, I, P, P)
 _gemm = _sig("eagle3_gemm", I, ctypes.POINTER(GemmArgs), P)
 _gemm_ws = _sig("eagle3_gemm_workspace", SZ, ctypes.POINTER(GemmArgs))
 _silu_mul = _sig("eagle3_silu_mul", I, P, I, I, I, P, P)
@@ -126,7 +127,7 @@ def eagle3_tree_mask(parent, W, mask, depth=None, status=None, stream=None):
 
 
 def tree_attn_args(q, k_tree, v_tree, k_cache, v_cache, block_table, prefix_len, out, mask=None, parent=None,
-                   lse=None, scale=None, split_keys=0, norm_out=None, norm_eps=1e-5) -> TreeAttnArgs:
+                   lse=None, scale=None, split_keys=0, norm_out=None, norm_eps=1e-5, status=None) -> TreeAttnArgs:
     B, Tq, Hq, D = q.shape
     Tk, Hkv = k_tree.shape[1], k_tree.shape[2]
     W = mask.shape[-1] if mask is not None else (Tq + 63) // 64
@@ -141,6 +142,7 @@ def tree_attn_args(q, k_tree, v_tree, k_cache, v_cache, block_table, prefix_len,
     a.mask, a.parent, a.out, a.lse = _ptr(mask), _ptr(parent), _ptr(out), _ptr(lse)
     a.split_keys = int(split_keys)
     a.norm_out, a.norm_eps = _ptr(norm_out), float(norm_eps)
+    a.status = _ptr(status)
     return a
 
 
@@ -173,11 +175,12 @@ def eagle3_lmhead_argmax(hidden, w, topk, idx, val=None, gap=None, lse=None, ws=
                    _ptr(ws), ws_bytes, _stream(stream)), "eagle3_lmhead_argmax")
 
 
-def eagle3_accept_path(tokens, target_idx, accept_len, path, out_tokens, parent=None, mask=None, stream=None):
+def eagle3_accept_path(tokens, target_idx, accept_len, path, out_tokens, parent=None, mask=None, V=0, status=None,
+                       stream=None):
     B, T = tokens.shape
     W = mask.shape[-1] if mask is not None else (T + 63) // 64
     _check(_accept(_ptr(tokens), _ptr(parent), _ptr(mask), W, _ptr(target_idx), B, T, _ptr(accept_len), _ptr(path),
-                   _ptr(out_tokens), _stream(stream)), "eagle3_accept_path")
+                   _ptr(out_tokens), int(V), _ptr(status), _stream(stream)), "eagle3_accept_path")
 
 
 def _gemm_args(a, b, c, residual, a_rows, ldc, M, ws):

@@ -14,4 +14,4 @@ extern "C" const char *eagle3_status_string(int status) {
     }
 }
 
-extern "C" int eagle3_abi_version(void) { return 2; }
+extern "C" int eagle3_abi_version(void) { return 3; }

@@ -67,18 +67,30 @@ __global__ __launch_bounds__(64) void accept_kernel(const int32_t *__restrict__ 
                                                     const uint64_t *__restrict__ mask,
                                                     const int32_t *__restrict__ target, int T,
                                                     int32_t *__restrict__ accept_len, int32_t *__restrict__ path,
-                                                    int32_t *__restrict__ out_tokens) {
+                                                    int32_t *__restrict__ out_tokens, int V,
+                                                    int32_t *__restrict__ status) {
     __shared__ int32_t par[kMaxT];
     __shared__ int32_t tgt[kMaxT];
     __shared__ int32_t tok[kMaxT];
     __shared__ int32_t slot[kMaxT];
     const int b = blockIdx.x, lane = threadIdx.x;
     const size_t row = (size_t)b * T;
+    bool range_bad = false, tree_bad = false;
     for (int n = lane; n < T; n += 64) {
         tgt[n] = target[row + n];
         tok[n] = tokens[row + n];
         if (parent) par[n] = parent[row + n];
         slot[n] = -1;
+        if (status) {
+            // validate mode: every token and target id a vocabulary id; a
+            // parent[] given in topological order with the root first
+            range_bad |= tok[n] < 0 || tok[n] >= V || tgt[n] < 0 || tgt[n] >= V;
+            if (parent) tree_bad |= n == 0 ? par[n] != -1 : (par[n] < 0 || par[n] >= n);
+        }
+    }
+    if (status) {
+        const bool rb = __ballot(range_bad) != 0, tb = __ballot(tree_bad) != 0;
+        if (lane == 0) status[b] = tb ? EAGLE3_ERR_TREE : rb ? EAGLE3_ERR_RANGE : EAGLE3_OK;
     }
     __syncthreads();
 
@@ -205,18 +217,19 @@ extern "C" int eagle3_tree_mask(const int32_t *parent, int B, int T, int W, uint
 
 extern "C" int eagle3_accept_path(const int32_t *tokens, const int32_t *parent, const uint64_t *mask, int W,
                                   const int32_t *target_idx, int B, int T, int32_t *accept_len, int32_t *path,
-                                  int32_t *out_tokens, void *stream) {
+                                  int32_t *out_tokens, int V, int32_t *status, void *stream) {
     if (B < 0 || T < 1) return EAGLE3_ERR_ARG;
     if (W < 1 || W > 2 || T > 64 * W) return EAGLE3_ERR_UNSUPPORTED;
+    if (status && V < 1) return EAGLE3_ERR_ARG;
     if (B == 0) return EAGLE3_OK;
     if (!tokens || !target_idx || !accept_len || !path || !out_tokens) return EAGLE3_ERR_ARG;
     if ((parent == nullptr) == (mask == nullptr)) return EAGLE3_ERR_ARG;
     if (W == 1)
         accept_kernel<1><<<B, 64, 0, e3_stream(stream)>>>(tokens, parent, mask, target_idx, T, accept_len, path,
-                                                         out_tokens);
+                                                         out_tokens, V, status);
     else
         accept_kernel<2><<<B, 64, 0, e3_stream(stream)>>>(tokens, parent, mask, target_idx, T, accept_len, path,
-                                                         out_tokens);
+                                                         out_tokens, V, status);
     E3_LAUNCH_CHECK();
     return EAGLE3_OK;
 }

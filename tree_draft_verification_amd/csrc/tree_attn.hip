@@ -805,6 +805,31 @@ __global__ __launch_bounds__(64) void tree_attn_f32_kernel(AttnF32 p) {
     if (p.lse && lane == 0) p.lse[((size_t)b * p.Tq + t) * p.Hq + hq] = l_run > 0.f ? m_run + logf(l_run) : -INFINITY;
 }
 
+// Validate mode: one wave per sequence checks the prefix length, the block
+// ids the prefix uses and (parent[] mode) the tree order; writes status[b].
+__global__ __launch_bounds__(64) void tree_attn_validate_kernel(const int32_t *__restrict__ block_table,
+                                                                const int32_t *__restrict__ prefix_len,
+                                                                const int32_t *__restrict__ parent, int Tq,
+                                                                int max_blocks, int block_size, int num_blocks,
+                                                                int32_t *__restrict__ status) {
+    const int b = blockIdx.x, lane = threadIdx.x;
+    const int L = prefix_len[b];
+    bool range_bad = L < 0 || (long)L > (long)max_blocks * block_size;
+    const int nb = range_bad ? 0 : (L + block_size - 1) / block_size;
+    for (int j = lane; j < nb; j += 64) {
+        const int id = block_table[(size_t)b * max_blocks + j];
+        range_bad |= id < 0 || id >= num_blocks;
+    }
+    bool tree_bad = false;
+    if (parent)
+        for (int n = lane; n < Tq; n += 64) {
+            const int pn = parent[(size_t)b * Tq + n];
+            tree_bad |= n == 0 ? pn != -1 : (pn < 0 || pn >= n);
+        }
+    const bool rb = __ballot(range_bad) != 0, tb = __ballot(tree_bad) != 0;
+    if (lane == 0) status[b] = rb ? EAGLE3_ERR_RANGE : tb ? EAGLE3_ERR_TREE : EAGLE3_OK;
+}
+
 // ---------------------------------------------------------------- host side
 
 struct Plan {
@@ -877,6 +902,10 @@ extern "C" int eagle3_tree_attn(const eagle3_tree_attn_args *a, void *ws, size_t
     if (pl.ws_bytes > 0 && !e3_aligned16(ws)) return EAGLE3_ERR_ARG;
     const hipStream_t st = e3_stream(stream);
     const int G = a->Hq / a->Hkv;
+    if (a->status)
+        tree_attn_validate_kernel<<<a->B, 64, 0, st>>>(a->block_table, a->prefix_len, a->mask ? nullptr : a->parent,
+                                                        a->Tq, a->max_blocks, a->block_size, a->num_blocks,
+                                                        a->status);
     if (a->dtype == EAGLE3_BF16) {
         AttnParams p;
         p.q = (const uint16_t *)a->q; p.k_tree = (const uint16_t *)a->k_tree; p.v_tree = (const uint16_t *)a->v_tree;
