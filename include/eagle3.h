@@ -181,6 +181,24 @@ int eagle3_lmhead_argmax(const void *hidden, const void *w, int M, int N, int K,
                          void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * eagle3_lmhead_argmax for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid it):
+ * same arguments and results, no workspace argument. The per-tile records go
+ * to a device array inside the library, EAGLE3_LMHEAD_NOALLOC_MAX_BYTES long,
+ * one copy per GPU, held until the process ends. A call whose records need
+ * more (eagle3_lmhead_workspace() of the same arguments) returns
+ * EAGLE3_ERR_WORKSPACE before any launch; the limit covers a 64-sequence
+ * verify batch of 61-node trees over a 128256-row head (3904 rows, top-2) and
+ * the draft head's 640-row top-10 calls. The call allocates nothing (the
+ * array's address is looked up once per device, on the first call with that
+ * device current). All calls on one GPU share the array: calls that overlap
+ * in time on one GPU (other streams, other host threads) race.
+ */
+#define EAGLE3_LMHEAD_NOALLOC_MAX_BYTES ((size_t)96 << 20)
+int eagle3_lmhead_argmax_noalloc(const void *hidden, const void *w, int M, int N, int K, int topk, int dtype,
+                                 int32_t *idx, float *val, float *gap, float *lse, void *stream);
+
+/*
  * Greedy acceptance on a tree ([lesson] "Verify-accept semantics", applied to
  * every root-to-leaf path). A non-root node is accepted when its parent is
  * accepted and tokens[n] == target_idx[parent[n]]; the root always is.

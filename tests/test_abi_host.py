@@ -104,6 +104,15 @@ def test_lmhead_errors(lib):
     assert f(MISALIGNED, FAKE, 61, 128256, 4096, 1, 1, FAKE, None, None, None, FAKE, need, None) == -1
 
 
+def test_lmhead_noalloc_rejects_calls_past_its_array(lib):
+    f = lib.eagle3_lmhead_argmax_noalloc
+    f.argtypes = [ctypes.c_void_p, ctypes.c_void_p] + [ctypes.c_int] * 5 + [ctypes.c_void_p] * 5
+    # 100000 rows over a 128256-row head need ~2.4 GB of records: refused before any launch
+    assert f(FAKE, FAKE, 100000, 128256, 4096, 1, 1, FAKE, None, None, None, None) == -6
+    assert f(FAKE, FAKE, 61, 128256, 4096, 17, 1, FAKE, None, None, None, None) == -2
+    assert f(None, None, 0, 128256, 4096, 1, 1, None, None, None, None, None) == 0
+
+
 def test_tree_attn_errors(lib):
     from tree_draft_verification_amd.binding import TreeAttnArgs
     f = lib.eagle3_tree_attn

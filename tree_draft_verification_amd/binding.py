@@ -63,6 +63,7 @@ _tree_attn = _sig("eagle3_tree_attn", I, ctypes.POINTER(TreeAttnArgs), P, SZ, P)
 _rmsnorm = _sig("eagle3_rmsnorm", I, P, P, I, I, F, I, P, P)
 _lmhead_ws = _sig("eagle3_lmhead_workspace", SZ, I, I, I, I, I)
 _lmhead = _sig("eagle3_lmhead_argmax", I, P, P, I, I, I, I, I, P, P, P, P, P, SZ, P)
+_lmhead_noalloc = _sig("eagle3_lmhead_argmax_noalloc", I, P, P, I, I, I, I, I, P, P, P, P, P)
 _accept = _sig("eagle3_accept_path", I, P, P, P, I, P, I, I, P, P, P, I, P, P)
 _gemm = _sig("eagle3_gemm", I, ctypes.POINTER(GemmArgs), P)
 _gemm_ws = _sig("eagle3_gemm_workspace", SZ, ctypes.POINTER(GemmArgs))
@@ -173,6 +174,14 @@ def eagle3_lmhead_argmax(hidden, w, topk, idx, val=None, gap=None, lse=None, ws=
     ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
     _check(_lmhead(_ptr(hidden), _ptr(w), M, N, K, topk, _dtype(hidden), _ptr(idx), _ptr(val), _ptr(gap), _ptr(lse),
                    _ptr(ws), ws_bytes, _stream(stream)), "eagle3_lmhead_argmax")
+
+
+def eagle3_lmhead_argmax_noalloc(hidden, w, topk, idx, val=None, gap=None, lse=None, stream=None):
+    K = hidden.shape[-1]
+    M = hidden.numel() // K
+    N = w.shape[0]
+    _check(_lmhead_noalloc(_ptr(hidden), _ptr(w), M, N, K, topk, _dtype(hidden), _ptr(idx), _ptr(val), _ptr(gap),
+                           _ptr(lse), _stream(stream)), "eagle3_lmhead_argmax_noalloc")
 
 
 def eagle3_accept_path(tokens, target_idx, accept_len, path, out_tokens, parent=None, mask=None, V=0, status=None,

@@ -32,6 +32,8 @@
 // merged by lane shuffles; one record per (row, tile) goes to the workspace.
 // Pass 2 (one work-group per row): merges all tiles' records in a fixed order,
 // so results are deterministic.
+#include <mutex>
+
 #include "common.h"
 #include "gemm_core.h"
 
@@ -621,4 +623,51 @@ extern "C" int eagle3_lmhead_argmax(const void *hidden, const void *w, int M, in
     }
     E3_LAUNCH_CHECK();
     return EAGLE3_OK;
+}
+
+// ------------------------------------------------ entry point that allocates nothing
+// For callers that cannot allocate (code under graph capture, tight serving
+// loops): the same LM-head argmax with its per-tile records in a file-scope
+// device array instead of a caller workspace. Each GPU the library runs on
+// holds its own copy of the array until the process ends; every call on that
+// GPU reuses it, so calls that overlap on one GPU race. The records are all
+// written before they are read, so nothing needs clearing between calls.
+static __device__ __align__(256) unsigned char scratch[EAGLE3_LMHEAD_NOALLOC_MAX_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];  // device address of `scratch` per device, from hipGetSymbolAddress
+
+// The array's device address on the current device (looked up once per
+// device, with that device current). In host code the array's own name is
+// not a device address and is never passed to a kernel or a copy.
+int scratch_address(void **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return EAGLE3_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return EAGLE3_ERR_HIP;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return EAGLE3_OK;
+}
+}  // namespace
+
+extern "C" int eagle3_lmhead_argmax_noalloc(const void *hidden, const void *w, int M, int N, int K, int topk,
+                                            int dtype, int32_t *idx, float *val, float *gap, float *lse,
+                                            void *stream) {
+    if (M < 0 || N < 0 || K < 1 || topk < 1) return EAGLE3_ERR_ARG;
+    if (topk > 16 || N < 2 || topk > N) return EAGLE3_ERR_UNSUPPORTED;
+    if (dtype != EAGLE3_BF16 && dtype != EAGLE3_F32) return EAGLE3_ERR_UNSUPPORTED;
+    if (M == 0) return EAGLE3_OK;
+    // the records this call needs must fit the array (checked before any HIP call)
+    if (eagle3_lmhead_workspace(M, N, K, topk, dtype) > EAGLE3_LMHEAD_NOALLOC_MAX_BYTES) return EAGLE3_ERR_WORKSPACE;
+    void *ptr = nullptr;
+    const int rc = scratch_address(&ptr);
+    if (rc != EAGLE3_OK) return rc;
+    return eagle3_lmhead_argmax(hidden, w, M, N, K, topk, dtype, idx, val, gap, lse, ptr,
+                                EAGLE3_LMHEAD_NOALLOC_MAX_BYTES, stream);
 }
