@@ -138,7 +138,6 @@ def test_tree_attn_errors(lib):
     assert f(ctypes.byref(args(mask=None)), None, 0, None) == -1      # neither mask nor parent
     assert f(ctypes.byref(args(q=MISALIGNED)), None, 0, None) == -1
     assert f(ctypes.byref(args(split_keys=128)), None, 0, None) == -2  # prefix splits are switched off
-    assert f(ctypes.byref(args(max_blocks=1025)), None, 0, None) == -2  # > 16384 keys for one work-group
     assert wsq(ctypes.byref(args())) == 0                              # one work-group per prefix: no scratch
     assert wsq(ctypes.byref(args(B=64))) == 0
 

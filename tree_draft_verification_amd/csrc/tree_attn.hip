@@ -4,27 +4,27 @@
 // pass over the whole tree, masked so a token sees only its ancestors).
 // GQA reading: query head h uses KV head h / (Hq / Hkv).
 //
-// bf16, D = 128 (MFMA path). One work-group per (prefix split, KV head,
-// sequence, block of 256 query rows); a query row is (node, head-in-group),
-// so the G query heads sharing a KV head share every K/V tile read.
-//   - K/V tiles of 64 keys are copied from the paged cache into LDS with
-//     16-byte loads; each 16-token cache block is one contiguous 4 KB run for
-//     K ([block, head, slot, d]) and for V ([block, head, d, slot]). The V
-//     layout keeps keys contiguous per dimension, which is what the PV
-//     product needs as its contraction operand.
-//   - Each wave owns 32 query rows. S^T = K . Q^T by MFMA 32x32x16, so every
-//     lane holds one query's scores: the softmax max and sum are in-lane plus
-//     one exchange between the two half-waves. Online softmax in fp32 with
-//     log2(e) folded into the scale, raw v_exp_f32, and a lazily refreshed
-//     running max (O is rescaled only when the max grows by more than 2^8).
-//     K rows sit in LDS in a permuted key order so that each lane's 8 scores
-//     per 16-key step are consecutive keys and the V operand is one read. O^T += V^T . P^T by MFMA with P split
-//     into bf16 hi + lo parts, so P keeps ~16 significant bits.
-//   - Prefix keys are split across work-groups when there are too few
-//     (sequence, head) pairs to fill the chip; the split holding the end of
-//     the prefix also processes the tree keys under the ancestor mask.
-//     Split partials (normalised O, max, sum) are merged in split order by a
-//     second kernel, so results are deterministic.
+// bf16, D = 128 (MFMA path). One work-group of 4 waves per (sequence, KV
+// head, prefix split, block of 256 query rows); a query row is (node,
+// head-in-group), so the G query heads sharing a KV head share every K/V tile.
+//   - K/V tiles of 64 keys are staged from the paged cache through registers
+//     into a double buffer in LDS with 16-byte loads; each 16-token cache
+//     block is one contiguous 4 KB run for K ([block, head, slot, d]) and for
+//     V ([block, head, d, slot]). The V layout keeps keys contiguous per
+//     dimension, which is what the PV product needs as its contraction operand.
+//   - Each wave owns 2 x 32 query rows. S^T = K . Q^T by MFMA 32x32x16, so
+//     every lane holds one query's scores: the softmax max and sum are in-lane
+//     plus one exchange between the two half-waves. Online softmax in fp32
+//     with log2(e) folded into the scale, raw v_exp_f32, and a lazily
+//     refreshed running max (O is rescaled only when the max grows by more
+//     than 2^8). K rows sit in LDS in a permuted key order so that each lane's
+//     8 scores per 16-key step are consecutive keys and the V operand is one
+//     read. O^T += V^T . P^T on the fp16 MFMA: V tiles are converted from
+//     bf16 to fp16 when staged (exact for |v| in [2^-14, 65504]; larger
+//     values saturate), P is rounded to fp16 (11 significant bits).
+//   - The work-group holding the end of a prefix also processes the tree keys
+//     under the ancestor mask. Prefix splits over work-groups write partials
+//     (normalised O, max, sum) that a second kernel merges in split order.
 // fp32 (any D <= 128): one 64-lane wave per query row, lanes over keys for
 // the scores and over dimensions for P.V; for small models.
 #include "common.h"
@@ -49,7 +49,7 @@ struct AttnParams {
     float *ws_o;   // [B, Hkv, nsplit, Rpad, D]
     float *ws_ml;  // [B, Hkv, nsplit, Rpad, 2]
     int B, Tq, Tk, Hq, Hkv, W, G, R, Rpad, nrb, nsplit, split_keys, max_blocks, num_blocks;
-    int tree_split;  // 1: the tree keys are a split of their own (after the prefix splits)
+    int nunits;      // B * Hkv * nsplit work units of nrb work-groups each
     float scale_log2;
 };
 
@@ -61,12 +61,11 @@ __device__ __forceinline__ int clamped_len(const int32_t *prefix_len, int b, int
     return max(0, min(L, max_blocks * bs));
 }
 
-// Splits of one sequence: prefix splits of split_keys keys, plus (tree_split)
-// one more for the tree keys; without tree_split the last prefix split also
+// Splits of one sequence: prefix splits of split_keys keys; the last one also
 // takes the tree keys (an empty prefix still makes one split).
-__device__ __forceinline__ int splits_of(int L, int split_keys, int tree_split) {
+__device__ __forceinline__ int splits_of(int L, int split_keys) {
     const int npre = L > 0 ? (L + split_keys - 1) / split_keys : 0;
-    return tree_split ? npre + 1 : (npre > 0 ? npre : 1);
+    return npre > 0 ? npre : 1;
 }
 
 // Sequences are dealt to work-group slots longest (clamped) prefix first,
@@ -117,12 +116,15 @@ __device__ __forceinline__ void query_mask(const AttnParams &p, int b, int t, ui
     }
 }
 
-typedef __attribute__((address_space(3))) void lds_void_t;
+enum TileKind { TILE_FULL = 0, TILE_PARTIAL = 1, TILE_TREE = 2 };
 
-constexpr int NSTAGE = 3;                  // depth of the K/V ring
-constexpr int STAGE = 2 * KT * DH * 2;     // bytes per stage: K tile + V tile (16 KB each)
-constexpr int VOFF = KT * DH * 2;          // V tile offset inside a stage
-constexpr int MAX_SPLIT_BLOCKS = 1024;     // cache blocks one work-group may cover (prefixes up to 16384 keys)
+// Softmax bookkeeping is in log2 units with a lazily refreshed running max:
+// m_run only moves when a score exceeds it by more than 2^8 (so exp2 values
+// stay below 256, harmless in fp32), which makes O rescaling rare.
+constexpr float kLazyMax = 8.f;
+
+constexpr int TILE_BYTES = 2 * KT * DH * 2;  // K tile + V tile, 16 KB each
+constexpr int VOFF = KT * DH * 2;          // V tile offset inside a buffer
 
 // 16-byte column swizzle of K rows (a tile row is one key, 256 B): K reads of
 // 16 consecutive rows then hit 16 distinct bank groups.
@@ -136,37 +138,31 @@ __device__ __forceinline__ int vswz(int d) { return (d >> 3) & 1; }
 // is one 16-byte half of a V row, so the PV operand is a single LDS read.
 __device__ __forceinline__ int row_key(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8_t;
+typedef __attribute__((__vector_size__(2 * sizeof(_Float16)))) _Float16 f16x2_t;
+
+// Two bf16 values (low half first) to two fp16 values. Exact for magnitudes
+// in [2^-14, 65504]; smaller ones keep 10 bits of absolute precision below
+// 2^-14 (an error under 3e-8), larger ones saturate at 65504 (round toward
+// zero never overflows to infinity).
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(__uint_as_float(w << 16),
+                                                                   __uint_as_float(w & 0xffff0000u)));
+}
+// Two fp32 values to two fp16 values, round to nearest even.
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+    const f32x2_t v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
 }
 
-enum TileKind { TILE_FULL = 0, TILE_PARTIAL = 1, TILE_TREE = 2 };
-
-// Softmax bookkeeping is in log2 units with a lazily refreshed running max:
-// m_run only moves when a score exceeds it by more than 2^8 (so exp2 values
-// stay below 256, harmless in fp32), which makes O rescaling rare.
-constexpr float kLazyMax = 8.f;
-
-// LDS fragment reads are inline ds_read_b128: the compiler cannot tell ring
-// stages apart and would otherwise wait for every K/V DMA still in flight
-// (the whole ring) before the first read of a tile. Each read is awaited
-// explicitly (lgkmcnt), with the wait tied to its destination register.
-__device__ __forceinline__ void lds_read16(u32x4_t &r, uint32_t addr) {
-    __asm__ volatile("ds_read_b128 %0, %1" : "=v"(r) : "v"(addr));
-}
-template <int N>
-__device__ __forceinline__ void lgkm_wait1(u32x4_t &r) {
-    __asm__ volatile("s_waitcnt lgkmcnt(%1)" : "+v"(r) : "i"(N));
-}
-// wait until at most n (0..2) LDS reads are outstanding
-__device__ __forceinline__ void lgkm_upto(int n, u32x4_t &r) {
-    if (n >= 2) lgkm_wait1<2>(r);
-    else if (n == 1) lgkm_wait1<1>(r);
-    else lgkm_wait1<0>(r);
-}
-
+// One 64-key tile for one wave and its RB blocks of 32 query rows: S^T =
+// K.Q^T, online softmax, O^T += V^T.P^T. Every K / V fragment read from LDS
+// feeds the MFMAs of all RB row blocks. kind is wave-uniform.
+//   QK step (s, kb): K rows 32 kb + lr, 16-byte column 2 s + lh (swizzled),
+//   i.e. keys of block kb and d = 16 s + 8 lh .. +7; the Q^T operand holds
+//   the same d of this lane's query row.
+//   PV step (ks, db): V row (16-key block ks, d = 32 db + lr), half lh: keys
+//   16 ks + 8 lh .. +7; the P^T operand holds this lane's P for those keys.
 // compile-time unrolled loop: f(std::integral_constant<int, i>) for i in [I, N)
 template <int I, int N, typename F>
 __device__ __forceinline__ void sfor(F &&f) {
@@ -176,233 +172,183 @@ __device__ __forceinline__ void sfor(F &&f) {
     }
 }
 
-// LDS fragment read at a per-lane address plus a constant byte offset (the
-// instruction's offset field), so the constant parts take no registers
-template <int OFF>
-__device__ __forceinline__ void lds_read16_at(u32x4_t &r, uint32_t addr) {
-    static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
-    __asm__ volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
-}
+constexpr int QK_AHEAD = 4;  // K fragment reads in flight ahead of the MFMAs
 
-// Per-lane parts of the fragment addresses inside a ring stage. QK step j
-// (key block kb = j & 1, d-step s = j >> 1) reads koff[s] + 8192 kb: row
-// 32 kb + lr, 16-byte column (2 s + lh) ^ kswz(lr) (kswz of the row only sees
-// lr); lane half lh holds d = 16 s + 8 lh .. +7. PV step j (16-key step
-// ks = j >> 2, d block db = j & 3) reads voff + 4096 ks + 1024 db: row
-// (ks, d = 32 db + lr), half lh ^ vswz(lr).
-struct FragOffsets {
-    uint32_t k[8];
-    uint32_t v;
-};
-__device__ __forceinline__ FragOffsets frag_offsets(int lr, int lh) {
-    FragOffsets f;
-#pragma unroll
-    for (int s = 0; s < 8; ++s) f.k[s] = lr * 256 + (((2 * s + lh) ^ kswz(lr)) << 4);
-    f.v = VOFF + lr * 32 + ((lh ^ vswz(lr)) << 4);
-    return f;
-}
-
-// Fragment reads run RA steps ahead through an NF-slot buffer: with one
-// 32 x 32 x 16 MFMA (QK) or two (PV) per read, two reads ahead left the
-// LDS latency exposed at every step.
-constexpr int RA = 4, NF = RA + 2;
-
-// One 64-key tile for one wave and its RB blocks of 32 query rows: S^T =
-// K.Q^T, online softmax, O^T += V^T.P^T. Every K / V fragment read from LDS
-// feeds the MFMAs of all RB row blocks, and the row blocks' independent
-// softmax work interleaves with the MFMAs of the others. kind is wave-uniform.
-// Operand fragments are read two steps ahead through a 4-slot buffer.
 template <int RB>
-__device__ __forceinline__ void attend_tile(int kind, const unsigned char *stage, const u32x4_t (&qb)[RB][8],
+__device__ __forceinline__ void attend_tile(int kind, const unsigned char *tile, const u32x4_t (&qb)[RB][8],
                                             f32x16_t (&ot)[RB][4], float (&m_run)[RB], float (&l_run)[RB],
-                                            const FragOffsets &fo, int lh, int nvalid, const uint64_t (&mword)[RB],
+                                            int lr, int lh, int nvalid, const uint64_t (&mword)[RB],
                                             float scale_log2) {
-    const uint32_t sb = (uint32_t)(uintptr_t)(lds_void_t *)stage;
-    u32x4_t fr[NF];
-    // QK step j: key block kb = j & 1 (alternating accumulators), d-step s = j >> 1
-    auto kread = [&](auto J) {
-        constexpr int j = J;
-        lds_read16_at<(j & 1) * 8192>(fr[j % NF], sb + fo.k[j >> 1]);
-    };
     f32x16_t st[RB][2];
-    // the score accumulators start as registers holding zero, not the MFMA's
-    // inline-zero operand: with the inline zero the destination is not tied
-    // to an input and the compiler placed it over the A operand's registers
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
+    for (int k = 0; k < RB; ++k)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) st[rb][kb][r] = 0.f;
-            __asm__ volatile("" : "+v"(st[rb][kb]));
-        }
-    sfor<0, RA>(kread);
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) st[k][kb][r] = 0.f;
+    // QK step j: key block kb = j & 1, d-step s = j >> 1. Fragment reads run
+    // QK_AHEAD steps ahead of the MFMAs; the scheduling barriers keep the
+    // compiler from sinking each read next to its MFMA (which leaves the LDS
+    // latency exposed at every step)
+    const unsigned char *krow = tile + lr * 256;
+    u32x4_t fk[16];
+    auto kread = [&](auto J) {
+        constexpr int j = J, kb = j & 1, s = j >> 1;
+        fk[j] = *reinterpret_cast<const u32x4_t *>(krow + kb * 8192 + (((2 * s + lh) ^ kswz(lr)) << 4));
+    };
+    sfor<0, QK_AHEAD>(kread);
     sfor<0, 16>([&](auto J) {
         constexpr int j = J, kb = j & 1, s = j >> 1;
-        if constexpr (j + RA < 16) kread(std::integral_constant<int, j + RA>{});
-        lgkm_wait1<(15 - j < RA ? 15 - j : RA)>(fr[j % NF]);
+        if constexpr (j + QK_AHEAD < 16) kread(std::integral_constant<int, j + QK_AHEAD>{});
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-            st[rb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, fr[j % NF]),
-                                                                 __builtin_bit_cast(bf16x8_t, qb[rb][s]), st[rb][kb],
-                                                                 0, 0, 0);
+        for (int k = 0; k < RB; ++k)
+            st[k][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, fk[j]),
+                                                                __builtin_bit_cast(bf16x8_t, qb[k][s]), st[k][kb], 0,
+                                                                0, 0);
+        __builtin_amdgcn_sched_barrier(0);
     });
-    // PV step j: 16-key step ks = j >> 2, d block db = j & 3; the first RA V
-    // fragments are read now and land during the softmax
-    auto vread = [&](auto J) {
-        constexpr int j = J;
-        lds_read16_at<(j >> 2) * 4096 + (j & 3) * 1024>(fr[j % NF], sb + fo.v);
-    };
-    sfor<0, RA>(vread);
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
+    for (int k = 0; k < RB; ++k) {
         // register r of block kb holds key 32 kb + 16 (r / 8) + 8 lh + (r % 8)
         if (kind != TILE_FULL) {
+            // visible keys of the tile (bit kk); each group of 8 registers
+            // holds 8 consecutive keys, whose bits are one byte of the word
+            uint64_t vis = nvalid >= KT ? ~0ull : (1ull << nvalid) - 1;
+            if (kind == TILE_TREE) vis &= mword[k];
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int kk = kb * 32 + 16 * (r >> 3) + 8 * lh + (r & 7);
-                    const bool vis = kk < nvalid && (kind != TILE_TREE || ((mword[rb] >> kk) & 1u));
-                    st[rb][kb][r] = vis ? st[rb][kb][r] : -INFINITY;
+                for (int a = 0; a < 2; ++a) {
+                    const uint32_t byte = (uint32_t)(vis >> (kb * 32 + 16 * a + 8 * lh));
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const uint32_t m = (uint32_t)((int32_t)(byte << (31 - e)) >> 31);  // all ones iff visible
+                        const uint32_t x = __float_as_uint(st[k][kb][8 * a + e]);
+                        st[k][kb][8 * a + e] = __uint_as_float((x & m) | (0xff800000u & ~m));
+                    }
                 }
         }
         float tmax = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, st[rb][kb][r]);
+            for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, st[k][kb][r]);
         tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * scale_log2;
         // refresh the running max only when it is exceeded by more than 2^kLazyMax
-        const bool grow = tmax > m_run[rb] + kLazyMax;
+        const bool grow = tmax > m_run[k] + kLazyMax;
         if (__ballot(grow)) {
-            const float m_new = grow ? tmax : m_run[rb];
-            const float alpha = (m_run[rb] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run[rb] - m_new);
-            l_run[rb] *= alpha;
+            const float m_new = grow ? tmax : m_run[k];
+            const float alpha = (m_run[k] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run[k] - m_new);
+            l_run[k] *= alpha;
 #pragma unroll
             for (int db = 0; db < 4; ++db)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) ot[rb][db][r] *= alpha;
-            m_run[rb] = m_new;
+                for (int r = 0; r < 16; ++r) ot[k][db][r] *= alpha;
+            m_run[k] = m_new;
         }
-        const float msub = (m_run[rb] == -INFINITY) ? 0.f : m_run[rb];
+        const float msub = (m_run[k] == -INFINITY) ? 0.f : m_run[k];
         float psum = 0.f;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const float pv = __builtin_amdgcn_exp2f(fmaf(st[rb][kb][r], scale_log2, -msub));
-                st[rb][kb][r] = pv;
+                const float pv = __builtin_amdgcn_exp2f(fmaf(st[k][kb][r], scale_log2, -msub));
+                st[k][kb][r] = pv;
                 psum += pv;
             }
-        l_run[rb] += psum;
+        l_run[k] += psum;
     }
-    // 16 keys per step = one cache block of the tile; this lane's 8 P values
-    // are keys 8 lh .. 8 lh + 7 of the block. P enters as bf16 hi + lo (two
-    // MFMAs on the same V operand): a single bf16 rounding of P would leave
-    // ~2e-3 relative error in the output.
-    u32x4_t ph[RB], pl[RB];
+    // P . V runs on the fp16 MFMA: V was converted from bf16 when its tile
+    // was staged (exact in fp16's range) and P (at most 2^8 with the lazy
+    // max) is rounded to fp16, 11 significant bits against bf16's 8.
+    // PV step j: 16-key step ks = j >> 2, d block db = j & 3; reads run
+    // QK_AHEAD steps ahead as in the QK loop
+    const unsigned char *vrow = tile + VOFF + lr * 32 + ((lh ^ vswz(lr)) << 4);
+    u32x4_t fv[16];
+    auto vread = [&](auto J) {
+        constexpr int j = J, ks = j >> 2, db = j & 3;
+        fv[j] = *reinterpret_cast<const u32x4_t *>(vrow + ks * 4096 + db * 1024);
+    };
+    sfor<0, QK_AHEAD>(vread);
+    u32x4_t ph[RB];
     sfor<0, 16>([&](auto J) {
         constexpr int j = J, ks = j >> 2, db = j & 3;
         if constexpr (db == 0) {
             constexpr int kb = ks >> 1, r0 = 8 * (ks & 1);
 #pragma unroll
-            for (int rb = 0; rb < RB; ++rb)
+            for (int k = 0; k < RB; ++k)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    uint32_t h2, l2;
-                    e3_split_bf16x2(st[rb][kb][r0 + 2 * e], st[rb][kb][r0 + 2 * e + 1], h2, l2);
-                    ph[rb][e] = h2;
-                    pl[rb][e] = l2;
-                }
+                for (int e = 0; e < 4; ++e) ph[k][e] = pack_f16x2(st[k][kb][r0 + 2 * e], st[k][kb][r0 + 2 * e + 1]);
         }
-        if constexpr (j + RA < 16) vread(std::integral_constant<int, j + RA>{});
-        lgkm_wait1<(15 - j < RA ? 15 - j : RA)>(fr[j % NF]);
-        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, fr[j % NF]);
+        if constexpr (j + QK_AHEAD < 16) vread(std::integral_constant<int, j + QK_AHEAD>{});
+        const f16x8_t a = __builtin_bit_cast(f16x8_t, fv[j]);
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-            ot[rb][db] =
-                __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, ph[rb]), ot[rb][db], 0, 0, 0);
-            ot[rb][db] =
-                __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, pl[rb]), ot[rb][db], 0, 0, 0);
-        }
+        for (int k = 0; k < RB; ++k)
+            ot[k][db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, __builtin_bit_cast(f16x8_t, ph[k]), ot[k][db], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
     });
 }
 
-// NW waves of RB x 32 query rows each (NW * RB * 32 = ROWS_PER_WG).
+// Work-group -> work unit. Work-groups are dealt to the 8 XCDs round-robin
+// (work-group i runs on XCD i mod 8, each XCD with its own L2). The nrb row
+// blocks of one (sequence, KV head, split) read the same K/V, so they are
+// given ids i, i + 8, ...: one XCD, dispatched together, and the second
+// read of every tile is an L2 hit. Units are numbered so that dispatch order
+// follows the slot order (longest prefix first).
+struct WorkUnit {
+    int unit, rblk;
+};
+__device__ __forceinline__ WorkUnit work_unit(int i, int nrb) {
+    const int xcd = i & 7, j = i >> 3;
+    WorkUnit w;
+    w.rblk = j % nrb;
+    w.unit = (j / nrb) * 8 + xcd;
+    return w;
+}
+
+// One work-group per (sequence slot, KV head, prefix split, block of 256 query
+// rows); NW waves of RB x 32 rows. K/V tiles are double-buffered in LDS: while
+// a tile is attended, every thread holds its share of the next tile (NCH
+// 16-byte chunks of K and NCH of V) in registers, loaded at the start of the
+// tile and written to the other buffer at its end; one barrier per tile.
 template <int NW, int RB>
 __global__ __launch_bounds__(NW * 64) void tree_attn_bf16_kernel(AttnParams p) {
     static_assert(NW * RB * 32 == ROWS_PER_WG, "a work-group covers one block of query rows");
-    __shared__ __attribute__((aligned(1024))) unsigned char ring[NSTAGE * STAGE];
-    __shared__ int bids[MAX_SPLIT_BLOCKS];
     constexpr int NT = NW * 64;
-    constexpr int LOADS = 32 / NW;  // 1 KB DMA loads per wave per stage (16 for K, 16 for V)
+    constexpr int NCH = KT * DH / 8 / NT;  // 16-byte chunks of K (and of V) per thread and tile
+    static_assert(NCH * NT * 8 == KT * DH && NT % 256 == 0, "whole 4 KB cache blocks per 256 threads");
+    __shared__ __attribute__((aligned(1024))) unsigned char buf[2 * TILE_BYTES];
 
-    const int split = blockIdx.x / p.nrb, rb = blockIdx.x % p.nrb;
-    const int kvh = blockIdx.y;
-    const int b = __builtin_amdgcn_readfirstlane(seq_of_slot(p.prefix_len, p.B, blockIdx.z, p.max_blocks, p.num_blocks));
+    const WorkUnit wu = work_unit(blockIdx.x, p.nrb);
+    if (wu.unit >= p.nunits) return;
+    const int split = wu.unit % p.nsplit, kvh = (wu.unit / p.nsplit) % p.Hkv, slot = wu.unit / (p.nsplit * p.Hkv);
+    const int rblk = wu.rblk;
+    const int b = __builtin_amdgcn_readfirstlane(seq_of_slot(p.prefix_len, p.B, slot, p.max_blocks, p.num_blocks));
     const int L = clamped_len(p.prefix_len, b, p.max_blocks, 16, p.num_blocks);
     const int C = p.split_keys;
-    const int nsplit_b = splits_of(L, C, p.tree_split);
+    const int nsplit_b = splits_of(L, C);
     if (split >= nsplit_b) return;
-    const bool last = split == nsplit_b - 1;           // this split takes the tree keys
-    const bool tree_only = p.tree_split && last;       // ... and no prefix keys
-    const int k_begin = tree_only ? 0 : split * C;
-    const int k_end = tree_only ? 0 : min(L, k_begin + C);
+    const bool last = split == nsplit_b - 1;  // this split also takes the tree keys
+    const int k_begin = split * C;
+    const int k_end = min(L, k_begin + C);
+    const int npre = (k_end - k_begin + KT - 1) / KT;
+    const int ntiles = npre + (last ? (p.Tk + KT - 1) / KT : 0);
 
     // the wave index is wave-uniform; saying so keeps the branches on it scalar
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int lr = lane & 31, lh = lane >> 5;
-    // this lane's query rows, one per row block
     int row[RB], t[RB], hq[RB];
     bool row_ok[RB];
 #pragma unroll
     for (int k = 0; k < RB; ++k) {
-        row[k] = rb * ROWS_PER_WG + (wave * RB + k) * 32 + lr;
+        row[k] = rblk * ROWS_PER_WG + (wave * RB + k) * 32 + lr;
         row_ok[k] = row[k] < p.R;
         t[k] = row_ok[k] ? row[k] / p.G : 0;
         hq[k] = kvh * p.G + (row_ok[k] ? row[k] % p.G : 0);
     }
-    const bool wave_active = rb * ROWS_PER_WG + wave * RB * 32 < p.R;
-
-    // physical ids of the cache blocks this split reads
-    const int blk0 = k_begin / 16;
-    const int nblk = (k_end - k_begin + 15) / 16;
-    const int32_t *btab = p.block_table + (size_t)b * p.max_blocks;
-    for (int i = tid; i < nblk; i += NT) bids[i] = clamped_block(btab, blk0 + i, p.num_blocks);
-
-    // this lane's part of each DMA load: element offset inside a cache block
-    // ([16 slots][128 d] for K, [128 d][16 slots] for V)
-    int dma_off[LOADS];
-#pragma unroll
-    for (int j = 0; j < LOADS; ++j) {
-        const int q = wave * LOADS + j;
-        if (q < 16) {
-            const int rib = 4 * (q & 3) + lane / 16;    // tile row in block (rows are 16-aligned per block)
-            dma_off[j] = row_key(rib) * DH + 8 * ((lane & 15) ^ kswz(rib));
-        } else {
-            const int d = 32 * ((q - 16) & 3) + lane / 2;
-            dma_off[j] = d * 16 + 8 * ((lane & 1) ^ vswz(d));
-        }
-    }
-    const size_t head_off = (size_t)kvh * 16 * DH;
-    const size_t blk_stride = (size_t)p.Hkv * 16 * DH;
-    // a wave's LOADS = 4 loads of a stage all come from one cache block (K
-    // for waves 0-3, V for waves 4-7): its address is a scalar base plus a
-    // 32-bit per-lane offset
-    static_assert(LOADS == 4, "one cache block per wave and stage");
-    auto issue = [&](int stage, int tile) {
-        unsigned char *base = ring + stage * STAGE;
-        const int lb = min(4 * tile + (wave & 3), nblk - 1);  // blocks past the prefix re-read the last
-        const int bid = __builtin_amdgcn_readfirstlane(bids[lb]);
-        const uint16_t *blk = (wave < 4 ? p.k_cache : p.v_cache) + (size_t)bid * blk_stride + head_off;
-#pragma unroll
-        for (int j = 0; j < LOADS; ++j) {
-            const int q = wave * LOADS + j;
-            __builtin_amdgcn_global_load_lds((const void *)(blk + dma_off[j]), (lds_void_t *)(base + q * 1024), 16,
-                                             0, 0);
-        }
-    };
+    const bool wave_active = rblk * ROWS_PER_WG + wave * RB * 32 < p.R;
 
     // Q^T operand: d = 16 s + 8 lh + i
     u32x4_t qb[RB][8];
@@ -429,84 +375,139 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_bf16_kernel(AttnParams p) {
         l_run[k] = 0.f;
     }
 
-    const FragOffsets fo = frag_offsets(lr, lh);
-    const int ntile = (k_end - k_begin + KT - 1) / KT;
-    // q and mask words have landed before any K/V DMA is queued behind them
-    // (otherwise the first use of q inside the tile loop waits for the ring)
-    wait_vmcnt<0>();
-    __syncthreads();  // block ids are in
+    // Staging. Chunk i of a thread is 16-key block jb = i NT / 256 + tid / 256
+    // of the tile and the w-th 16 bytes of it, w = tid % 256: for K the key
+    // 16 jb + w / 16, 16-byte column w % 16; for V (cache layout [d][16 slots]
+    // per block) the dimension d = w / 2, slots 8 (w % 2) .. +7. In the cache
+    // both are the w-th 16 bytes of the block's contiguous 4 KB run.
+    const int32_t *btab = p.block_table + (size_t)b * p.max_blocks;
+    const size_t head_off = (size_t)kvh * 16 * DH;
+    const size_t blk_stride = (size_t)p.Hkv * 16 * DH;
+    // jb_t is wave-uniform: block ids are then scalar loads, which do not
+    // hold up the vector loads of the tile behind them
+    const int w = tid & 255, jb_t = __builtin_amdgcn_readfirstlane(tid >> 8);
+    u32x4_t sk[NCH], sv[NCH];
+    // Loads are unconditional, from clamped addresses (blocks past the end of
+    // the range re-read its last block, tree keys past Tk re-read key Tk - 1);
+    // write_tile zeroes what they stand for. A conditional load into a
+    // zeroed register would make every later write of that register wait
+    // for the load.
+    const int last_blk = max(k_end - 1, k_begin) / 16;
+    // block ids are fetched one tile ahead of the staging loads that use them
+    int raw_id[NCH];
+    auto fetch_ids = [&](int it) {
+        if (it < npre) {
+            const int blk0 = (k_begin + it * KT) / 16;
 #pragma unroll
-    for (int st = 0; st < NSTAGE - 1; ++st)
-        if (st < ntile) issue(st, st);
-
-    // prefix tiles stream through the ring; the tree keys (only in the split
-    // holding the end of the prefix) follow through registers, since their V
-    // rows must be transposed into the [block][d][slot] layout
-    const int ntree = last ? (p.Tk + KT - 1) / KT : 0;
-    for (int it = 0; it < ntile + ntree; ++it) {
-        const unsigned char *stage;
-        int kind, nvalid;
-        uint64_t mword[RB];
+            for (int i = 0; i < NCH; ++i) raw_id[i] = btab[min(blk0 + i * (NT / 256) + jb_t, last_blk)];
+        }
+    };
+    auto load_tile = [&](int it) {
+        if (it < npre) {
 #pragma unroll
-        for (int k = 0; k < RB; ++k) mword[k] = 0;
-        if (it < ntile) {
-            // all of this wave's ring loads, not just those of tile it: the
-            // wait then holds whatever order the DMA completions take (tile
-            // it + 1 was issued a tile earlier and has landed by now; measured
-            // at no cost against waiting for tile it alone)
-            wait_vmcnt<0>();
-            // tile it has landed for every wave and every wave is done with the
-            // buffer refilled below; a fenced barrier would also wait for the
-            // compiler's own outstanding operations
-            __builtin_amdgcn_s_barrier();
-            __asm__ volatile("" ::: "memory");
-            stage = ring + (it % NSTAGE) * STAGE;
-            nvalid = k_end - (k_begin + it * KT);
-            kind = nvalid >= KT ? TILE_FULL : TILE_PARTIAL;
-            if (nvalid < KT) {
-                // last, partial tile: zero the V slots past the prefix (the
-                // cache may hold anything there, and 0 * NaN would poison the sum)
-                unsigned char *vb = ring + (it % NSTAGE) * STAGE + VOFF;
-                for (int r = tid; r < 4 * DH; r += NT) {
-                    const int jb = r / DH, d = r % DH;
-                    uint16_t *rowp = reinterpret_cast<uint16_t *>(vb + jb * 4096 + d * 32);
-                    for (int sl = 0; sl < 16; ++sl)
-                        if (16 * jb + sl >= nvalid) rowp[((sl >> 3) ^ vswz(d)) * 8 + (sl & 7)] = 0;
-                }
-                __syncthreads();
+            for (int i = 0; i < NCH; ++i) {
+                const int bid = __builtin_amdgcn_readfirstlane(min(max(raw_id[i], 0), p.num_blocks - 1));
+                const size_t off = (size_t)bid * blk_stride + head_off + (size_t)w * 8;
+                sk[i] = *reinterpret_cast<const u32x4_t *>(p.k_cache + off);
+                sv[i] = *reinterpret_cast<const u32x4_t *>(p.v_cache + off);
             }
-            if (it + NSTAGE - 1 < ntile) issue((it + NSTAGE - 1) % NSTAGE, it + NSTAGE - 1);
         } else {
-            const int tt = it - ntile;
-            __syncthreads();  // everyone is done with stage 0 (and the ring is drained)
-            unsigned char *Kb = ring, *Vb = ring + VOFF;
-            for (int c = tid; c < KT * DH / 8; c += NT) {
-                const int key = c >> 4, d8 = (c & 15) * 8;
-                const int tk = tt * KT + key;
-                u32x4_t kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
-                if (tk < p.Tk) {
-                    const size_t off = (((size_t)b * p.Tk + tk) * p.Hkv + kvh) * DH + d8;
-                    kv = *reinterpret_cast<const u32x4_t *>(p.k_tree + off);
-                    vv = *reinterpret_cast<const u32x4_t *>(p.v_tree + off);
+            const int tk0 = (it - npre) * KT;
+#pragma unroll
+            for (int i = 0; i < NCH; ++i) {
+                const int jb = i * (NT / 256) + jb_t;
+                const int tk = min(tk0 + 16 * jb + (w >> 4), p.Tk - 1);
+                const size_t off = (((size_t)b * p.Tk + tk) * p.Hkv + kvh) * DH + (w & 15) * 8;
+                sk[i] = *reinterpret_cast<const u32x4_t *>(p.k_tree + off);
+                sv[i] = *reinterpret_cast<const u32x4_t *>(p.v_tree + off);
+            }
+        }
+    };
+    auto write_tile = [&](int it, unsigned char *dst) {
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) {
+            const int jb = i * (NT / 256) + jb_t;
+            const int r = 16 * jb + row_key(w >> 4);  // the row holding key 16 jb + w / 16
+            *reinterpret_cast<u32x4_t *>(dst + r * 256 + (((w & 15) ^ kswz(r)) << 4)) = sk[i];
+        }
+        if (it < npre) {
+            const int nval = min(KT, k_end - (k_begin + it * KT));
+            const int d = w >> 1, half = w & 1;
+#pragma unroll
+            for (int i = 0; i < NCH; ++i) {
+                const int jb = i * (NT / 256) + jb_t;
+                u32x4_t v = sv[i];
+                // slots past the prefix are zeroed: the cache may hold anything
+                // there, and 0 * NaN would poison the sum
+                const int k0 = 16 * jb + 8 * half;
+                if (k0 + 8 > nval) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const uint32_t lo = (k0 + 2 * e < nval) ? 0x0000ffffu : 0u;
+                        const uint32_t hi = (k0 + 2 * e + 1 < nval) ? 0xffff0000u : 0u;
+                        v[e] &= lo | hi;
+                    }
                 }
-                const int krow = row_key(key);  // the row holding this key (the permutation is an involution)
-                *reinterpret_cast<u32x4_t *>(Kb + krow * 256 + (((c & 15) ^ kswz(krow)) << 4)) = kv;
-                const int jb = key >> 4, sl = key & 15;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = bf16x2_to_f16x2(v[e]);
+                *reinterpret_cast<u32x4_t *>(dst + VOFF + jb * 4096 + d * 32 + ((half ^ vswz(d)) << 4)) = v;
+            }
+        } else {
+            // tree V rows arrive key-major ([key][d]): transpose into the
+            // [block][d][slot] layout, one 2-byte store per element
+            const int d8 = (w & 15) * 8, sl = w >> 4;
+#pragma unroll
+            for (int i = 0; i < NCH; ++i) {
+                const int jb = i * (NT / 256) + jb_t;
+                const bool key_ok = (it - npre) * KT + 16 * jb + sl < p.Tk;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const int d = d8 + e;
-                    const uint16_t val = (uint16_t)((e & 1) ? (vv[e >> 1] >> 16) : (vv[e >> 1] & 0xffffu));
-                    reinterpret_cast<uint16_t *>(Vb + jb * 4096 + d * 32)[((sl >> 3) ^ vswz(d)) * 8 + (sl & 7)] = val;
+                    const uint32_t word = key_ok ? bf16x2_to_f16x2(sv[i][e >> 1]) : 0u;
+                    const uint16_t val = (uint16_t)((e & 1) ? (word >> 16) : (word & 0xffffu));
+                    reinterpret_cast<uint16_t *>(dst + VOFF + jb * 4096 + d * 32)[((sl >> 3) ^ vswz(d)) * 8 + (sl & 7)] =
+                        val;
                 }
             }
-            __syncthreads();
-            stage = ring;
-            kind = TILE_TREE;
+        }
+    };
+
+    // q and the mask words have landed before the loop: otherwise the wait
+    // for them, placed inside the loop, would also wait for the staging
+    // loads of the next tile
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt and lgkmcnt not waited
+    if (ntiles > 0) {
+        fetch_ids(0);
+        load_tile(0);
+        fetch_ids(1);
+        write_tile(0, buf);
+    }
+    __syncthreads();
+    for (int it = 0; it < ntiles; ++it) {
+        const bool more = it + 1 < ntiles;
+        if (more) {
+            load_tile(it + 1);
+            fetch_ids(it + 2);
+        }
+        int kind, nvalid;
+        uint64_t mword[RB];
+        if (it < npre) {
+            nvalid = k_end - (k_begin + it * KT);
+            kind = nvalid >= KT ? TILE_FULL : TILE_PARTIAL;
+#pragma unroll
+            for (int k = 0; k < RB; ++k) mword[k] = 0;
+        } else {
+            const int tt = it - npre;
             nvalid = p.Tk - tt * KT;
+            kind = TILE_TREE;
 #pragma unroll
             for (int k = 0; k < RB; ++k) mword[k] = tt == 0 ? mw0[k] : mw1[k];
         }
-        if (wave_active) attend_tile<RB>(kind, stage, qb, ot, m_run, l_run, fo, lh, nvalid, mword, p.scale_log2);
+        if (wave_active)
+            attend_tile<RB>(kind, buf + (it & 1) * TILE_BYTES, qb, ot, m_run, l_run, lr, lh, nvalid, mword, p.scale_log2);
+        // the other buffer was last read before the previous barrier
+        if (more) write_tile(it + 1, buf + ((it + 1) & 1) * TILE_BYTES);
+        __syncthreads();
     }
 
 #pragma unroll
@@ -555,7 +556,7 @@ __global__ __launch_bounds__(128) void tree_attn_combine_kernel(AttnParams p) {
     const int idx = blockIdx.x;  // (b, t, hq)
     const int hq = idx % p.Hq, t = (idx / p.Hq) % p.Tq, b = idx / (p.Hq * p.Tq);
     const int L = clamped_len(p.prefix_len, b, p.max_blocks, 16, p.num_blocks);
-    const int nsplit_b = splits_of(L, p.split_keys, p.tree_split);
+    const int nsplit_b = splits_of(L, p.split_keys);
     if (nsplit_b <= 1) return;
     const int kvh = hq / p.G, row = t * p.G + hq % p.G;
     const size_t base = ((size_t)b * p.Hkv + kvh) * p.nsplit;
@@ -598,7 +599,7 @@ __global__ __launch_bounds__(CN_NT) void tree_attn_combine_norm_kernel(AttnParam
     __shared__ float red[CN_NT / 64];
     const int t = blockIdx.x % p.Tq, b = blockIdx.x / p.Tq;
     const int L = clamped_len(p.prefix_len, b, p.max_blocks, 16, p.num_blocks);
-    const int nsplit_b = splits_of(L, p.split_keys, p.tree_split);
+    const int nsplit_b = splits_of(L, p.split_keys);
     const bool direct = nsplit_b == 1;  // uniform over the work-group
     // split weights: 8 lanes per head, lane j takes splits j, j+8, j+16, j+24
     // (all loads issued together), max and sum over the 8 lanes by shuffles
@@ -833,7 +834,7 @@ __global__ __launch_bounds__(64) void tree_attn_validate_kernel(const int32_t *_
 // ---------------------------------------------------------------- host side
 
 struct Plan {
-    int nrb, nsplit, split_keys, tree_split;
+    int nrb, nsplit, split_keys;
     size_t ws_bytes;
 };
 
@@ -857,8 +858,6 @@ int check_args(const eagle3_tree_attn_args *a) {
     // 0), because the split path gave sporadic wrong rows whose cause was not
     // found; block ids of one work-group must fit its LDS table
     if (a->split_keys != 0) return EAGLE3_ERR_UNSUPPORTED;
-    if (a->dtype == EAGLE3_BF16 && (long)a->max_blocks * a->block_size > 16L * MAX_SPLIT_BLOCKS)
-        return EAGLE3_ERR_UNSUPPORTED;
     if (a->mask == nullptr) {
         if (a->parent == nullptr || a->Tq != a->Tk) return EAGLE3_ERR_ARG;
     }
@@ -875,7 +874,6 @@ Plan make_plan(const eagle3_tree_attn_args *a) {
     const long keys = lmax > 0 ? (lmax + KT - 1) / KT * KT : KT;
     pl.split_keys = (int)keys;
     pl.nsplit = 1;
-    pl.tree_split = 0;
     pl.ws_bytes = 0;
     return pl;
 }
@@ -915,7 +913,7 @@ extern "C" int eagle3_tree_attn(const eagle3_tree_attn_args *a, void *ws, size_t
         p.B = a->B; p.Tq = a->Tq; p.Tk = a->Tk; p.Hq = a->Hq; p.Hkv = a->Hkv; p.W = a->W; p.G = G;
         p.R = a->Tq * G; p.nrb = pl.nrb; p.Rpad = pl.nrb * ROWS_PER_WG; p.nsplit = pl.nsplit;
         p.split_keys = pl.split_keys; p.max_blocks = a->max_blocks; p.num_blocks = a->num_blocks;
-        p.tree_split = pl.tree_split;
+        p.nunits = a->B * a->Hkv * pl.nsplit;
         p.scale_log2 = a->scale * kLog2e;
         p.ws_o = nullptr; p.ws_ml = nullptr;
         if (pl.ws_bytes > 0) {
@@ -923,10 +921,12 @@ extern "C" int eagle3_tree_attn(const eagle3_tree_attn_args *a, void *ws, size_t
             p.ws_o = (float *)ws;
             p.ws_ml = (float *)((char *)ws + ((rows * DH * 4 + 255) & ~(size_t)255));
         }
-        dim3 grid(pl.nsplit * pl.nrb, a->Hkv, a->B);
-        // 8 waves of 32 rows cover the 256-row block (two row blocks per wave
-        // would share every fragment read, but 64 rows of Q, scores and output
-        // accumulators do not fit the register file)
+        // the row blocks of a unit go to one XCD (ids 8 apart): the grid is a
+        // whole number of 8-unit groups, surplus work-groups exit at once
+        const int grid = (p.nunits + 7) / 8 * 8 * pl.nrb;
+        // 8 waves of 32 rows: two waves per SIMD, 256 registers each (two row
+        // blocks per wave would share every fragment read, but 64 rows of Q,
+        // scores and output accumulators do not fit without spilling)
         tree_attn_bf16_kernel<8, 1><<<grid, 512, 0, st>>>(p);
         const bool fused_norm = a->norm_out && pl.nsplit > 1 && pl.nsplit <= CN_MAXS && a->Hq <= CN_MAXH;
         if (fused_norm)
