@@ -50,6 +50,7 @@ struct AttnParams {
     float *ws_ml;  // [B, Hkv, nsplit, Rpad, 2]
     int B, Tq, Tk, Hq, Hkv, W, G, R, Rpad, nrb, nsplit, split_keys, max_blocks, num_blocks;
     int nunits;      // B * Hkv * nsplit work units of nrb work-groups each
+    float zero;      // 0.0f, a value the compiler cannot fold (see attend_tile)
     float scale_log2;
 };
 
@@ -178,16 +179,17 @@ template <int RB>
 __device__ __forceinline__ void attend_tile(int kind, const unsigned char *tile, const u32x4_t (&qb)[RB][8],
                                             f32x16_t (&ot)[RB][4], float (&m_run)[RB], float (&l_run)[RB],
                                             int lr, int lh, int nvalid, const uint64_t (&mword)[RB],
-                                            float scale_log2) {
+                                            float scale_log2, float zero) {
+    // the score accumulators start as registers holding a zero the compiler
+    // cannot see: with a literal zero the first MFMA takes the inline-zero C
+    // operand, and its destination is then free to overlap the A operand
     f32x16_t st[RB][2];
 #pragma unroll
     for (int k = 0; k < RB; ++k)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) st[k][kb][r] = 0.f;
+            for (int r = 0; r < 16; ++r) st[k][kb][r] = zero;
     // QK step j: key block kb = j & 1, d-step s = j >> 1. Fragment reads run
     // QK_AHEAD steps ahead of the MFMAs; the scheduling barriers keep the
     // compiler from sinking each read next to its MFMA (which leaves the LDS
@@ -504,7 +506,8 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_bf16_kernel(AttnParams p) {
             for (int k = 0; k < RB; ++k) mword[k] = tt == 0 ? mw0[k] : mw1[k];
         }
         if (wave_active)
-            attend_tile<RB>(kind, buf + (it & 1) * TILE_BYTES, qb, ot, m_run, l_run, lr, lh, nvalid, mword, p.scale_log2);
+            attend_tile<RB>(kind, buf + (it & 1) * TILE_BYTES, qb, ot, m_run, l_run, lr, lh, nvalid, mword, p.scale_log2,
+                            p.zero);
         // the other buffer was last read before the previous barrier
         if (more) write_tile(it + 1, buf + ((it + 1) & 1) * TILE_BYTES);
         __syncthreads();
@@ -914,6 +917,7 @@ extern "C" int eagle3_tree_attn(const eagle3_tree_attn_args *a, void *ws, size_t
         p.R = a->Tq * G; p.nrb = pl.nrb; p.Rpad = pl.nrb * ROWS_PER_WG; p.nsplit = pl.nsplit;
         p.split_keys = pl.split_keys; p.max_blocks = a->max_blocks; p.num_blocks = a->num_blocks;
         p.nunits = a->B * a->Hkv * pl.nsplit;
+        p.zero = 0.f;
         p.scale_log2 = a->scale * kLog2e;
         p.ws_o = nullptr; p.ws_ml = nullptr;
         if (pl.ws_bytes > 0) {
