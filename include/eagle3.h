@@ -109,10 +109,15 @@ int eagle3_tree_mask(const int32_t *parent, int B, int T, int W,
  * Supported: bf16 with D = 128; fp32 with D = 64 or 128; block_size 16;
  * Tk <= 64 * W, W in {1, 2}; Hq % Hkv == 0. A query row that sees no key gets
  * out = 0 and lse = -inf. Slots of the cache past prefix_len are never read.
- * split_keys: must be 0 (any other value gives EAGLE3_ERR_UNSUPPORTED): one
- * work-group walks the whole prefix of its (sequence, KV head, block of 256
- * query rows); bf16 calls need max_blocks * block_size <= 16384. Results do
- * not depend on the call's batch composition.
+ * split_keys: prefixes are cut into splits of split_keys keys (a positive
+ * multiple of 64; EAGLE3_ERR_UNSUPPORTED otherwise), each attended by its own
+ * work-groups, and the partial results merged in split order. 0 = automatic:
+ * no split when the call has at least one (sequence, KV head, block of 256
+ * query rows) work-group per CU, else enough splits of at least 256 keys to
+ * cover the CUs, cut from max_blocks * block_size. Splits need the workspace
+ * eagle3_tree_attn_workspace() reports (0 without splits; the fp32 path never
+ * splits). For a given split_keys, results do not depend on the call's batch
+ * composition.
  * norm_out (nullable): the RMSNorm (gamma = 1, eps = norm_eps) of each output
  * row [Hq * D], as eagle3_rmsnorm on out would give (a second launch).
  * Validate mode: with status [B] int32 non-NULL, each sequence's status is

@@ -66,7 +66,9 @@ CASES = [
     (1, 16, 4, 4, [129], 0),             # MHA, small tree
     (2, 1, 8, 2, [17, 0], 0),            # root only
     (2, 100, 4, 1, [40, 90], 0),         # W = 2
-    (4, 61, 32, 8, [700, 1100, 64, 0], 64),  # split, too many work-groups for a tree split
+    (4, 61, 32, 8, [700, 1100, 64, 0], 64),  # explicit 64-key splits, some sequences unsplit
+    (2, 61, 64, 8, [2000, 900], 0),      # G = 8 (two row blocks) with automatic splits
+    (1, 61, 32, 8, [1500], 320),         # one sequence, splits of 320 keys (last one partial)
     # sequences are dealt to work-groups longest prefix first: more than 64
     # sequences (two ranking passes) with tied lengths, and more than 256
     # (batch order kept)
@@ -75,16 +77,10 @@ CASES = [
 ]
 
 
-SPLIT_OFF = ("prefix splits over work-groups are switched off (EAGLE3_ERR_UNSUPPORTED): the split path "
-             "gave sporadic wrong rows whose cause was not found")
-
-
 @pytest.mark.parametrize("case", range(len(CASES)))
 @pytest.mark.parametrize("mode", ["mask", "parent"])
 def test_bf16_parity(orc, lib, case, mode):
     B, T, Hq, Hkv, plen, split = CASES[case]
-    if split:
-        pytest.skip(SPLIT_OFF)
     parent, inp = make(100 + case, B, T, Hq, Hkv, plen)
     W = (T + 63) // 64
     mask, _ = orc.tree_mask(parent, W)
@@ -183,13 +179,11 @@ NORM_CASES = [
     (1, 32, 8, [1100], 4096),
     # one launch with several splits for some sequences and a single split for
     # others (prefix within one split, or empty): the merge-and-norm pass must
-    # keep the rows the attention pass wrote itself. 8 sequences x 8 KV heads
-    # x 6 splits exceed one work-group per CU, so the tree keys are not a split
-    # of their own there; with 4 sequences they are.
+    # keep the rows the attention pass wrote itself
     (8, 32, 8, [1100, 60, 0, 700, 256, 257, 5, 900], 256),
     (4, 32, 8, [1100, 60, 0, 700], 256),
-    # the automatic plan at 16 sequences: two prefix splits of 576 keys, no
-    # tree split; every prefix up to 576 keys is a single split
+    # the automatic plan at 16 sequences (128 work-groups without splits):
+    # two splits, so prefixes up to one split length stay a single split
     (16, 32, 8, [1100, 60, 0, 700, 256, 257, 5, 900, 1000, 30, 512, 577, 800, 1, 1024, 576], 0),
     # more than 32 splits: the merge and the norm run as two launches
     (2, 32, 8, [2200, 40], 64),
@@ -205,8 +199,6 @@ def test_norm_out(orc, lib, B, Hq, Hkv, plen, split, dtype):
     """The optional RMS-normalised copy of the output (the hidden row the LM
     head reads). It must equal RMSNorm of the attention output the same call
     wrote, and the oracle's RMSNorm of the oracle attention."""
-    if split:
-        pytest.skip(SPLIT_OFF)
     T = 61
     parent, inp = make(130, B, T, Hq, Hkv, plen, dtype=dtype)
     W = (T + 63) // 64

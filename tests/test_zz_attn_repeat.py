@@ -1,15 +1,12 @@
-"""Repeated split tree-attention calls on the same device buffers.
+"""Repeated tree-attention calls on the same device buffers.
 
 Three calls of the masked tree attention are enqueued back to back on one
-stream (no synchronisation between them), each into its own output, for
-batches whose prefixes are split across work-groups and merged. All three
-outputs must be bit-identical and within the parity tolerance of the oracle.
-
-This pattern has shown sporadic wrong rows (a few percent of calls), in
-both the mask and the parent[] mode, with the tree keys as a split of their
-own or not, and never without a split; the cause is not known. The test
-sits last in collection order so that a failure here leaves every other GPU
-test run and reported."""
+stream (no synchronisation between them), each into its own output, with and
+without prefixes split across work-groups and merged, the calls sharing one
+workspace. All three outputs must be bit-identical and within the parity
+tolerance of the oracle: a race between the calls, or inside one, shows as
+calls that differ. The test sits last in collection order so that a failure
+here leaves every other GPU test run and reported."""
 import numpy as np
 import pytest
 import torch
@@ -37,9 +34,6 @@ def lib():
 @pytest.mark.parametrize("case", range(len(CASES)))
 def test_back_to_back_calls_identical(orc, lib, case):
     B, T, Hq, Hkv, plen, split = CASES[case]
-    if split:
-        pytest.skip("prefix splits over work-groups are switched off (EAGLE3_ERR_UNSUPPORTED): the split path "
-                    "gave sporadic wrong rows whose cause was not found")
     rng = np.random.default_rng(7000 + case)
     parent = np.stack([synth.topk_tree(rng, T - 1, 7, 10) for _ in range(B)])
     inp = synth.attn_inputs(700 + case, 0, B, T, T, Hq, Hkv, 128, plen, "bf16")

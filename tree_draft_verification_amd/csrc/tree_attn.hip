@@ -29,6 +29,7 @@
 // the scores and over dimensions for P.V; for small models.
 #include "common.h"
 
+#include <algorithm>
 #include <type_traits>
 
 namespace {
@@ -38,6 +39,7 @@ constexpr int DH = 128;      // head dim of the MFMA path
 constexpr int ROWS_PER_WG = 256;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr long MIN_SPLIT_KEYS = 256;  // shortest automatic prefix split
 
 struct AttnParams {
     const uint16_t *q, *k_tree, *v_tree, *k_cache, *v_cache;
@@ -46,8 +48,8 @@ struct AttnParams {
     const int32_t *parent;
     uint16_t *out;
     float *lse;
-    float *ws_o;   // [B, Hkv, nsplit, Rpad, D]
-    float *ws_ml;  // [B, Hkv, nsplit, Rpad, 2]
+    uint16_t *ws_o;  // [B, Hkv, nsplit, Rpad, D] fp16: normalised O of each split
+    float *ws_ml;    // [B, Hkv, nsplit, Rpad, 2]: running max (log2 units) and sum
     int B, Tq, Tk, Hq, Hkv, W, G, R, Rpad, nrb, nsplit, split_keys, max_blocks, num_blocks;
     int nunits;      // B * Hkv * nsplit work units of nrb work-groups each
     float zero;      // 0.0f, a value the compiler cannot fold (see attend_tile)
@@ -535,16 +537,19 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_bf16_kernel(AttnParams p) {
                 p.lse[((size_t)b * p.Tq + t[k]) * p.Hq + hq[k]] =
                     l_tot > 0.f ? (m_run[k] + log2f(l_tot)) * kLn2 : -INFINITY;
         } else {
+            // the split's normalised O in fp16: a convex combination of V
+            // rows, so within V's range, kept to 11 significant bits
             const size_t prow = (((size_t)b * p.Hkv + kvh) * p.nsplit + split) * p.Rpad + row[k];
-            float *orow = p.ws_o + prow * DH;
+            uint16_t *orow = p.ws_o + prow * DH;
 #pragma unroll
             for (int db = 0; db < 4; ++db)
 #pragma unroll
                 for (int g4 = 0; g4 < 4; ++g4) {
                     const int d = db * 32 + 8 * g4 + 4 * lh;
-                    f32x4_t o = {ot[k][db][4 * g4] * inv, ot[k][db][4 * g4 + 1] * inv, ot[k][db][4 * g4 + 2] * inv,
-                                 ot[k][db][4 * g4 + 3] * inv};
-                    *reinterpret_cast<f32x4_t *>(orow + d) = o;
+                    u32x2_t o;
+                    o[0] = pack_f16x2(ot[k][db][4 * g4] * inv, ot[k][db][4 * g4 + 1] * inv);
+                    o[1] = pack_f16x2(ot[k][db][4 * g4 + 2] * inv, ot[k][db][4 * g4 + 3] * inv);
+                    *reinterpret_cast<u32x2_t *>(orow + d) = o;
                 }
             if (lh == 0) {
                 p.ws_ml[prow * 2] = m_run[k];
@@ -571,7 +576,7 @@ __global__ __launch_bounds__(128) void tree_attn_combine_kernel(AttnParams p) {
         const size_t prow = (base + s) * p.Rpad + row;
         const float ms = p.ws_ml[prow * 2], ls = p.ws_ml[prow * 2 + 1];
         const float wgt = (ms == -INFINITY) ? 0.f : ls * exp2f(ms - M);
-        acc += wgt * p.ws_o[prow * DH + d];
+        acc += wgt * (float)__builtin_bit_cast(_Float16, p.ws_o[prow * DH + d]);
         den += wgt;
     }
     const float o = den > 0.f ? acc / den : 0.f;
@@ -656,21 +661,19 @@ __global__ __launch_bounds__(CN_NT) void tree_attn_combine_norm_kernel(AttnParam
             const size_t base = ((size_t)b * p.Hkv + kvh) * p.nsplit;
             float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
             for (int s0 = 0; s0 < nsplit_b; s0 += CN_BATCH) {
-                f32x4_t a[CN_BATCH], c4[CN_BATCH];
+                u32x4_t a[CN_BATCH];
 #pragma unroll
                 for (int u = 0; u < CN_BATCH; ++u) {
-                    if (s0 + u < nsplit_b) {  // uniform
-                        const float *src = p.ws_o + ((base + s0 + u) * p.Rpad + row) * DH + d;
-                        a[u] = *reinterpret_cast<const f32x4_t *>(src);
-                        c4[u] = *reinterpret_cast<const f32x4_t *>(src + 4);
-                    }
+                    if (s0 + u < nsplit_b)  // uniform
+                        a[u] = *reinterpret_cast<const u32x4_t *>(p.ws_o + ((base + s0 + u) * p.Rpad + row) * DH + d);
                 }
 #pragma unroll
                 for (int u = 0; u < CN_BATCH; ++u) {
                     if (s0 + u < nsplit_b) {
                         const float w = wgt[hq][s0 + u];
+                        const f16x8_t h = __builtin_bit_cast(f16x8_t, a[u]);
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) { o[i] += w * a[u][i]; o[4 + i] += w * c4[u][i]; }
+                        for (int i = 0; i < 8; ++i) o[i] += w * (float)h[i];
                     }
                 }
             }
@@ -860,7 +863,7 @@ int check_args(const eagle3_tree_attn_args *a) {
     // splitting a prefix over work-groups is switched off (split_keys must be
     // 0), because the split path gave sporadic wrong rows whose cause was not
     // found; block ids of one work-group must fit its LDS table
-    if (a->split_keys != 0) return EAGLE3_ERR_UNSUPPORTED;
+    if (a->split_keys < 0 || a->split_keys % KT != 0) return EAGLE3_ERR_UNSUPPORTED;
     if (a->mask == nullptr) {
         if (a->parent == nullptr || a->Tq != a->Tk) return EAGLE3_ERR_ARG;
     }
@@ -872,12 +875,28 @@ Plan make_plan(const eagle3_tree_attn_args *a) {
     const int G = a->Hq / a->Hkv;
     const int R = a->Tq * G;
     pl.nrb = (R + ROWS_PER_WG - 1) / ROWS_PER_WG;
-    // a single split covering the largest prefix the block table can address
+    // keys a prefix can have: the block table's capacity (the lengths
+    // themselves are device data)
     const long lmax = (long)a->max_blocks * a->block_size;
-    const long keys = lmax > 0 ? (lmax + KT - 1) / KT * KT : KT;
-    pl.split_keys = (int)keys;
-    pl.nsplit = 1;
+    long C = a->split_keys;
+    if (C == 0) {
+        // automatic: split when there are fewer (sequence, KV head, row
+        // block) work-groups than CUs, into enough splits to cover the CUs,
+        // none shorter than MIN_SPLIT_KEYS
+        const long base = (long)a->B * a->Hkv * pl.nrb;
+        long S = 1;
+        if (a->dtype == EAGLE3_BF16 && base > 0 && base < e3_cu_count())
+            S = std::min((e3_cu_count() + base - 1) / base, std::max(1L, lmax / MIN_SPLIT_KEYS));
+        C = (lmax + S - 1) / S;
+    }
+    C = std::max<long>(KT, (C + KT - 1) / KT * KT);
+    pl.split_keys = (int)std::min<long>(C, 1L << 30);
+    pl.nsplit = lmax > 0 ? (int)((lmax + pl.split_keys - 1) / pl.split_keys) : 1;
     pl.ws_bytes = 0;
+    if (a->dtype == EAGLE3_BF16 && pl.nsplit > 1) {
+        const size_t rows = (size_t)a->B * a->Hkv * pl.nsplit * (size_t)pl.nrb * ROWS_PER_WG;
+        pl.ws_bytes = ((rows * DH * 2 + 255) & ~(size_t)255) + rows * 8;
+    }
     return pl;
 }
 
@@ -922,8 +941,8 @@ extern "C" int eagle3_tree_attn(const eagle3_tree_attn_args *a, void *ws, size_t
         p.ws_o = nullptr; p.ws_ml = nullptr;
         if (pl.ws_bytes > 0) {
             const size_t rows = (size_t)a->B * a->Hkv * pl.nsplit * (size_t)pl.nrb * ROWS_PER_WG;
-            p.ws_o = (float *)ws;
-            p.ws_ml = (float *)((char *)ws + ((rows * DH * 4 + 255) & ~(size_t)255));
+            p.ws_o = (uint16_t *)ws;
+            p.ws_ml = (float *)((char *)ws + ((rows * DH * 2 + 255) & ~(size_t)255));
         }
         // the row blocks of a unit go to one XCD (ids 8 apart): the grid is a
         // whole number of 8-unit groups, surplus work-groups exit at once
