@@ -75,27 +75,36 @@ __device__ __forceinline__ int splits_of(int L, int split_keys) {
 // ties by lower index: the long sequences start in the first pass over the
 // CUs and the short ones fill in behind them (longest-processing-time-first
 // list order), instead of the batch order, which can leave a CU with two
-// long sequences. Every wave ranks the sequences by counting; slot r takes
-// the sequence of rank r. Past LPT_MAX_B sequences the batch order is kept.
+// long sequences. The work-group puts the clamped lengths in LDS, thread j
+// ranks sequence j by counting, and slot r takes the sequence of rank r.
+// Past LPT_MAX_B sequences the batch order is kept.
 constexpr int LPT_MAX_B = 256;
-__device__ __forceinline__ int seq_of_slot(const int32_t *prefix_len, int B, int r, int max_blocks, int num_blocks) {
+struct LptShared {
+    int len[LPT_MAX_B];
+    int sel;
+};
+template <int NT>
+__device__ __forceinline__ int seq_of_slot(LptShared &sh, const int32_t *prefix_len, int B, int r, int max_blocks,
+                                           int num_blocks) {
+    static_assert(NT >= LPT_MAX_B, "one ranking thread per sequence");
     if (B > LPT_MAX_B) return r;
-    const int lane = threadIdx.x & 63;
-    for (int j0 = 0; j0 < B; j0 += 64) {
-        const int j = j0 + lane;
-        int rank = -1;
-        if (j < B) {
-            const int Lj = clamped_len(prefix_len, j, max_blocks, 16, num_blocks);
-            rank = 0;
-            for (int k = 0; k < B; ++k) {
-                const int Lk = clamped_len(prefix_len, k, max_blocks, 16, num_blocks);
-                rank += (Lk > Lj || (Lk == Lj && k < j)) ? 1 : 0;
-            }
+    const int j = threadIdx.x;
+    const int Lj = j < B ? clamped_len(prefix_len, j, max_blocks, 16, num_blocks) : -1;
+    if (j < LPT_MAX_B) sh.len[j] = Lj;  // -1 past B: never ranked ahead
+    __syncthreads();
+    if (j < B) {
+        int rank = 0;
+        for (int k0 = 0; k0 < B; k0 += 4) {
+            const int4 l4 = *reinterpret_cast<const int4 *>(&sh.len[k0]);  // same address in every lane
+            rank += (l4.x > Lj || (l4.x == Lj && k0 < j)) ? 1 : 0;
+            rank += (l4.y > Lj || (l4.y == Lj && k0 + 1 < j)) ? 1 : 0;
+            rank += (l4.z > Lj || (l4.z == Lj && k0 + 2 < j)) ? 1 : 0;
+            rank += (l4.w > Lj || (l4.w == Lj && k0 + 3 < j)) ? 1 : 0;
         }
-        const uint64_t hit = __ballot(rank == r);
-        if (hit) return j0 + __ffsll((unsigned long long)hit) - 1;
+        if (rank == r) sh.sel = j;
     }
-    return r;  // not reached: the ranks are a permutation of 0..B-1
+    __syncthreads();
+    return sh.sel;
 }
 
 __device__ __forceinline__ int clamped_block(const int32_t *btab, int j, int num_blocks) {
@@ -126,12 +135,15 @@ enum TileKind { TILE_FULL = 0, TILE_PARTIAL = 1, TILE_TREE = 2 };
 // stay below 256, harmless in fp32), which makes O rescaling rare.
 constexpr float kLazyMax = 8.f;
 
-constexpr int TILE_BYTES = 2 * KT * DH * 2;  // K tile + V tile, 16 KB each
-constexpr int VOFF = KT * DH * 2;          // V tile offset inside a buffer
-
-// 16-byte column swizzle of K rows (a tile row is one key, 256 B): K reads of
-// 16 consecutive rows then hit 16 distinct bank groups.
-__device__ __forceinline__ int kswz(int row) { return row & 15; }
+// K rows (one key, 256 B of d) are padded to KROW = 272 bytes: a K fragment
+// read takes 32 consecutive rows at one column, and the 16-byte shift per row
+// spreads each 8 lanes over 8 distinct bank groups. The padding (rather than a
+// lane-dependent column swizzle) keeps the column offset of every QK step a
+// constant, so the reads need one address register.
+constexpr int KROW = DH * 2 + 16;
+constexpr int VOFF = KT * KROW;            // V tile offset inside a buffer
+constexpr int TILE_BYTES = VOFF + KT * DH * 2;  // K tile (17 KB) + V tile (16 KB)
+constexpr int NBUF = 2;                    // tile buffers in LDS
 // V rows are (block, d) pairs of 32 B = 16 slots; the two 16-byte halves are
 // swapped on every other group of 8 rows, halving bank conflicts of PV reads.
 __device__ __forceinline__ int vswz(int d) { return (d >> 3) & 1; }
@@ -158,14 +170,6 @@ __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
 }
 
-// One 64-key tile for one wave and its RB blocks of 32 query rows: S^T =
-// K.Q^T, online softmax, O^T += V^T.P^T. Every K / V fragment read from LDS
-// feeds the MFMAs of all RB row blocks. kind is wave-uniform.
-//   QK step (s, kb): K rows 32 kb + lr, 16-byte column 2 s + lh (swizzled),
-//   i.e. keys of block kb and d = 16 s + 8 lh .. +7; the Q^T operand holds
-//   the same d of this lane's query row.
-//   PV step (ks, db): V row (16-key block ks, d = 32 db + lr), half lh: keys
-//   16 ks + 8 lh .. +7; the P^T operand holds this lane's P for those keys.
 // compile-time unrolled loop: f(std::integral_constant<int, i>) for i in [I, N)
 template <int I, int N, typename F>
 __device__ __forceinline__ void sfor(F &&f) {
@@ -175,32 +179,40 @@ __device__ __forceinline__ void sfor(F &&f) {
     }
 }
 
-constexpr int QK_AHEAD = 4;  // K fragment reads in flight ahead of the MFMAs
+constexpr int QK_AHEAD = 4;  // fragment reads in flight ahead of the MFMAs
 
+// A 64-key tile for one wave and its RB blocks of 32 query rows runs in three
+// phases: qk_tile (S^T = K.Q^T), softmax_tile (online softmax, P to fp16)
+// and pv_tile (O^T += V^T.P^T). Every K / V fragment read from LDS feeds the
+// MFMAs of all RB row blocks.
+//   QK step (s, kb): K rows 32 kb + lr, 16-byte column 2 s + lh,
+//   i.e. keys of block kb and d = 16 s + 8 lh .. +7; the Q^T operand holds
+//   the same d of this lane's query row.
+//   PV step (ks, db): V row (16-key block ks, d = 32 db + lr), half lh: keys
+//   16 ks + 8 lh .. +7; the P^T operand holds this lane's P for those keys.
+// Register r of score block kb holds key 32 kb + 16 (r / 8) + 8 lh + (r % 8).
+
+// QK step j: key block kb = j & 1, d-step s = j >> 1. Fragment reads run
+// QK_AHEAD steps ahead of the MFMAs; the scheduling barriers keep the
+// compiler from sinking each read next to its MFMA (which leaves the LDS
+// latency exposed at every step). The score accumulators start as registers
+// holding a zero the compiler cannot see: with a literal zero the first MFMA
+// takes the inline-zero C operand, and its destination is then free to
+// overlap the A operand.
 template <int RB>
-__device__ __forceinline__ void attend_tile(int kind, const unsigned char *tile, const u32x4_t (&qb)[RB][8],
-                                            f32x16_t (&ot)[RB][4], float (&m_run)[RB], float (&l_run)[RB],
-                                            int lr, int lh, int nvalid, const uint64_t (&mword)[RB],
-                                            float scale_log2, float zero) {
-    // the score accumulators start as registers holding a zero the compiler
-    // cannot see: with a literal zero the first MFMA takes the inline-zero C
-    // operand, and its destination is then free to overlap the A operand
-    f32x16_t st[RB][2];
+__device__ __forceinline__ void qk_tile(const unsigned char *tile, const u32x4_t (&qb)[RB][8], f32x16_t (&st)[RB][2],
+                                        int lr, int lh, float zero) {
 #pragma unroll
     for (int k = 0; k < RB; ++k)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) st[k][kb][r] = zero;
-    // QK step j: key block kb = j & 1, d-step s = j >> 1. Fragment reads run
-    // QK_AHEAD steps ahead of the MFMAs; the scheduling barriers keep the
-    // compiler from sinking each read next to its MFMA (which leaves the LDS
-    // latency exposed at every step)
-    const unsigned char *krow = tile + lr * 256;
+    const unsigned char *krow = tile + lr * KROW + lh * 16;
     u32x4_t fk[16];
     auto kread = [&](auto J) {
         constexpr int j = J, kb = j & 1, s = j >> 1;
-        fk[j] = *reinterpret_cast<const u32x4_t *>(krow + kb * 8192 + (((2 * s + lh) ^ kswz(lr)) << 4));
+        fk[j] = *reinterpret_cast<const u32x4_t *>(krow + kb * 32 * KROW + s * 32);
     };
     sfor<0, QK_AHEAD>(kread);
     sfor<0, 16>([&](auto J) {
@@ -213,9 +225,20 @@ __device__ __forceinline__ void attend_tile(int kind, const unsigned char *tile,
                                                                 0, 0);
         __builtin_amdgcn_sched_barrier(0);
     });
+}
+
+// Online softmax of one tile's scores into fp16 P: pp[k][ks] holds this
+// lane's P for keys 16 ks + 8 lh .. +7 (the PV operand). P . V runs on the
+// fp16 MFMA: V was converted from bf16 when its tile was staged (exact in
+// fp16's range) and P (at most 2^8 with the lazy max) is rounded to fp16,
+// 11 significant bits against bf16's 8; the running sum adds P in fp32.
+// kind is wave-uniform.
+template <int RB>
+__device__ __forceinline__ void softmax_tile(int kind, int nvalid, const uint64_t (&mword)[RB], f32x16_t (&st)[RB][2],
+                                             u32x4_t (&pp)[RB][4], f32x16_t (&ot)[RB][4], float (&m_run)[RB],
+                                             float (&l_run)[RB], int lh, float scale_log2) {
 #pragma unroll
     for (int k = 0; k < RB; ++k) {
-        // register r of block kb holds key 32 kb + 16 (r / 8) + 8 lh + (r % 8)
         if (kind != TILE_FULL) {
             // visible keys of the tile (bit kk); each group of 8 registers
             // holds 8 consecutive keys, whose bits are one byte of the word
@@ -255,20 +278,24 @@ __device__ __forceinline__ void attend_tile(int kind, const unsigned char *tile,
         const float msub = (m_run[k] == -INFINITY) ? 0.f : m_run[k];
         float psum = 0.f;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float pv = __builtin_amdgcn_exp2f(fmaf(st[k][kb][r], scale_log2, -msub));
-                st[k][kb][r] = pv;
-                psum += pv;
+            for (int e = 0; e < 4; ++e) {
+                const int kb = ks >> 1, r = 8 * (ks & 1) + 2 * e;
+                const float p0 = __builtin_amdgcn_exp2f(fmaf(st[k][kb][r], scale_log2, -msub));
+                const float p1 = __builtin_amdgcn_exp2f(fmaf(st[k][kb][r + 1], scale_log2, -msub));
+                pp[k][ks][e] = pack_f16x2(p0, p1);
+                psum += p0 + p1;
             }
         l_run[k] += psum;
     }
-    // P . V runs on the fp16 MFMA: V was converted from bf16 when its tile
-    // was staged (exact in fp16's range) and P (at most 2^8 with the lazy
-    // max) is rounded to fp16, 11 significant bits against bf16's 8.
-    // PV step j: 16-key step ks = j >> 2, d block db = j & 3; reads run
-    // QK_AHEAD steps ahead as in the QK loop
+}
+
+// PV step j: 16-key step ks = j >> 2, d block db = j & 3; reads run QK_AHEAD
+// steps ahead as in qk_tile.
+template <int RB>
+__device__ __forceinline__ void pv_tile(const unsigned char *tile, const u32x4_t (&pp)[RB][4], f32x16_t (&ot)[RB][4],
+                                        int lr, int lh) {
     const unsigned char *vrow = tile + VOFF + lr * 32 + ((lh ^ vswz(lr)) << 4);
     u32x4_t fv[16];
     auto vread = [&](auto J) {
@@ -276,21 +303,14 @@ __device__ __forceinline__ void attend_tile(int kind, const unsigned char *tile,
         fv[j] = *reinterpret_cast<const u32x4_t *>(vrow + ks * 4096 + db * 1024);
     };
     sfor<0, QK_AHEAD>(vread);
-    u32x4_t ph[RB];
     sfor<0, 16>([&](auto J) {
         constexpr int j = J, ks = j >> 2, db = j & 3;
-        if constexpr (db == 0) {
-            constexpr int kb = ks >> 1, r0 = 8 * (ks & 1);
-#pragma unroll
-            for (int k = 0; k < RB; ++k)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) ph[k][e] = pack_f16x2(st[k][kb][r0 + 2 * e], st[k][kb][r0 + 2 * e + 1]);
-        }
         if constexpr (j + QK_AHEAD < 16) vread(std::integral_constant<int, j + QK_AHEAD>{});
         const f16x8_t a = __builtin_bit_cast(f16x8_t, fv[j]);
 #pragma unroll
         for (int k = 0; k < RB; ++k)
-            ot[k][db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, __builtin_bit_cast(f16x8_t, ph[k]), ot[k][db], 0, 0, 0);
+            ot[k][db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, __builtin_bit_cast(f16x8_t, pp[k][ks]), ot[k][db], 0,
+                                                               0, 0);
         __builtin_amdgcn_sched_barrier(0);
     });
 }
@@ -323,13 +343,15 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_bf16_kernel(AttnParams p) {
     constexpr int NT = NW * 64;
     constexpr int NCH = KT * DH / 8 / NT;  // 16-byte chunks of K (and of V) per thread and tile
     static_assert(NCH * NT * 8 == KT * DH && NT % 256 == 0, "whole 4 KB cache blocks per 256 threads");
-    __shared__ __attribute__((aligned(1024))) unsigned char buf[2 * TILE_BYTES];
+    __shared__ __attribute__((aligned(1024))) unsigned char buf[NBUF * TILE_BYTES];
 
     const WorkUnit wu = work_unit(blockIdx.x, p.nrb);
     if (wu.unit >= p.nunits) return;
     const int split = wu.unit % p.nsplit, kvh = (wu.unit / p.nsplit) % p.Hkv, slot = wu.unit / (p.nsplit * p.Hkv);
     const int rblk = wu.rblk;
-    const int b = __builtin_amdgcn_readfirstlane(seq_of_slot(p.prefix_len, p.B, slot, p.max_blocks, p.num_blocks));
+    __shared__ __attribute__((aligned(16))) LptShared lpt;
+    const int b =
+        __builtin_amdgcn_readfirstlane(seq_of_slot<NT>(lpt, p.prefix_len, p.B, slot, p.max_blocks, p.num_blocks));
     const int L = clamped_len(p.prefix_len, b, p.max_blocks, 16, p.num_blocks);
     const int C = p.split_keys;
     const int nsplit_b = splits_of(L, C);
@@ -353,31 +375,6 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_bf16_kernel(AttnParams p) {
         hq[k] = kvh * p.G + (row_ok[k] ? row[k] % p.G : 0);
     }
     const bool wave_active = rblk * ROWS_PER_WG + wave * RB * 32 < p.R;
-
-    // Q^T operand: d = 16 s + 8 lh + i
-    u32x4_t qb[RB][8];
-    uint64_t mw0[RB], mw1[RB];
-#pragma unroll
-    for (int k = 0; k < RB; ++k) {
-        const uint16_t *qrow = p.q + (((size_t)b * p.Tq + t[k]) * p.Hq + hq[k]) * DH + 8 * lh;
-#pragma unroll
-        for (int s = 0; s < 8; ++s)
-            qb[k][s] = row_ok[k] ? *reinterpret_cast<const u32x4_t *>(qrow + 16 * s) : u32x4_t{0u, 0u, 0u, 0u};
-        mw0[k] = 0; mw1[k] = 0;
-        if (last && row_ok[k]) query_mask(p, b, t[k], mw0[k], mw1[k]);
-    }
-
-    f32x16_t ot[RB][4];
-    float m_run[RB], l_run[RB];
-#pragma unroll
-    for (int k = 0; k < RB; ++k) {
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) ot[k][db][r] = 0.f;
-        m_run[k] = -INFINITY;
-        l_run[k] = 0.f;
-    }
 
     // Staging. Chunk i of a thread is 16-key block jb = i NT / 256 + tid / 256
     // of the tile and the w-th 16 bytes of it, w = tid % 256: for K the key
@@ -432,7 +429,7 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_bf16_kernel(AttnParams p) {
         for (int i = 0; i < NCH; ++i) {
             const int jb = i * (NT / 256) + jb_t;
             const int r = 16 * jb + row_key(w >> 4);  // the row holding key 16 jb + w / 16
-            *reinterpret_cast<u32x4_t *>(dst + r * 256 + (((w & 15) ^ kswz(r)) << 4)) = sk[i];
+            *reinterpret_cast<u32x4_t *>(dst + r * KROW + (w & 15) * 16) = sk[i];
         }
         if (it < npre) {
             const int nval = min(KT, k_end - (k_begin + it * KT));
@@ -476,43 +473,76 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_bf16_kernel(AttnParams p) {
         }
     };
 
-    // q and the mask words have landed before the loop: otherwise the wait
-    // for them, placed inside the loop, would also wait for the staging
+    // Prologue: the block ids of tile 0 go out first, then q and the mask
+    // words, then tile 0 itself (two memory round trips in all)
+    fetch_ids(0);
+    // Q^T operand: d = 16 s + 8 lh + i
+    u32x4_t qb[RB][8];
+    uint64_t mw0[RB], mw1[RB];
+#pragma unroll
+    for (int k = 0; k < RB; ++k) {
+        const uint16_t *qrow = p.q + (((size_t)b * p.Tq + t[k]) * p.Hq + hq[k]) * DH + 8 * lh;
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+            qb[k][s] = row_ok[k] ? *reinterpret_cast<const u32x4_t *>(qrow + 16 * s) : u32x4_t{0u, 0u, 0u, 0u};
+        mw0[k] = 0; mw1[k] = 0;
+        if (last && row_ok[k]) query_mask(p, b, t[k], mw0[k], mw1[k]);
+    }
+
+    f32x16_t ot[RB][4];
+    float m_run[RB], l_run[RB];
+#pragma unroll
+    for (int k = 0; k < RB; ++k) {
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) ot[k][db][r] = 0.f;
+        m_run[k] = -INFINITY;
+        l_run[k] = 0.f;
+    }
+
+    if (ntiles > 0) load_tile(0);
+    fetch_ids(1);
+    // everything above has landed before the loop: otherwise a wait for q or
+    // the mask words, placed inside the loop, would also wait for the staging
     // loads of the next tile
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt and lgkmcnt not waited
-    if (ntiles > 0) {
-        fetch_ids(0);
-        load_tile(0);
-        fetch_ids(1);
-        write_tile(0, buf);
-    }
+    if (ntiles > 0) write_tile(0, buf);
     __syncthreads();
+    if (ntiles > 1) load_tile(1);
+    fetch_ids(2);
+
+    // Every wave attends tile it (QK, softmax, PV from buffer it % 2), then
+    // writes its share of tile it+1 (loaded since the previous barrier) into
+    // the other buffer, whose last readers finished before that barrier, and
+    // meets the barrier; the loads of tile it+2 go out right after it.
+    f32x16_t st[RB][2];
+    u32x4_t pp[RB][4];
     for (int it = 0; it < ntiles; ++it) {
-        const bool more = it + 1 < ntiles;
-        if (more) {
-            load_tile(it + 1);
-            fetch_ids(it + 2);
-        }
-        int kind, nvalid;
-        uint64_t mword[RB];
-        if (it < npre) {
-            nvalid = k_end - (k_begin + it * KT);
-            kind = nvalid >= KT ? TILE_FULL : TILE_PARTIAL;
+        const unsigned char *cur = buf + (it % NBUF) * TILE_BYTES;
+        if (wave_active) {
+            int kind, nvalid;
+            uint64_t mword[RB];
+            if (it < npre) {
+                nvalid = k_end - (k_begin + it * KT);
+                kind = nvalid >= KT ? TILE_FULL : TILE_PARTIAL;
 #pragma unroll
-            for (int k = 0; k < RB; ++k) mword[k] = 0;
-        } else {
-            const int tt = it - npre;
-            nvalid = p.Tk - tt * KT;
-            kind = TILE_TREE;
+                for (int k = 0; k < RB; ++k) mword[k] = 0;
+            } else {
+                const int tt = it - npre;
+                nvalid = p.Tk - tt * KT;
+                kind = TILE_TREE;
 #pragma unroll
-            for (int k = 0; k < RB; ++k) mword[k] = tt == 0 ? mw0[k] : mw1[k];
+                for (int k = 0; k < RB; ++k) mword[k] = tt == 0 ? mw0[k] : mw1[k];
+            }
+            qk_tile<RB>(cur, qb, st, lr, lh, p.zero);
+            softmax_tile<RB>(kind, nvalid, mword, st, pp, ot, m_run, l_run, lh, p.scale_log2);
+            pv_tile<RB>(cur, pp, ot, lr, lh);
         }
-        if (wave_active)
-            attend_tile<RB>(kind, buf + (it & 1) * TILE_BYTES, qb, ot, m_run, l_run, lr, lh, nvalid, mword, p.scale_log2,
-                            p.zero);
-        // the other buffer was last read before the previous barrier
-        if (more) write_tile(it + 1, buf + ((it + 1) & 1) * TILE_BYTES);
+        if (it + 1 < ntiles) write_tile(it + 1, buf + ((it + 1) % NBUF) * TILE_BYTES);
         __syncthreads();
+        if (it + 2 < ntiles) load_tile(it + 2);
+        fetch_ids(it + 3);
     }
 
 #pragma unroll
