@@ -140,10 +140,10 @@ def test_tree_attn_errors(lib):
     assert f(ctypes.byref(args(split_keys=100)), None, 0, None) == -2  # not a multiple of 64 keys
     assert f(ctypes.byref(args(split_keys=-64)), None, 0, None) == -2
     # one sequence x 8 KV heads is 8 work-groups: split automatically into 4
-    # splits of 256 keys (1024-key table), partials in fp16 + (max, sum)
+    # splits of 256 keys (1024-key table), partials in fp32 + (max, sum)
     rows = 1 * 8 * 4 * 256
-    assert wsq(ctypes.byref(args())) == rows * 128 * 2 + rows * 8
-    assert wsq(ctypes.byref(args(split_keys=512))) == (rows // 2) * 128 * 2 + (rows // 2) * 8
+    assert wsq(ctypes.byref(args())) == rows * 128 * 4 + rows * 8
+    assert wsq(ctypes.byref(args(split_keys=512))) == (rows // 2) * 128 * 4 + (rows // 2) * 8
     assert wsq(ctypes.byref(args(split_keys=1024))) == 0              # one split: no partials
     assert wsq(ctypes.byref(args(B=64))) == 0                         # 512 work-groups: no split
 

@@ -19,9 +19,8 @@
 //     refreshed running max (O is rescaled only when the max grows by more
 //     than 2^8). K rows sit in LDS in a permuted key order so that each lane's
 //     8 scores per 16-key step are consecutive keys and the V operand is one
-//     read. O^T += V^T . P^T on the fp16 MFMA: V tiles are converted from
-//     bf16 to fp16 when staged (exact for |v| in [2^-14, 65504]; larger
-//     values saturate), P is rounded to fp16 (11 significant bits).
+//     read. O^T += V^T . P^T by MFMA with P split into bf16 hi + lo parts, so
+//     P keeps ~16 significant bits.
 //   - The work-group holding the end of a prefix also processes the tree keys
 //     under the ancestor mask. Prefix splits over work-groups write partials
 //     (normalised O, max, sum) that a second kernel merges in split order.
@@ -48,7 +47,7 @@ struct AttnParams {
     const int32_t *parent;
     uint16_t *out;
     float *lse;
-    uint16_t *ws_o;  // [B, Hkv, nsplit, Rpad, D] fp16: normalised O of each split
+    float *ws_o;     // [B, Hkv, nsplit, Rpad, D]: normalised O of each split
     float *ws_ml;    // [B, Hkv, nsplit, Rpad, 2]: running max (log2 units) and sum
     int B, Tq, Tk, Hq, Hkv, W, G, R, Rpad, nrb, nsplit, split_keys, max_blocks, num_blocks;
     int nunits;      // B * Hkv * nsplit work units of nrb work-groups each
@@ -153,23 +152,6 @@ __device__ __forceinline__ int vswz(int d) { return (d >> 3) & 1; }
 // is one 16-byte half of a V row, so the PV operand is a single LDS read.
 __device__ __forceinline__ int row_key(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
-typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8_t;
-typedef __attribute__((__vector_size__(2 * sizeof(_Float16)))) _Float16 f16x2_t;
-
-// Two bf16 values (low half first) to two fp16 values. Exact for magnitudes
-// in [2^-14, 65504]; smaller ones keep 10 bits of absolute precision below
-// 2^-14 (an error under 3e-8), larger ones saturate at 65504 (round toward
-// zero never overflows to infinity).
-__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
-    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(__uint_as_float(w << 16),
-                                                                   __uint_as_float(w & 0xffff0000u)));
-}
-// Two fp32 values to two fp16 values, round to nearest even.
-__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
-    const f32x2_t v = {lo, hi};
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
-}
-
 // compile-time unrolled loop: f(std::integral_constant<int, i>) for i in [I, N)
 template <int I, int N, typename F>
 __device__ __forceinline__ void sfor(F &&f) {
@@ -182,7 +164,7 @@ __device__ __forceinline__ void sfor(F &&f) {
 constexpr int QK_AHEAD = 4;  // fragment reads in flight ahead of the MFMAs
 
 // A 64-key tile for one wave and its RB blocks of 32 query rows runs in three
-// phases: qk_tile (S^T = K.Q^T), softmax_tile (online softmax, P to fp16)
+// phases: qk_tile (S^T = K.Q^T), softmax_tile (online softmax)
 // and pv_tile (O^T += V^T.P^T). Every K / V fragment read from LDS feeds the
 // MFMAs of all RB row blocks.
 //   QK step (s, kb): K rows 32 kb + lr, 16-byte column 2 s + lh,
@@ -227,15 +209,11 @@ __device__ __forceinline__ void qk_tile(const unsigned char *tile, const u32x4_t
     });
 }
 
-// Online softmax of one tile's scores into fp16 P: pp[k][ks] holds this
-// lane's P for keys 16 ks + 8 lh .. +7 (the PV operand). P . V runs on the
-// fp16 MFMA: V was converted from bf16 when its tile was staged (exact in
-// fp16's range) and P (at most 2^8 with the lazy max) is rounded to fp16,
-// 11 significant bits against bf16's 8; the running sum adds P in fp32.
+// Online softmax of one tile's scores, in place: st then holds P (fp32).
 // kind is wave-uniform.
 template <int RB>
 __device__ __forceinline__ void softmax_tile(int kind, int nvalid, const uint64_t (&mword)[RB], f32x16_t (&st)[RB][2],
-                                             u32x4_t (&pp)[RB][4], f32x16_t (&ot)[RB][4], float (&m_run)[RB],
+                                             f32x16_t (&ot)[RB][4], float (&m_run)[RB],
                                              float (&l_run)[RB], int lh, float scale_log2) {
 #pragma unroll
     for (int k = 0; k < RB; ++k) {
@@ -278,23 +256,25 @@ __device__ __forceinline__ void softmax_tile(int kind, int nvalid, const uint64_
         const float msub = (m_run[k] == -INFINITY) ? 0.f : m_run[k];
         float psum = 0.f;
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int kb = ks >> 1, r = 8 * (ks & 1) + 2 * e;
-                const float p0 = __builtin_amdgcn_exp2f(fmaf(st[k][kb][r], scale_log2, -msub));
-                const float p1 = __builtin_amdgcn_exp2f(fmaf(st[k][kb][r + 1], scale_log2, -msub));
-                pp[k][ks][e] = pack_f16x2(p0, p1);
-                psum += p0 + p1;
+            for (int r = 0; r < 16; ++r) {
+                const float pv = __builtin_amdgcn_exp2f(fmaf(st[k][kb][r], scale_log2, -msub));
+                st[k][kb][r] = pv;
+                psum += pv;
             }
         l_run[k] += psum;
     }
 }
 
 // PV step j: 16-key step ks = j >> 2, d block db = j & 3; reads run QK_AHEAD
-// steps ahead as in qk_tile.
+// steps ahead as in qk_tile. P enters as bf16 hi + lo parts (two MFMAs on
+// the same V operand), so it keeps ~16 significant bits: a single rounding to
+// bf16 (8 bits) or fp16 (11 bits) moves enough output elements across a bf16
+// rounding boundary to flip argmax decisions downstream whose top-2 logit
+// gap is above 1e-3.
 template <int RB>
-__device__ __forceinline__ void pv_tile(const unsigned char *tile, const u32x4_t (&pp)[RB][4], f32x16_t (&ot)[RB][4],
+__device__ __forceinline__ void pv_tile(const unsigned char *tile, const f32x16_t (&st)[RB][2], f32x16_t (&ot)[RB][4],
                                         int lr, int lh) {
     const unsigned char *vrow = tile + VOFF + lr * 32 + ((lh ^ vswz(lr)) << 4);
     u32x4_t fv[16];
@@ -303,14 +283,30 @@ __device__ __forceinline__ void pv_tile(const unsigned char *tile, const u32x4_t
         fv[j] = *reinterpret_cast<const u32x4_t *>(vrow + ks * 4096 + db * 1024);
     };
     sfor<0, QK_AHEAD>(vread);
+    u32x4_t ph[RB], pl[RB];
     sfor<0, 16>([&](auto J) {
         constexpr int j = J, ks = j >> 2, db = j & 3;
-        if constexpr (j + QK_AHEAD < 16) vread(std::integral_constant<int, j + QK_AHEAD>{});
-        const f16x8_t a = __builtin_bit_cast(f16x8_t, fv[j]);
+        if constexpr (db == 0) {
+            constexpr int kb = ks >> 1, r0 = 8 * (ks & 1);
 #pragma unroll
-        for (int k = 0; k < RB; ++k)
-            ot[k][db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, __builtin_bit_cast(f16x8_t, pp[k][ks]), ot[k][db], 0,
-                                                               0, 0);
+            for (int k = 0; k < RB; ++k)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    uint32_t h2, l2;
+                    e3_split_bf16x2(st[k][kb][r0 + 2 * e], st[k][kb][r0 + 2 * e + 1], h2, l2);
+                    ph[k][e] = h2;
+                    pl[k][e] = l2;
+                }
+        }
+        if constexpr (j + QK_AHEAD < 16) vread(std::integral_constant<int, j + QK_AHEAD>{});
+        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, fv[j]);
+#pragma unroll
+        for (int k = 0; k < RB; ++k) {
+            ot[k][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, ph[k]), ot[k][db], 0, 0,
+                                                               0);
+            ot[k][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, pl[k]), ot[k][db], 0, 0,
+                                                               0);
+        }
         __builtin_amdgcn_sched_barrier(0);
     });
 }
@@ -449,8 +445,7 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_bf16_kernel(AttnParams p) {
                         v[e] &= lo | hi;
                     }
                 }
-#pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = bf16x2_to_f16x2(v[e]);
+
                 *reinterpret_cast<u32x4_t *>(dst + VOFF + jb * 4096 + d * 32 + ((half ^ vswz(d)) << 4)) = v;
             }
         } else {
@@ -464,7 +459,7 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_bf16_kernel(AttnParams p) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const int d = d8 + e;
-                    const uint32_t word = key_ok ? bf16x2_to_f16x2(sv[i][e >> 1]) : 0u;
+                    const uint32_t word = key_ok ? sv[i][e >> 1] : 0u;
                     const uint16_t val = (uint16_t)((e & 1) ? (word >> 16) : (word & 0xffffu));
                     reinterpret_cast<uint16_t *>(dst + VOFF + jb * 4096 + d * 32)[((sl >> 3) ^ vswz(d)) * 8 + (sl & 7)] =
                         val;
@@ -517,7 +512,6 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_bf16_kernel(AttnParams p) {
     // the other buffer, whose last readers finished before that barrier, and
     // meets the barrier; the loads of tile it+2 go out right after it.
     f32x16_t st[RB][2];
-    u32x4_t pp[RB][4];
     for (int it = 0; it < ntiles; ++it) {
         const unsigned char *cur = buf + (it % NBUF) * TILE_BYTES;
         if (wave_active) {
@@ -536,8 +530,8 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_bf16_kernel(AttnParams p) {
                 for (int k = 0; k < RB; ++k) mword[k] = tt == 0 ? mw0[k] : mw1[k];
             }
             qk_tile<RB>(cur, qb, st, lr, lh, p.zero);
-            softmax_tile<RB>(kind, nvalid, mword, st, pp, ot, m_run, l_run, lh, p.scale_log2);
-            pv_tile<RB>(cur, pp, ot, lr, lh);
+            softmax_tile<RB>(kind, nvalid, mword, st, ot, m_run, l_run, lh, p.scale_log2);
+            pv_tile<RB>(cur, st, ot, lr, lh);
         }
         if (it + 1 < ntiles) write_tile(it + 1, buf + ((it + 1) % NBUF) * TILE_BYTES);
         __syncthreads();
@@ -567,19 +561,18 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_bf16_kernel(AttnParams p) {
                 p.lse[((size_t)b * p.Tq + t[k]) * p.Hq + hq[k]] =
                     l_tot > 0.f ? (m_run[k] + log2f(l_tot)) * kLn2 : -INFINITY;
         } else {
-            // the split's normalised O in fp16: a convex combination of V
-            // rows, so within V's range, kept to 11 significant bits
+            // the split's normalised O in fp32 (rounding it to 16 bits here
+            // would cost the merged result more than its final bf16 rounding)
             const size_t prow = (((size_t)b * p.Hkv + kvh) * p.nsplit + split) * p.Rpad + row[k];
-            uint16_t *orow = p.ws_o + prow * DH;
+            float *orow = p.ws_o + prow * DH;
 #pragma unroll
             for (int db = 0; db < 4; ++db)
 #pragma unroll
                 for (int g4 = 0; g4 < 4; ++g4) {
                     const int d = db * 32 + 8 * g4 + 4 * lh;
-                    u32x2_t o;
-                    o[0] = pack_f16x2(ot[k][db][4 * g4] * inv, ot[k][db][4 * g4 + 1] * inv);
-                    o[1] = pack_f16x2(ot[k][db][4 * g4 + 2] * inv, ot[k][db][4 * g4 + 3] * inv);
-                    *reinterpret_cast<u32x2_t *>(orow + d) = o;
+                    f32x4_t o = {ot[k][db][4 * g4] * inv, ot[k][db][4 * g4 + 1] * inv, ot[k][db][4 * g4 + 2] * inv,
+                                 ot[k][db][4 * g4 + 3] * inv};
+                    *reinterpret_cast<f32x4_t *>(orow + d) = o;
                 }
             if (lh == 0) {
                 p.ws_ml[prow * 2] = m_run[k];
@@ -606,7 +599,7 @@ __global__ __launch_bounds__(128) void tree_attn_combine_kernel(AttnParams p) {
         const size_t prow = (base + s) * p.Rpad + row;
         const float ms = p.ws_ml[prow * 2], ls = p.ws_ml[prow * 2 + 1];
         const float wgt = (ms == -INFINITY) ? 0.f : ls * exp2f(ms - M);
-        acc += wgt * (float)__builtin_bit_cast(_Float16, p.ws_o[prow * DH + d]);
+        acc += wgt * p.ws_o[prow * DH + d];
         den += wgt;
     }
     const float o = den > 0.f ? acc / den : 0.f;
@@ -691,19 +684,21 @@ __global__ __launch_bounds__(CN_NT) void tree_attn_combine_norm_kernel(AttnParam
             const size_t base = ((size_t)b * p.Hkv + kvh) * p.nsplit;
             float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
             for (int s0 = 0; s0 < nsplit_b; s0 += CN_BATCH) {
-                u32x4_t a[CN_BATCH];
+                f32x4_t a[CN_BATCH], c4[CN_BATCH];
 #pragma unroll
                 for (int u = 0; u < CN_BATCH; ++u) {
-                    if (s0 + u < nsplit_b)  // uniform
-                        a[u] = *reinterpret_cast<const u32x4_t *>(p.ws_o + ((base + s0 + u) * p.Rpad + row) * DH + d);
+                    if (s0 + u < nsplit_b) {  // uniform
+                        const float *src = p.ws_o + ((base + s0 + u) * p.Rpad + row) * DH + d;
+                        a[u] = *reinterpret_cast<const f32x4_t *>(src);
+                        c4[u] = *reinterpret_cast<const f32x4_t *>(src + 4);
+                    }
                 }
 #pragma unroll
                 for (int u = 0; u < CN_BATCH; ++u) {
                     if (s0 + u < nsplit_b) {
                         const float w = wgt[hq][s0 + u];
-                        const f16x8_t h = __builtin_bit_cast(f16x8_t, a[u]);
 #pragma unroll
-                        for (int i = 0; i < 8; ++i) o[i] += w * (float)h[i];
+                        for (int i = 0; i < 4; ++i) { o[i] += w * a[u][i]; o[4 + i] += w * c4[u][i]; }
                     }
                 }
             }
@@ -925,7 +920,7 @@ Plan make_plan(const eagle3_tree_attn_args *a) {
     pl.ws_bytes = 0;
     if (a->dtype == EAGLE3_BF16 && pl.nsplit > 1) {
         const size_t rows = (size_t)a->B * a->Hkv * pl.nsplit * (size_t)pl.nrb * ROWS_PER_WG;
-        pl.ws_bytes = ((rows * DH * 2 + 255) & ~(size_t)255) + rows * 8;
+        pl.ws_bytes = ((rows * DH * 4 + 255) & ~(size_t)255) + rows * 8;
     }
     return pl;
 }
@@ -971,8 +966,8 @@ extern "C" int eagle3_tree_attn(const eagle3_tree_attn_args *a, void *ws, size_t
         p.ws_o = nullptr; p.ws_ml = nullptr;
         if (pl.ws_bytes > 0) {
             const size_t rows = (size_t)a->B * a->Hkv * pl.nsplit * (size_t)pl.nrb * ROWS_PER_WG;
-            p.ws_o = (uint16_t *)ws;
-            p.ws_ml = (float *)((char *)ws + ((rows * DH * 2 + 255) & ~(size_t)255));
+            p.ws_o = (float *)ws;
+            p.ws_ml = (float *)((char *)ws + ((rows * DH * 4 + 255) & ~(size_t)255));
         }
         // the row blocks of a unit go to one XCD (ids 8 apart): the grid is a
         // whole number of 8-unit groups, surplus work-groups exit at once
