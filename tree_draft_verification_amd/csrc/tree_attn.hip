@@ -35,7 +35,9 @@ namespace {
 
 constexpr int KT = 64;       // keys per tile
 constexpr int DH = 128;      // head dim of the MFMA path
-constexpr int ROWS_PER_WG = 256;
+constexpr int ATT_NW = 8;                           // waves per work-group
+constexpr int ROWS_PER_WG = ATT_NW * 32;            // query rows per work-group
+constexpr int ATT_WG_PER_CU = 1;                    // work-groups resident per CU
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr long MIN_SPLIT_KEYS = 256;  // shortest automatic prefix split
@@ -334,7 +336,7 @@ __device__ __forceinline__ WorkUnit work_unit(int i, int nrb) {
 // 16-byte chunks of K and NCH of V) in registers, loaded at the start of the
 // tile and written to the other buffer at its end; one barrier per tile.
 template <int NW, int RB>
-__global__ __launch_bounds__(NW * 64) void tree_attn_bf16_kernel(AttnParams p) {
+__global__ __launch_bounds__(NW * 64, ATT_WG_PER_CU) void tree_attn_bf16_kernel(AttnParams p) {
     static_assert(NW * RB * 32 == ROWS_PER_WG, "a work-group covers one block of query rows");
     constexpr int NT = NW * 64;
     constexpr int NCH = KT * DH / 8 / NT;  // 16-byte chunks of K (and of V) per thread and tile
@@ -399,14 +401,19 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_bf16_kernel(AttnParams p) {
             for (int i = 0; i < NCH; ++i) raw_id[i] = btab[min(blk0 + i * (NT / 256) + jb_t, last_blk)];
         }
     };
+    const uint32_t lane_off = (uint32_t)w * 16;
     auto load_tile = [&](int it) {
         if (it < npre) {
 #pragma unroll
             for (int i = 0; i < NCH; ++i) {
+                // the block's base address is wave-uniform (scalar); each lane
+                // adds its fixed 32-bit byte offset w * 16
                 const int bid = __builtin_amdgcn_readfirstlane(min(max(raw_id[i], 0), p.num_blocks - 1));
-                const size_t off = (size_t)bid * blk_stride + head_off + (size_t)w * 8;
-                sk[i] = *reinterpret_cast<const u32x4_t *>(p.k_cache + off);
-                sv[i] = *reinterpret_cast<const u32x4_t *>(p.v_cache + off);
+                const size_t boff = (size_t)bid * blk_stride + head_off;
+                const unsigned char *kb = reinterpret_cast<const unsigned char *>(p.k_cache + boff);
+                const unsigned char *vb = reinterpret_cast<const unsigned char *>(p.v_cache + boff);
+                sk[i] = *reinterpret_cast<const u32x4_t *>(kb + lane_off);
+                sv[i] = *reinterpret_cast<const u32x4_t *>(vb + lane_off);
             }
         } else {
             const int tk0 = (it - npre) * KT;
@@ -910,8 +917,9 @@ Plan make_plan(const eagle3_tree_attn_args *a) {
         // none shorter than MIN_SPLIT_KEYS
         const long base = (long)a->B * a->Hkv * pl.nrb;
         long S = 1;
-        if (a->dtype == EAGLE3_BF16 && base > 0 && base < e3_cu_count())
-            S = std::min((e3_cu_count() + base - 1) / base, std::max(1L, lmax / MIN_SPLIT_KEYS));
+        const long slots = (long)ATT_WG_PER_CU * e3_cu_count();
+        if (a->dtype == EAGLE3_BF16 && base > 0 && base < slots)
+            S = std::min((slots + base - 1) / base, std::max(1L, lmax / MIN_SPLIT_KEYS));
         C = (lmax + S - 1) / S;
     }
     C = std::max<long>(KT, (C + KT - 1) / KT * KT);
@@ -972,10 +980,12 @@ extern "C" int eagle3_tree_attn(const eagle3_tree_attn_args *a, void *ws, size_t
         // the row blocks of a unit go to one XCD (ids 8 apart): the grid is a
         // whole number of 8-unit groups, surplus work-groups exit at once
         const int grid = (p.nunits + 7) / 8 * 8 * pl.nrb;
-        // 8 waves of 32 rows: two waves per SIMD, 256 registers each (two row
-        // blocks per wave would share every fragment read, but 64 rows of Q,
-        // scores and output accumulators do not fit without spilling)
-        tree_attn_bf16_kernel<8, 1><<<grid, 512, 0, st>>>(p);
+        // 8 waves of 32 rows: two waves per SIMD, 256 registers each. (Two
+        // row blocks per wave would share every fragment read, but 64 rows of
+        // Q, scores and output accumulators do not fit without spilling; two
+        // independent 128-row work-groups per CU measured slower, as each K/V
+        // tile is then read twice.)
+        tree_attn_bf16_kernel<ATT_NW, 1><<<grid, ATT_NW * 64, 0, st>>>(p);
         const bool fused_norm = a->norm_out && pl.nsplit > 1 && pl.nsplit <= CN_MAXS && a->Hq <= CN_MAXH;
         if (fused_norm)
             tree_attn_combine_norm_kernel<<<a->B * a->Tq, CN_NT, 0, st>>>(p, (uint16_t *)a->norm_out, a->norm_eps);
