@@ -54,6 +54,9 @@ def parse():
     ap.add_argument("--w-copies", type=int, default=3, help="LM-head copies cycled by the timed steps")
     ap.add_argument("--no-graph", dest="graph", action="store_false",
                     help="skip the extra HIP-graph replay of the steps after the timed region")
+    ap.add_argument("--no-clock-query", dest="clock_query", action="store_false",
+                    help="skip the rocm-smi shader-clock query after the timed region (for runs under a profiler, "
+                         "whose preloaded library would start the GPU in that child process too)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for scaling HBM counters)")
     return ap.parse_args()
@@ -202,7 +205,7 @@ def bench_verify(args, name):
         run(i, ev[i])
     torch.cuda.synchronize()
     t_end = time.perf_counter()
-    sclk = gpu_sclk_mhz()
+    sclk = gpu_sclk_mhz() if args.clock_query else None
     ms_per_step = (t_end - t_start) * 1e3 / args.steps
     graph_ms = None
     if args.graph:
@@ -337,7 +340,7 @@ def bench_draft(args):
         step(evs[i])
     torch.cuda.synchronize()
     ms_per_step = (time.perf_counter() - t_start) * 1e3 / args.steps
-    sclk = gpu_sclk_mhz()
+    sclk = gpu_sclk_mhz() if args.clock_query else None
     ing = float(np.mean([e["t0"].elapsed_time(e["t1"]) for e in evs]))
     grow = float(np.mean([e["t1"].elapsed_time(e["t2"]) for e in evs]))
     ver = float(np.mean([e["t2"].elapsed_time(e["t3"]) for e in evs]))
