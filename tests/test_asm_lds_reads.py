@@ -146,11 +146,21 @@ def _asm(src, out_dir):
     return src, open(out).read()
 
 
-@pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not available")
-def test_no_read_of_in_flight_lds_fragments(tmp_path):
+@pytest.fixture(scope="module")
+def compiled(tmp_path_factory):
+    """(source, gfx950 assembly text) of every HIP source, compiled once."""
+    if not os.path.exists(HIPCC):
+        pytest.skip("hipcc not available")
+    out = tmp_path_factory.mktemp("asm")
     srcs = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(4, os.cpu_count() or 1)) as ex:
-        results = list(ex.map(lambda s: _asm(s, str(tmp_path)), srcs))
+        results = list(ex.map(lambda s: _asm(s, str(out)), srcs))
+    yield results
+    shutil.rmtree(out, ignore_errors=True)
+
+
+def test_no_read_of_in_flight_lds_fragments(compiled):
+    results = compiled
     problems, nfun = [], 0
     for src, text in results:
         for name, lines in functions(text):
@@ -164,4 +174,71 @@ def test_no_read_of_in_flight_lds_fragments(tmp_path):
     overlaps = [f"{os.path.basename(src)} line {ln}: {ins}" for src, text in results
                 for (ln, ins) in mfma_overlaps(text.splitlines())]
     assert not overlaps, "\n".join(overlaps[:20])
-    shutil.rmtree(tmp_path, ignore_errors=True)
+
+
+VMEM_LOAD = ("global_load", "buffer_load", "flat_load", "scratch_load")
+VMEM_STORE = ("global_store", "buffer_store", "flat_store", "scratch_store", "global_atomic", "buffer_atomic")
+
+
+def scan_vmcnt(lines):
+    """`s_waitcnt vmcnt(N)` with N > 0 along the fall-through path of one
+    function that retire an ordinary vector load while an LDS-DMA load
+    issued after it is still counted: (line, "load-before-dma")."""
+    queue, found = [], []
+    for i, raw in enumerate(lines):
+        s = raw.split(";")[0].strip()
+        if not s or s.startswith(".") or s.endswith(":"):
+            continue
+        op = s.split()[0]
+        if op in ("s_branch", "s_endpgm", "s_setpc_b64"):
+            queue = []
+            continue
+        if op.startswith(VMEM_LOAD):
+            queue.append("dma" if "_lds" in op else "load")
+            continue
+        if op.startswith(VMEM_STORE):
+            queue.append("store")
+            continue
+        if op in ("s_waitcnt", "s_waitcnt_vmcnt"):
+            m = re.search(r"vmcnt\((\d+)\)", s)
+            if not m:
+                continue
+            n = int(m.group(1))
+            cut = max(0, len(queue) - n)
+            retired, keep = queue[:cut], queue[cut:]
+            if n > 0 and "load" in retired and "dma" in keep:
+                found.append((i + 1, "load-before-dma"))
+            queue = keep
+    return found
+
+
+def test_vmcnt_scanner_flags_planted_cases():
+    lines = ["global_load_dwordx4 v[0:3], v[4:5], off",
+             "global_load_lds_dwordx4 v[6:7], off",
+             "s_waitcnt vmcnt(1)",                      # retires the load, the later DMA still counted
+             "global_load_lds_dwordx4 v[6:7], off",
+             "global_load_lds_dwordx4 v[6:7], off",
+             "s_waitcnt vmcnt(1)",                      # DMA behind DMA: the stage rule, not flagged
+             "global_load_dword v1, v[4:5], off",
+             "s_waitcnt vmcnt(0)"]
+    assert scan_vmcnt(lines) == [(3, "load-before-dma")]
+
+
+def test_no_vmcnt_wait_relies_on_order_across_kinds(compiled):
+    """In the generated code of every kernel that uses LDS-DMA, no partial
+    vmcnt wait retires an ordinary load while a later LDS-DMA load is still
+    counted. Partial waits over LDS-DMA loads alone are the ring rule (a
+    stage is read once the loads issued after it are all that may remain);
+    they assume only that one wave's loads complete in issue order, the
+    assumption the compiler makes for every partial vmcnt wait it emits."""
+    results = compiled
+    problems, n_dma = [], 0
+    for src, text in results:
+        for name, lines in functions(text):
+            if not any("global_load_lds" in l for l in lines):
+                continue
+            n_dma += 1
+            for (line, kind) in scan_vmcnt(lines):
+                problems.append(f"{os.path.basename(src)} {name[:80]} line {line}: {kind}")
+    assert n_dma > 0
+    assert not problems, "\n".join(problems[:20])
