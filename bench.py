@@ -13,6 +13,12 @@ starts):
   draft-b64   the EAGLE-3 draft head at batch 64 (context ingest of 1024 rows,
               8 growth steps with top-10 expansion, rerank to 60 nodes)
               followed by the verify step on the drafted trees (8B shapes)
+  draft-b64-trim  the same with a trimmed draft vocabulary: the draft LM head
+              keeps 64128 of the 128256 rows and maps its picks back to
+              full-vocabulary ids
+  chain60-b64, tree60-b64, chain40-b64, tree40-b64
+              chain vs tree drafts at equal node budgets (8B shapes, batch 64);
+              chain-vs-tree runs all four and reports tau against nodes/s
 
 Prints ONE JSON line: verified tree nodes/s (value), accepted tokens per
 verify step (verify workloads: draft tokens planted against the oracle's
@@ -37,6 +43,7 @@ PEAK_BF16_TFLOPS = 2500.0
 METRIC = "verified tree nodes/s + accepted tok/step at 1 GPU; % HBM/MFMA roofline"
 LMHEAD_SRC = os.path.join(ROOT, "tree_draft_verification_amd", "csrc", "lmhead.hip")
 VERIFY_WORKLOADS = ("llama8b-b1", "llama8b-b64", "llama70b-b8")
+CHAIN_TREE_WORKLOADS = ("chain60-b64", "tree60-b64", "chain40-b64", "tree40-b64")
 
 
 def log(*a):
@@ -48,7 +55,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="llama8b-b64", choices=VERIFY_WORKLOADS + ("draft-b64",))
+    ap.add_argument("--workload", default="llama8b-b64",
+                    choices=VERIFY_WORKLOADS + CHAIN_TREE_WORKLOADS + ("draft-b64", "draft-b64-trim", "chain-vs-tree"))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="minimum oracle time in the CPU-baseline sample")
     ap.add_argument("--w-copies", type=int, default=3, help="LM-head copies cycled by the timed steps")
@@ -252,7 +260,7 @@ def bench_verify(args, name):
         log(f"[bench] cpu baseline: {n_seq} oracle sequence steps in {tsum:.1f}s on {threads} threads")
         cpu = {"value": round(shape.n_drafts * n_seq / tsum, 2), "unit": "nodes/s", "cores": threads,
                "kind": "oracle",
-               "sample": f"{n_seq} single-sequence verify steps of {name} (60 drafts each), {tsum:.1f} s total, "
+               "sample": f"{n_seq} single-sequence verify steps of {name} ({shape.n_drafts} drafts each), {tsum:.1f} s total, "
                          f"fp64 C oracle with OpenMP"}
 
     return {
@@ -283,10 +291,40 @@ def bench_verify(args, name):
     }
 
 
-def bench_draft(args):
+def bench_chain_vs_tree(args):
+    """Chain vs tree drafts at equal node budgets (60 and 40 draft tokens) on
+    the same verify kernels, 8B shapes at batch 64, per-sequence match
+    probability uniform in 0.6-0.95 with siblings as alternatives (at most one
+    sibling is the target's token). Each configuration is a full verify
+    workload (parity against its stored oracle results, timed steps); the line
+    reports accepted tokens per step and per second next to nodes/s."""
+    rows, outs = [], {}
+    for name in CHAIN_TREE_WORKLOADS:
+        o = bench_verify(args, name)
+        outs[name] = o
+        steps_per_s = 1e3 / o["ms_per_step"]
+        rows.append({"workload": name, "draft_nodes": o["config"]["draft_nodes"],
+                     "shape": "chain" if name.startswith("chain") else "top-10 tree, depth 7",
+                     "accepted_tok_per_step": o["accepted_tok_per_step"],
+                     "accepted_tok_per_step_std": o["accepted_tok_per_step_std"],
+                     "verified_nodes_per_s": o["value"], "ms_per_step": o["ms_per_step"],
+                     "accepted_tok_per_s": round(o["accepted_tok_per_step"] * o["config"]["batch"] * steps_per_s, 1),
+                     "parity_vs_oracle": o["parity_vs_oracle"], "flagged_sequences": o["flagged_sequences"]})
+        log(f"[bench] {name}: tau {o['accepted_tok_per_step']:.3f}, {o['value']:.0f} nodes/s, "
+            f"{rows[-1]['accepted_tok_per_s']:.0f} accepted tok/s, parity {o['parity_vs_oracle']}")
+    head = dict(outs["tree60-b64"])
+    head["config"] = dict(head["config"], workload="chain-vs-tree")
+    head["parity_vs_oracle"] = "pass" if all(r["parity_vs_oracle"] == "pass" for r in rows) else "FAIL"
+    head["chain_vs_tree"] = rows
+    return head
+
+
+def bench_draft(args, name="draft-b64"):
     """EAGLE-3 draft head + tree build on 64 sequences, then the verify step on
     the drafted trees. One step = context ingest + 8 growth steps + rerank +
-    verify; the dominant kernel is the draft LM head (640 rows, top-10)."""
+    verify; the dominant kernel is the draft LM head (640 rows, top-10).
+    draft-b64-trim: the same with a trimmed draft vocabulary (half of the
+    128256 LM-head rows kept, ids mapped back before the tree)."""
     import dataclasses
 
     import numpy as np
@@ -295,7 +333,8 @@ def bench_draft(args):
     import synth
     import tree_draft_verification_amd as e3
 
-    s = synth.DRAFT_B64
+    s = {"draft-b64": synth.DRAFT_B64, "draft-b64-trim": synth.DRAFT_B64_TRIM}[name]
+    vocab = synth.draft_vocab(s)
     t0 = time.time()
     W = synth.draft_weights(s)
     Wd = {k: to_dev(v) for k, v in W.items()}
@@ -307,8 +346,10 @@ def bench_draft(args):
     vin = synth.verify_inputs(vshape, 0)
     vd = dict(kc=to_dev(vin.kv.k_cache), vc=to_dev(vin.kv.v_cache), bt=to_dev(vin.kv.block_table),
               pl=to_dev(vin.kv.prefix_len), q=to_dev(vin.q), kt=to_dev(vin.k_tree), vt=to_dev(vin.v_tree))
-    log(f"[bench] draft-b64: inputs ready in {time.time() - t0:.1f}s")
-    head = e3.DraftHead(Wd, s.B, s.ctx, s.Hq, s.Hkv, s.D, s.steps, s.topk, s.n_drafts, s.theta, s.eps)
+    log(f"[bench] {name}: inputs ready in {time.time() - t0:.1f}s")
+    head = e3.DraftHead(Wd, s.B, s.ctx, s.Hq, s.Hkv, s.D, s.steps, s.topk, s.n_drafts, s.theta, s.eps,
+                        vocab=None if vocab is None else to_dev(vocab))
+    v_head = s.V if vocab is None else len(vocab)
     vstep = e3.VerifyStep(vshape.B, vshape.T, vshape.Hq, vshape.Hkv, vshape.D, vshape.V, vd["kc"], vd["vc"],
                           vd["bt"], vd["pl"], Wd["lm_head"])
     E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
@@ -347,7 +388,7 @@ def bench_draft(args):
     # LM-head launches of growth steps 2..8 (640 rows each)
     lm_list = [a.elapsed_time(b) * 1e3 for pairs in lm_ev for (a, b) in pairs[1:]]
     lm_us = float(np.mean(lm_list))
-    roofline = lm_roofline(s.B * s.topk, s.k, s.V, lm_us, "draft-b64", lm_list)
+    roofline = lm_roofline(s.B * s.topk, s.k, v_head, lm_us, name, lm_list)
     al = vstep.accept_len.cpu().numpy()
     parent, tokens = head.parent.cpu().numpy(), head.tokens.cpu().numpy()
     nodes = s.B * s.n_drafts
@@ -359,22 +400,23 @@ def bench_draft(args):
         threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
         l0, m0, h0, t00 = synth.draft_inputs(s, 0, batch=slice(0, 1))
         t0 = time.perf_counter()
-        r = oracle.draft_tree(s, W, l0, m0, h0, t00)
+        r = oracle.draft_tree(s, W, l0, m0, h0, t00, vocab=vocab)
         one = dataclasses.replace(synth.verify_inputs(vshape, 0, batch=slice(0, 1)), parent=r["parent"])
         oracle.verify_step(one, W["lm_head"], tokens=r["tokens"])
         tsum = time.perf_counter() - t0
         tree_same = bool(np.array_equal(r["parent"][0], parent[0]) and np.array_equal(r["tokens"][0], tokens[0]))
         log(f"[bench] cpu baseline: 1 sequence (draft + verify) in {tsum:.1f}s on {threads} threads")
         cpu = {"value": round(s.n_drafts / tsum, 3), "unit": "nodes/s", "cores": threads, "kind": "oracle",
-               "sample": f"sequence 0 of draft-b64: context ingest of 1024 rows, 8 growth steps, rerank and the "
+               "sample": f"sequence 0 of {name}: context ingest of 1024 rows, 8 growth steps, rerank and the "
                          f"verify step, {tsum:.1f} s, fp64 C oracle with OpenMP"}
 
     return {
         "metric": METRIC, "value": round(value, 1), "unit": "nodes/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": "draft-b64", "batch": s.B, "context": s.ctx, "hidden": s.k, "vocab": s.V,
-                   "draft_steps": s.steps, "topk": s.topk, "draft_nodes": s.n_drafts, "verify_prefix": 1024},
+        "config": {"workload": name, "batch": s.B, "context": s.ctx, "hidden": s.k, "vocab": s.V,
+                   "draft_vocab": v_head, "draft_steps": s.steps, "topk": s.topk, "draft_nodes": s.n_drafts,
+                   "verify_prefix": 1024},
         "accepted_tok_per_step": round(float(np.mean(al + 1)), 3), "tau_samples": int(len(al)),
         "tau_note": "independent random draft and target: acceptance is rare by construction",
         "phase_ms": {"context_ingest": round(ing, 3), "tree_growth": round(grow, 3), "verify": round(ver, 3)},
@@ -402,7 +444,12 @@ def main():
         return
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
-    out = bench_draft(args) if args.workload == "draft-b64" else bench_verify(args, args.workload)
+    if args.workload in ("draft-b64", "draft-b64-trim"):
+        out = bench_draft(args, args.workload)
+    elif args.workload == "chain-vs-tree":
+        out = bench_chain_vs_tree(args)
+    else:
+        out = bench_verify(args, args.workload)
     print(json.dumps(out), flush=True)
 
 

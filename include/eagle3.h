@@ -229,6 +229,23 @@ int eagle3_accept_path(const int32_t *tokens, const int32_t *parent, const uint6
 
 
 /*
+ * Trimmed draft vocabulary ([blog] sections 1, 3.2 and 5.1: VocabTrim, FR-Spec
+ * and SpecVocab shrink the draft's search space by 40-60%). The draft LM head
+ * runs over V_sub kept rows, row i being full-vocabulary id vmap[i] (gather
+ * them once, e.g. with eagle3_copy_rows), so eagle3_lmhead_argmax returns row
+ * numbers of the trimmed head; this maps them back before they enter the tree:
+ *   out[i] = vmap[ids[i]]  for i < n;  an id outside [0, V_sub) gives -1.
+ * ids, out [n] int32 device (out may be ids: in place); vmap [V_sub] int32
+ * device, strictly ascending (caller's duty), so that the lowest-row rule of
+ * eagle3_lmhead_argmax on ties is the lowest-full-id rule. With status [1]
+ * int32 non-NULL, status[0] = EAGLE3_ERR_RANGE if any id was out of range,
+ * else EAGLE3_OK (written also for n == 0). One work-group of 1024 threads:
+ * sized for the few thousand ids of a draft step.
+ */
+int eagle3_vocab_map(const int32_t *ids, int n, const int32_t *vmap, int V_sub, int32_t *out, int32_t *status,
+                     void *stream);
+
+/*
  * Dense layers for the EAGLE-3 draft head and small decoders.
  *
  * [news] draft stage: an FC reduces the concatenated low/mid/high features

@@ -288,7 +288,7 @@ def flags(parent, tokens, idx, gap, thresh=GAP_FLAG):
 def verify_step(inp: synth.VerifyInputs, W_lm, tokens=None):
     fw = verify_forward(inp, W_lm)
     if tokens is None:
-        tokens = synth.plant_tokens(inp.parent, fw["idx"], inp.p_seq, inp.plant_u, inp.plant_id)
+        tokens = synth.plant_for(inp, fw["idx"])
     alen, path, out, end = accept(tokens, inp.parent, fw["idx"])
     fw.update(tokens=tokens, accept_len=alen, path=path, out_tokens=out, end=end,
               flagged=flags(inp.parent, tokens, fw["idx"], fw["gap"]))
@@ -461,7 +461,7 @@ class OwnChoice:
         return select_topk(pool_score, np.tile(np.arange(P, dtype=np.int32), (pool_score.shape[0], 1)), N)
 
 
-def draft_tree(shape, W, l, m, h, ctx_tok, gap=GAP_FLAG, chooser=None):
+def draft_tree(shape, W, l, m, h, ctx_tok, gap=GAP_FLAG, chooser=None, vocab=None):
     """EAGLE-3 draft head and EAGLE-2 style tree growth, for B sequences.
 
     News write-up of the EAGLE-3 paper, draft stage: context row t fuses the
@@ -486,7 +486,15 @@ def draft_tree(shape, W, l, m, h, ctx_tok, gap=GAP_FLAG, chooser=None):
     `gap` of the n-th pool score, or the final rerank boundary); "choices"
     (the selections made); "rows": per growth step s >= 2 the frontier's
     tokens, the row of each frontier node's parent in the previous step's
-    outputs (a_root for step 2), the position and the fused inputs x."""
+    outputs (a_root for step 2), the position and the fused inputs x.
+
+    vocab: a trimmed draft vocabulary (Spec-Bench blog post, sections 1, 3.2
+    and 5.1: VocabTrim / FR-Spec / SpecVocab shrink the draft's search space
+    by 40-60%): the kept token ids, strictly ascending. reading: the draft LM
+    head keeps only those rows of the LM-head weight, its top-k, lse and logp
+    range over the kept rows alone, and each chosen row maps back to its full
+    vocabulary id before it enters the tree (and the next step's embedding).
+    Ascending ids make the lowest kept row on a tie the lowest full id."""
     s = shape
     B, ctx, k = l.shape
     qd, kvd, C = s.Hq * s.D, s.Hkv * s.D, s.topk
@@ -502,8 +510,19 @@ def draft_tree(shape, W, l, m, h, ctx_tok, gap=GAP_FLAG, chooser=None):
         f = silu_mul(gemm(rmsnorm(x, eps=s.eps), W["wgu"]))
         return gemm(f, W["wd"], R=x)
 
+    if vocab is not None:
+        vocab = np.asarray(vocab, np.int64)
+        if vocab.ndim != 1 or len(vocab) <= C or (np.diff(vocab) <= 0).any() or vocab[0] < 0 \
+                or vocab[-1] >= W["lm_head"].shape[0]:
+            raise ValueError("vocab must be strictly ascending ids of the LM head's rows, more than topk of them")
+        w_head = W["lm_head"][vocab]
+    else:
+        w_head = W["lm_head"]
+
     def head(a, step):
-        idx, val, _, lse = lmhead(rmsnorm(a, eps=s.eps), W["lm_head"], topk=ch.wide)
+        idx, val, _, lse = lmhead(rmsnorm(a, eps=s.eps), w_head, topk=ch.wide)
+        if vocab is not None:
+            idx = vocab[idx]
         ids, v = ch.children(step, idx, val)
         ids = np.asarray(ids).reshape(-1, C).astype(np.int32)
         v = np.asarray(v).reshape(-1, C)

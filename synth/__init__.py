@@ -29,7 +29,7 @@ BF16_NAN = np.uint16(0x7FC0)
 
 # component ids of the child generators
 C_TREE, C_PLEN, C_WLM, C_KPRE, C_VPRE, C_Q, C_KTREE, C_VTREE, C_PERM, C_PLANT = range(10)
-C_WEIGHTS, C_PROMPT, C_FEAT, C_CTX, C_EMB = range(10, 15)
+C_WEIGHTS, C_PROMPT, C_FEAT, C_CTX, C_EMB, C_VOCAB = range(10, 16)
 
 
 def child_rng(workload_id: int, seed: int, component: int) -> np.random.Generator:
@@ -253,6 +253,8 @@ class VerifyShape:
     prefix: tuple = (1024, 1024)   # inclusive range of prefix lengths
     p_match: tuple = (0.88, 0.88)  # per-sequence match probability range
     dtype: str = "bf16"
+    tree: str = "topk"             # "topk" (top-`branch` expansion) or "chain"
+    planting: str = "independent"  # "independent" or "ranked" (see plant_tokens_ranked)
 
     @property
     def T(self):
@@ -268,7 +270,15 @@ LLAMA8B_B64 = VerifyShape("llama8b-b64", 3, B=64, Hq=32, Hkv=8, D=128, V=128256,
                           prefix=(200, 1500), p_match=(0.6, 0.95))
 LLAMA70B_B8 = VerifyShape("llama70b-b8", 4, B=8, Hq=64, Hkv=8, D=128, V=128256, n_drafts=60, depth=8,
                           prefix=(4096, 4096))
-VERIFY_SHAPES = {s.name: s for s in (LLAMA8B_B1, LLAMA8B_B64, LLAMA70B_B8)}
+# chain vs tree at equal node budgets (60 and 40 draft tokens), 8B shapes at
+# batch 64, per-sequence match probability uniform in 0.6-0.95; siblings of a
+# tree are alternatives (at most one of them is the target's token)
+CHAIN_TREE = tuple(
+    VerifyShape(f"{kind}{n}-b64", wid, B=64, Hq=32, Hkv=8, D=128, V=128256, n_drafts=n,
+                depth=n if kind == "chain" else 7, branch=1 if kind == "chain" else 10, prefix=(200, 1500),
+                p_match=(0.6, 0.95), tree="chain" if kind == "chain" else "topk", planting="ranked")
+    for wid, (kind, n) in enumerate((("chain", 60), ("tree", 60), ("chain", 40), ("tree", 40)), start=5))
+VERIFY_SHAPES = {s.name: s for s in (LLAMA8B_B1, LLAMA8B_B64, LLAMA70B_B8) + CHAIN_TREE}
 
 
 @dataclasses.dataclass
@@ -295,7 +305,10 @@ def verify_inputs(shape: VerifyShape, seed: int, batch: slice | None = None) -> 
     drawn for every sequence up to the last requested one)."""
     B, T = shape.B, shape.T
     rt = child_rng(shape.wid, seed, C_TREE)
-    parent = np.stack([topk_tree(rt, shape.n_drafts, shape.depth, shape.branch) for _ in range(B)])
+    if shape.tree == "chain":
+        parent = np.stack([chain_tree(shape.n_drafts) for _ in range(B)])
+    else:
+        parent = np.stack([topk_tree(rt, shape.n_drafts, shape.depth, shape.branch) for _ in range(B)])
     rl = child_rng(shape.wid, seed, C_PLEN)
     lo, hi = shape.prefix
     plen = rl.integers(lo, hi + 1, size=B).astype(np.int32)
@@ -370,6 +383,37 @@ def plant_tokens(parent: np.ndarray, target_idx: np.ndarray, p_seq, plant_u, pla
     return tok
 
 
+def plant_tokens_ranked(parent: np.ndarray, target_idx: np.ndarray, p_seq, plant_u, plant_id) -> np.ndarray:
+    """Draft tokens planted with siblings as alternatives.
+
+    The children of a node, in index order, are its draft's ranked
+    candidates: child j (rank j) carries the target's token at the parent
+    when its uniform is below the sequence's match probability and no earlier
+    sibling does (so rank j matches with probability p (1 - p)^(j - 1), and at
+    most one sibling matches); every other child carries its random id (which
+    can still match by chance). For a chain this is plant_tokens. The root's
+    token is its random id. ``target_idx`` must come from the oracle."""
+    parent = np.atleast_2d(parent)
+    target_idx = np.atleast_2d(target_idx)
+    B, T = parent.shape
+    tok = np.array(np.atleast_2d(plant_id), dtype=np.int32, copy=True)
+    p_seq = np.broadcast_to(np.asarray(p_seq, dtype=np.float64), (B,))
+    for b in range(B):
+        taken = np.zeros(T, dtype=bool)   # parent already has its matching child
+        for n in range(1, T):
+            p = parent[b, n]
+            if not taken[p] and plant_u[b][n] < p_seq[b]:
+                tok[b, n] = target_idx[b, p]
+                taken[p] = True
+    return tok
+
+
+def plant_for(inp, target_idx) -> np.ndarray:
+    """Draft tokens of a verify workload, by its planting rule."""
+    f = plant_tokens_ranked if inp.shape.planting == "ranked" else plant_tokens
+    return f(inp.parent, target_idx, inp.p_seq, inp.plant_u, inp.plant_id)
+
+
 # ---------------------------------------------------------------- toy decoder
 
 @dataclasses.dataclass
@@ -442,6 +486,7 @@ class DraftShape:
     eps: float = 1e-5
     std: float = 0.02
     lm_std: float = 0.02
+    vocab_keep: int = 0          # rows of a trimmed draft LM head (0: the full vocabulary)
 
     @property
     def pool_len(self):
@@ -452,6 +497,20 @@ DRAFT_B64 = DraftShape()
 # small draft head for element-wise parity; a 15x larger LM-head scale spreads
 # the draft logits so fewer selection boundaries are near-ties
 DRAFT_SMALL = DraftShape("draft-small", 25, B=6, k=256, V=2000, ctx=96, Hq=4, Hkv=2, D=128, F=512, lm_std=0.3)
+# trimmed draft vocabularies (Spec-Bench blog post, sections 1 and 5.1: the
+# draft's search space shrinks by 40-60%): half of the rows kept; same weights
+DRAFT_B64_TRIM = dataclasses.replace(DRAFT_B64, name="draft-b64-trim", vocab_keep=64128)
+DRAFT_SMALL_TRIM = dataclasses.replace(DRAFT_SMALL, name="draft-small-trim", vocab_keep=1000)
+
+
+def draft_vocab(shape: DraftShape) -> np.ndarray | None:
+    """The kept ids of a trimmed draft vocabulary: vocab_keep distinct ids of
+    [0, V), ascending, drawn uniformly (a stand-in for a frequency-ranked
+    subset, which needs corpus statistics); None for the full vocabulary."""
+    if not shape.vocab_keep:
+        return None
+    rng = child_rng(shape.wid, 0, C_VOCAB)
+    return np.sort(rng.choice(shape.V, shape.vocab_keep, replace=False)).astype(np.int32)
 
 
 def _blocks_bf16(wid: int, comp: int, shape, std: float, rb: int = 2048, threads: int | None = None) -> np.ndarray:

@@ -54,10 +54,11 @@ class Replay:
         return sel
 
 
-def replay(orc, shape, W, l, m, h, ctx_tok, follow):
-    """oracle.draft_tree along `follow`'s selections; the result carries the
-    margins under "margin"."""
+def replay(orc, shape, W, l, m, h, ctx_tok, follow, vocab=None):
+    """oracle.draft_tree along `follow`'s selections (with the trimmed draft
+    vocabulary `vocab`, if any); the result carries the margins under
+    "margin"."""
     ch = Replay(shape.topk, follow)
-    r = orc.draft_tree(shape, W, l, m, h, ctx_tok, chooser=ch)
+    r = orc.draft_tree(shape, W, l, m, h, ctx_tok, chooser=ch, vocab=vocab)
     r["margin"] = ch.margin
     return r

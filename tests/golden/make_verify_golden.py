@@ -1,7 +1,8 @@
 """Write the oracle's results for a full-size verify workload (default: the
 8B-shaped batch-1 step, seeds 0..4) to verify_<workload>.json: the draft tokens planted against the
-oracle's argmax, the oracle's per-node argmax and top-2 gap, and the accepted
-path. The benchmark reads the planted tokens from here (so no planting ever
+oracle's argmax (by the workload's planting rule), the oracle's per-node argmax and top-2 gap, and
+the accepted path. The stored files: llama8b-b1 (5 seeds), llama8b-b64 (2), llama70b-b8 (5), and
+the chain-vs-tree workloads chain60-b64, tree60-b64, chain40-b64, tree40-b64 (1 seed each). The benchmark reads the planted tokens from here (so no planting ever
 uses the GPU's own argmax) and the GPU tests compare against the rest.
 
 Calls only the oracle and the seeded generators. Usage:

@@ -174,3 +174,15 @@ def test_empty_batches_are_no_ops(lib):
     f = lib.eagle3_draft_fuse
     f.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_void_p] * 3 + [ctypes.c_int] * 4 + [ctypes.c_void_p] * 3 + [ctypes.c_size_t, ctypes.c_void_p]
     assert f(None, None, None, None, None, None, None, None, 0, 4096, 128256, 1, None, None, None, 0, None) == 0
+
+
+def test_vocab_map_errors(lib):
+    f = lib.eagle3_vocab_map
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                  ctypes.c_void_p]
+    assert f(FAKE, -1, FAKE, 10, FAKE, None, None) == -1      # n < 0
+    assert f(FAKE, 4, FAKE, 0, FAKE, None, None) == -1        # empty trimmed vocabulary
+    assert f(FAKE, 4, None, 10, FAKE, None, None) == -1       # no map
+    assert f(None, 4, FAKE, 10, FAKE, None, None) == -1       # no ids
+    assert f(FAKE, 4, FAKE, 10, None, None, None) == -1       # no output
+    assert f(None, 0, FAKE, 10, None, None, None) == 0        # nothing to map, no status: a no-op

@@ -17,6 +17,10 @@ section 4.2 for top-k 10 / 60 drafts).
   than twice that tolerance (2 x 2e-2 x the largest |logit| or |score|: a
   selection that is best for some values within the tolerance of the
   oracle's); the tree equals the renumbered selection exactly.
+* Trimmed draft vocabulary (half of the rows kept; small shape and full
+  size): the vocab_map kernel exactly (ids out of range give -1 and the
+  range status), and the trimmed draft head by the same replay, through the
+  oracle's trimmed head; every drafted token a kept id.
 """
 import numpy as np
 import pytest
@@ -129,11 +133,11 @@ def _f32(W, *arrays):
     return {k: cv(v) for k, v in W.items()}, [cv(a) for a in arrays]
 
 
-def _gpu_draft(shape, W, l, m, h, tok):
+def _gpu_draft(shape, W, l, m, h, tok, vocab=None):
     import tree_draft_verification_amd as e3
     wd = {k: dev(v) for k, v in W.items()}
     head = e3.DraftHead(wd, l.shape[0], shape.ctx, shape.Hq, shape.Hkv, shape.D, shape.steps, shape.topk,
-                        shape.n_drafts, shape.theta, shape.eps)
+                        shape.n_drafts, shape.theta, shape.eps, vocab=None if vocab is None else dev(vocab))
     dl, dm, dh, dt = dev(l), dev(m), dev(h), dev(tok)
     record = []
     head.run(dl, dm, dh, dt, record=record)
@@ -142,7 +146,7 @@ def _gpu_draft(shape, W, l, m, h, tok):
     return head, rec
 
 
-def _check_choices(orc, s, W, l, m, h, tok, head, rec, seqs, tol=2e-2):
+def _check_choices(orc, s, W, l, m, h, tok, head, rec, seqs, tol=2e-2, vocab=None):
     """The GPU's choices, replayed through the oracle's arithmetic: every
     number the GPU produced along them within `tol` (normwise), and no choice
     worse than the best alternative in the oracle's numbers by more than
@@ -157,7 +161,7 @@ def _check_choices(orc, s, W, l, m, h, tok, head, rec, seqs, tol=2e-2):
     follow = dict(ids=[r["ids"][seqs] for r in rec],
                   frontier=[r["next_pool"][seqs] - (r["pool_len"] if i else 0) for i, r in enumerate(rec)],
                   selected=selected)
-    f = replay(orc, s, W, l, m, h, tok, follow)
+    f = replay(orc, s, W, l, m, h, tok, follow, vocab=vocab)
     assert np.array_equal(host(head.parent)[seqs], f["parent"]), "tree structure differs"
     assert np.array_equal(host(head.tokens)[seqs], f["tokens"])
     assert normwise_rel(host(head.a_root)[seqs], f["a_root"])[0] <= tol
@@ -284,3 +288,68 @@ def test_verify_on_drafted_trees(orc, full_size_draft):
             assert np.array_equal(host(getattr(step, name))[:1], ref[name]), name
     print(f"verify on drafted trees: accept_len mean {acc_len.mean():.3f} (sequence 0: {acc_len[0]}, "
           f"flagged {bool(ref['flagged'][0])}), attention rel err {rel:.2e}")
+
+
+def test_vocab_map_kernel():
+    import tree_draft_verification_amd as e3
+    rng = np.random.default_rng(3)
+    vmap = np.sort(rng.choice(50000, 3000, replace=False)).astype(np.int32)
+    for n in (1, 1023, 1024, 6400):
+        ids = rng.integers(0, 3000, size=n).astype(np.int32)
+        d_ids, d_map = dev(ids), dev(vmap)
+        out = torch.full((n,), -7, dtype=torch.int32, device="cuda")
+        st = torch.full((1,), 99, dtype=torch.int32, device="cuda")
+        e3.eagle3_vocab_map(d_ids, d_map, out=out, status=st)
+        e3.eagle3_vocab_map(d_ids, d_map)                          # in place
+        torch.cuda.synchronize()
+        assert np.array_equal(host(out), vmap[ids]) and np.array_equal(host(d_ids), vmap[ids])
+        assert int(host(st)[0]) == 0
+    # out-of-range ids: -1 there, the rest mapped, the range status set
+    ids = np.array([0, 2999, 3000, -1, 17, 1 << 30], np.int32)
+    out = torch.empty(len(ids), dtype=torch.int32, device="cuda")
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    e3.eagle3_vocab_map(dev(ids), dev(vmap), out=out, status=st)
+    torch.cuda.synchronize()
+    assert host(out).tolist() == [vmap[0], vmap[2999], -1, -1, vmap[17], -1]
+    assert int(host(st)[0]) == -4                                   # EAGLE3_ERR_RANGE
+    # nothing to map: the status still reads OK
+    e3.eagle3_vocab_map(torch.empty(0, dtype=torch.int32, device="cuda"), dev(vmap), status=st)
+    torch.cuda.synchronize()
+    assert int(host(st)[0]) == 0
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_draft_head_small_trimmed_vocab_matches_oracle(orc, seed):
+    s = synth.DRAFT_SMALL_TRIM
+    vocab = synth.draft_vocab(s)
+    W = synth.draft_weights(s)
+    l, m, h, tok = synth.draft_inputs(s, seed)
+    head, rec = _gpu_draft(s, W, l, m, h, tok, vocab)
+    tk = host(head.tokens)
+    assert np.isin(tk[:, 1:], vocab).all() and np.isin(host(head.pool_token)[:, :s.pool_len], vocab).all()
+    info = _check_choices(orc, s, W, l, m, h, tok, head, rec, range(s.B), vocab=vocab)
+    ref = orc.draft_tree(s, W, l, m, h, tok, vocab=vocab)
+    same = sum(_paths(host(head.parent)[b], tk[b]) == _paths(ref["parent"][b], ref["tokens"][b])
+               for b in range(s.B))
+    print(f"trimmed vocab ({s.vocab_keep} of {s.V}), seed {seed}: {same}/{s.B} trees identical to the "
+          f"oracle's own; {info}")
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(400)
+def test_draft_head_full_size_trimmed_vocab_sequence0(orc):
+    """The full-size draft head with half of the 128256 vocabulary rows
+    kept; sequence 0 replayed through the oracle's trimmed head."""
+    s = synth.DRAFT_B64_TRIM
+    vocab = synth.draft_vocab(s)
+    W = synth.draft_weights(s)
+    l, m, h, tok = synth.draft_inputs(s, 0)
+    head, rec = _gpu_draft(s, W, l, m, h, tok, vocab)
+    del l, m, h
+    assert all(_valid(p) for p in host(head.parent))
+    assert np.isin(host(head.tokens)[:, 1:], vocab).all()
+    l0, m0, h0, t0 = synth.draft_inputs(s, 0, batch=slice(0, 1))
+    info = _check_choices(orc, s, W, l0, m0, h0, t0, head, rec, [0], vocab=vocab)
+    print(f"full size, trimmed vocab, sequence 0: {info}")
+    del head
+    torch.cuda.empty_cache()

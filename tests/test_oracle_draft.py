@@ -16,6 +16,11 @@
   run's choices): replaying its own choices reproduces its own tree with zero
   margins; swapping one taken child for the next one down costs exactly that
   logit gap.
+* Trimmed draft vocabulary (VocabTrim / FR-Spec reading): the root's children
+  equal a brute-force top-k of fp64 logits (numpy matmul of a hand-written
+  RMSNorm) with every dropped id set to -inf, their logp is taken against the
+  log-sum-exp of the kept ids alone, every drafted token is a kept id, and
+  keeping every id reproduces the untrimmed draft exactly.
 """
 import dataclasses
 
@@ -240,3 +245,57 @@ def test_bf16_draft_logits_move_with_last_bit_noise(orc):
     f32 = replay(orc, s, W32, n32, cv(m), cv(h), tok, r32["choices"])
     g32 = replay(orc, s, W32, cv(l), cv(m), cv(h), tok, r32["choices"])
     assert max(np.abs(a - b).max() for a, b in zip(f32["lm_val"], g32["lm_val"])) < 1e-4
+
+
+def test_trimmed_vocab_root_children_are_the_restricted_top_k(orc):
+    s = synth.DRAFT_SMALL_TRIM
+    vocab = synth.draft_vocab(s)
+    assert len(vocab) == s.vocab_keep and (np.diff(vocab) > 0).all()
+    W = synth.draft_weights(s)
+    l, m, h, tok = synth.draft_inputs(s, 0)
+    r = orc.draft_tree(s, W, l, m, h, tok, vocab=vocab)
+    C = s.topk
+    a = f64(r["a_root"])
+    hn = f64(_bf16(a / np.sqrt(np.mean(a * a, axis=1, keepdims=True) + s.eps)))
+    logits = hn @ f64(W["lm_head"]).T                                    # [B, V] fp64
+    dropped = np.ones(s.V, bool)
+    dropped[vocab] = False
+    masked = np.where(dropped[None, :], -np.inf, logits)
+    ids1 = np.asarray(r["choices"]["ids"][0]).reshape(s.B, C)
+    for b in range(s.B):
+        order = np.lexsort((np.arange(s.V), -masked[b]))[:C]
+        assert np.array_equal(ids1[b], order), b
+        kept = logits[b, vocab]
+        lse = kept.max() + np.log(np.exp(kept - kept.max()).sum())
+        want = (logits[b, order] - lse).astype(np.float32)
+        # step-1 pool entries are the root's children, score = logp
+        assert np.allclose(r["pool_score"][b, :C], want, rtol=0, atol=1e-5)
+        # the full-vocabulary lse is larger: dropping rows raises every logp
+        full = logits[b].max() + np.log(np.exp(logits[b] - logits[b].max()).sum())
+        assert full > lse
+    # every drafted token is a kept id (the root is the context's own token)
+    assert np.isin(r["tokens"][:, 1:], vocab).all()
+    assert np.isin(r["pool_token"], vocab).all()
+
+
+def test_trimmed_vocab_keeping_every_id_is_the_full_draft(orc):
+    s = dataclasses.replace(synth.DRAFT_SMALL, B=2, steps=4, n_drafts=30)
+    W = synth.draft_weights(s)
+    l, m, h, tok = (a[:2] for a in synth.draft_inputs(s, 1))
+    r = orc.draft_tree(s, W, l, m, h, tok)
+    t = orc.draft_tree(s, W, l, m, h, tok, vocab=np.arange(s.V, dtype=np.int32))
+    for key in ("parent", "tokens", "pool_score", "pool_token", "pool_parent"):
+        assert np.array_equal(r[key], t[key]), key
+    with pytest.raises(ValueError):
+        orc.draft_tree(s, W, l, m, h, tok, vocab=np.array([5, 3] + list(range(10, 30)), np.int32))
+
+
+def test_trimmed_vocab_replay_of_own_choices(orc):
+    s = dataclasses.replace(synth.DRAFT_SMALL_TRIM, B=2, steps=4, n_drafts=30)
+    vocab = synth.draft_vocab(s)
+    W = synth.draft_weights(s)
+    l, m, h, tok = (a[:2] for a in synth.draft_inputs(s, 2))
+    r = orc.draft_tree(s, W, l, m, h, tok, vocab=vocab)
+    f = replay(orc, s, W, l, m, h, tok, r["choices"], vocab=vocab)
+    assert np.array_equal(f["parent"], r["parent"]) and np.array_equal(f["tokens"], r["tokens"])
+    assert all((v == 0).all() for v in f["margin"].values())

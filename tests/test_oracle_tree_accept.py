@@ -203,3 +203,75 @@ def test_mean_tau_matches_closed_form(orc, tree, p, V):
     want = closed_form_tau(parent, p, V)
     se = tau.std() / np.sqrt(B)
     assert abs(tau.mean() - want) < 4 * se, (tau.mean(), want, se)
+
+
+def closed_form_tau_ranked(parent, p, V):
+    """E[tau] with siblings as alternatives (synth.plant_tokens_ranked): rank
+    j of a node's children carries the target's token with probability
+    q_j = p (1 - p)^(j - 1), exclusively; any other child matches by chance
+    with probability 1/V. With P_n(d) = P(a path from n accepts >= d drafts):
+    P_n(d) = sum_j q_j P_cj(d-1) + r_n(d), where r_n(d) (no ranked match) is
+    (1 - sum_j q_j) times the chance-match term of the independent formula,
+    and the chance term is dropped to first order when V is large."""
+    T = len(parent)
+    kids = [[] for _ in range(T)]
+    for n in range(1, T):
+        kids[parent[n]].append(n)
+    f = np.ones((T, T + 1))
+    for d in range(1, T + 1):
+        for n in range(T):
+            if not kids[n]:
+                f[n, d] = 0.0
+                continue
+            q = [p * (1 - p) ** j for j in range(len(kids[n]))]
+            ranked = sum(qj * f[c, d - 1] for qj, c in zip(q, kids[n]))
+            none = 1 - sum(q)
+            chance = 1 - np.prod([1 - f[c, d - 1] / V for c in kids[n]])
+            f[n, d] = ranked + none * chance
+    return 1 + f[0, 1:].sum()
+
+
+def test_ranked_planting_is_the_independent_one_on_a_chain():
+    rng = np.random.default_rng(5)
+    parent = np.tile(synth.chain_tree(40), (3, 1))
+    idx = rng.integers(0, 1000, size=parent.shape).astype(np.int32)
+    u = rng.random(parent.shape)
+    rid = rng.integers(0, 1000, size=parent.shape).astype(np.int32)
+    p = np.array([0.6, 0.8, 0.95])
+    assert np.array_equal(synth.plant_tokens_ranked(parent, idx, p, u, rid), synth.plant_tokens(parent, idx, p, u, rid))
+
+
+def test_ranked_planting_plants_at_most_one_sibling():
+    rng = np.random.default_rng(6)
+    parent = np.stack([synth.topk_tree(rng, 60, 7, 10) for _ in range(50)])
+    V = 10 ** 6
+    idx = rng.integers(0, V, size=parent.shape).astype(np.int32)
+    u = rng.random(parent.shape)
+    rid = rng.integers(0, V, size=parent.shape).astype(np.int32)
+    tok = synth.plant_tokens_ranked(parent, idx, np.full(50, 0.9), u, rid)
+    for b in range(50):
+        for n in range(len(parent[b])):
+            kids = np.nonzero(parent[b] == n)[0]
+            hits = [c for c in kids if tok[b, c] == idx[b, n] and tok[b, c] != rid[b, c]]
+            assert len(hits) <= 1
+            if hits:  # the planted child is the first one whose uniform passes
+                first = next(c for c in kids if u[b, c] < 0.9)
+                assert hits[0] == first
+
+
+@pytest.mark.parametrize("kind,p", [("chain", 0.7), ("topk", 0.7), ("topk", 0.9)])
+def test_mean_tau_ranked_matches_closed_form(orc, kind, p):
+    rng = np.random.default_rng(12)
+    parent = synth.chain_tree(40) if kind == "chain" else synth.topk_tree(rng, 40, 7, 10)
+    T, B, V = len(parent), 20000, 128256
+    idx = rng.integers(0, V, size=(B, T)).astype(np.int32)
+    u = rng.random((B, T))
+    rid = rng.integers(0, V, size=(B, T)).astype(np.int32)
+    tok = synth.plant_tokens_ranked(np.tile(parent, (B, 1)), idx, np.full(B, p), u, rid)
+    alen, _, _, _ = orc.accept(tok, np.tile(parent, (B, 1)), idx)
+    tau = alen + 1.0
+    want = closed_form_tau_ranked(parent, p, V)
+    se = tau.std() / np.sqrt(B)
+    assert abs(tau.mean() - want) < 4 * se, (tau.mean(), want, se)
+    if kind == "chain":
+        assert abs(want - closed_form_tau(parent, p, V)) < 1e-9

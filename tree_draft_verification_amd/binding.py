@@ -72,6 +72,7 @@ _rope = _sig("eagle3_rope", I, P, I, I, I, I, P, I, F, I, P)
 _embed = _sig("eagle3_embed", I, P, P, I, I, I, I, P, P)
 _commit_kv = _sig("eagle3_commit_kv", I, P, P, I, P, I, I, I, I, I, P, P, P, I, I, P, P)
 _copy_rows = _sig("eagle3_copy_rows", I, P, P, I, P, P, I, I, SZ, P)
+_vocab_map = _sig("eagle3_vocab_map", I, P, I, P, I, P, P, P)
 _draft_fuse_ws = _sig("eagle3_draft_fuse_workspace", SZ, I, I, I)
 _draft_fuse = _sig("eagle3_draft_fuse", I, P, P, P, P, P, P, P, P, I, I, I, I, P, P, P, SZ, P)
 _tree_expand = _sig("eagle3_tree_expand", I, P, P, P, I, I, P, P, P, I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P)
@@ -246,6 +247,16 @@ def eagle3_copy_rows(src, dst, n, src_rows=None, dst_rows=None, stream=None):
         raise ValueError("row sizes differ")
     _check(_copy_rows(_ptr(src), _ptr(src_rows), src.shape[0], _ptr(dst), _ptr(dst_rows), dst.shape[0], int(n), rb,
                       _stream(stream)), "eagle3_copy_rows")
+
+
+def eagle3_vocab_map(ids, vmap, out=None, status=None, stream=None):
+    """out[i] = vmap[ids[i]] over every element of ids (out defaults to ids:
+    in place); -1 for an id outside [0, len(vmap))."""
+    out = ids if out is None else out
+    if out.numel() != ids.numel():
+        raise ValueError("ids and out differ in size")
+    _check(_vocab_map(_ptr(ids), ids.numel(), _ptr(vmap), vmap.numel(), _ptr(out), _ptr(status), _stream(stream)),
+           "eagle3_vocab_map")
 
 
 def eagle3_commit_kv(k_rows, v_rows, src, start, k_cache, v_cache, block_table, max_n=None, stream=None):

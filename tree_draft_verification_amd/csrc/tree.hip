@@ -199,6 +199,27 @@ __global__ __launch_bounds__(64) void accept_kernel(const int32_t *__restrict__ 
     if (lane == 0) accept_len[b] = a;
 }
 
+// Trimmed draft vocabulary: row i of the trimmed LM head is full-vocabulary id
+// vmap[i]. One work-group walks the list (a draft step maps a few thousand
+// ids); an id outside [0, V_sub) becomes -1 and sets the flag.
+__global__ __launch_bounds__(1024) void vocab_map_kernel(const int32_t *__restrict__ ids, int n,
+                                                         const int32_t *__restrict__ vmap, int V_sub,
+                                                         int32_t *__restrict__ out, int32_t *__restrict__ status) {
+    __shared__ int bad_any;
+    if (threadIdx.x == 0) bad_any = 0;
+    __syncthreads();
+    bool bad = false;
+    for (int i = threadIdx.x; i < n; i += blockDim.x) {
+        const int r = ids[i];
+        const bool ok = r >= 0 && r < V_sub;
+        out[i] = ok ? vmap[r] : -1;
+        bad |= !ok;
+    }
+    if (__ballot(bad) != 0 && (threadIdx.x & 63) == 0) bad_any = 1;
+    __syncthreads();
+    if (status && threadIdx.x == 0) status[0] = bad_any ? EAGLE3_ERR_RANGE : EAGLE3_OK;
+}
+
 }  // namespace
 
 extern "C" int eagle3_tree_mask(const int32_t *parent, int B, int T, int W, uint64_t *mask, int32_t *depth,
@@ -230,6 +251,16 @@ extern "C" int eagle3_accept_path(const int32_t *tokens, const int32_t *parent, 
     else
         accept_kernel<2><<<B, 64, 0, e3_stream(stream)>>>(tokens, parent, mask, target_idx, T, accept_len, path,
                                                          out_tokens, V, status);
+    E3_LAUNCH_CHECK();
+    return EAGLE3_OK;
+}
+
+extern "C" int eagle3_vocab_map(const int32_t *ids, int n, const int32_t *vmap, int V_sub, int32_t *out,
+                                int32_t *status, void *stream) {
+    if (n < 0 || V_sub < 1) return EAGLE3_ERR_ARG;
+    if (n == 0 && !status) return EAGLE3_OK;
+    if ((n > 0 && (!ids || !out)) || !vmap) return EAGLE3_ERR_ARG;
+    vocab_map_kernel<<<1, 1024, 0, e3_stream(stream)>>>(ids, n, vmap, V_sub, out, status);
     E3_LAUNCH_CHECK();
     return EAGLE3_OK;
 }

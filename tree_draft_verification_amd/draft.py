@@ -20,6 +20,13 @@ of the pool, renumbered in creation order under the root.
 readings: Llama decoder layer (pre-norm, GQA, SwiGLU); logp from the target's
 LM head applied to RMSNorm(a); ties rank by creation index.
 
+Trimmed draft vocabulary (Spec-Bench blog post, sections 1, 3.2 and 5.1:
+VocabTrim / FR-Spec / SpecVocab): with `vocab` (kept ids, strictly
+ascending), the draft LM head holds only those rows (gathered once), its
+top-k, lse and logp range over them, and eagle3_vocab_map turns the chosen
+rows back into full-vocabulary ids before the tree and the next step's
+embedding see them.
+
 This module owns buffers and launch order only; every step is a kernel.
 """
 from __future__ import annotations
@@ -31,7 +38,7 @@ from . import binding as B_
 
 class DraftHead:
     def __init__(self, weights: dict, B: int, ctx: int, Hq: int, Hkv: int, D: int, steps: int = 8, topk: int = 10,
-                 n_drafts: int = 60, theta: float = 500000.0, eps: float = 1e-5, device="cuda"):
+                 n_drafts: int = 60, theta: float = 500000.0, eps: float = 1e-5, device="cuda", vocab=None):
         self.dev = torch.device(device)
         self.w = {k: v.to(self.dev).contiguous() for k, v in weights.items()}
         E = self.w["embed"]
@@ -81,7 +88,15 @@ class DraftHead:
         self.ids = torch.empty(M, C, dtype=i32, device=dv)
         self.val = torch.empty(M, C, dtype=torch.float32, device=dv)
         self.lse = torch.empty(M, dtype=torch.float32, device=dv)
-        self.lm_ws = torch.empty(B_.eagle3_lmhead_workspace(M, self.V, self.k, C, B_._dtype(E)),
+        self.lm_w, self.vmap = self.w["lm_head"], None
+        if vocab is not None:
+            vh = torch.as_tensor(vocab).to("cpu", torch.int64).reshape(-1)
+            if len(vh) <= C or not bool((vh[1:] > vh[:-1]).all()) or vh[0] < 0 or vh[-1] >= self.lm_w.shape[0]:
+                raise ValueError("vocab must be strictly ascending LM-head row ids, more than topk of them")
+            self.vmap = vh.to(dv, i32)
+            self.lm_w = torch.empty(len(vh), self.k, dtype=bf, device=dv)
+            B_.eagle3_copy_rows(self.w["lm_head"], self.lm_w, len(vh), src_rows=self.vmap)
+        self.lm_ws = torch.empty(B_.eagle3_lmhead_workspace(M, self.lm_w.shape[0], self.k, C, B_._dtype(E)),
                                  dtype=torch.uint8, device=dv)
         f32 = torch.float32
         self.pool_score = torch.empty(B, self.pool_cap, dtype=f32, device=dv)
@@ -176,10 +191,12 @@ class DraftHead:
         ev = self.events.pop(0) if self.events else None
         if ev:
             ev[0].record()
-        B_.eagle3_lmhead_argmax(hn, self.w["lm_head"], self.C, self.ids[:M], self.val[:M], None, self.lse[:M],
+        B_.eagle3_lmhead_argmax(hn, self.lm_w, self.C, self.ids[:M], self.val[:M], None, self.lse[:M],
                                 self.lm_ws)
         if ev:
             ev[1].record()
+        if self.vmap is not None:
+            B_.eagle3_vocab_map(self.ids[:M], self.vmap)
 
     # ----------------------------------------------------------- growth
     def grow(self, record=None):
