@@ -19,6 +19,8 @@ starts):
   chain60-b64, tree60-b64, chain40-b64, tree40-b64
               chain vs tree drafts at equal node budgets (8B shapes, batch 64);
               chain-vs-tree runs all four and reports tau against nodes/s
+  target8b-b64 the target model's own 32 decoder layers over the 64 trees
+              (8B shapes, random weights), LM head and acceptance
 
 Prints ONE JSON line: verified tree nodes/s (value), accepted tokens per
 verify step (verify workloads: draft tokens planted against the oracle's
@@ -56,7 +58,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama8b-b64",
-                    choices=VERIFY_WORKLOADS + CHAIN_TREE_WORKLOADS + ("draft-b64", "draft-b64-trim", "chain-vs-tree"))
+                    choices=VERIFY_WORKLOADS + CHAIN_TREE_WORKLOADS + ("draft-b64", "draft-b64-trim", "chain-vs-tree",
+                                                                         "target8b-b64"))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="minimum oracle time in the CPU-baseline sample")
     ap.add_argument("--w-copies", type=int, default=3, help="LM-head copies cycled by the timed steps")
@@ -431,6 +434,99 @@ def bench_draft(args, name="draft-b64"):
     }
 
 
+def bench_target(args, name="target8b-b64"):
+    """The target model's own pass over 64 draft trees of 61 nodes at 8B
+    shapes: embedding, 32 decoder layers (QKV / O / gate-up / down GEMMs at
+    M = 3904 rows, RoPE at cached length + depth, tree attention over each
+    layer's paged prefix of 200-1500 tokens), final RMSNorm, LM-head argmax,
+    acceptance. Random weights and random draft tokens (acceptance is rare by
+    construction). The dominant kernel is the gate/up GEMM (3904 x 28672 x
+    4096 per layer)."""
+    import numpy as np
+    import torch
+
+    import synth
+    import tree_draft_verification_amd as e3
+
+    s = synth.TARGET_8B
+    t0 = time.time()
+    W = synth.target_weights(s)
+    inp = synth.target_inputs(s, 0)
+    Wd = {k: to_dev(v) for k, v in W.items()}
+    kc = [to_dev(c) for c in inp.k_cache]
+    vc = [to_dev(c) for c in inp.v_cache]
+    log(f"[bench] {name}: weights and caches ready in {time.time() - t0:.1f}s")
+    model = e3.TargetModel(Wd, s.layers, s.B, s.T, s.Hq, s.Hkv, s.D, kc, vc, to_dev(inp.block_table),
+                           to_dev(inp.prefix_len), s.theta, s.eps)
+    parent, tokens = to_dev(inp.parent), to_dev(inp.tokens)
+    for _ in range(max(1, args.warmup)):
+        model.run(parent, tokens)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        model.run(parent, tokens)
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t_start) * 1e3 / args.steps
+    sclk = gpu_sclk_mhz() if args.clock_query else None
+    # one more step with HIP events around every layer's gate/up GEMM and
+    # attention (outside the timed region)
+    E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    model.events = {k: [(E(), E()) for _ in range(s.layers)] for k in ("gu", "attn")}
+    model.run(parent, tokens)
+    torch.cuda.synchronize()
+    gu_list = [a.elapsed_time(b) * 1e3 for a, b in model.events["gu"]]
+    at_list = [a.elapsed_time(b) * 1e3 for a, b in model.events["attn"]]
+    model.events = None
+    gu_us, at_us = float(np.mean(gu_list)), float(np.mean(at_list))
+    M = s.B * s.T
+    fl = 2.0 * M * (2 * s.F) * s.k
+    ach = fl / (gu_us * 1e-6) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "kernel": "eagle3_gemm (gate/up projection, 3904 x 28672 x 4096)", "flops_per_launch": fl,
+                "avg_launch_us": round(gu_us, 2), "launch_us_p10_p50_p90": pcts(gu_list)}
+    qd, kvd = s.Hq * s.D, s.Hkv * s.D
+    step_flops = 2.0 * M * s.k * (qd + 2 * kvd + qd + 3 * s.F) * s.layers + 2.0 * M * s.k * s.V
+    al = model.accept_len.cpu().numpy()
+    nodes = s.B * s.n_drafts
+    value = nodes / (ms_per_step * 1e-3)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+        one = synth.target_inputs(s, 0, batch=slice(0, 1))
+        n_l = 2
+        t0 = time.perf_counter()
+        oracle.target_forward(one, W, batch=slice(0, 1), layers=n_l)
+        t_part = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        oracle.target_forward(one, W, batch=slice(0, 1), layers=1)
+        t_one = time.perf_counter() - t0
+        t_layer = t_part - t_one                      # one layer
+        t_step = t_one - t_layer + s.layers * t_layer  # embedding + head + every layer
+        log(f"[bench] cpu baseline: one layer {t_layer:.1f}s, est. whole step {t_step:.1f}s on {threads} threads")
+        cpu = {"value": round(s.n_drafts / t_step, 3), "unit": "nodes/s", "cores": threads, "kind": "oracle",
+               "sample": f"sequence 0 of {name} through the oracle with 2 layers and with 1 layer "
+                         f"({t_part + t_one:.1f} s); the step time is scaled to 32 layers from their difference"}
+    return {
+        "metric": METRIC, "value": round(value, 1), "unit": "nodes/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": name, "batch": s.B, "draft_nodes": s.n_drafts, "tree_depth": s.depth,
+                   "layers": s.layers, "hidden": s.k, "heads_q_kv": [s.Hq, s.Hkv], "head_dim": s.D, "ffn": s.F,
+                   "vocab": s.V, "prefix": list(s.prefix)},
+        "accepted_tok_per_step": round(float(np.mean(al + 1)), 3), "tau_samples": int(len(al)),
+        "tau_note": "random weights and random draft tokens: acceptance is rare by construction",
+        "step_tflop": round(step_flops / 1e12, 2),
+        "step_pflops": round(step_flops / (ms_per_step * 1e-3) / 1e15, 3),
+        "attn_avg_launch_us": round(at_us, 2),
+        "sclk_mhz_after_timed_region": sclk, "launch": "eager",
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -446,6 +542,8 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.workload in ("draft-b64", "draft-b64-trim"):
         out = bench_draft(args, args.workload)
+    elif args.workload == "target8b-b64":
+        out = bench_target(args)
     elif args.workload == "chain-vs-tree":
         out = bench_chain_vs_tree(args)
     else:

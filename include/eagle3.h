@@ -229,6 +229,16 @@ int eagle3_accept_path(const int32_t *tokens, const int32_t *parent, const uint6
 
 
 /*
+ * Node positions for the target's pass over a tree ([lesson] "Verify-accept
+ * semantics": the drafts continue the committed sequence; reading: a node at
+ * depth d sits d places after the root, and the root takes the first free
+ * position): pos[b][t] = prefix_len[b] + depth[b][t]. prefix_len [B], depth
+ * and pos [B, T] int32 device (depth from eagle3_tree_mask); B * T < 2^31.
+ */
+int eagle3_node_positions(const int32_t *prefix_len, const int32_t *depth, int B, int T, int32_t *pos,
+                          void *stream);
+
+/*
  * Trimmed draft vocabulary ([blog] sections 1, 3.2 and 5.1: VocabTrim, FR-Spec
  * and SpecVocab shrink the draft's search space by 40-60%). The draft LM head
  * runs over V_sub kept rows, row i being full-vocabulary id vmap[i] (gather

@@ -415,6 +415,67 @@ def toy_speculative(shape=synth.TOY, seed=0, n_new=None, parent=None, p_match=No
     return np.asarray(out[:n_new], np.int32), steps
 
 
+# ------------------------------------------------------------------ target model
+
+def target_layer(shape, W, i, x, pos, mask, kv):
+    """Decoder layer i of the target over the tree rows of B sequences.
+
+    Course lesson "EAGLE-3 speculative decoding: the tree-verifier method":
+    the target runs once over the whole tree, each token attending to the
+    cached context and its own ancestors. reading: a Llama decoder layer
+    (pre-norm RMSNorm with gamma = 1, GQA projections, rotate-half RoPE at
+    position prefix length + depth, tree attention over the layer's paged
+    prefix plus the ancestor-masked tree rows, output projection + residual,
+    RMSNorm, SwiGLU MLP + residual), every intermediate stored in x's type.
+    x [B, T, k]; pos [B, T]; mask [B, T, W]. Returns (x_out, k_rows, v_rows)
+    with the rows' K (after RoPE) and V [B, T, Hkv, D] for the cache."""
+    s = shape
+    B, T, k = x.shape
+    qd, kvd = s.Hq * s.D, s.Hkv * s.D
+    wqkv = W[f"l{i}.wqkv"]
+    xr = x.reshape(B * T, k)
+    h = rmsnorm(xr, eps=s.eps)
+    p = pos.reshape(-1)
+    q = rope(gemm(h, wqkv[:qd]).reshape(B * T, s.Hq, s.D), p, s.theta)
+    kr = rope(gemm(h, wqkv[qd:qd + kvd]).reshape(B * T, s.Hkv, s.D), p, s.theta)
+    vr = gemm(h, wqkv[qd + kvd:]).reshape(B * T, s.Hkv, s.D)
+    q4, k4, v4 = q.reshape(B, T, s.Hq, s.D), kr.reshape(B, T, s.Hkv, s.D), vr.reshape(B, T, s.Hkv, s.D)
+    attn, _ = tree_attn(q4, k4, v4, kv, mask, want_lse=False)
+    xr = gemm(attn.reshape(B * T, qd), W[f"l{i}.wo"], R=xr)
+    f = silu_mul(gemm(rmsnorm(xr, eps=s.eps), W[f"l{i}.wgu"]))
+    xr = gemm(f, W[f"l{i}.wd"], R=xr)
+    return xr.reshape(B, T, k), k4, v4
+
+
+def target_forward(inp: synth.TargetInputs, W, batch=None, layers=None):
+    """The target's pass over the draft trees: embedding of every node's
+    token, the decoder layers, final RMSNorm, LM head (top-2) and the greedy
+    acceptance of the nodes' tokens. ``batch`` selects sequences; ``layers``
+    runs only the first n layers. Returns the per-layer inputs "x" (x[0] is
+    the embedding, x[n] the last layer's output), the tree K/V rows per layer,
+    argmax / gap per node and the accepted path."""
+    s = inp.shape
+    sel = np.arange(s.B) if batch is None else np.arange(s.B)[batch]
+    parent, tokens = inp.parent[sel], inp.tokens[sel]
+    B, T = parent.shape
+    n_layers = s.layers if layers is None else layers
+    mask, depth = tree_mask(parent)
+    pos = (inp.prefix_len[sel][:, None] + depth).astype(np.int32)
+    x = embed(W["embed"], tokens.reshape(-1)).reshape(B, T, s.k)
+    xs, rows = [x], []
+    for i in range(n_layers):
+        x, kr, vr = target_layer(s, W, i, x, pos, mask, inp.kv(i, sel))
+        xs.append(x)
+        rows.append((kr, vr))
+    hf = rmsnorm(x.reshape(B * T, s.k), eps=s.eps)
+    idx, val, gap, _ = lmhead(hf, W["lm_head"], topk=2)
+    idx1 = idx[:, 0].reshape(B, T).copy()
+    alen, path, out, end = accept(tokens, parent, idx1)
+    return dict(x=xs, rows=rows, mask=mask, depth=depth, pos=pos, hidden=hf, idx=idx1, gap=gap.reshape(B, T),
+                accept_len=alen, path=path, out_tokens=out, end=end,
+                flagged=flags(parent, tokens, idx1, gap.reshape(B, T)))
+
+
 # ------------------------------------------------------------------ draft head
 
 def _page(rows_k, rows_v, bs=16):

@@ -132,6 +132,40 @@ def topk_level_sizes(rng: np.random.Generator, n_drafts: int, depth: int, branch
     return sizes
 
 
+def ranked_tree(p: float, n_drafts: int = 60, depth: int = 8, branch: int = 10) -> np.ndarray:
+    """The tree a confidence-ranked drafter keeps when its confidence is
+    calibrated to the ranked match model (plant_tokens_ranked): the rank-j
+    child of a node is on the target's path with probability
+    p (1 - p)^(j - 1) given its parent is, so a node's path probability is
+    the product over its path; the tree is the n_drafts nodes of highest path
+    probability (ties: first created first) with at most `branch` children
+    per node and depth at most `depth`, grown best-first. Creation order is
+    the numbering, so parents precede children and a node's children appear
+    in rank order."""
+    import heapq
+    parent = [-1]
+    heap, made = [], 0        # entries: (-path probability, creation counter, parent node, rank)
+
+    def push_children(node, prob):
+        nonlocal made
+        for j in range(1, branch + 1):
+            heapq.heappush(heap, (-prob * p * (1.0 - p) ** (j - 1), made, node, j))
+            made += 1
+
+    depth_of = [0]
+    prob_of = [1.0]
+    push_children(0, 1.0)
+    while len(parent) < n_drafts + 1:
+        negp, _, par, _ = heapq.heappop(heap)
+        node = len(parent)
+        parent.append(par)
+        depth_of.append(depth_of[par] + 1)
+        prob_of.append(-negp)
+        if depth_of[node] < depth:
+            push_children(node, -negp)
+    return np.asarray(parent, dtype=np.int32)
+
+
 def topk_tree(rng: np.random.Generator, n_drafts: int = 60, depth: int = 7, branch: int = 10) -> np.ndarray:
     """Random parent[] consistent with top-`branch` expansion, BFS numbered.
 
@@ -253,7 +287,7 @@ class VerifyShape:
     prefix: tuple = (1024, 1024)   # inclusive range of prefix lengths
     p_match: tuple = (0.88, 0.88)  # per-sequence match probability range
     dtype: str = "bf16"
-    tree: str = "topk"             # "topk" (top-`branch` expansion) or "chain"
+    tree: str = "topk"             # "topk" (random top-`branch` expansion), "chain" or "ranked" (ranked_tree)
     planting: str = "independent"  # "independent" or "ranked" (see plant_tokens_ranked)
 
     @property
@@ -272,12 +306,16 @@ LLAMA70B_B8 = VerifyShape("llama70b-b8", 4, B=8, Hq=64, Hkv=8, D=128, V=128256, 
                           prefix=(4096, 4096))
 # chain vs tree at equal node budgets (60 and 40 draft tokens), 8B shapes at
 # batch 64, per-sequence match probability uniform in 0.6-0.95; siblings of a
-# tree are alternatives (at most one of them is the target's token)
+# tree are alternatives (at most one of them is the target's token) and the
+# tree is the one a calibrated drafter keeps (ranked_tree: depth <= 8, the
+# number of draft steps; top-10 children). A chain and a tree of one budget
+# share the workload id, so their prefixes, match probabilities and planting
+# draws are the same: a paired comparison
 CHAIN_TREE = tuple(
     VerifyShape(f"{kind}{n}-b64", wid, B=64, Hq=32, Hkv=8, D=128, V=128256, n_drafts=n,
-                depth=n if kind == "chain" else 7, branch=1 if kind == "chain" else 10, prefix=(200, 1500),
-                p_match=(0.6, 0.95), tree="chain" if kind == "chain" else "topk", planting="ranked")
-    for wid, (kind, n) in enumerate((("chain", 60), ("tree", 60), ("chain", 40), ("tree", 40)), start=5))
+                depth=n if kind == "chain" else 8, branch=1 if kind == "chain" else 10, prefix=(200, 1500),
+                p_match=(0.6, 0.95), tree=kind if kind == "chain" else "ranked", planting="ranked")
+    for wid, (kind, n) in ((5, ("chain", 60)), (5, ("tree", 60)), (7, ("chain", 40)), (7, ("tree", 40))))
 VERIFY_SHAPES = {s.name: s for s in (LLAMA8B_B1, LLAMA8B_B64, LLAMA70B_B8) + CHAIN_TREE}
 
 
@@ -304,11 +342,6 @@ def verify_inputs(shape: VerifyShape, seed: int, batch: slice | None = None) -> 
     then sliced for the small arrays; the prefix KV, the only large one, is
     drawn for every sequence up to the last requested one)."""
     B, T = shape.B, shape.T
-    rt = child_rng(shape.wid, seed, C_TREE)
-    if shape.tree == "chain":
-        parent = np.stack([chain_tree(shape.n_drafts) for _ in range(B)])
-    else:
-        parent = np.stack([topk_tree(rt, shape.n_drafts, shape.depth, shape.branch) for _ in range(B)])
     rl = child_rng(shape.wid, seed, C_PLEN)
     lo, hi = shape.prefix
     plen = rl.integers(lo, hi + 1, size=B).astype(np.int32)
@@ -317,6 +350,14 @@ def verify_inputs(shape: VerifyShape, seed: int, batch: slice | None = None) -> 
     p_seq = rp.uniform(plo, phi, size=B) if phi > plo else np.full(B, plo)
     plant_u = rp.random((B, T))
     plant_id = rp.integers(0, shape.V, size=(B, T)).astype(np.int32)
+    rt = child_rng(shape.wid, seed, C_TREE)
+    if shape.tree == "chain":
+        parent = np.stack([chain_tree(shape.n_drafts) for _ in range(B)])
+    elif shape.tree == "ranked":
+        parent = np.stack([ranked_tree(float(p_seq[b]), shape.n_drafts, shape.depth, shape.branch)
+                           for b in range(B)])
+    else:
+        parent = np.stack([topk_tree(rt, shape.n_drafts, shape.depth, shape.branch) for _ in range(B)])
     q = normal_bf16(child_rng(shape.wid, seed, C_Q), (B, T, shape.Hq, shape.D))
     kt = normal_bf16(child_rng(shape.wid, seed, C_KTREE), (B, T, shape.Hkv, shape.D))
     vt = normal_bf16(child_rng(shape.wid, seed, C_VTREE), (B, T, shape.Hkv, shape.D))
@@ -579,3 +620,129 @@ def attn_inputs(workload_id: int, seed: int, B: int, Tq: int, Tk: int, Hq: int, 
     kt = draw(child_rng(workload_id, seed, C_KTREE), (B, Tk, Hkv, D))
     vt = draw(child_rng(workload_id, seed, C_VTREE), (B, Tk, Hkv, D))
     return AttnInputs(q, kt, vt, kv)
+
+
+# ---------------------------------------------------------------- target model
+
+@dataclasses.dataclass(frozen=True)
+class TargetShape:
+    """A Llama-style target decoder run over a batch of draft trees (the
+    verify pass with the target's own layers: QKV / O / MLP GEMMs at
+    M = B * T rows, RoPE at P + depth, tree attention over a paged prefix per
+    layer). 8B shapes by default (LLaMA-3-8B: 32 layers, hidden 4096, 32 / 8
+    heads of 128, FFN 14336, vocab 128256); random weights."""
+    name: str = "target8b-b64"
+    wid: int = 9
+    layers: int = 32
+    B: int = 64
+    k: int = 4096
+    Hq: int = 32
+    Hkv: int = 8
+    D: int = 128
+    F: int = 14336
+    V: int = 128256
+    n_drafts: int = 60
+    depth: int = 7
+    branch: int = 10
+    prefix: tuple = (200, 1500)
+    theta: float = 500000.0
+    eps: float = 1e-5
+    std: float = 0.02
+    # the layers whose outputs feed a draft head as low / mid / high features
+    features: tuple = (2, 16, 29)
+
+    @property
+    def T(self):
+        return self.n_drafts + 1
+
+
+TARGET_8B = TargetShape()
+# small shapes for element-wise parity: two layers, several tiles, ragged tails
+TARGET_SMALL = TargetShape("target-small", 31, layers=2, B=3, k=256, Hq=4, Hkv=2, D=128, F=512, V=2000,
+                           n_drafts=40, depth=6, prefix=(37, 300), features=(0, 1))
+
+
+def target_weights(shape: TargetShape) -> dict:
+    """bf16 N(0, std^2) weights, output-major ([out, in]): embed [V, k],
+    lm_head [V, k], and per layer i: l{i}.wqkv [(Hq + 2 Hkv) D, k] (q rows,
+    then k, then v), l{i}.wo [k, Hq D], l{i}.wgu [2F, k] (gate rows, then up),
+    l{i}.wd [k, F]. Each matrix from its own row-block streams."""
+    k, F, V = shape.k, shape.F, shape.V
+    qd, kvd = shape.Hq * shape.D, shape.Hkv * shape.D
+    W = {"embed": _blocks_bf16(shape.wid, 300, (V, k), shape.std),
+         "lm_head": _blocks_bf16(shape.wid, 301, (V, k), shape.std)}
+    for i in range(shape.layers):
+        for j, (name, shp) in enumerate((("wqkv", (qd + 2 * kvd, k)), ("wo", (k, qd)), ("wgu", (2 * F, k)),
+                                         ("wd", (k, F)))):
+            W[f"l{i}.{name}"] = _blocks_bf16(shape.wid, 400 + 4 * i + j, shp, shape.std)
+    return W
+
+
+@dataclasses.dataclass
+class TargetInputs:
+    shape: TargetShape
+    seed: int
+    parent: np.ndarray      # int32 [B, T]
+    tokens: np.ndarray      # int32 [B, T] (node 0: the last committed token)
+    prefix_len: np.ndarray  # int32 [B]
+    block_table: np.ndarray  # int32 [B, max_blocks], shared by every layer
+    k_cache: list           # per layer [num_blocks, Hkv, 16, D]
+    v_cache: list           # per layer [num_blocks, Hkv, D, 16]
+
+    def kv(self, layer: int, batch=None) -> PagedKV:
+        bt, pl = self.block_table, self.prefix_len
+        if batch is not None:
+            bt, pl = bt[batch], pl[batch]
+        return PagedKV(self.k_cache[layer], self.v_cache[layer], bt, pl, 16)
+
+
+def target_inputs(shape: TargetShape, seed: int, batch: slice | None = None, dtype: str = "bf16",
+                  threads: int | None = None, reserve: int = 16) -> TargetInputs:
+    """Trees (random top-`branch` expansion), uniform random tokens and a
+    per-layer prefix K/V ~ N(0, 1) standing in for a committed context of
+    prefix_len tokens (uniform in shape.prefix). One shuffled block pool per
+    layer under one block table; every sequence owns blocks for `reserve`
+    more tokens after its prefix (room to commit accepted rows); unused slots
+    hold NaN. Each (layer, sequence) prefix comes from its own stream, so
+    ``batch`` draws only the sequences it keeps (the block table is still the
+    full batch's)."""
+    import concurrent.futures
+    import os
+    B, T, bs = shape.B, shape.T, 16
+    rt = child_rng(shape.wid, seed, C_TREE)
+    parent = np.stack([topk_tree(rt, shape.n_drafts, shape.depth, shape.branch) for _ in range(B)])
+    tokens = child_rng(shape.wid, seed, C_PROMPT).integers(0, shape.V, size=(B, T)).astype(np.int32)
+    lo, hi = shape.prefix
+    plen = child_rng(shape.wid, seed, C_PLEN).integers(lo, hi + 1, size=B).astype(np.int32)
+    nb = (plen + bs - 1) // bs
+    own = (plen + reserve + bs - 1) // bs            # blocks a sequence owns
+    nblk = int(own.sum()) + 1
+    perm = child_rng(shape.wid, seed, C_PERM).permutation(nblk).astype(np.int32)
+    max_blocks = int(own.max())
+    table = np.full((B, max_blocks), perm[-1], np.int32)
+    off = np.concatenate([[0], np.cumsum(own)])
+    for b in range(B):
+        table[b, :own[b]] = perm[off[b]:off[b + 1]]
+    keep = np.arange(B) if batch is None else np.arange(B)[batch]
+    f32 = dtype == "f32"
+    npdt, nan = (np.float32, np.float32(np.nan)) if f32 else (np.uint16, BF16_NAN)
+    draw = normal_f32 if f32 else normal_bf16
+    Hkv, D = shape.Hkv, shape.D
+    kc = [np.full((nblk, Hkv, bs, D), nan, npdt) for _ in range(shape.layers)]
+    vc = [np.full((nblk, Hkv, D, bs), nan, npdt) for _ in range(shape.layers)]
+
+    def fill(job):
+        layer, b = job
+        L = int(plen[b])
+        kb = draw(np.random.default_rng([shape.wid, seed, C_KPRE, layer, b]), (L, Hkv, D))
+        vb = draw(np.random.default_rng([shape.wid, seed, C_VPRE, layer, b]), (L, Hkv, D))
+        for j in range(nb[b]):
+            phys = table[b, j]
+            r0, r1 = j * bs, min(L, (j + 1) * bs)
+            kc[layer][phys, :, :r1 - r0, :] = kb[r0:r1].transpose(1, 0, 2)
+            vc[layer][phys, :, :, :r1 - r0] = vb[r0:r1].transpose(1, 2, 0)
+
+    jobs = [(layer, int(b)) for layer in range(shape.layers) for b in keep]
+    with concurrent.futures.ThreadPoolExecutor(threads or min(16, os.cpu_count() or 1)) as ex:
+        list(ex.map(fill, jobs))
+    return TargetInputs(shape, seed, parent, tokens, plen, table, kc, vc)

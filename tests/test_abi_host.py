@@ -186,3 +186,13 @@ def test_vocab_map_errors(lib):
     assert f(None, 4, FAKE, 10, FAKE, None, None) == -1       # no ids
     assert f(FAKE, 4, FAKE, 10, None, None, None) == -1       # no output
     assert f(None, 0, FAKE, 10, None, None, None) == 0        # nothing to map, no status: a no-op
+
+
+def test_node_positions_errors(lib):
+    f = lib.eagle3_node_positions
+    f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    assert f(FAKE, FAKE, -1, 4, FAKE, None) == -1
+    assert f(FAKE, FAKE, 2, 0, FAKE, None) == -1
+    assert f(None, FAKE, 2, 4, FAKE, None) == -1
+    assert f(FAKE, FAKE, 2, 4, None, None) == -1
+    assert f(None, None, 0, 4, None, None) == 0

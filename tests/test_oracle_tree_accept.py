@@ -10,7 +10,12 @@ What fixes the answers here, independently of oracle.c:
   and bit tests instead of path enumeration, checked exhaustively on all 2^15
   match patterns of the 15-draft binary tree and on thousands of random trees;
 * the closed-form expected acceptance length under independent per-edge
-  matches, checked statistically.
+  matches, checked statistically, and under ranked sibling matches (siblings
+  as alternatives) on chains, random top-k trees and the best-first trees of
+  a calibrated drafter;
+* the best-first tree (synth.ranked_tree) against brute-force enumeration of
+  every rank path of a small tree, and its expected acceptance length against
+  a chain of the same size.
 """
 import itertools
 import json
@@ -259,10 +264,11 @@ def test_ranked_planting_plants_at_most_one_sibling():
                 assert hits[0] == first
 
 
-@pytest.mark.parametrize("kind,p", [("chain", 0.7), ("topk", 0.7), ("topk", 0.9)])
+@pytest.mark.parametrize("kind,p", [("chain", 0.7), ("topk", 0.7), ("topk", 0.9), ("ranked", 0.7), ("ranked", 0.9)])
 def test_mean_tau_ranked_matches_closed_form(orc, kind, p):
     rng = np.random.default_rng(12)
-    parent = synth.chain_tree(40) if kind == "chain" else synth.topk_tree(rng, 40, 7, 10)
+    parent = {"chain": lambda: synth.chain_tree(40), "topk": lambda: synth.topk_tree(rng, 40, 7, 10),
+              "ranked": lambda: synth.ranked_tree(p, 40, 8, 10)}[kind]()
     T, B, V = len(parent), 20000, 128256
     idx = rng.integers(0, V, size=(B, T)).astype(np.int32)
     u = rng.random((B, T))
@@ -275,3 +281,44 @@ def test_mean_tau_ranked_matches_closed_form(orc, kind, p):
     assert abs(tau.mean() - want) < 4 * se, (tau.mean(), want, se)
     if kind == "chain":
         assert abs(want - closed_form_tau(parent, p, V)) < 1e-9
+
+
+def _rank_paths(parent):
+    """Each node's path as the tuple of its ranks (1-based position among its
+    siblings in index order), root = ()."""
+    out = [()]
+    for n in range(1, len(parent)):
+        sib = [c for c in range(1, len(parent)) if parent[c] == parent[n]]
+        out.append(out[parent[n]] + (sib.index(n) + 1,))
+    return out
+
+
+@pytest.mark.parametrize("p,N", [(0.7, 12), (0.55, 20), (0.9, 9)])
+def test_ranked_tree_is_the_top_n_by_path_probability(p, N):
+    depth, branch = 3, 3
+    parent = synth.ranked_tree(p, N, depth, branch)
+    assert len(parent) == N + 1 and parent[0] == -1 and all(0 <= parent[n] < n for n in range(1, N + 1))
+    paths = _rank_paths(parent)
+    assert len(set(paths)) == N + 1 and all(len(t) <= depth and max(t, default=1) <= branch for t in paths)
+    prob = lambda t: float(np.prod([p * (1 - p) ** (j - 1) for j in t]))  # noqa: E731
+    every = [t for d in range(1, depth + 1) for t in itertools.product(range(1, branch + 1), repeat=d)]
+    best = sorted((prob(t) for t in every), reverse=True)[:N]
+    got = sorted((prob(t) for t in paths[1:]), reverse=True)
+    assert np.allclose(got, best, rtol=0, atol=1e-15)
+    # closed under parents and siblings of lower rank (both at least as likely)
+    have = set(paths)
+    for t in paths[1:]:
+        assert t[:-1] in have and (t[-1] == 1 or t[:-1] + (t[-1] - 1,) in have)
+
+
+@pytest.mark.parametrize("p", [0.6, 0.8, 0.95])
+def test_ranked_tree_beats_a_chain_of_the_same_size(p):
+    """Without a depth limit the chain is one of the candidate trees, so the
+    best-first tree's expected acceptance is at least the chain's; with the
+    8-step limit it still beats a chain of 8."""
+    V = 128256
+    for N in (20, 40):
+        free = closed_form_tau_ranked(synth.ranked_tree(p, N, N, 10), p, V)
+        assert free >= closed_form_tau_ranked(synth.chain_tree(N), p, V) - 1e-12
+    assert closed_form_tau_ranked(synth.ranked_tree(p, 40, 8, 10), p, V) > \
+        closed_form_tau_ranked(synth.chain_tree(8), p, V)

@@ -73,6 +73,7 @@ _embed = _sig("eagle3_embed", I, P, P, I, I, I, I, P, P)
 _commit_kv = _sig("eagle3_commit_kv", I, P, P, I, P, I, I, I, I, I, P, P, P, I, I, P, P)
 _copy_rows = _sig("eagle3_copy_rows", I, P, P, I, P, P, I, I, SZ, P)
 _vocab_map = _sig("eagle3_vocab_map", I, P, I, P, I, P, P, P)
+_node_pos = _sig("eagle3_node_positions", I, P, P, I, I, P, P)
 _draft_fuse_ws = _sig("eagle3_draft_fuse_workspace", SZ, I, I, I)
 _draft_fuse = _sig("eagle3_draft_fuse", I, P, P, P, P, P, P, P, P, I, I, I, I, P, P, P, SZ, P)
 _tree_expand = _sig("eagle3_tree_expand", I, P, P, P, I, I, P, P, P, I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P)
@@ -247,6 +248,12 @@ def eagle3_copy_rows(src, dst, n, src_rows=None, dst_rows=None, stream=None):
         raise ValueError("row sizes differ")
     _check(_copy_rows(_ptr(src), _ptr(src_rows), src.shape[0], _ptr(dst), _ptr(dst_rows), dst.shape[0], int(n), rb,
                       _stream(stream)), "eagle3_copy_rows")
+
+
+def eagle3_node_positions(prefix_len, depth, pos, stream=None):
+    """pos[b, t] = prefix_len[b] + depth[b, t]; depth, pos [B, T] int32."""
+    B, T = depth.shape
+    _check(_node_pos(_ptr(prefix_len), _ptr(depth), B, T, _ptr(pos), _stream(stream)), "eagle3_node_positions")
 
 
 def eagle3_vocab_map(ids, vmap, out=None, status=None, stream=None):

@@ -220,6 +220,17 @@ __global__ __launch_bounds__(1024) void vocab_map_kernel(const int32_t *__restri
     if (status && threadIdx.x == 0) status[0] = bad_any ? EAGLE3_ERR_RANGE : EAGLE3_OK;
 }
 
+// Position of every tree node: the sequence's cached length plus the node's
+// depth (the root, the last emitted token, is not cached yet and takes the
+// first free position).
+__global__ __launch_bounds__(256) void node_positions_kernel(const int32_t *__restrict__ prefix_len,
+                                                             const int32_t *__restrict__ depth, int B, int T,
+                                                             int32_t *__restrict__ pos) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= B * T) return;
+    pos[i] = prefix_len[i / T] + depth[i];
+}
+
 }  // namespace
 
 extern "C" int eagle3_tree_mask(const int32_t *parent, int B, int T, int W, uint64_t *mask, int32_t *depth,
@@ -261,6 +272,17 @@ extern "C" int eagle3_vocab_map(const int32_t *ids, int n, const int32_t *vmap, 
     if (n == 0 && !status) return EAGLE3_OK;
     if ((n > 0 && (!ids || !out)) || !vmap) return EAGLE3_ERR_ARG;
     vocab_map_kernel<<<1, 1024, 0, e3_stream(stream)>>>(ids, n, vmap, V_sub, out, status);
+    E3_LAUNCH_CHECK();
+    return EAGLE3_OK;
+}
+
+extern "C" int eagle3_node_positions(const int32_t *prefix_len, const int32_t *depth, int B, int T, int32_t *pos,
+                                     void *stream) {
+    if (B < 0 || T < 1 || (long)B * T > 0x7fffffffL) return EAGLE3_ERR_ARG;
+    if (B == 0) return EAGLE3_OK;
+    if (!prefix_len || !depth || !pos) return EAGLE3_ERR_ARG;
+    const int n = B * T;
+    node_positions_kernel<<<(n + 255) / 256, 256, 0, e3_stream(stream)>>>(prefix_len, depth, B, T, pos);
     E3_LAUNCH_CHECK();
     return EAGLE3_OK;
 }
