@@ -239,6 +239,31 @@ int eagle3_node_positions(const int32_t *prefix_len, const int32_t *depth, int B
                           void *stream);
 
 /*
+ * Bookkeeping after acceptance for a decoding loop that stays on the device
+ * ([lesson] "Verify-accept semantics": the accepted drafts and the target's
+ * own token at the end node extend the sequence; [news] draft stage: a
+ * context row of the draft pairs the target's features of a token with the
+ * embedding of the token after it). For sequence b with a = accept_len[b]
+ * (from eagle3_accept_path; a < min(T, R) is required, larger values are
+ * clamped) and P = prefix_len[b] on entry:
+ *   start[b] = P;  prefix_len[b] = P + a + 1     (in place)
+ *   path_rows[b][j] = b * T + path[b][j] for j <= a, else -1   [B, R]: the
+ *       accepted rows of the [B * T] tree rows, in path order (for a row gather)
+ *   tok_ahead[b][j] = out_tokens[b][j] for j <= a, else 0      [B, R]: the
+ *       token after row j (the next accepted draft, then the target's token)
+ *   last_rows[b] = b * R + a;   root[b] = out_tokens[b][a]   (the next root)
+ *   out_seq [B, cap] (nullable; needs out_len [B]): out_tokens[b][0..a] are
+ *       written at out_seq[b][out_len[b]..] (entries past cap dropped), then
+ *       out_len[b] += a + 1.
+ * All int32 device arrays; accept_len, path, out_tokens as written by
+ * eagle3_accept_path ([B], [B, T], [B, T]). No output may alias an input.
+ */
+int eagle3_spec_advance(const int32_t *accept_len, const int32_t *path, const int32_t *out_tokens, int B, int T,
+                        int R, int32_t *prefix_len, int32_t *start, int32_t *path_rows, int32_t *tok_ahead,
+                        int32_t *last_rows, int32_t *root, int32_t *out_seq, int32_t *out_len, int cap,
+                        void *stream);
+
+/*
  * Trimmed draft vocabulary ([blog] sections 1, 3.2 and 5.1: VocabTrim, FR-Spec
  * and SpecVocab shrink the draft's search space by 40-60%). The draft LM head
  * runs over V_sub kept rows, row i being full-vocabulary id vmap[i] (gather

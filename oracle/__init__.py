@@ -24,6 +24,7 @@ file that pins it; functions with no independent pin say "parity unpinned".
 from __future__ import annotations
 
 import ctypes
+import dataclasses
 import os
 
 import numpy as np
@@ -474,6 +475,41 @@ def target_forward(inp: synth.TargetInputs, W, batch=None, layers=None):
     return dict(x=xs, rows=rows, mask=mask, depth=depth, pos=pos, hidden=hf, idx=idx1, gap=gap.reshape(B, T),
                 accept_len=alen, path=path, out_tokens=out, end=end,
                 flagged=flags(parent, tokens, idx1, gap.reshape(B, T)))
+
+
+def target_greedy(inp: synth.TargetInputs, W, root, n: int):
+    """The target's own greedy continuation, one token at a time (course
+    lesson, "Verify-accept semantics": speculative decoding must emit exactly
+    these tokens). For every sequence: feed `root` at position prefix_len,
+    take the argmax, append that node's K/V to the cache of every layer (in
+    the reserved blocks after the prefix), feed the argmax next, n times.
+    Returns tokens [B, n] and the top-2 gap of each choice [B, n]; the caches
+    of `inp` are not modified."""
+    s = inp.shape
+    B = s.B
+    kc = [c.copy() for c in inp.k_cache]
+    vc = [c.copy() for c in inp.v_cache]
+    bs = 16
+    toks = np.zeros((B, n), np.int32)
+    gaps = np.zeros((B, n))
+    for b in range(B):
+        P = int(inp.prefix_len[b])
+        cur = int(root[b])
+        for t in range(n):
+            if (P + t) // bs >= inp.block_table.shape[1]:
+                raise ValueError("the block table has no room for the continuation")
+            one = synth.TargetInputs(dataclasses.replace(s, B=1, n_drafts=0, depth=0), inp.seed,
+                                     np.array([[-1]], np.int32), np.array([[cur]], np.int32),
+                                     np.array([P + t], np.int32), inp.block_table[b:b + 1], kc, vc)
+            r = target_forward(one, W)
+            for layer, (kr, vr) in enumerate(r["rows"]):
+                blk, slot = inp.block_table[b, (P + t) // bs], (P + t) % bs
+                kc[layer][blk, :, slot, :] = kr[0, 0]
+                vc[layer][blk, :, :, slot] = vr[0, 0]
+            cur = int(r["idx"][0, 0])
+            toks[b, t] = cur
+            gaps[b, t] = r["gap"][0, 0]
+    return toks, gaps
 
 
 # ------------------------------------------------------------------ draft head

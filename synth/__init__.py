@@ -746,3 +746,14 @@ def target_inputs(shape: TargetShape, seed: int, batch: slice | None = None, dty
     with concurrent.futures.ThreadPoolExecutor(threads or min(16, os.cpu_count() or 1)) as ex:
         list(ex.map(fill, jobs))
     return TargetInputs(shape, seed, parent, tokens, plen, table, kc, vc)
+
+
+# device-resident speculative loop: a target and a draft head sharing the
+# vocabulary (the draft uses the target's embedding and LM head). The small
+# pair has 16 tokens, so a top-10 draft often holds the target's choice and
+# multi-token acceptances occur; both contexts hold `ctx` committed tokens.
+LOOP_TARGET_SMALL = TargetShape("loop-target-small", 33, layers=2, B=3, k=256, Hq=4, Hkv=2, D=128, F=512, V=16,
+                                n_drafts=20, depth=4, prefix=(96, 96), features=(0, 1, 1))
+LOOP_DRAFT_SMALL = DraftShape("loop-draft-small", 34, B=3, k=256, V=16, ctx=96, Hq=4, Hkv=2, D=128, F=512, steps=4,
+                              topk=10, n_drafts=20, lm_std=0.3)
+LOOP_TARGET_8B = dataclasses.replace(TARGET_8B, name="loop-target8b", prefix=(1024, 1024))

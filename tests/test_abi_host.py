@@ -196,3 +196,16 @@ def test_node_positions_errors(lib):
     assert f(None, FAKE, 2, 4, FAKE, None) == -1
     assert f(FAKE, FAKE, 2, 4, None, None) == -1
     assert f(None, None, 0, 4, None, None) == 0
+
+
+def test_spec_advance_errors(lib):
+    f = lib.eagle3_spec_advance
+    f.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int] * 3 + [ctypes.c_void_p] * 8 + [ctypes.c_int, ctypes.c_void_p]
+    ok = [FAKE] * 6
+    assert f(FAKE, FAKE, FAKE, 2, 0, 9, *ok, None, None, 0, None) == -1           # T < 1
+    assert f(FAKE, FAKE, FAKE, 2, 61, 0, *ok, None, None, 0, None) == -1          # R < 1
+    assert f(FAKE, FAKE, FAKE, 2, 61, 9, *ok, FAKE, None, 8, None) == -1          # out_seq without out_len
+    assert f(FAKE, FAKE, FAKE, 2, 61, 9, *ok, FAKE, FAKE, 0, None) == -1          # out_seq of no room
+    assert f(None, FAKE, FAKE, 2, 61, 9, *ok, None, None, 0, None) == -1          # no accept_len
+    assert f(FAKE, FAKE, FAKE, 2, 61, 9, *([FAKE] * 5 + [None]), None, None, 0, None) == -1   # no root
+    assert f(None, None, None, 0, 61, 9, *([None] * 6), None, None, 0, None) == 0             # empty batch

@@ -12,7 +12,8 @@ What fixes the answers, independently of the oracle's own composition:
 * a chain through the tree pass equals feeding its tokens one at a time and
   appending each one's K/V to the cache (causal decoding);
 * every node of a random tree sees only its root path: its output equals the
-  last node's output of the chain made of that path.
+  last node's output of the chain made of that path;
+* the greedy continuation fed back as one chain reproduces itself.
 """
 import dataclasses
 
@@ -151,3 +152,24 @@ def test_every_node_sees_only_its_root_path(orc):
             want = r["x"][-1][b, n].astype(np.float64)
             got = c["x"][-1][0, -1].astype(np.float64)
             assert np.abs(got - want).max() <= 1e-5 * np.abs(want).max(), (b, n)
+
+
+def test_greedy_continuation_is_the_chain_pass_of_its_own_tokens(orc):
+    """Feeding the greedy tokens back as one chain through the tree pass gives
+    the same argmax at every node (and each next token is that argmax)."""
+    s = dataclasses.replace(S, B=2)
+    _, W = f32_inputs(s, 5)
+    inp = synth.target_inputs(s, 5, dtype="f32", reserve=32)
+    root = inp.tokens[:, 0]
+    n = 9
+    toks, gaps = orc.target_greedy(inp, W, root, n)
+    for b in range(s.B):
+        chain = np.concatenate([[root[b]], toks[b, :-1]]).astype(np.int32)
+        one = _chain_inputs(inp, b, chain, int(inp.prefix_len[b]), inp.k_cache, inp.v_cache,
+                            inp.block_table[b:b + 1])
+        r = orc.target_forward(one, W)
+        clear = gaps[b] >= 1e-5
+        assert np.array_equal(r["idx"][0][clear], toks[b][clear])
+    # the caches of the inputs are left alone
+    again, _ = orc.target_greedy(inp, W, root, n)
+    assert np.array_equal(again, toks)

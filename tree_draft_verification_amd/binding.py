@@ -74,6 +74,7 @@ _commit_kv = _sig("eagle3_commit_kv", I, P, P, I, P, I, I, I, I, I, P, P, P, I, 
 _copy_rows = _sig("eagle3_copy_rows", I, P, P, I, P, P, I, I, SZ, P)
 _vocab_map = _sig("eagle3_vocab_map", I, P, I, P, I, P, P, P)
 _node_pos = _sig("eagle3_node_positions", I, P, P, I, I, P, P)
+_spec_adv = _sig("eagle3_spec_advance", I, P, P, P, I, I, I, P, P, P, P, P, P, P, P, I, P)
 _draft_fuse_ws = _sig("eagle3_draft_fuse_workspace", SZ, I, I, I)
 _draft_fuse = _sig("eagle3_draft_fuse", I, P, P, P, P, P, P, P, P, I, I, I, I, P, P, P, SZ, P)
 _tree_expand = _sig("eagle3_tree_expand", I, P, P, P, I, I, P, P, P, I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P)
@@ -254,6 +255,17 @@ def eagle3_node_positions(prefix_len, depth, pos, stream=None):
     """pos[b, t] = prefix_len[b] + depth[b, t]; depth, pos [B, T] int32."""
     B, T = depth.shape
     _check(_node_pos(_ptr(prefix_len), _ptr(depth), B, T, _ptr(pos), _stream(stream)), "eagle3_node_positions")
+
+
+def eagle3_spec_advance(accept_len, path, out_tokens, prefix_len, start, path_rows, tok_ahead, last_rows, root,
+                        out_seq=None, out_len=None, stream=None):
+    """Bookkeeping after acceptance: path_rows, tok_ahead [B, R]; the rest [B]."""
+    B, T = path.shape
+    R = path_rows.shape[-1]
+    cap = out_seq.shape[-1] if out_seq is not None else 0
+    _check(_spec_adv(_ptr(accept_len), _ptr(path), _ptr(out_tokens), B, T, R, _ptr(prefix_len), _ptr(start),
+                     _ptr(path_rows), _ptr(tok_ahead), _ptr(last_rows), _ptr(root), _ptr(out_seq), _ptr(out_len), cap,
+                     _stream(stream)), "eagle3_spec_advance")
 
 
 def eagle3_vocab_map(ids, vmap, out=None, status=None, stream=None):

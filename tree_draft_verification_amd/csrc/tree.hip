@@ -231,6 +231,36 @@ __global__ __launch_bounds__(256) void node_positions_kernel(const int32_t *__re
     pos[i] = prefix_len[i / T] + depth[i];
 }
 
+// Bookkeeping after acceptance, one wave per sequence: the accepted rows
+// (root, accepted drafts) become the next context rows, the sequence length
+// grows by accept_len + 1, the target's token at the end node is the next
+// root, and the emitted tokens are appended.
+__global__ __launch_bounds__(64) void spec_advance_kernel(
+    const int32_t *__restrict__ accept_len, const int32_t *__restrict__ path, const int32_t *__restrict__ out_tokens,
+    int T, int R, int32_t *__restrict__ prefix_len, int32_t *__restrict__ start, int32_t *__restrict__ path_rows,
+    int32_t *__restrict__ tok_ahead, int32_t *__restrict__ last_rows, int32_t *__restrict__ root,
+    int32_t *__restrict__ out_seq, int32_t *__restrict__ out_len, int cap) {
+    const int b = blockIdx.x, lane = threadIdx.x;
+    const size_t row = (size_t)b * T;
+    const int a = min(max(accept_len[b], 0), min(T, R) - 1);
+    const int P = prefix_len[b];
+    const int n0 = out_len ? out_len[b] : 0;
+    for (int j = lane; j < R; j += 64) {
+        const bool ok = j <= a;
+        path_rows[(size_t)b * R + j] = ok ? (int)row + path[row + j] : -1;
+        tok_ahead[(size_t)b * R + j] = ok ? out_tokens[row + j] : 0;
+        if (out_seq && ok && n0 + j < cap) out_seq[(size_t)b * cap + n0 + j] = out_tokens[row + j];
+    }
+    __syncthreads();
+    if (lane == 0) {
+        start[b] = P;
+        prefix_len[b] = P + a + 1;
+        last_rows[b] = b * R + a;
+        root[b] = out_tokens[row + a];
+        if (out_len) out_len[b] = n0 + a + 1;
+    }
+}
+
 }  // namespace
 
 extern "C" int eagle3_tree_mask(const int32_t *parent, int B, int T, int W, uint64_t *mask, int32_t *depth,
@@ -283,6 +313,23 @@ extern "C" int eagle3_node_positions(const int32_t *prefix_len, const int32_t *d
     if (!prefix_len || !depth || !pos) return EAGLE3_ERR_ARG;
     const int n = B * T;
     node_positions_kernel<<<(n + 255) / 256, 256, 0, e3_stream(stream)>>>(prefix_len, depth, B, T, pos);
+    E3_LAUNCH_CHECK();
+    return EAGLE3_OK;
+}
+
+extern "C" int eagle3_spec_advance(const int32_t *accept_len, const int32_t *path, const int32_t *out_tokens, int B,
+                                   int T, int R, int32_t *prefix_len, int32_t *start, int32_t *path_rows,
+                                   int32_t *tok_ahead, int32_t *last_rows, int32_t *root, int32_t *out_seq,
+                                   int32_t *out_len, int cap, void *stream) {
+    if (B < 0 || T < 1 || R < 1 || (long)B * T > 0x7fffffffL || (long)B * R > 0x7fffffffL) return EAGLE3_ERR_ARG;
+    if (out_seq && (!out_len || cap < 1)) return EAGLE3_ERR_ARG;
+    if (B == 0) return EAGLE3_OK;
+    if (!accept_len || !path || !out_tokens || !prefix_len || !start || !path_rows || !tok_ahead || !last_rows ||
+        !root)
+        return EAGLE3_ERR_ARG;
+    spec_advance_kernel<<<B, 64, 0, e3_stream(stream)>>>(accept_len, path, out_tokens, T, R, prefix_len, start,
+                                                         path_rows, tok_ahead, last_rows, root, out_seq, out_len,
+                                                         cap);
     E3_LAUNCH_CHECK();
     return EAGLE3_OK;
 }

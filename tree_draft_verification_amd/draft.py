@@ -38,7 +38,13 @@ from . import binding as B_
 
 class DraftHead:
     def __init__(self, weights: dict, B: int, ctx: int, Hq: int, Hkv: int, D: int, steps: int = 8, topk: int = 10,
-                 n_drafts: int = 60, theta: float = 500000.0, eps: float = 1e-5, device="cuda", vocab=None):
+                 n_drafts: int = 60, theta: float = 500000.0, eps: float = 1e-5, device="cuda", vocab=None,
+                 prefix_len=None, reserve: int = 0, extend_rows: int = 0):
+        """prefix_len: an int32 [B] device tensor to use as the draft cache's
+        length (shared with a target model that advances it; it must read
+        ctx for every sequence when ingest runs), else one of its own;
+        reserve: cache room for that many rows after the context;
+        extend_rows: rows per sequence that extend() takes (0: no extend)."""
         self.dev = torch.device(device)
         self.w = {k: v.to(self.dev).contiguous() for k, v in weights.items()}
         E = self.w["embed"]
@@ -63,11 +69,16 @@ class DraftHead:
         bf, i32, dv = self.dtype, torch.int32, self.dev
         C, M = topk, B * topk
         # paged draft cache: identity block table, one run of blocks per sequence
-        self.nb = (ctx + 15) // 16
+        self.nb = (ctx + reserve + 15) // 16
         self.k_cache = torch.zeros(B * self.nb, Hkv, 16, D, dtype=bf, device=dv)
         self.v_cache = torch.zeros(B * self.nb, Hkv, D, 16, dtype=bf, device=dv)
         self.table = (torch.arange(B, device=dv)[:, None] * self.nb + torch.arange(self.nb, device=dv)).to(i32)
-        self.plen = torch.full((B,), ctx, dtype=i32, device=dv)
+        self.plen = prefix_len if prefix_len is not None else torch.full((B,), ctx, dtype=i32, device=dv)
+        # frontier positions of growth step s: cache length + s - 2 (depth s - 1)
+        self.step_depth = torch.arange(steps - 1, dtype=i32, device=dv)[:, None, None].expand(steps - 1, B, C) \
+            .contiguous()
+        self.fr_pos = torch.empty(B, C, dtype=i32, device=dv)
+        self.root = torch.zeros(B, dtype=i32, device=dv)    # node 0 of the next tree
         self.zero_start = torch.zeros(B, dtype=i32, device=dv)
         self.last = (torch.arange(B, device=dv) * ctx + ctx - 1).to(i32)
         self.ctx_pos = torch.arange(ctx, device=dv).repeat(B).to(i32)
@@ -114,8 +125,19 @@ class DraftHead:
         self._ctx_bufs = None
         self._ws = None
         self._gws = None   # K-split workspace of the few-tile GEMMs (shared: one stream)
-        self._fws = torch.empty(max(256, B_.eagle3_draft_fuse_workspace(M, self.k, B_._dtype(E))),
+        self._fws = torch.empty(max(256, B_.eagle3_draft_fuse_workspace(max(M, B * extend_rows), self.k,
+                                                                        B_._dtype(E))),
                                 dtype=torch.uint8, device=dv)
+        self.R = extend_rows
+        if extend_rows:
+            Re = B * extend_rows
+            z = lambda *s: torch.zeros(*s, dtype=bf, device=dv)  # noqa: E731
+            self.ext = dict(l=z(Re, self.k), m=z(Re, self.k), h=z(Re, self.k), g=z(Re, self.k), x=z(Re, self.k),
+                            hn=z(Re, self.k), k=z(Re, self.kvd), v=z(Re, self.kvd),
+                            pos=torch.empty(Re, dtype=i32, device=dv),
+                            depth=torch.arange(extend_rows, dtype=i32, device=dv).repeat(B, 1),
+                            last_pos=torch.empty(B, dtype=i32, device=dv),
+                            minus1=torch.full((B, 1), -1, dtype=i32, device=dv))
         # optional (start, end) event pairs, one taken per LM-head call, in call order
         self.events = []
 
@@ -138,6 +160,7 @@ class DraftHead:
         cb = self._ctx_buffers()
         w = self.w
         self.ctx_tok = ctx_tok
+        self.root.copy_(ctx_tok[:, -1])
         B_.eagle3_draft_fuse(ctx_tok.reshape(R), w["embed"], w["w_in"], cb["x"], w_fuse=w["w_fuse"],
                              l=l.reshape(R, k), m=m.reshape(R, k), h=h.reshape(R, k), g_out=cb["g"])
         B_.eagle3_rmsnorm(cb["x"], cb["hn"], eps=self.eps)
@@ -226,9 +249,10 @@ class DraftHead:
             self._gemm([self.hs], self.wq, self.q)
             self._gemm([self.hs], self.wk, self.kt)
             self._gemm([self.hs], self.wv, self.vt)
-            pos = self.ctx + s - 2
-            B_.eagle3_rope(self.q, M, self.Hq, D, self.qd, self.zero_pos, pos, self.theta)
-            B_.eagle3_rope(self.kt, M, self.Hkv, D, self.kvd, self.zero_pos, pos, self.theta)
+            B_.eagle3_node_positions(self.plen, self.step_depth[s - 2], self.fr_pos)
+            pos = self.fr_pos.view(-1)
+            B_.eagle3_rope(self.q, M, self.Hq, D, self.qd, pos, 0, self.theta)
+            B_.eagle3_rope(self.kt, M, self.Hkv, D, self.kvd, pos, 0, self.theta)
             rows = self.key_rows[s - 2]
             tk2, tv2 = self.tk.view(B * self.Tk, self.kvd), self.tv.view(B * self.Tk, self.kvd)
             B_.eagle3_copy_rows(self.kt, tk2, M, dst_rows=rows)
@@ -249,11 +273,45 @@ class DraftHead:
             pool_len += C * C
             a_src = a_out
         self.pool_len = pool_len
-        root = self.ctx_tok[:, -1].contiguous()
-        self._root = root
-        B_.eagle3_tree_rerank(self.pool_score, self.pool_token, self.pool_parent, pool_len, root, self.parent,
+        B_.eagle3_tree_rerank(self.pool_score, self.pool_token, self.pool_parent, pool_len, self.root, self.parent,
                               self.tokens)
         return self.parent, self.tokens
+
+    # ----------------------------------------------------------- extend
+    def extend(self, l, m, h, path_rows, tok_ahead, start, last_rows):
+        """New context rows after an acceptance (arguments as written by
+        eagle3_spec_advance): for every sequence, R = extend_rows rows whose
+        features are rows path_rows of the target's l, m, h [rows, k] and
+        whose next tokens are tok_ahead; their K/V go to the cache at
+        positions start.. (rows past the accepted ones land after the new
+        length, where nothing reads them until the next extend overwrites
+        them), and the full layer at row last_rows (the end node, at position
+        prefix_len - 1 with prefix_len already advanced) gives a_root."""
+        B, R, k = self.B, self.R, self.k
+        Re = B * R
+        e, w = self.ext, self.w
+        for src, dst in ((l, e["l"]), (m, e["m"]), (h, e["h"])):
+            B_.eagle3_copy_rows(src, dst, Re, src_rows=path_rows.view(-1))
+        B_.eagle3_draft_fuse(tok_ahead.view(-1), w["embed"], w["w_in"], e["x"], w_fuse=w["w_fuse"], l=e["l"],
+                             m=e["m"], h=e["h"], g_out=e["g"], ws=self._fws)
+        B_.eagle3_rmsnorm(e["x"], e["hn"], eps=self.eps)
+        self._gemm([e["hn"]], self.wk, e["k"])
+        self._gemm([e["hn"]], self.wv, e["v"])
+        B_.eagle3_node_positions(start, e["depth"], e["pos"].view(B, R))
+        B_.eagle3_rope(e["k"], Re, self.Hkv, self.D, self.kvd, e["pos"], 0, self.theta)
+        B_.eagle3_commit_kv(e["k"].view(B, R, self.Hkv, self.D), e["v"].view(B, R, self.Hkv, self.D), None, start,
+                            self.k_cache, self.v_cache, self.table, max_n=R)
+        B_.eagle3_copy_rows(e["x"], self.x1, B, src_rows=last_rows)
+        h1, q, attn = self.hs[:B], self.q[:B], self.attn[:B]
+        B_.eagle3_rmsnorm(self.x1, h1, eps=self.eps)
+        self._gemm([h1], self.wq, q)
+        B_.eagle3_node_positions(self.plen, e["minus1"], e["last_pos"].view(B, 1))
+        B_.eagle3_rope(q, B, self.Hq, self.D, self.qd, e["last_pos"], 0, self.theta)
+        none = self.tk[:, :0]
+        a = B_.tree_attn_args(q.view(B, 1, self.Hq, self.D), none, none, self.k_cache, self.v_cache, self.table,
+                              self.plen, attn.view(B, 1, self.Hq, self.D), mask=self.root_mask)
+        B_.eagle3_tree_attn(a, self._attn_ws(a))
+        self._layer_tail(self.x1, attn, self.a_root, B)
 
     def run(self, l, m, h, ctx_tok, record=None):
         self.ingest(l, m, h, ctx_tok)

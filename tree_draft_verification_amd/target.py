@@ -143,9 +143,11 @@ class TargetModel:
         self.forward(parent, tokens, record)
         self.accept(tokens)
 
-    def commit(self):
+    def commit(self, start=None):
         """Append the accepted path's K/V rows of every layer to that layer's
-        cache at positions prefix_len.. (the caller advances prefix_len)."""
+        cache at positions start.. (default: prefix_len, which the caller
+        then advances)."""
+        st = self.plen if start is None else start
         for i in range(self.layers):
-            B_.eagle3_commit_kv(self.k_rows[i], self.v_rows[i], self.path, self.plen, self.k_caches[i],
+            B_.eagle3_commit_kv(self.k_rows[i], self.v_rows[i], self.path, st, self.k_caches[i],
                                 self.v_caches[i], self.table)
