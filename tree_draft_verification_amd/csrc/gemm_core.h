@@ -84,13 +84,19 @@ __device__ __forceinline__ void tile_of(int L, int nwg, int MT, int NT, int &mt,
 
 // Source row of each tile row, per segment (rows past M clamp to M - 1; their
 // results are dropped by the epilogue).
+// The segment index is a compile-time constant in every access to p: a
+// run-time index would place the whole parameter block in private memory.
 template <int BM>
 __device__ __forceinline__ void fill_arow(const GemmParams &p, int m0, int (*arow)[BM]) {
-    for (int i = threadIdx.x; i < 3 * BM; i += 256) {
-        const int s = i / BM, r = i % BM;
-        int m = min(m0 + r, p.M - 1);
-        if (s < p.nseg && p.a_rows[s]) m = min(max(p.a_rows[s][m], 0), p.a_nrows[s] - 1);
-        arow[s][r] = m;
+#pragma unroll
+    for (int s = 0; s < 3; ++s) {
+        const int32_t *rows = s == 0 ? p.a_rows[0] : s == 1 ? p.a_rows[1] : p.a_rows[2];
+        const int nrows = s == 0 ? p.a_nrows[0] : s == 1 ? p.a_nrows[1] : p.a_nrows[2];
+        for (int r = threadIdx.x; r < BM; r += 256) {
+            int m = min(m0 + r, p.M - 1);
+            if (s < p.nseg && rows) m = min(max(rows[m], 0), nrows - 1);
+            arow[s][r] = m;
+        }
     }
     __syncthreads();
 }

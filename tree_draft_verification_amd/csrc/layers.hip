@@ -26,7 +26,13 @@ using namespace e3g;
 // [s nch / S, (s + 1) nch / S) of split s = w / tiles, and stores its fp32
 // partial tile to part[s][M][N]; gemm_reduce_kernel adds the splits in
 // order (plus the residual) and rounds once.
-template <int BM, int NS, bool SPLIT>
+//
+// VEC: the output rows are 16-byte aligned with N % 8 == 0 (chosen on the
+// host), so the epilogue stages the results in LDS and writes 16-byte
+// pieces; otherwise each element is stored on its own. The two epilogues are
+// separate instantiations: compiled into one kernel, the scattered one's
+// register pressure made the compiler spill accumulators after the main loop.
+template <int BM, int NS, bool SPLIT, bool VEC = false>
 __global__ __launch_bounds__(256, NS == 3 ? 2 : 1) void gemm_bf16_kernel(GemmParams p, int nsplit, float *part) {
     using T = GTile<BM, NS>;
     __shared__ __attribute__((aligned(1024))) unsigned char ring[T::RING];
@@ -61,6 +67,73 @@ __global__ __launch_bounds__(256, NS == 3 ? 2 : 1) void gemm_bf16_kernel(GemmPar
     // D[m][n]: lane holds n = lr of its block, m = 8 (r / 4) + 4 lh + r % 4
     const uint16_t *res = (const uint16_t *)p.res;
     uint16_t *cc = (uint16_t *)p.c;
+    if constexpr (VEC) {
+        // Each wave stages one 32 x 128 block of its fp32 results at a time in
+        // the (now idle) ring, then writes 16-byte rows of 8 outputs: 32
+        // stores of 1 KB per wave and block instead of 2-byte scattered
+        // stores (those cost a quarter of the 3904 x 28672 x 4096 GEMM's
+        // time). The residual is added in fp32 and the sum rounded once, as
+        // in the direct path. Row pitch 136 floats: the two lane halves
+        // (4 rows apart) write disjoint banks.
+        constexpr int PITCH = 136;
+        static_assert(4 * 32 * PITCH * sizeof(float) <= T::RING, "staging must fit the ring");
+        __syncthreads();  // every wave is done with the ring
+        // lane-dependent addresses are formed from an opaque copy of the
+        // thread id, so none of them is computed before the main loop and
+        // kept live (spilled) across it
+        int tx = threadIdx.x;
+        __asm__ volatile("" : "+v"(tx));
+        const int wv = tx >> 6, ln = tx & 63;
+        float *stg = reinterpret_cast<float *>(ring) + wv * 32 * PITCH;
+        float *wr = stg + 4 * (ln >> 5) * PITCH + (ln & 31);           // accumulator layout
+        const float *rdp = stg + (ln >> 4) * PITCH + (ln & 15) * 8;    // 16-byte chunks, row-major
+        const int mrow = m0 + (wv >> 1) * (BM / 2) + (ln >> 4);
+        const int ncol = n0 + (wv & 1) * 128 + (ln & 15) * 8;
+        const bool ncol_ok = ncol < p.N;
+#pragma unroll
+        for (int mb = 0; mb < T::MB; ++mb) {
+#pragma unroll
+            for (int nb = 0; nb < T::NB; ++nb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) wr[(8 * (r >> 2) + (r & 3)) * PITCH + nb * 32] = acc[mb][nb][r];
+            // the block's residual pieces are requested now (in the registers
+            // its accumulators just left), so they arrive during the LDS pass
+            u32x4_t rv[8];
+            if (res) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int m = mrow + mb * 32 + 4 * i;
+                    rv[i] = m < p.M && ncol_ok ? *reinterpret_cast<const u32x4_t *>(res + (size_t)m * p.ldc + ncol)
+                                               : u32x4_t{0, 0, 0, 0};
+                }
+            }
+            // a wave's LDS accesses complete in order: the reads see the writes,
+            // and the next block's writes follow these reads
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int m = mrow + mb * 32 + 4 * i;
+                if (m < p.M && ncol_ok) {
+                    const f32x4_t lo = *reinterpret_cast<const f32x4_t *>(rdp + 4 * i * PITCH);
+                    const f32x4_t hi = *reinterpret_cast<const f32x4_t *>(rdp + 4 * i * PITCH + 4);
+                    float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                    const size_t off = (size_t)m * p.ldc + ncol;
+                    if (res) {
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            v[2 * q] += e3_bf16_to_f32((uint16_t)(rv[i][q] & 0xffffu));
+                            v[2 * q + 1] += e3_bf16_to_f32((uint16_t)(rv[i][q] >> 16));
+                        }
+                    }
+                    u32x4_t o;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        o[q] = (uint32_t)e3_f32_to_bf16(v[2 * q]) | ((uint32_t)e3_f32_to_bf16(v[2 * q + 1]) << 16);
+                    *reinterpret_cast<u32x4_t *>(cc + off) = o;
+                }
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int mb = 0; mb < T::MB; ++mb)
 #pragma unroll
@@ -317,15 +390,20 @@ extern "C" int eagle3_gemm(const eagle3_gemm_args *a, void *stream) {
         const long t256 = (long)((a->M + 255) / 256) * nt, t128 = (long)((a->M + 127) / 128) * nt;
         const long cus = e3_cu_count();
         p.nt = nt;
+        const bool vec = a->N % 8 == 0 && ldc % 8 == 0 && e3_aligned16(a->c) &&
+                         (!a->residual || e3_aligned16(a->residual));
         if (t256 >= 4 * cus || (t128 < 2 * cus && t256 >= cus)) {
             p.mt = (a->M + 255) / 256;
-            gemm_bf16_kernel<256, 4, false><<<p.mt * nt, 256, 0, st>>>(p, 1, nullptr);
+            if (vec) gemm_bf16_kernel<256, 4, false, true><<<p.mt * nt, 256, 0, st>>>(p, 1, nullptr);
+            else gemm_bf16_kernel<256, 4, false><<<p.mt * nt, 256, 0, st>>>(p, 1, nullptr);
         } else if (t128 >= 2 * cus) {
             p.mt = (a->M + 127) / 128;
-            gemm_bf16_kernel<128, 3, false><<<p.mt * nt, 256, 0, st>>>(p, 1, nullptr);
+            if (vec) gemm_bf16_kernel<128, 3, false, true><<<p.mt * nt, 256, 0, st>>>(p, 1, nullptr);
+            else gemm_bf16_kernel<128, 3, false><<<p.mt * nt, 256, 0, st>>>(p, 1, nullptr);
         } else {
             p.mt = (a->M + 127) / 128;
-            gemm_bf16_kernel<128, 4, false><<<p.mt * nt, 256, 0, st>>>(p, 1, nullptr);
+            if (vec) gemm_bf16_kernel<128, 4, false, true><<<p.mt * nt, 256, 0, st>>>(p, 1, nullptr);
+            else gemm_bf16_kernel<128, 4, false><<<p.mt * nt, 256, 0, st>>>(p, 1, nullptr);
         }
     } else {
         dim3 grid((a->M + 15) / 16, (a->N + 15) / 16);
