@@ -115,7 +115,7 @@ def test_verify_full_size(orc, lib, name, mode):
     print(f"{name}: sequences checked {len(sel)}, flagged {n_flag}, tau {got['accept_len'][sel] + 1}")
 
 
-GOLDEN = ["llama8b-b1", "llama8b-b64", "llama70b-b8"]
+GOLDEN = ["llama8b-b1", "llama8b-b64", "llama70b-b8", "chain60-b64", "tree60-b64", "chain40-b64", "tree40-b64"]
 
 
 @pytest.mark.parametrize("name", GOLDEN)
