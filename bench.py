@@ -310,7 +310,7 @@ def bench_chain_vs_tree(args):
         outs[name] = o
         steps_per_s = 1e3 / o["ms_per_step"]
         rows.append({"workload": name, "draft_nodes": o["config"]["draft_nodes"],
-                     "shape": "chain" if name.startswith("chain") else "top-10 tree, depth 7",
+                     "shape": "chain" if name.startswith("chain") else "best-first tree, depth <= 8, <= 10 children",
                      "accepted_tok_per_step": o["accepted_tok_per_step"],
                      "accepted_tok_per_step_std": o["accepted_tok_per_step_std"],
                      "verified_nodes_per_s": o["value"], "ms_per_step": o["ms_per_step"],
