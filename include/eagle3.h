@@ -335,6 +335,17 @@ int eagle3_gemm(const eagle3_gemm_args *args, void *stream);
  * with silu(g) = g / (1 + exp(-g)); gu [M, 2F] (gate columns first), y [M, F]. */
 int eagle3_silu_mul(const void *gu, int M, int F, int dtype, void *y, void *stream);
 
+/* The gate/up projection and the SwiGLU gating in one call (reading: Llama's
+ * MLP), y[m][f] = silu(g[m][f]) * u[m][f] with g = A . Wg^T and u = A . Wu^T
+ * rounded to bf16 first, so y equals eagle3_gemm followed by eagle3_silu_mul
+ * bit for bit. bf16 only. args as for eagle3_gemm except: b is the gate/up
+ * weight [N = 2F, K] in paired layout (rows 256 j .. 256 j + 127 are gate rows
+ * 128 j .. 128 j + 127, the next 128 rows the up rows of the same outputs;
+ * eagle3_copy_rows with a row table builds it from [Wg; Wu]); N % 256 == 0;
+ * c is y [M, F] with row stride ldc (0: F; a multiple of 8; 16-byte aligned);
+ * no residual, no workspace (ws ignored). */
+int eagle3_gemm_swiglu(const eagle3_gemm_args *args, void *stream);
+
 /* Rotary embedding, rotate-half convention (reading): in place on x viewed as
  * [M][H][D] with row stride ld (elements, >= H * D); row m sits at position
  * p = pos_offset + pos[m] (e.g. the committed length plus the node's depth)

@@ -1,5 +1,6 @@
 """GPU parity of the dense layers (GEMM with segmented / gathered A, SiLU
-gating, RoPE, embedding gather, KV commit) and of the EAGLE-3 draft fusion,
+gating, the fused gate/up projection + gating, RoPE, embedding gather, KV
+commit) and of the EAGLE-3 draft fusion,
 against the oracle on the same inputs. bf16 normwise <= 2e-2, fp32 <= 1e-5;
 copies bit-exact."""
 import numpy as np
@@ -119,6 +120,37 @@ def test_silu_mul(orc, lib, dtype):
     torch.cuda.synchronize()
     rel, _ = normwise_rel(host(y), ref)
     assert rel <= (2e-2 if dtype == "bf16" else 1e-5)
+
+
+@pytest.mark.parametrize("M,F,k", [(1, 128, [64]), (200, 256, [128, 64, 192]), (1000, 384, [256]),
+                                   (640, 512, [4096])])
+def test_gemm_swiglu_fused(orc, lib, M, F, k):
+    """The fused gate/up projection + gating against the oracle's
+    silu_mul(gemm(A, [Wg; Wu])), and bit for bit against the two separate
+    calls on the GPU (the weight turned into the paired layout by
+    eagle3_copy_rows)."""
+    rng = np.random.default_rng(M + F)
+    segs = [synth.normal_bf16(rng, (M if s != 1 else 50, ks)) for s, ks in enumerate(k)]
+    rows = [None] * len(k)
+    if len(k) > 1:
+        rows[1] = rng.integers(0, 50, size=M).astype(np.int32)
+    Wgu = synth.normal_bf16(rng, (2 * F, sum(k)), 0.05)
+    A = np.concatenate([s if r is None else s[r] for s, r in zip(segs, rows)], axis=1)
+    ref = orc.silu_mul(orc.gemm(A, Wgu))
+    sd = [dev(s) for s in segs]
+    rd = [None if r is None else dev(r) for r in rows]
+    w = dev(Wgu)
+    wp = torch.empty_like(w)
+    lib.eagle3_copy_rows(w, wp, 2 * F, src_rows=lib.pair_gate_up_rows(F, "cuda"))
+    y = torch.full((M, F), 3.0, dtype=torch.bfloat16, device="cuda")
+    lib.eagle3_gemm_swiglu(sd, wp, y, a_rows=rd)
+    gu = torch.empty(M, 2 * F, dtype=torch.bfloat16, device="cuda")
+    lib.eagle3_gemm(sd, w, gu, a_rows=rd)
+    y2 = torch.empty(M, F, dtype=torch.bfloat16, device="cuda")
+    lib.eagle3_silu_mul(gu, y2)
+    torch.cuda.synchronize()
+    assert normwise_rel(host(y), ref)[0] <= 2e-2
+    assert np.array_equal(host(y), host(y2))
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])

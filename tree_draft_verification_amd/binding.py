@@ -66,6 +66,7 @@ _lmhead = _sig("eagle3_lmhead_argmax", I, P, P, I, I, I, I, I, P, P, P, P, P, SZ
 _lmhead_noalloc = _sig("eagle3_lmhead_argmax_noalloc", I, P, P, I, I, I, I, I, P, P, P, P, P)
 _accept = _sig("eagle3_accept_path", I, P, P, P, I, P, I, I, P, P, P, I, P, P)
 _gemm = _sig("eagle3_gemm", I, ctypes.POINTER(GemmArgs), P)
+_gemm_swiglu = _sig("eagle3_gemm_swiglu", I, ctypes.POINTER(GemmArgs), P)
 _gemm_ws = _sig("eagle3_gemm_workspace", SZ, ctypes.POINTER(GemmArgs))
 _silu_mul = _sig("eagle3_silu_mul", I, P, I, I, I, P, P)
 _rope = _sig("eagle3_rope", I, P, I, I, I, I, P, I, F, I, P)
@@ -225,6 +226,26 @@ def eagle3_gemm(a, b, c, residual=None, a_rows=None, a_nrows=None, ldc=0, M=None
     that lets a call with few output tiles split K)."""
     g = _gemm_args(a, b, c, residual, a_rows, ldc, M, ws)
     _check(_gemm(ctypes.byref(g), _stream(stream)), "eagle3_gemm")
+
+
+def eagle3_gemm_swiglu(a, b, y, a_rows=None, ldc=0, M=None, stream=None):
+    """y = silu(A . Wg^T) * (A . Wu^T) with b the gate/up weight in paired
+    layout (see pair_gate_up_rows); y [M, N / 2]."""
+    g = _gemm_args(a, b, y, None, a_rows, ldc, M if M is not None else y.shape[0], None)
+    _check(_gemm_swiglu(ctypes.byref(g), _stream(stream)), "eagle3_gemm_swiglu")
+
+
+def pair_gate_up_rows(F, device):
+    """int32 row table that eagle3_copy_rows uses to turn [Wg; Wu] ([2F, K],
+    gate rows first) into the paired layout of eagle3_gemm_swiglu: row r of
+    the result is gate row 128 (r / 256) + r % 256 for r % 256 < 128, else up
+    row 128 (r / 256) + r % 256 - 128."""
+    if F % 128:
+        raise ValueError("the paired gate/up layout needs F % 128 == 0")
+    r = torch.arange(2 * F)
+    j, q = r // 256, r % 256
+    src = torch.where(q < 128, 128 * j + q, F + 128 * j + q - 128)
+    return src.to(device=device, dtype=torch.int32)
 
 
 def eagle3_silu_mul(gu, y, stream=None):

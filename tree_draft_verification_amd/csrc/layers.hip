@@ -32,7 +32,13 @@ using namespace e3g;
 // pieces; otherwise each element is stored on its own. The two epilogues are
 // separate instantiations: compiled into one kernel, the scattered one's
 // register pressure made the compiler spill accumulators after the main loop.
-template <int BM, int NS, bool SPLIT, bool VEC = false>
+//
+// SWIGLU (with VEC): B is a gate/up weight in paired layout (each 256-row
+// tile = 128 gate rows, then the 128 up rows of the same outputs), so the
+// tile's two column halves are the gate and up values of 128 outputs; the
+// epilogue writes y = silu(g) * u to C [M, N / 2] with g and u first rounded
+// to bf16 and the product formed as the separate gating kernel forms it.
+template <int BM, int NS, bool SPLIT, bool VEC = false, bool SWIGLU = false>
 __global__ __launch_bounds__(256, NS == 3 ? 2 : 1) void gemm_bf16_kernel(GemmParams p, int nsplit, float *part) {
     using T = GTile<BM, NS>;
     __shared__ __attribute__((aligned(1024))) unsigned char ring[T::RING];
@@ -67,7 +73,59 @@ __global__ __launch_bounds__(256, NS == 3 ? 2 : 1) void gemm_bf16_kernel(GemmPar
     // D[m][n]: lane holds n = lr of its block, m = 8 (r / 4) + 4 lh + r % 4
     const uint16_t *res = (const uint16_t *)p.res;
     uint16_t *cc = (uint16_t *)p.c;
-    if constexpr (VEC) {
+    if constexpr (SWIGLU) {
+        // Waves (wm, 0) and (wm, 1) hold the gate and the up values of the
+        // same 128 outputs. Each stages its 32 x 128 block (rounded to bf16)
+        // in the ring; after a barrier the pair reads both and writes 16
+        // rows each.
+        constexpr int PITCH = 136;
+        static_assert(4 * 32 * PITCH * sizeof(float) <= T::RING, "staging must fit the ring");
+        __syncthreads();  // every wave is done with the ring
+        int tx = threadIdx.x;
+        __asm__ volatile("" : "+v"(tx));
+        const int wv = tx >> 6, ln = tx & 63, wmv = wv >> 1, half = wv & 1;
+        float *stg = reinterpret_cast<float *>(ring) + wv * 32 * PITCH;
+        float *wr = stg + 4 * (ln >> 5) * PITCH + (ln & 31);
+        const float *gate = reinterpret_cast<float *>(ring) + (2 * wmv) * 32 * PITCH;
+        const float *up = gate + 32 * PITCH;
+        const int rsub = 16 * half + (ln >> 4);                        // rows rsub + 4 i, i < 4
+        const float *gp = gate + rsub * PITCH + (ln & 15) * 8;
+        const float *upp = up + rsub * PITCH + (ln & 15) * 8;
+        const int mrow = m0 + wmv * (BM / 2) + rsub;
+        const int ncol = (n0 >> 1) + (ln & 15) * 8;                    // output column (p.N / 2 of them)
+        const bool ncol_ok = ncol < (p.N >> 1);
+#pragma unroll
+        for (int mb = 0; mb < T::MB; ++mb) {
+#pragma unroll
+            for (int nb = 0; nb < T::NB; ++nb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    wr[(8 * (r >> 2) + (r & 3)) * PITCH + nb * 32] = e3_bf16_to_f32(e3_f32_to_bf16(acc[mb][nb][r]));
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int m = mrow + mb * 32 + 4 * i;
+                if (m < p.M && ncol_ok) {
+                    const f32x4_t g0 = *reinterpret_cast<const f32x4_t *>(gp + 4 * i * PITCH);
+                    const f32x4_t g1 = *reinterpret_cast<const f32x4_t *>(gp + 4 * i * PITCH + 4);
+                    const f32x4_t u0 = *reinterpret_cast<const f32x4_t *>(upp + 4 * i * PITCH);
+                    const f32x4_t u1 = *reinterpret_cast<const f32x4_t *>(upp + 4 * i * PITCH + 4);
+                    const float g[8] = {g0[0], g0[1], g0[2], g0[3], g1[0], g1[1], g1[2], g1[3]};
+                    const float u[8] = {u0[0], u0[1], u0[2], u0[3], u1[0], u1[1], u1[2], u1[3]};
+                    u32x4_t o;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const float a = g[2 * q] / (1.f + expf(-g[2 * q])) * u[2 * q];
+                        const float b = g[2 * q + 1] / (1.f + expf(-g[2 * q + 1])) * u[2 * q + 1];
+                        o[q] = (uint32_t)e3_f32_to_bf16(a) | ((uint32_t)e3_f32_to_bf16(b) << 16);
+                    }
+                    *reinterpret_cast<u32x4_t *>(cc + (size_t)m * p.ldc + ncol) = o;
+                }
+            }
+            __syncthreads();  // the pair is done before the next block overwrites
+        }
+        return;
+    } else if constexpr (VEC) {
         // Each wave stages one 32 x 128 block of its fp32 results at a time in
         // the (now idle) ring, then writes 16-byte rows of 8 outputs: 32
         // stores of 1 KB per wave and block instead of 2-byte scattered
@@ -408,6 +466,50 @@ extern "C" int eagle3_gemm(const eagle3_gemm_args *a, void *stream) {
     } else {
         dim3 grid((a->M + 15) / 16, (a->N + 15) / 16);
         gemm_f32_kernel<<<grid, 256, 0, st>>>(p);
+    }
+    E3_LAUNCH_CHECK();
+    return EAGLE3_OK;
+}
+
+extern "C" int eagle3_gemm_swiglu(const eagle3_gemm_args *a, void *stream) {
+    if (!a) return EAGLE3_ERR_ARG;
+    if (a->M < 0 || a->N < 1 || a->nseg < 1 || a->nseg > 3) return EAGLE3_ERR_ARG;
+    if (a->dtype != EAGLE3_BF16 || a->N % 256 != 0 || a->residual) return EAGLE3_ERR_UNSUPPORTED;
+    if (a->M == 0) return EAGLE3_OK;
+    if (!a->b || !a->c) return EAGLE3_ERR_ARG;
+    const int F = a->N / 2;
+    const int ldc = a->ldc > 0 ? a->ldc : F;
+    if (ldc < F || ldc % 8 != 0 || !e3_aligned16(a->c) || !e3_aligned16(a->b)) return EAGLE3_ERR_ARG;
+    GemmParams p{};
+    int K = 0;
+    for (int s = 0; s < a->nseg; ++s) {
+        if (!a->a[s] || a->k[s] < 1) return EAGLE3_ERR_ARG;
+        if (a->a_rows[s] && a->a_nrows[s] < 1) return EAGLE3_ERR_ARG;
+        if (a->k[s] % GSEG_ALIGN != 0 || !e3_aligned16(a->a[s])) return EAGLE3_ERR_UNSUPPORTED;
+        p.a[s] = a->a[s];
+        p.a_rows[s] = a->a_rows[s];
+        p.a_nrows[s] = a->a_rows[s] ? a->a_nrows[s] : a->M;
+        p.k[s] = a->k[s];
+        p.kofs[s] = K;
+        K += a->k[s];
+    }
+    p.nseg = a->nseg; p.b = a->b; p.res = nullptr; p.c = a->c;
+    p.M = a->M; p.N = a->N; p.K = K; p.ldc = ldc;
+    const hipStream_t st = e3_stream(stream);
+    // tile shape as eagle3_gemm chooses it for the same product
+    const int nt = a->N / GBN;
+    const long t256 = (long)((a->M + 255) / 256) * nt, t128 = (long)((a->M + 127) / 128) * nt;
+    const long cus = e3_cu_count();
+    p.nt = nt;
+    if (t256 >= 4 * cus || (t128 < 2 * cus && t256 >= cus)) {
+        p.mt = (a->M + 255) / 256;
+        gemm_bf16_kernel<256, 4, false, true, true><<<p.mt * nt, 256, 0, st>>>(p, 1, nullptr);
+    } else if (t128 >= 2 * cus) {
+        p.mt = (a->M + 127) / 128;
+        gemm_bf16_kernel<128, 3, false, true, true><<<p.mt * nt, 256, 0, st>>>(p, 1, nullptr);
+    } else {
+        p.mt = (a->M + 127) / 128;
+        gemm_bf16_kernel<128, 4, false, true, true><<<p.mt * nt, 256, 0, st>>>(p, 1, nullptr);
     }
     E3_LAUNCH_CHECK();
     return EAGLE3_OK;

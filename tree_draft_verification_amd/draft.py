@@ -57,6 +57,11 @@ class DraftHead:
         if self.dtype not in (torch.bfloat16, torch.float32):
             raise TypeError("draft weights must be bf16 or fp32")
         self.F = self.w["wd"].shape[1]
+        self.wgu_paired = None
+        if self.dtype == torch.bfloat16 and self.F % 128 == 0:
+            self.wgu_paired = torch.empty_like(self.w["wgu"])
+            B_.eagle3_copy_rows(self.w["wgu"], self.wgu_paired, 2 * self.F,
+                                src_rows=B_.pair_gate_up_rows(self.F, self.dev))
         self.Tk = (steps - 1) * topk                      # tree keys: one row per frontier node per step
         self.W = (self.Tk + 63) // 64
         self.pool_cap = topk + (steps - 1) * topk * topk
@@ -204,8 +209,13 @@ class DraftHead:
         x2, h2, gu, f = self.x2[:M], self.h2[:M], self.gu[:M], self.f[:M]
         self._gemm([attn], w["wo"], x2, residual=x)
         B_.eagle3_rmsnorm(x2, h2, eps=self.eps)
-        self._gemm([h2], w["wgu"], gu)
-        B_.eagle3_silu_mul(gu, f)
+        # the fused projection + gating where the separate projection would
+        # not split K (few rows keep the split, which fills the chip)
+        if self.wgu_paired is not None and not B_.eagle3_gemm_workspace([h2], w["wgu"], gu):
+            B_.eagle3_gemm_swiglu([h2], self.wgu_paired, f)
+        else:
+            self._gemm([h2], w["wgu"], gu)
+            B_.eagle3_silu_mul(gu, f)
         self._gemm([f], w["wd"], out, residual=x2)
 
     def _head(self, a, M):

@@ -9,7 +9,8 @@ Per layer, over M = B * T tree rows: RMSNorm -> Q, K, V projections -> RoPE
 at the sequence's cached length + the node's depth -> tree attention over
 that layer's paged prefix plus the ancestor-masked tree rows -> output
 projection + residual -> RMSNorm -> gate/up projection -> SiLU(gate) * up ->
-down projection + residual. The tree rows' K/V of every layer stay in
+down projection + residual (in bf16 the gate/up projection and the gating
+are one call, eagle3_gemm_swiglu, on the weight in paired layout). The tree rows' K/V of every layer stay in
 device buffers, so the accepted path can be appended to each layer's cache
 (eagle3_commit_kv) after acceptance. readings: pre-norm layer with gamma = 1,
 GQA (query head h reads KV head h / (Hq / Hkv)), rotate-half RoPE.
@@ -47,6 +48,17 @@ class TargetModel:
         for i in range(layers):
             wqkv = weights[f"l{i}.wqkv"]
             self.proj.append((wqkv[:self.qd], wqkv[self.qd:self.qd + self.kvd], wqkv[self.qd + self.kvd:]))
+        # bf16: the gate/up weights in the paired layout of the fused
+        # projection + gating call (one extra copy of those weights)
+        self.fused_mlp = self.dtype == torch.bfloat16 and self.F % 128 == 0
+        self.wgu_paired = []
+        if self.fused_mlp:
+            tab = B_.pair_gate_up_rows(self.F, self.dev)
+            for i in range(layers):
+                w = weights[f"l{i}.wgu"]
+                wp = torch.empty_like(w)
+                B_.eagle3_copy_rows(w, wp, 2 * self.F, src_rows=tab)
+                self.wgu_paired.append(wp)
         M, dt, dv = B * T, self.dtype, self.dev
         i32 = dict(dtype=torch.int32, device=dv)
         e = lambda *s: torch.empty(*s, dtype=dt, device=dv)  # noqa: E731
@@ -124,9 +136,13 @@ class TargetModel:
             B_.eagle3_gemm([self.attn], self.w[f"l{i}.wo"], self.x, residual=self.x, ws=ws)
             B_.eagle3_rmsnorm(self.x, self.h, eps=self.eps)
             self._ev("gu", i, 0)
-            B_.eagle3_gemm([self.h], self.w[f"l{i}.wgu"], self.gu, ws=ws)
+            if self.fused_mlp:
+                B_.eagle3_gemm_swiglu([self.h], self.wgu_paired[i], self.f)
+            else:
+                B_.eagle3_gemm([self.h], self.w[f"l{i}.wgu"], self.gu, ws=ws)
             self._ev("gu", i, 1)
-            B_.eagle3_silu_mul(self.gu, self.f)
+            if not self.fused_mlp:
+                B_.eagle3_silu_mul(self.gu, self.f)
             B_.eagle3_gemm([self.f], self.w[f"l{i}.wd"], self.x, residual=self.x, ws=ws)
             if i in self.feat:
                 B_.eagle3_copy_rows(self.x, self.feat[i], M)
