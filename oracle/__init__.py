@@ -529,6 +529,53 @@ def _page(rows_k, rows_v, bs=16):
     return synth.PagedKV(kc, vc, table, np.full(B, L, np.int32), bs)
 
 
+def _draft_layer_tail(s, W, x, attn):
+    """Output projection + residual, RMSNorm, SwiGLU MLP + residual of the
+    draft's decoder layer (reading R15: a Llama layer)."""
+    x = gemm(attn, W["wo"], R=x)
+    f = silu_mul(gemm(rmsnorm(x, eps=s.eps), W["wgu"]))
+    return gemm(f, W["wd"], R=x)
+
+
+def draft_context(shape, W, l, m, h, tok_ahead, start, prev_k=None, prev_v=None, last=None):
+    """Context rows entering the draft (news write-up of the EAGLE-3 paper,
+    draft stage: row t fuses the target's low / mid / high features of token
+    t with the embedding of token t + 1, its K/V at position t join the
+    draft's cache, and the whole layer runs at the newest row to give the
+    output the next tree grows from).
+
+    l, m, h [B, n, k]; tok_ahead [B, n]; start [B]: position of row 0;
+    prev_k, prev_v [B, >= start, Hkv, D]: the rows already cached (rows
+    0..start[b]-1 of sequence b are used); last [B]: the row that runs the
+    whole layer (default n - 1); it attends to the cached rows and new rows
+    0..last. Returns the new rows' K (after RoPE) and V [B, n, Hkv, D] and the
+    layer output at row last [B, k]."""
+    s = shape
+    B, n, k = l.shape
+    qd, kvd = s.Hq * s.D, s.Hkv * s.D
+    wq, wk, wv = W["wqkv"][:qd], W["wqkv"][qd:qd + kvd], W["wqkv"][qd + kvd:]
+    start = np.asarray(start, np.int32)
+    last = np.full(B, n - 1, np.int64) if last is None else np.asarray(last, np.int64)
+    x = draft_fuse(np.asarray(tok_ahead, np.int32).reshape(-1), W["embed"], W["w_fuse"], W["w_in"],
+                   l=l.reshape(-1, k), m=m.reshape(-1, k), h=h.reshape(-1, k))
+    hn = rmsnorm(x, eps=s.eps)
+    pos = (start[:, None] + np.arange(n, dtype=np.int32)[None, :]).reshape(-1)
+    kr = rope(gemm(hn, wk).reshape(B * n, s.Hkv, s.D), pos, s.theta).reshape(B, n, s.Hkv, s.D)
+    vr = gemm(hn, wv).reshape(B, n, s.Hkv, s.D)
+    out = np.empty((B, k), x.dtype)
+    for b in range(B):
+        L0, j = int(start[b]), int(last[b])
+        old_k = prev_k[b, :L0] if L0 else np.zeros((0, s.Hkv, s.D), kr.dtype)
+        old_v = prev_v[b, :L0] if L0 else np.zeros((0, s.Hkv, s.D), vr.dtype)
+        cache = _page(np.concatenate([old_k, kr[b, :j + 1]])[None], np.concatenate([old_v, vr[b, :j + 1]])[None])
+        row = b * n + j
+        q = rope(gemm(hn[row:row + 1], wq).reshape(1, s.Hq, s.D), np.array([L0 + j], np.int32), s.theta)
+        empty = np.zeros((1, 0, s.Hkv, s.D), x.dtype)
+        attn, _ = tree_attn(q[:, None], empty, empty, cache, np.zeros((1, 1, 1), np.uint64), want_lse=False)
+        out[b] = _draft_layer_tail(s, W, x[row:row + 1], attn.reshape(1, qd))[0]
+    return kr, vr, out
+
+
 class OwnChoice:
     """The selections of draft_tree itself: a node's children are its top-k
     logits by (value desc, id asc); the next frontier and the final tree are
@@ -603,9 +650,7 @@ def draft_tree(shape, W, l, m, h, ctx_tok, gap=GAP_FLAG, chooser=None, vocab=Non
     choices = {"ids": [], "frontier": []}
 
     def layer_tail(x, attn):
-        x = gemm(attn, W["wo"], R=x)
-        f = silu_mul(gemm(rmsnorm(x, eps=s.eps), W["wgu"]))
-        return gemm(f, W["wd"], R=x)
+        return _draft_layer_tail(s, W, x, attn)
 
     if vocab is not None:
         vocab = np.asarray(vocab, np.int64)

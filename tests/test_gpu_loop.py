@@ -8,6 +8,11 @@ one fixed launch sequence per step).
   the oracle's own greedy continuation of the target, token by token, up to
   the first oracle near-tie (top-2 gap below 1e-3); the sequence lengths
   grow by exactly the emitted count.
+* the draft's context extension of every step (fp32 and bf16) replayed
+  through the oracle's draft_context on the same inputs (the target's
+  feature rows of the accepted path, the tokens after them, the cache rows
+  before the step): the new cache rows and the draft output a_root within
+  1e-5 (fp32) / 2e-2 (bf16) normwise.
 * bf16 storage: the same against the bf16 oracle up to its first gap below
   2e-2 (bf16 rounding moves these logits by a few 1e-3); a loop replayed
   from a captured HIP graph reproduces the eager loop bit for bit (emitted
@@ -18,7 +23,7 @@ import pytest
 import torch
 
 import synth
-from tests._gpu import dev, host
+from tests._gpu import dev, host, normwise_rel
 
 pytestmark = pytest.mark.gpu
 
@@ -81,6 +86,7 @@ def _build(seed, S, f32):
                          ds.n_drafts, ds.theta, ds.eps, prefix_len=target.plen, reserve=S * R + 16, extend_rows=R)
     draft.ingest(dev(l), dev(m), dev(h), dev(ctx_tok))
     loop = e3.SpecLoop(target, draft, cap=S * R)
+    loop.host_draft_weights = Wd
     return loop, tin, Wt, ctx_tok
 
 
@@ -139,3 +145,47 @@ def test_loop_bf16_graph_replay_equals_eager_and_greedy(orc):
     assert np.array_equal(host(rep.d.k_cache), host(eager.d.k_cache))
     checked = _check_greedy(orc, eager, tin, Wt, ctx_tok, 2e-2)
     print(f"bf16: {host(eager.out_len).tolist()} tokens emitted in {S} steps, {checked} checked against greedy")
+
+
+def _draft_rows(cache, B, nb):
+    """Paged draft cache with its identity table -> rows [B, nb * 16, Hkv, D]."""
+    if cache.ndim == 4 and cache.shape[2] == 16:                      # K: [blocks, Hkv, 16, D]
+        x = cache.reshape(B, nb, cache.shape[1], 16, cache.shape[3]).transpose(0, 1, 3, 2, 4)
+    else:                                                              # V: [blocks, Hkv, D, 16]
+        x = cache.reshape(B, nb, cache.shape[1], cache.shape[2], 16).transpose(0, 1, 4, 2, 3)
+    return x.reshape(B, nb * 16, x.shape[-2], x.shape[-1])
+
+
+@pytest.mark.parametrize("f32", [True, False])
+def test_loop_draft_extension_matches_oracle(orc, f32):
+    S = 3
+    loop, tin, Wt, ctx_tok = _build(3, S, f32)
+    ts, ds = synth.LOOP_TARGET_SMALL, synth.LOOP_DRAFT_SMALL
+    d, t = loop.d, loop.t
+    tol = 1e-5 if f32 else 2e-2
+    B, T, R = ds.B, ts.T, d.R
+    worst = 0.0
+    for step in range(S):
+        kc0, vc0 = host(d.k_cache), host(d.v_cache)
+        loop.step()
+        torch.cuda.synchronize()
+        a, path, out, start = host(t.accept_len), host(t.path), host(t.out_tokens), host(loop.start)
+        feats = [host(t.feat[i]) for i in ts.features]
+        rows = np.stack([b * T + np.where(np.arange(R) <= a[b], path[b, :R], path[b, 0]) for b in range(B)])
+        l, m, h = (f[rows] for f in feats)
+        tok = np.where(np.arange(R)[None, :] <= a[:, None], out[:, :R], 0).astype(np.int32)
+        pk, pv = _draft_rows(kc0, B, d.nb), _draft_rows(vc0, B, d.nb)
+        kn, vn, a_last = orc.draft_context(ds, loop.host_draft_weights, l, m, h, tok, start, pk, pv, last=a)
+        k1, v1 = _draft_rows(host(d.k_cache), B, d.nb), _draft_rows(host(d.v_cache), B, d.nb)
+        for b in range(B):
+            sl = slice(int(start[b]), int(start[b]) + int(a[b]) + 1)
+            for got, want in ((k1[b, sl], kn[b, :a[b] + 1]), (v1[b, sl], vn[b, :a[b] + 1])):
+                rel = normwise_rel(got, want)[0]
+                worst = max(worst, rel)
+                assert rel <= tol, (step, b, rel)
+            # the rows before the step are untouched
+            assert np.array_equal(k1[b, :start[b]], pk[b, :start[b]])
+        rel = normwise_rel(host(d.a_root), a_last)[0]
+        worst = max(worst, rel)
+        assert rel <= tol, (step, rel)
+    print(f"{'fp32' if f32 else 'bf16'}: draft extension over {S} steps within {worst:.2e}")

@@ -299,3 +299,30 @@ def test_trimmed_vocab_replay_of_own_choices(orc):
     f = replay(orc, s, W, l, m, h, tok, r["choices"], vocab=vocab)
     assert np.array_equal(f["parent"], r["parent"]) and np.array_equal(f["tokens"], r["tokens"])
     assert all((v == 0).all() for v in f["margin"].values())
+
+
+def test_draft_context_in_pieces_equals_the_whole_ingest(orc):
+    """The draft's context rows taken in two pieces (the second on top of the
+    first's cached rows) give the whole ingest's K/V rows and output: the
+    piecewise form the decoding loop uses after each acceptance."""
+    s = dataclasses.replace(synth.DRAFT_SMALL, B=2, ctx=40)
+    cv = lambda a: synth.bf16_to_f32(a) if a.dtype == np.uint16 else a  # noqa: E731
+    W = {k: cv(v) for k, v in synth.draft_weights(s).items()}
+    l, m, h, tok = (cv(a)[:2, :40] if a.dtype == np.uint16 else a[:2, :40] for a in synth.draft_inputs(s, 3))
+    r = orc.draft_tree(s, W, l, m, h, tok)
+    B = 2
+    k1, v1, _ = orc.draft_context(s, W, l[:, :23], m[:, :23], h[:, :23], tok[:, :23], np.zeros(B, np.int32))
+    k2, v2, a = orc.draft_context(s, W, l[:, 23:], m[:, 23:], h[:, 23:], tok[:, 23:], np.full(B, 23, np.int32),
+                                  prev_k=k1, prev_v=v1)
+    kk, vv = np.concatenate([k1, k2], 1), np.concatenate([v1, v2], 1)
+    assert np.abs(kk - r["k_ctx"]).max() <= 1e-6 * np.abs(r["k_ctx"]).max()
+    assert np.abs(vv - r["v_ctx"]).max() <= 1e-6 * np.abs(r["v_ctx"]).max()
+    assert np.abs(a - r["a_root"]).max() <= 1e-5 * np.abs(r["a_root"]).max()
+    # an earlier row as `last`: only the rows up to it are visible to it
+    _, _, a_mid = orc.draft_context(s, W, l[:, 23:], m[:, 23:], h[:, 23:], tok[:, 23:], np.full(B, 23, np.int32),
+                                    prev_k=k1, prev_v=v1, last=np.array([5, 9]))
+    for b, j in ((0, 5), (1, 9)):
+        n = 23 + j + 1
+        _, _, a_ref = orc.draft_context(s, W, l[b:b + 1, :n], m[b:b + 1, :n], h[b:b + 1, :n], tok[b:b + 1, :n],
+                                        np.zeros(1, np.int32))
+        assert np.abs(a_mid[b] - a_ref[0]).max() <= 1e-5 * np.abs(a_ref).max()
