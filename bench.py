@@ -486,7 +486,7 @@ def bench_target(args, name="target8b-b64"):
     ach = fl / (gu_us * 1e-6) / 1e12
     roofline = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                "kernel": "eagle3_gemm (gate/up projection, 3904 x 28672 x 4096)", "flops_per_launch": fl,
+                "kernel": "eagle3_gemm_swiglu (gate/up projection + gating, 3904 x 28672 x 4096)", "flops_per_launch": fl,
                 "avg_launch_us": round(gu_us, 2), "launch_us_p10_p50_p90": pcts(gu_list)}
     qd, kvd = s.Hq * s.D, s.Hkv * s.D
     step_flops = 2.0 * M * s.k * (qd + 2 * kvd + qd + 3 * s.F) * s.layers + 2.0 * M * s.k * s.V
@@ -598,7 +598,7 @@ def bench_loop(args, name="loop8b-b64"):
     ach = fl / (gu_us * 1e-6) / 1e12
     roofline = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                "kernel": "eagle3_gemm (target gate/up projection, 3904 x 28672 x 4096)", "flops_per_launch": fl,
+                "kernel": "eagle3_gemm_swiglu (target gate/up projection + gating, 3904 x 28672 x 4096)", "flops_per_launch": fl,
                 "avg_launch_us": round(gu_us, 2), "launch_us_p10_p50_p90": pcts(gu_list)}
     nodes = ts.B * ds.n_drafts
     value = nodes / (ms_per_step * 1e-3)
