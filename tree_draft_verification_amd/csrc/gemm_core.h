@@ -127,7 +127,12 @@ __device__ __forceinline__ void mainloop(const GemmParams &p, int m0, int n0, in
     int seg = 0;
     // segment fields by constant index only (a run-time index would turn
     // these kernel-argument reads into per-chunk memory loads)
-    const int kofs1 = p.nseg > 1 ? p.kofs[1] : 0x7fffffff, kofs2 = p.nseg > 2 ? p.kofs[2] : 0x7fffffff;
+    // wave-uniform copies (readfirstlane): values read through p are not
+    // known to be uniform, and a per-lane segment test or loop bound turns
+    // the loop control into exec-mask arithmetic
+    const int kofs1 = __builtin_amdgcn_readfirstlane(p.nseg > 1 ? p.kofs[1] : 0x7fffffff);
+    const int kofs2 = __builtin_amdgcn_readfirstlane(p.nseg > 2 ? p.kofs[2] : 0x7fffffff);
+    const bool multi_seg = kofs1 != 0x7fffffff;
     auto set_bases = [&](int sg) {
         const uint16_t *aseg = (const uint16_t *)(sg == 0 ? p.a[0] : sg == 1 ? p.a[1] : p.a[2]);
         const int kseg = sg == 0 ? p.k[0] : sg == 1 ? p.k[1] : p.k[2];
@@ -259,7 +264,7 @@ __device__ __forceinline__ void mainloop(const GemmParams &p, int m0, int n0, in
     // when `refill`, the loads of chunk c + NS into chunk c's slot.
     auto phase_c = [&](int c, bool next, bool refill) {
         const int sl = (c + 1) % T::NS, kc = (c_begin + c + T::NS) * GBK;
-        if (refill) select_seg(kc);
+        if (refill && multi_seg) select_seg(kc);
         if (next && refill) {
 #pragma unroll
             for (int j = 0; j < NMF; ++j) {
@@ -297,7 +302,7 @@ __device__ __forceinline__ void mainloop(const GemmParams &p, int m0, int n0, in
         for (int i = 0; i < NRD; ++i) rd(0, 0, i, av0, bv0);
     }
     // steady state: every chunk refills a slot, wait depth is fixed
-    const int steady = nch - T::NS;
+    const int steady = __builtin_amdgcn_readfirstlane(nch - T::NS);
     for (int c = 0; c < steady; ++c) {
         phase_a(c);
         wait_vmcnt<(T::NS - 2) * T::LOADS>();  // chunk c + 1 has landed (later ones may be in flight)
