@@ -326,6 +326,9 @@ typedef struct eagle3_gemm_args {
     size_t ws_bytes;
 } eagle3_gemm_args;
 
+/* bf16: each A segment (M rows, or a_nrows rows when gathered) must be under
+ * 4 GiB (EAGLE3_ERR_UNSUPPORTED otherwise); the same holds for the hidden
+ * state of eagle3_lmhead_argmax. */
 /* bytes of workspace the call would use to split K (0: it would not split) */
 size_t eagle3_gemm_workspace(const eagle3_gemm_args *args);
 

@@ -102,6 +102,8 @@ def test_lmhead_errors(lib):
     assert f(FAKE, FAKE, 61, 128256, 4000, 1, 1, FAKE, None, None, None, FAKE, need, None) == -2  # K % 64
     assert f(FAKE, FAKE, 61, 128256, 4096, 17, 1, FAKE, None, None, None, FAKE, 1 << 30, None) == -2
     assert f(MISALIGNED, FAKE, 61, 128256, 4096, 1, 1, FAKE, None, None, None, FAKE, need, None) == -1
+    # a hidden state of 4 GiB or more is beyond the 32-bit load offsets of the GEMM core
+    assert f(FAKE, FAKE, 1 << 19, 128256, 4096, 1, 1, FAKE, None, None, None, FAKE, 1 << 62, None) == -2
 
 
 def test_lmhead_noalloc_rejects_calls_past_its_array(lib):

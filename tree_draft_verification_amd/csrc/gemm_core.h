@@ -112,6 +112,12 @@ __device__ __forceinline__ void fill_arow(const GemmParams &p, int m0, int (*aro
 // so a lane's registers hold one row of A's tile.
 // The waves run at raised issue priority for the loop (measured on the
 // 3904 x 128256 x 4096 LM-head shape with random bf16 data: 3.75 -> 3.53 ms).
+__device__ __forceinline__ const uint16_t *e3_uniform_ptr(const uint16_t *q) {
+    const uint64_t v = (uint64_t)q;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return (const uint16_t *)(((uint64_t)hi << 32) | lo);
+}
+
 template <int BM, int NS, bool TRANS = false>
 __device__ __forceinline__ void mainloop(const GemmParams &p, int m0, int n0, int c_begin, int nch,
                                          unsigned char *ring, const int (*arow)[BM],
@@ -123,7 +129,13 @@ __device__ __forceinline__ void mainloop(const GemmParams &p, int m0, int n0, in
     // 64 B; A rows first, then B rows); lane -> row 16 blk + lane / 4, slot lane % 4.
     // Source pointers are formed once per A segment; a chunk only adds its k offset.
     const int slot = lane & 3;
-    const uint16_t *src_base[T::LOADS];
+    // Each load address is a wave-uniform base (scalar registers) plus a
+    // 32-bit per-lane byte offset fixed for the whole loop, so a chunk's loads
+    // only add the chunk's k offset to the scalar base. The LDS destination
+    // of a load is wave-uniform too (the wave index from readfirstlane).
+    const int wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const char *abase = nullptr;  // the current A segment's base (wave-uniform)
+    uint32_t voff[T::LOADS];
     int seg = 0;
     // segment fields by constant index only (a run-time index would turn
     // these kernel-argument reads into per-chunk memory loads)
@@ -133,22 +145,27 @@ __device__ __forceinline__ void mainloop(const GemmParams &p, int m0, int n0, in
     const int kofs1 = __builtin_amdgcn_readfirstlane(p.nseg > 1 ? p.kofs[1] : 0x7fffffff);
     const int kofs2 = __builtin_amdgcn_readfirstlane(p.nseg > 2 ? p.kofs[2] : 0x7fffffff);
     const bool multi_seg = kofs1 != 0x7fffffff;
+    const int kfull = __builtin_amdgcn_readfirstlane(p.K);
+    const char *bbase = (const char *)e3_uniform_ptr((const uint16_t *)p.b + (size_t)n0 * kfull);
     auto set_bases = [&](int sg) {
         const uint16_t *aseg = (const uint16_t *)(sg == 0 ? p.a[0] : sg == 1 ? p.a[1] : p.a[2]);
-        const int kseg = sg == 0 ? p.k[0] : sg == 1 ? p.k[1] : p.k[2];
+        const int kseg = __builtin_amdgcn_readfirstlane(sg == 0 ? p.k[0] : sg == 1 ? p.k[1] : p.k[2]);
         const int oseg = sg == 0 ? 0 : sg == 1 ? kofs1 : kofs2;
+        abase = (const char *)e3_uniform_ptr(aseg - oseg);
 #pragma unroll
         for (int j = 0; j < T::LOADS; ++j) {
-            const int blk = wave * T::LOADS + j;
+            const int blk = wave_u * T::LOADS + j;
             const int row = blk * 16 + (lane >> 2);
-            if (row < BM) {
-                src_base[j] = aseg + (size_t)arow[sg][row] * kseg - oseg + 8 * (slot ^ gswz(row));
+            if (blk * 16 < BM) {
+                voff[j] = (uint32_t)(((size_t)arow[sg][row] * kseg + 8 * (slot ^ gswz(row))) * 2);
             } else {
                 const int n = min(n0 + row - BM, p.N - 1);
-                src_base[j] = (const uint16_t *)p.b + (size_t)n * p.K + 8 * (slot ^ gswz(row));
+                voff[j] = (uint32_t)(((size_t)(n - n0) * kfull + 8 * (slot ^ gswz(row))) * 2);
             }
         }
     };
+    // the scalar base of load j: A rows (the first BM rows of a stage) or B rows
+    auto sbase = [&](int j) { return (wave_u * T::LOADS + j) * 16 < BM ? abase : bbase; };
     set_bases(0);
     // B rows use the full K offset kc; A rows the offset within the segment (kofs folded into the base)
     auto issue = [&](int stage, int kc) {
@@ -160,9 +177,9 @@ __device__ __forceinline__ void mainloop(const GemmParams &p, int m0, int n0, in
         unsigned char *base = ring + stage * T::STAGE;
 #pragma unroll
         for (int j = 0; j < T::LOADS; ++j) {
-            const int blk = wave * T::LOADS + j;
-            __builtin_amdgcn_global_load_lds((const void *)(src_base[j] + kc), (lds_void_t *)(base + blk * 1024), 16,
-                                             0, 0);
+            const int blk = wave_u * T::LOADS + j;
+            __builtin_amdgcn_global_load_lds((const void *)(sbase(j) + (size_t)kc * 2 + voff[j]),
+                                             (lds_void_t *)(base + blk * 1024), 16, 0, 0);
         }
     };
 
@@ -230,8 +247,8 @@ __device__ __forceinline__ void mainloop(const GemmParams &p, int m0, int n0, in
                                                                   0, 0, 0);
     };
     auto dma = [&](int stage, int kc, int j) {
-        const int blk = wave * T::LOADS + j;
-        __builtin_amdgcn_global_load_lds((const void *)(src_base[j] + kc),
+        const int blk = wave_u * T::LOADS + j;
+        __builtin_amdgcn_global_load_lds((const void *)(sbase(j) + (size_t)kc * 2 + voff[j]),
                                          (lds_void_t *)(ring + stage * T::STAGE + blk * 1024), 16, 0, 0);
     };
     auto select_seg = [&](int kc) {

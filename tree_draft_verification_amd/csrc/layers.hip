@@ -413,6 +413,9 @@ extern "C" int eagle3_gemm(const eagle3_gemm_args *a, void *stream) {
     for (int s = 0; s < a->nseg; ++s) {
         if (!a->a[s] || a->k[s] < 1) return EAGLE3_ERR_ARG;
         if (a->a_rows[s] && a->a_nrows[s] < 1) return EAGLE3_ERR_ARG;
+        // the core addresses an A segment by 32-bit byte offsets
+        if (a->dtype == EAGLE3_BF16 && (uint64_t)(a->a_rows[s] ? a->a_nrows[s] : a->M) * a->k[s] * 2 >= (1ull << 32))
+            return EAGLE3_ERR_UNSUPPORTED;
         if (a->dtype == EAGLE3_BF16 && (a->k[s] % GSEG_ALIGN != 0 || !e3_aligned16(a->a[s])))
             return EAGLE3_ERR_UNSUPPORTED;
         p.a[s] = a->a[s];
@@ -485,6 +488,9 @@ extern "C" int eagle3_gemm_swiglu(const eagle3_gemm_args *a, void *stream) {
     for (int s = 0; s < a->nseg; ++s) {
         if (!a->a[s] || a->k[s] < 1) return EAGLE3_ERR_ARG;
         if (a->a_rows[s] && a->a_nrows[s] < 1) return EAGLE3_ERR_ARG;
+        // the core addresses an A segment by 32-bit byte offsets
+        if (a->dtype == EAGLE3_BF16 && (uint64_t)(a->a_rows[s] ? a->a_nrows[s] : a->M) * a->k[s] * 2 >= (1ull << 32))
+            return EAGLE3_ERR_UNSUPPORTED;
         if (a->k[s] % GSEG_ALIGN != 0 || !e3_aligned16(a->a[s])) return EAGLE3_ERR_UNSUPPORTED;
         p.a[s] = a->a[s];
         p.a_rows[s] = a->a_rows[s];

@@ -607,6 +607,7 @@ extern "C" int eagle3_lmhead_argmax(const void *hidden, const void *w, int M, in
     if (topk > 16 || N < 2 || topk > N) return EAGLE3_ERR_UNSUPPORTED;
     if (dtype != EAGLE3_BF16 && dtype != EAGLE3_F32) return EAGLE3_ERR_UNSUPPORTED;
     if (dtype == EAGLE3_BF16 && K % 64 != 0) return EAGLE3_ERR_UNSUPPORTED;
+    if (dtype == EAGLE3_BF16 && (uint64_t)M * K * 2 >= (1ull << 32)) return EAGLE3_ERR_UNSUPPORTED;
     if (dtype == EAGLE3_F32 && K % 4 != 0) return EAGLE3_ERR_UNSUPPORTED;
     if (M == 0) return EAGLE3_OK;
     if (!hidden || !w || !idx || !ws) return EAGLE3_ERR_ARG;
