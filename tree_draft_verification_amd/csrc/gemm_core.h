@@ -164,8 +164,15 @@ __device__ __forceinline__ void mainloop(const GemmParams &p, int m0, int n0, in
             }
         }
     };
-    // the scalar base of load j: A rows (the first BM rows of a stage) or B rows
-    auto sbase = [&](int j) { return (wave_u * T::LOADS + j) * 16 < BM ? abase : bbase; };
+    // the scalar base of load j: A rows (the first BM rows of a stage) or B
+    // rows. When BM is a multiple of one wave's rows per stage, all loads of
+    // a wave are A rows or all are B rows: one base per wave, no per-load
+    // select (which the compiler forms in vector registers)
+    constexpr bool WAVE_SIDE = BM % (T::LOADS * 16) == 0;
+    auto sbase = [&](int j) {
+        if constexpr (WAVE_SIDE) return wave_u * T::LOADS * 16 < BM ? abase : bbase;
+        else return (wave_u * T::LOADS + j) * 16 < BM ? abase : bbase;
+    };
     set_bases(0);
     // B rows use the full K offset kc; A rows the offset within the segment (kofs folded into the base)
     auto issue = [&](int stage, int kc) {
