@@ -18,11 +18,16 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 constexpr int GBN = 256, GBK = 32, GROW = GBK * 2;  // LDS row: 32 bf16 = 64 B
 constexpr int GSEG_ALIGN = 64;                                 // segment widths are multiples of this
 
-template <int BM, int NS_ = 4>
+// NW = 4: waves 2 x 2, each (BM/2) x 128; NW = 8: waves 2 x 4, each
+// (BM/2) x 64 (two waves per SIMD share the same ring and tile).
+template <int BM, int NS_ = 4, int NW_ = 4>
 struct GTile {
-    static constexpr int STAGE = (BM + GBN) * GROW;  // bytes per ring stage
-    static constexpr int LOADS = STAGE / 1024 / 4;   // 1 KB DMA loads per wave per stage
-    static constexpr int MB = BM / 64, NB = GBN / 64;  // 32 x 32 blocks per wave
+    static constexpr int NW = NW_;                      // waves per work-group
+    static constexpr int WN = NW / 2;                   // waves along N
+    static constexpr int CW = GBN / WN;                 // columns per wave
+    static constexpr int STAGE = (BM + GBN) * GROW;    // bytes per ring stage
+    static constexpr int LOADS = STAGE / 1024 / NW;    // 1 KB DMA loads per wave per stage
+    static constexpr int MB = BM / 64, NB = CW / 32;    // 32 x 32 blocks per wave
     static constexpr int NS = NS_;                      // ring stages
     static constexpr int RING = NS * STAGE;             // ring bytes
 };
@@ -53,10 +58,15 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 // wait until at most N LDS reads are outstanding; the fragments are tied to
 // the wait so no use of them can be scheduled above it
-template <int N, int MB>
+template <int N, int MB, int NB = 4>
 __device__ __forceinline__ void lgkm_wait(u32x4_t *av, u32x4_t *bv) {
-    static_assert(MB == 2 || MB == 4, "fragment count");
-    if constexpr (MB == 4) {
+    static_assert((MB == 2 || MB == 4) && (NB == 2 || NB == 4), "fragment count");
+    if constexpr (NB == 2) {
+        static_assert(MB == 4, "fragment count");
+        __asm__ volatile("s_waitcnt lgkmcnt(%6)"
+                         : "+v"(av[0]), "+v"(av[1]), "+v"(av[2]), "+v"(av[3]), "+v"(bv[0]), "+v"(bv[1])
+                         : "i"(N));
+    } else if constexpr (MB == 4) {
         __asm__ volatile("s_waitcnt lgkmcnt(%8)"
                          : "+v"(av[0]), "+v"(av[1]), "+v"(av[2]), "+v"(av[3]), "+v"(bv[0]), "+v"(bv[1]),
                            "+v"(bv[2]), "+v"(bv[3])
@@ -92,7 +102,7 @@ __device__ __forceinline__ void fill_arow(const GemmParams &p, int m0, int (*aro
     for (int s = 0; s < 3; ++s) {
         const int32_t *rows = s == 0 ? p.a_rows[0] : s == 1 ? p.a_rows[1] : p.a_rows[2];
         const int nrows = s == 0 ? p.a_nrows[0] : s == 1 ? p.a_nrows[1] : p.a_nrows[2];
-        for (int r = threadIdx.x; r < BM; r += 256) {
+        for (int r = threadIdx.x; r < BM; r += blockDim.x) {
             int m = min(m0 + r, p.M - 1);
             if (s < p.nseg && rows) m = min(max(rows[m], 0), nrows - 1);
             arow[s][r] = m;
@@ -105,10 +115,11 @@ __device__ __forceinline__ void fill_arow(const GemmParams &p, int m0, int (*aro
 // c_begin + nch - 1 (32 columns each; a split of K, or all of it). ring:
 // GTile<BM, NS>::RING
 // bytes of LDS (1 KB aligned). On return acc holds the tile: wave (wm, wn) =
-// (wave / 2, wave % 2), block (mb, nb), register r of lane (lr, lh) is
-// C[m0 + wm BM/2 + 32 mb + 8 (r / 4) + 4 lh + r % 4][n0 + 128 wn + 32 nb + lr],
+// (wave / WN, wave % WN) with CW = 256 / WN columns per wave, block (mb, nb),
+// register r of lane (lr, lh) is
+// C[m0 + wm BM/2 + 32 mb + 8 (r / 4) + 4 lh + r % 4][n0 + CW wn + 32 nb + lr],
 // or with TRANS (the MFMA operands swapped, same loads) its transpose:
-// C[m0 + wm BM/2 + 32 mb + lr][n0 + 128 wn + 32 nb + 8 (r / 4) + 4 lh + r % 4],
+// C[m0 + wm BM/2 + 32 mb + lr][n0 + CW wn + 32 nb + 8 (r / 4) + 4 lh + r % 4],
 // so a lane's registers hold one row of A's tile.
 // The waves run at raised issue priority for the loop (measured on the
 // 3904 x 128256 x 4096 LM-head shape with random bf16 data: 3.75 -> 3.53 ms).
@@ -118,11 +129,11 @@ __device__ __forceinline__ const uint16_t *e3_uniform_ptr(const uint16_t *q) {
     return (const uint16_t *)(((uint64_t)hi << 32) | lo);
 }
 
-template <int BM, int NS, bool TRANS = false>
+template <int BM, int NS, bool TRANS = false, int NW = 4>
 __device__ __forceinline__ void mainloop(const GemmParams &p, int m0, int n0, int c_begin, int nch,
                                          unsigned char *ring, const int (*arow)[BM],
-                                         f32x16_t (&acc)[GTile<BM, NS>::MB][GTile<BM, NS>::NB]) {
-    using T = GTile<BM, NS>;
+                                         f32x16_t (&acc)[GTile<BM, NS, NW>::MB][GTile<BM, NS, NW>::NB]) {
+    using T = GTile<BM, NS, NW>;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int lr = lane & 31, lh = lane >> 5;
     // load j of this wave fills stage block blk = wave * LOADS + j (16 rows of
@@ -200,7 +211,7 @@ __device__ __forceinline__ void mainloop(const GemmParams &p, int m0, int n0, in
 #pragma unroll
     for (int st = 0; st < T::NS - 1; ++st)
         if (st < nch) issue(st, (c_begin + st) * GBK);
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / T::WN, wn = wave % T::WN;
     // per-lane LDS byte offsets of the operand rows (sub-step 0 and 1 differ by the column)
     int aoff[T::MB][2], boff[T::NB][2];
 #pragma unroll
@@ -213,7 +224,7 @@ __device__ __forceinline__ void mainloop(const GemmParams &p, int m0, int n0, in
         }
 #pragma unroll
         for (int nb = 0; nb < T::NB; ++nb) {
-            const int row = wn * 128 + nb * 32 + lr;
+            const int row = wn * T::CW + nb * 32 + lr;
             boff[nb][s] = BM * GROW + row * GROW + ((cl ^ gswz(row)) << 4);
         }
     }
@@ -271,7 +282,7 @@ __device__ __forceinline__ void mainloop(const GemmParams &p, int m0, int n0, in
     // MFMAs of the current one (scheduling barriers pin that order).
     // A: MFMAs of (c, first half) with the reads of (c, second half) between them.
     auto phase_a = [&](int c) {
-        lgkm_wait<0, T::MB>(av0, bv0);
+        lgkm_wait<0, T::MB, T::NB>(av0, bv0);
         const int sl = c % T::NS;
 #pragma unroll
         for (int j = 0; j < NMF; ++j) {
@@ -282,7 +293,7 @@ __device__ __forceinline__ void mainloop(const GemmParams &p, int m0, int n0, in
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
-        lgkm_wait<0, T::MB>(av1, bv1);
+        lgkm_wait<0, T::MB, T::NB>(av1, bv1);
     };
     // C: MFMAs of (c, second half) with the reads of (c + 1, first half) and,
     // when `refill`, the loads of chunk c + NS into chunk c's slot.

@@ -403,6 +403,65 @@ __global__ __launch_bounds__(256, BM == 128 ? 2 : 1) void lmhead_big_kernel(e3g:
     }
 }
 
+// Top-2 lists without a log-sum-exp over many rows with eight waves per
+// 256 x 256 tile (two per SIMD, each 128 rows x 64 vocabulary columns): while
+// one wave of a SIMD waits on a barrier or a load, the other issues MFMAs.
+// The two waves of each 128-column half merge their lists through LDS, so
+// the records are those of the four-wave kernel: one per (hidden row,
+// 128-column half tile).
+__global__ __launch_bounds__(512, 1) void lmhead_top2_w8_kernel(e3g::GemmParams gp, int nrec, Partials p) {
+    using T = e3g::GTile<256, 4, 8>;
+    constexpr int BM = 256;
+    __shared__ __attribute__((aligned(1024))) unsigned char ring[T::RING];
+    __shared__ int arow[3][BM];
+    static_assert(T::WN == 4 && T::CW == 64, "two waves per 128-column half");
+    int mt, nt;
+    e3g::tile_of<4>(blockIdx.x, gridDim.x, gp.mt, gp.nt, mt, nt);
+    const int m0 = mt * BM, n0 = nt * BIG_BN;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int lr = lane & 31, lh = lane >> 5, wm = wave / T::WN, wn = wave % T::WN;
+    e3g::fill_arow<BM>(gp, m0, arow);
+    f32x16_t acc[T::MB][T::NB];
+    e3g::mainloop<BM, T::NS, true, 8>(gp, m0, n0, 0, gp.K / e3g::GBK, ring, arow, acc);
+    const int vbase = n0 + wn * T::CW;
+    const int nvalid = gp.N - vbase;
+    uint64_t own[T::MB][2];
+#pragma unroll
+    for (int mb = 0; mb < T::MB; ++mb) {
+        float b0, b1;
+        int i0, i1;
+        top2_row<T::NB>(acc[mb], lh, nvalid, b0, i0, b1, i1);
+        own[mb][0] = i0 == NO_COL ? 0 : e3_key(b0, vbase + i0);
+        own[mb][1] = i1 == NO_COL ? 0 : e3_key(b1, vbase + i1);
+    }
+    // odd waves hand their lists to the even wave of the same half
+    __syncthreads();  // every wave is done with the ring
+    uint64_t *xk = reinterpret_cast<uint64_t *>(ring) + ((wm * 2 + (wn >> 1)) * T::MB) * 64;
+    if ((wn & 1) && lh == 0) {
+#pragma unroll
+        for (int mb = 0; mb < T::MB; ++mb) {
+            xk[mb * 64 + 2 * lr] = own[mb][0];
+            xk[mb * 64 + 2 * lr + 1] = own[mb][1];
+        }
+    }
+    __syncthreads();
+    if (!(wn & 1) && lh == 0) {
+        const int rec_tile = 2 * nt + (wn >> 1);
+#pragma unroll
+        for (int mb = 0; mb < T::MB; ++mb) {
+            const int m = m0 + wm * (BM / 2) + 32 * mb + lr;
+            if (m < gp.M) {
+                const uint64_t y0 = xk[mb * 64 + 2 * lr], y1 = xk[mb * 64 + 2 * lr + 1];
+                const uint64_t x0 = own[mb][0], x1 = own[mb][1];
+                uint64_t L[2];
+                if (x0 >= y0) { L[0] = x0; L[1] = x1 > y0 ? x1 : y0; }
+                else { L[0] = y0; L[1] = y1 > x0 ? y1 : x0; }
+                store_record<2>(p, (size_t)m * nrec + rec_tile, L);
+            }
+        }
+    }
+}
+
 template <int KK, bool LSE>
 __global__ __launch_bounds__(256) void lmhead_f32_kernel(const float *__restrict__ h, const float *__restrict__ w,
                                                          int M, int N, int K, int ntiles, Partials p) {
@@ -566,7 +625,10 @@ void launch(const void *hidden, const void *w, int M, int N, int K, int topk, in
         gp.b = w; gp.M = M; gp.N = N; gp.K = K; gp.ldc = N;
         constexpr int BM = big_bm(KK);
         gp.mt = (M + BM - 1) / BM; gp.nt = (N + BIG_BN - 1) / BIG_BN;
-        lmhead_big_kernel<BM, KK, LSE><<<gp.mt * gp.nt, 256, 0, st>>>(gp, ntiles, p);
+        if constexpr (KK == 2 && !LSE)
+            lmhead_top2_w8_kernel<<<gp.mt * gp.nt, 512, 0, st>>>(gp, ntiles, p);
+        else
+            lmhead_big_kernel<BM, KK, LSE><<<gp.mt * gp.nt, 256, 0, st>>>(gp, ntiles, p);
     } else if (dtype == EAGLE3_BF16) {
         dim3 grid((M + 63) / 64, ntiles);
         const uint16_t *hp = (const uint16_t *)hidden, *wp = (const uint16_t *)w;
