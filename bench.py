@@ -46,7 +46,9 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
 METRIC = "verified tree nodes/s + accepted tok/step at 1 GPU; % HBM/MFMA roofline"
-LMHEAD_SRC = os.path.join(ROOT, "tree_draft_verification_amd", "csrc", "lmhead.hip")
+# the LM-head kernels are built from these sources; counters are valid while they are unchanged
+LMHEAD_SRC = [os.path.join(ROOT, "tree_draft_verification_amd", "csrc", f) for f in ("lmhead.hip", "gemm_core.h",
+                                                                                       "common.h")]
 VERIFY_WORKLOADS = ("llama8b-b1", "llama8b-b64", "llama70b-b8")
 CHAIN_TREE_WORKLOADS = ("chain60-b64", "tree60-b64", "chain40-b64", "tree40-b64")
 
@@ -78,7 +80,8 @@ def parse():
 
 def traffic_from_profile(workload):
     """HBM bytes per LM-head launch from the committed rocprofv3 counter
-    summary of this workload, or None when the kernel source changed since."""
+    summary of this workload, or None when the kernel sources (the LM head,
+    the GEMM core it is built on, the common header) changed since."""
     path = os.path.join(ROOT, "profiles", f"lmhead_{workload}_pmc.txt")
     if not os.path.exists(path):
         return None
@@ -87,7 +90,7 @@ def traffic_from_profile(workload):
         parts = line.split()
         if len(parts) == 2:
             vals[parts[0]] = parts[1]
-    src_hash = hashlib.sha256(open(LMHEAD_SRC, "rb").read()).hexdigest()
+    src_hash = hashlib.sha256(b"".join(open(f, "rb").read() for f in LMHEAD_SRC)).hexdigest()
     if vals.get("lmhead_source_sha256") != src_hash or "traffic_bytes_per_launch" not in vals:
         return None
     return float(vals["traffic_bytes_per_launch"])
