@@ -278,29 +278,33 @@ __global__ __launch_bounds__(256) void silu_mul_kernel(const void *__restrict__ 
 // Rotate-half RoPE in place on x viewed as [M][H][D] with row stride ld
 // (elements): pair (i, i + D/2) at position p = pos_offset + pos[m] turns by
 // p * theta^(-2i/D); the angle is formed in double precision.
+// One thread per (row, pair index): the angle depends on the position and
+// the pair only, so its sine and cosine (double precision) are formed once
+// and applied to every head of the row.
 template <bool BF16>
 __global__ __launch_bounds__(256) void rope_kernel(void *__restrict__ x, int M, int H, int D, int ld,
                                                    const int32_t *__restrict__ pos, int pos_offset, double log_theta) {
     const int half = D / 2;
     const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= (size_t)M * H * half) return;
+    if (i >= (size_t)M * half) return;
     const int j = (int)(i % half);
-    const size_t mh = i / half;
-    const int h = (int)(mh % H), m = (int)(mh / H);
+    const int m = (int)(i / half);
     const double ang = (double)(pos_offset + pos[m]) * exp(-2.0 * j / D * log_theta);
     double sn, cs;
     sincos(ang, &sn, &cs);
-    const size_t base = (size_t)m * ld + (size_t)h * D;
-    if (BF16) {
-        uint16_t *p = (uint16_t *)x;
-        const double a = e3_bf16_to_f32(p[base + j]), b = e3_bf16_to_f32(p[base + j + half]);
-        p[base + j] = e3_f32_to_bf16((float)(a * cs - b * sn));
-        p[base + j + half] = e3_f32_to_bf16((float)(b * cs + a * sn));
-    } else {
-        float *p = (float *)x;
-        const double a = p[base + j], b = p[base + j + half];
-        p[base + j] = (float)(a * cs - b * sn);
-        p[base + j + half] = (float)(b * cs + a * sn);
+    for (int h = 0; h < H; ++h) {
+        const size_t base = (size_t)m * ld + (size_t)h * D;
+        if (BF16) {
+            uint16_t *p = (uint16_t *)x;
+            const double a = e3_bf16_to_f32(p[base + j]), b = e3_bf16_to_f32(p[base + j + half]);
+            p[base + j] = e3_f32_to_bf16((float)(a * cs - b * sn));
+            p[base + j + half] = e3_f32_to_bf16((float)(b * cs + a * sn));
+        } else {
+            float *p = (float *)x;
+            const double a = p[base + j], b = p[base + j + half];
+            p[base + j] = (float)(a * cs - b * sn);
+            p[base + j + half] = (float)(b * cs + a * sn);
+        }
     }
 }
 
@@ -540,7 +544,7 @@ extern "C" int eagle3_rope(void *x, int M, int H, int D, int ld, const int32_t *
     if (ld < H * D) return EAGLE3_ERR_ARG;
     if (M == 0) return EAGLE3_OK;
     if (!x || !pos) return EAGLE3_ERR_ARG;
-    const size_t n = (size_t)M * H * (D / 2);
+    const size_t n = (size_t)M * (D / 2);
     const double lt = log((double)theta);
     if (dtype == EAGLE3_BF16) rope_kernel<true><<<grid1(n), 256, 0, e3_stream(stream)>>>(x, M, H, D, ld, pos, pos_offset, lt);
     else rope_kernel<false><<<grid1(n), 256, 0, e3_stream(stream)>>>(x, M, H, D, ld, pos, pos_offset, lt);
