@@ -137,6 +137,38 @@ def test_exact_ties_many_rows(lib):
         assert gg[m] == 0.0
 
 
+# Duplicates of vocabulary row 1234 (tile 4, columns 192..255 of its tile in
+# one wave; column 18 of that wave's 64, lane half 0): 1217 and 1233 sit in
+# the same lane as 1234, 1220 in the other lane half, 1170 in the other wave of
+# the same 128-column half, 1300 in the next tile, 5 in the first and 2999 in
+# the ragged last tile.
+@pytest.mark.parametrize("dups", [[1217, 1233], [1220], [1170], [5, 1300, 2999], [1217, 1220, 1170, 1300, 5, 2999]],
+                         ids=["same-lane", "lane-halves", "waves", "tiles", "mixed"])
+def test_exact_ties_top2_many_rows(lib, dups):
+    """The verify step's list (top-2 without lse) on the many-row path: bitwise
+    equal logits of duplicate rows give the two lowest ids of the tied set in
+    ascending order and a gap of exactly 0, wherever the copies sit."""
+    rng = np.random.default_rng(8)
+    M, N, K = 200, 3000, 256
+    h = synth.normal_bf16(rng, (M, K))
+    wf = synth.bf16_to_f32(synth.normal_bf16(rng, (N, K), 0.02))
+    src = 1234
+    wf[src] *= 6.0
+    w = synth.f32_to_bf16(wf)
+    for d in dups:
+        w[d] = w[src]
+    ties = sorted(dups + [src])
+    ref = synth.bf16_to_f32(h).astype(np.float64) @ synth.bf16_to_f32(w).astype(np.float64).T
+    others = np.delete(ref, ties, axis=1).max(axis=1)
+    wins = ref[:, src] > others + 1e-3
+    assert wins.sum() >= 20
+    for topk in (1, 2):
+        gi, gv, gg, _ = gpu_lmhead(lib, h, w, topk, False)
+        for m in np.nonzero(wins)[0]:
+            assert list(gi[m, :topk]) == ties[:topk], (topk, m, gi[m])
+            assert gg[m] == 0.0
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_rmsnorm_parity(orc, lib, dtype):
     rng = np.random.default_rng(7)

@@ -243,30 +243,74 @@ constexpr int big_bm(int KK) { return KK >= 8 ? 128 : 256; }
 
 // Top-2 of one row over the 128 vocabulary columns a wave holds in the
 // transposed accumulator layout (lane lr: the row; lane half lh: every other
-// group of 4 columns). The scan runs in increasing column order, so the strict
-// comparison keeps the lowest column among equal values; NaN and -inf never
-// enter the list. The two lane halves then merge by (value desc, column asc).
+// group of 4 columns), with the lowest column first among equal values; NaN
+// and -inf never enter the list. The two lane halves then merge by (value
+// desc, column asc).
 constexpr int NO_COL = 0x7fffffff;
 __device__ __forceinline__ bool e3_before(float a, int ia, float b, int ib) { return a > b || (a == b && ia < ib); }
 
-template <int NB>
-__device__ __forceinline__ void top2_row(const f32x16_t (&blk)[NB], int lh, int nvalid, float &b0, int &i0, float &b1,
-                                         int &i1) {
-    b0 = -INFINITY; b1 = -INFINITY; i0 = NO_COL; i1 = NO_COL;
-    const bool full = nvalid >= NB * 32;  // uniform
+// max(a, b) as one v_max_f32 (a NaN operand yields the other); written out so
+// that no canonicalising copy of each operand is added
+__device__ __forceinline__ float e3_vmax(float a, float b) {
+    float r;
+    __asm__("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+
+// One lane's two largest values and their lowest columns; MASK: columns from
+// nvalid on hold no vocabulary row and count as -inf.
+template <int NB, bool MASK>
+__device__ __forceinline__ void top2_lane(const f32x16_t (&blk)[NB], int lh, int nvalid, float &b0, int &i0, float &b1,
+                                          int &i1) {
+    // the two largest values with multiplicity: b0 = max, b1 = the median of
+    // (b0, b1, v), two VALU operations per value; both pass over NaN
+    b0 = -INFINITY; b1 = -INFINITY;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int col = 32 * nb + 8 * (r >> 2) + 4 * lh + (r & 3);
-            float v = blk[nb][r];
-            if (!full && col >= nvalid) v = -INFINITY;
-            const bool g0 = v > b0, g1 = v > b1;
-            b1 = g0 ? b0 : (g1 ? v : b1);
-            i1 = g0 ? i0 : (g1 ? col : i1);
-            b0 = g0 ? v : b0;
-            i0 = g0 ? col : i0;
+            const float v = MASK && col >= nvalid ? -INFINITY : blk[nb][r];
+            const float t = __builtin_amdgcn_fmed3f(b0, b1, v);
+            b0 = e3_vmax(b0, v);
+            b1 = t;
         }
+    // their columns: a scan in decreasing column order keeps the lowest column
+    // holding each value; when b0 == b1 in some lane, the second column is the
+    // second-lowest holding b0 (a branch uniform over the wave)
+    i0 = NO_COL; i1 = NO_COL;
+    if (__builtin_amdgcn_ballot_w64(b0 == b1 && b0 > -INFINITY) == 0) {
+#pragma unroll
+        for (int nb = NB - 1; nb >= 0; --nb)
+#pragma unroll
+            for (int r = 15; r >= 0; --r) {
+                const int col = 32 * nb + 8 * (r >> 2) + 4 * lh + (r & 3);
+                const float v = MASK && col >= nvalid ? -INFINITY : blk[nb][r];
+                i0 = v == b0 ? col : i0;
+                i1 = v == b1 ? col : i1;
+            }
+    } else {
+#pragma unroll
+        for (int nb = NB - 1; nb >= 0; --nb)
+#pragma unroll
+            for (int r = 15; r >= 0; --r) {
+                const int col = 32 * nb + 8 * (r >> 2) + 4 * lh + (r & 3);
+                const float v = MASK && col >= nvalid ? -INFINITY : blk[nb][r];
+                const bool e0 = v == b0, e1 = v == b1;
+                i1 = e1 ? (e0 ? i0 : col) : i1;
+                i0 = e0 ? col : i0;
+            }
+    }
+    // -inf (and masked columns) never enter the list
+    if (!(b0 > -INFINITY)) i0 = NO_COL;
+    if (!(b1 > -INFINITY)) i1 = NO_COL;
+}
+
+template <int NB>
+__device__ __forceinline__ void top2_row(const f32x16_t (&blk)[NB], int lh, int nvalid, float &b0, int &i0, float &b1,
+                                         int &i1) {
+    if (nvalid >= NB * 32) top2_lane<NB, false>(blk, lh, nvalid, b0, i0, b1, i1);  // uniform
+    else top2_lane<NB, true>(blk, lh, nvalid, b0, i0, b1, i1);
     const float ob0 = __shfl_xor(b0, 32), ob1 = __shfl_xor(b1, 32);
     const int oi0 = __shfl_xor(i0, 32), oi1 = __shfl_xor(i1, 32);
     if (e3_before(ob0, oi0, b0, i0)) {
