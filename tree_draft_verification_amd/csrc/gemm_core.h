@@ -81,6 +81,16 @@ __device__ __forceinline__ void lgkm_wait(u32x4_t *av, u32x4_t *bv) {
 // Work-group id -> output tile. Work-groups are dealt to the 8 XCDs in turn;
 // give each XCD a contiguous run of tiles, ordered N-fastest within groups of
 // G M-tiles, so the tiles one XCD runs together share A rows and B rows in its L2.
+// Position t of the tile order -> tile (N-fastest within groups of G M-tiles).
+template <int G = 8>
+__device__ __forceinline__ void tile_at_order(int t, int MT, int NT, int &mt, int &nt) {
+    const int gsz_full = G * NT;
+    const int g = t / gsz_full, first = g * G, gs = min(G, MT - first);
+    const int u = t - g * gsz_full;
+    mt = first + u % gs;
+    nt = u / gs;
+}
+
 template <int G = 8>
 __device__ __forceinline__ void tile_of(int L, int nwg, int MT, int NT, int &mt, int &nt) {
     const int q = nwg >> 3, r = nwg & 7, x = L & 7, j = L >> 3;
@@ -355,6 +365,188 @@ __device__ __forceinline__ void mainloop(const GemmParams &p, int m0, int n0, in
         }
     }
     __builtin_amdgcn_s_setprio(0);
+}
+
+
+// Persistent form of the K loop for one A segment without a row gather (the
+// many-row LM head): the work-group runs its tiles tile_at(0 .. ntile - 1)
+// back to back and the DMA ring runs on across tile boundaries, so the first
+// chunks of a tile are loaded while the previous tile finishes and its
+// epilogue(i, acc) runs. Layout of acc, LDS ring and ordering rule as in
+// mainloop. At a tile boundary every wave waits for all of its outstanding
+// vector memory operations (the epilogue's stores among them) and meets a
+// barrier before the first fragment reads of the next tile, so the partial
+// vmcnt waits inside a tile count LDS-DMA loads only. Requires K / 32 >= NS.
+template <int BM, int NS, bool TRANS, int NW, class TileAt, class Epi>
+__device__ __forceinline__ void mainloop_persistent(const GemmParams &p, int ntile, TileAt tile_at, Epi epilogue,
+                                                    unsigned char *ring) {
+    using T = GTile<BM, NS, NW>;
+    static_assert(BM % (T::LOADS * 16) == 0, "a wave's stage rows are all A rows or all B rows");
+    static_assert(NS >= 3, "two chunks in flight beyond the one being read");
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int lr = lane & 31, lh = lane >> 5;
+    const int wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int kfull = __builtin_amdgcn_readfirstlane(p.K);
+    const int nch = kfull / GBK;
+    const bool a_side = wave_u * T::LOADS * 16 < BM;
+    // DMA issue state: stream position (tile, chunk) of the next load, that
+    // tile's wave-uniform base and the fixed per-lane byte offsets
+    int iss_tile = 0, iss_c = 0;
+    const char *ibase = nullptr;
+    uint32_t voff[T::LOADS];
+    auto set_issue_tile = [&](int i) {
+        int m0, n0;
+        tile_at(i, m0, n0);
+        m0 = __builtin_amdgcn_readfirstlane(m0);
+        n0 = __builtin_amdgcn_readfirstlane(n0);
+        ibase = a_side ? (const char *)e3_uniform_ptr((const uint16_t *)p.a[0] + (size_t)m0 * kfull)
+                       : (const char *)e3_uniform_ptr((const uint16_t *)p.b + (size_t)n0 * kfull);
+#pragma unroll
+        for (int j = 0; j < T::LOADS; ++j) {
+            const int row = (wave_u * T::LOADS + j) * 16 + (lane >> 2);
+            const int sw = 8 * ((lane & 3) ^ gswz(row));
+            if (a_side) voff[j] = (uint32_t)(((size_t)(min(m0 + row, p.M - 1) - m0) * kfull + sw) * 2);
+            else voff[j] = (uint32_t)(((size_t)(min(n0 + row - BM, p.N - 1) - n0) * kfull + sw) * 2);
+        }
+    };
+    auto prep_issue = [&]() {  // move the issue state to the next tile when this one is done
+        if (iss_c == nch) {
+            iss_c = 0;
+            set_issue_tile(min(++iss_tile, ntile - 1));
+        }
+    };
+    auto dma = [&](int stage, int j) {
+        const int blk = wave_u * T::LOADS + j;
+        __builtin_amdgcn_global_load_lds((const void *)(ibase + (size_t)iss_c * (GBK * 2) + voff[j]),
+                                         (lds_void_t *)(ring + stage * T::STAGE + blk * 1024), 16, 0, 0);
+    };
+    auto issue = [&](int stage) {
+        prep_issue();
+#pragma unroll
+        for (int j = 0; j < T::LOADS; ++j) dma(stage, j);
+        ++iss_c;
+    };
+    const int wm = wave / T::WN, wn = wave % T::WN;
+    int aoff[T::MB][2], boff[T::NB][2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        const int cl = 2 * s + lh;
+#pragma unroll
+        for (int mb = 0; mb < T::MB; ++mb) {
+            const int row = wm * (BM / 2) + mb * 32 + lr;
+            aoff[mb][s] = row * GROW + ((cl ^ gswz(row)) << 4);
+        }
+#pragma unroll
+        for (int nb = 0; nb < T::NB; ++nb) {
+            const int row = wn * T::CW + nb * 32 + lr;
+            boff[nb][s] = BM * GROW + row * GROW + ((cl ^ gswz(row)) << 4);
+        }
+    }
+    auto barrier = [&]() {
+        __builtin_amdgcn_s_barrier();
+        __asm__ volatile("" ::: "memory");
+    };
+    u32x4_t av0[T::MB], bv0[T::NB], av1[T::MB], bv1[T::NB];
+    const uint32_t ring_lds = (uint32_t)(uintptr_t)(lds_void_t *)ring;
+    constexpr int NMF = T::MB * T::NB;
+    constexpr int NRD = T::MB + T::NB;
+    static_assert(NRD <= NMF && T::LOADS <= NMF, "one read and one load per MFMA at most");
+    auto rd = [&](int slotk, int s, int i, u32x4_t *av, u32x4_t *bv) {
+        const uint32_t base = ring_lds + slotk * T::STAGE;
+        if (i < T::MB) __asm__ volatile("ds_read_b128 %0, %1" : "=v"(av[i]) : "v"(base + aoff[i][s]));
+        else __asm__ volatile("ds_read_b128 %0, %1" : "=v"(bv[i - T::MB]) : "v"(base + boff[i - T::MB][s]));
+    };
+    f32x16_t acc[T::MB][T::NB];
+    auto mf = [&](int j, const u32x4_t *av, const u32x4_t *bv) {
+        const int mb = j / T::NB, nb = j % T::NB;
+        if constexpr (TRANS)
+            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, bv[nb]),
+                                                                  __builtin_bit_cast(bf16x8_t, av[mb]), acc[mb][nb],
+                                                                  0, 0, 0);
+        else
+            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, av[mb]),
+                                                                  __builtin_bit_cast(bf16x8_t, bv[nb]), acc[mb][nb],
+                                                                  0, 0, 0);
+    };
+    // A: MFMAs of (g, first half) with the reads of (g, second half) between them
+    auto phase_a = [&](int g) {
+        lgkm_wait<0, T::MB, T::NB>(av0, bv0);
+        const int sl = g % T::NS;
+#pragma unroll
+        for (int j = 0; j < NMF; ++j) {
+            mf(j, av0, bv0);
+            __builtin_amdgcn_sched_barrier(0);
+            if (j < NRD) {
+                rd(sl, 1, j, av1, bv1);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        lgkm_wait<0, T::MB, T::NB>(av1, bv1);
+    };
+    // C: MFMAs of (g, second half) with the reads of (g + 1, first half) when
+    // NEXT, and the loads of the stream's next chunk into g's slot
+    auto phase_c = [&](int g, auto next_c) {
+        constexpr bool NEXT = decltype(next_c)::value;
+        const int sl = (g + 1) % T::NS, st = g % T::NS;
+        prep_issue();
+#pragma unroll
+        for (int j = 0; j < NMF; ++j) {
+            mf(j, av1, bv1);
+            __builtin_amdgcn_sched_barrier(0);
+            if (NEXT && j < NRD) {
+                rd(sl, 0, j, av0, bv0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if (j >= NMF - T::LOADS) {
+                dma(st, j - (NMF - T::LOADS));
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        ++iss_c;
+    };
+    if (ntile <= 0) return;
+    set_issue_tile(0);
+#pragma unroll
+    for (int st = 0; st < T::NS - 1; ++st) issue(st);
+    wait_vmcnt<(T::NS - 2) * T::LOADS>();  // chunk 0
+    barrier();
+    issue(T::NS - 1);
+#pragma unroll
+    for (int i = 0; i < NRD; ++i) rd(0, 0, i, av0, bv0);
+    // Every tile runs the same steps: the stream of loads continues past the
+    // final tile into a virtual next one that re-reads the final tile's rows
+    // (its NS chunks land in slots nobody reads and are drained before the
+    // end), so there is no separate draining code. With nch >= NS every chunk
+    // waits at full depth and refills a slot.
+    int g = 0;
+    for (int t = 0; t < ntile; ++t) {
+#pragma unroll
+        for (int i = 0; i < T::MB; ++i)
+#pragma unroll
+            for (int jj = 0; jj < T::NB; ++jj)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][jj][r] = 0.f;
+        __builtin_amdgcn_s_setprio(3);
+        for (int c = 0; c + 1 < nch; ++c, ++g) {
+            phase_a(g);
+            wait_vmcnt<(T::NS - 2) * T::LOADS>();
+            barrier();
+            phase_c(g, std::true_type{});
+        }
+        // the tile's last chunk: the next tile's chunks keep loading
+        phase_a(g);
+        barrier();
+        phase_c(g, std::false_type{});
+        ++g;
+        __builtin_amdgcn_s_setprio(0);
+        epilogue(t, acc);
+        wait_vmcnt<0>();
+        barrier();
+        if (t + 1 < ntile) {
+#pragma unroll
+            for (int i = 0; i < NRD; ++i) rd(g % T::NS, 0, i, av0, bv0);
+        }
+    }
 }
 
 }  // namespace e3g

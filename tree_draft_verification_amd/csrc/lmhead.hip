@@ -506,6 +506,81 @@ __global__ __launch_bounds__(512, 1) void lmhead_top2_w8_kernel(e3g::GemmParams 
     }
 }
 
+// The same top-2 tiles, persistent: one work-group per CU runs every W-th
+// tile of its XCD's run of the tile order (W work-groups per XCD; work-group w
+// is dispatched to XCD w mod 8), so the XCD's work-groups still work on
+// neighbouring tiles together, and the LDS-DMA ring runs on from one tile into
+// the next: the next tile's first chunks load during the last chunks and the
+// selection of the current one. The lists are exchanged through a buffer of
+// their own (the ring holds chunks in flight). Same records as above.
+__global__ __launch_bounds__(512, 1) void lmhead_top2_w8p_kernel(e3g::GemmParams gp, int nrec, Partials p) {
+    using T = e3g::GTile<256, 4, 8>;
+    constexpr int BM = 256;
+    __shared__ __attribute__((aligned(1024))) unsigned char ring[T::RING];
+    __shared__ uint64_t xk_all[2 * 2 * T::MB * 64];
+    static_assert(T::WN == 4 && T::CW == 64, "two waves per 128-column half");
+    const int P = gridDim.x, w = blockIdx.x, x = w & 7, j = w >> 3;
+    const int W = (P - x + 7) >> 3;  // work-groups on this XCD
+    const int ntiles_all = gp.mt * gp.nt, q = ntiles_all >> 3, r8 = ntiles_all & 7;
+    const int start = x * q + min(x, r8), cnt = q + (x < r8 ? 1 : 0);
+    const int ntile = j < cnt ? (cnt - j + W - 1) / W : 0;
+    auto tile_at = [&](int i, int &m0, int &n0) {
+        int mt, nt;
+        e3g::tile_at_order<4>(start + j + i * W, gp.mt, gp.nt, mt, nt);
+        m0 = mt * BM;
+        n0 = nt * BIG_BN;
+    };
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int lr = lane & 31, lh = lane >> 5, wm = wave / T::WN, wn = wave % T::WN;
+    auto epilogue = [&](int i, const f32x16_t (&acc)[T::MB][T::NB]) {
+        int m0, n0;
+        tile_at(i, m0, n0);
+        const int nt = n0 / BIG_BN;
+        const int vbase = n0 + wn * T::CW;
+        const int nvalid = gp.N - vbase;
+        uint64_t own[T::MB][2];
+#pragma unroll
+        for (int mb = 0; mb < T::MB; ++mb) {
+            float b0, b1;
+            int i0, i1;
+            top2_row<T::NB>(acc[mb], lh, nvalid, b0, i0, b1, i1);
+            own[mb][0] = i0 == NO_COL ? 0 : e3_key(b0, vbase + i0);
+            own[mb][1] = i1 == NO_COL ? 0 : e3_key(b1, vbase + i1);
+        }
+        // odd waves hand their lists to the even wave of the same half
+        uint64_t *xk = xk_all + ((wm * 2 + (wn >> 1)) * T::MB) * 64;
+        if ((wn & 1) && lh == 0) {
+#pragma unroll
+            for (int mb = 0; mb < T::MB; ++mb) {
+                xk[mb * 64 + 2 * lr] = own[mb][0];
+                xk[mb * 64 + 2 * lr + 1] = own[mb][1];
+            }
+        }
+        // LDS-only barrier: a full one would also wait for the next tile's chunks in flight
+        __asm__ volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        __builtin_amdgcn_s_barrier();
+        __asm__ volatile("" ::: "memory");
+        if (!(wn & 1) && lh == 0) {
+            const int rec_tile = 2 * nt + (wn >> 1);
+#pragma unroll
+            for (int mb = 0; mb < T::MB; ++mb) {
+                const int m = m0 + wm * (BM / 2) + 32 * mb + lr;
+                if (m < gp.M) {
+                    const uint64_t y0 = xk[mb * 64 + 2 * lr], y1 = xk[mb * 64 + 2 * lr + 1];
+                    const uint64_t x0 = own[mb][0], x1 = own[mb][1];
+                    uint64_t L[2];
+                    if (x0 >= y0) { L[0] = x0; L[1] = x1 > y0 ? x1 : y0; }
+                    else { L[0] = y0; L[1] = y1 > x0 ? y1 : x0; }
+                    store_record<2>(p, (size_t)m * nrec + rec_tile, L);
+                }
+            }
+        }
+        // the buffer is written again only after the next tile's K loop and its barriers
+    };
+    e3g::mainloop_persistent<BM, T::NS, true, 8>(gp, ntile, tile_at, epilogue, ring);
+}
+
 template <int KK, bool LSE>
 __global__ __launch_bounds__(256) void lmhead_f32_kernel(const float *__restrict__ h, const float *__restrict__ w,
                                                          int M, int N, int K, int ntiles, Partials p) {
@@ -669,9 +744,12 @@ void launch(const void *hidden, const void *w, int M, int N, int K, int topk, in
         gp.b = w; gp.M = M; gp.N = N; gp.K = K; gp.ldc = N;
         constexpr int BM = big_bm(KK);
         gp.mt = (M + BM - 1) / BM; gp.nt = (N + BIG_BN - 1) / BIG_BN;
-        if constexpr (KK == 2 && !LSE)
-            lmhead_top2_w8_kernel<<<gp.mt * gp.nt, 512, 0, st>>>(gp, ntiles, p);
-        else
+        if constexpr (KK == 2 && !LSE) {
+            if (K / e3g::GBK >= 4)  // the persistent loop keeps 4 chunks of one tile in flight
+                lmhead_top2_w8p_kernel<<<std::min(gp.mt * gp.nt, e3_cu_count()), 512, 0, st>>>(gp, ntiles, p);
+            else
+                lmhead_top2_w8_kernel<<<gp.mt * gp.nt, 512, 0, st>>>(gp, ntiles, p);
+        } else
             lmhead_big_kernel<BM, KK, LSE><<<gp.mt * gp.nt, 256, 0, st>>>(gp, ntiles, p);
     } else if (dtype == EAGLE3_BF16) {
         dim3 grid((M + 63) / 64, ntiles);
