@@ -369,16 +369,21 @@ __device__ __forceinline__ void mainloop(const GemmParams &p, int m0, int n0, in
 
 
 // Persistent form of the K loop for one A segment without a row gather (the
-// many-row LM head): the work-group runs its tiles tile_at(0 .. ntile - 1)
-// back to back and the DMA ring runs on across tile boundaries, so the first
+// many-row LM head): the work-group runs tile after tile as `queue` hands
+// them out and the DMA ring runs on across tile boundaries, so the first
 // chunks of a tile are loaded while the previous tile finishes and its
-// epilogue(i, acc) runs. Layout of acc, LDS ring and ordering rule as in
-// mainloop. At a tile boundary every wave waits for all of its outstanding
-// vector memory operations (the epilogue's stores among them) and meets a
-// barrier before the first fragment reads of the next tile, so the partial
-// vmcnt waits inside a tile count LDS-DMA loads only. Requires K / 32 >= NS.
-template <int BM, int NS, bool TRANS, int NW, class TileAt, class Epi>
-__device__ __forceinline__ void mainloop_persistent(const GemmParams &p, int ntile, TileAt tile_at, Epi epilogue,
+// epilogue(tile, acc) runs. queue.first(cur, nxt) gives the first two tiles
+// (-1: none) and queue.advance(nxt) the one after the new current tile; both
+// are called by every thread with no load in flight and return the same
+// values in every thread. tile_at(tile, m0, n0) gives a tile's origin.
+// Layout of acc, LDS ring and ordering rule as in mainloop. At a tile
+// boundary every wave waits for all of its outstanding vector memory
+// operations (the epilogue's stores among them) and meets a barrier before
+// the first fragment reads of the next tile, so the partial vmcnt waits
+// inside a tile count LDS-DMA loads (and older operations) only. Requires
+// K / 32 >= NS.
+template <int BM, int NS, bool TRANS, int NW, class TileAt, class Queue, class Epi>
+__device__ __forceinline__ void mainloop_persistent(const GemmParams &p, TileAt tile_at, Queue &queue, Epi epilogue,
                                                     unsigned char *ring) {
     using T = GTile<BM, NS, NW>;
     static_assert(BM % (T::LOADS * 16) == 0, "a wave's stage rows are all A rows or all B rows");
@@ -389,9 +394,13 @@ __device__ __forceinline__ void mainloop_persistent(const GemmParams &p, int nti
     const int kfull = __builtin_amdgcn_readfirstlane(p.K);
     const int nch = kfull / GBK;
     const bool a_side = wave_u * T::LOADS * 16 < BM;
-    // DMA issue state: stream position (tile, chunk) of the next load, that
-    // tile's wave-uniform base and the fixed per-lane byte offsets
-    int iss_tile = 0, iss_c = 0;
+    // the tile being computed and the one after it (-1: none)
+    int cur, nxt;
+    queue.first(cur, nxt);
+    if (cur < 0) return;
+    // DMA issue state: chunk of the next load within its tile, that tile's
+    // wave-uniform base and the fixed per-lane byte offsets
+    int iss_c = 0;
     const char *ibase = nullptr;
     uint32_t voff[T::LOADS];
     auto set_issue_tile = [&](int i) {
@@ -409,10 +418,14 @@ __device__ __forceinline__ void mainloop_persistent(const GemmParams &p, int nti
             else voff[j] = (uint32_t)(((size_t)(min(n0 + row - BM, p.N - 1) - n0) * kfull + sw) * 2);
         }
     };
-    auto prep_issue = [&]() {  // move the issue state to the next tile when this one is done
+    // move the issue state on to the next tile when this one is done (once
+    // per computed tile, during its last NS chunks); after the last tile a
+    // virtual one re-reads the current tile's rows: its chunks land in slots
+    // nobody reads and are drained at the tile boundary
+    auto prep_issue = [&]() {
         if (iss_c == nch) {
             iss_c = 0;
-            set_issue_tile(min(++iss_tile, ntile - 1));
+            set_issue_tile(nxt >= 0 ? nxt : cur);
         }
     };
     auto dma = [&](int stage, int j) {
@@ -504,8 +517,7 @@ __device__ __forceinline__ void mainloop_persistent(const GemmParams &p, int nti
         }
         ++iss_c;
     };
-    if (ntile <= 0) return;
-    set_issue_tile(0);
+    set_issue_tile(cur);
 #pragma unroll
     for (int st = 0; st < T::NS - 1; ++st) issue(st);
     wait_vmcnt<(T::NS - 2) * T::LOADS>();  // chunk 0
@@ -513,13 +525,10 @@ __device__ __forceinline__ void mainloop_persistent(const GemmParams &p, int nti
     issue(T::NS - 1);
 #pragma unroll
     for (int i = 0; i < NRD; ++i) rd(0, 0, i, av0, bv0);
-    // Every tile runs the same steps: the stream of loads continues past the
-    // final tile into a virtual next one that re-reads the final tile's rows
-    // (its NS chunks land in slots nobody reads and are drained before the
-    // end), so there is no separate draining code. With nch >= NS every chunk
-    // waits at full depth and refills a slot.
+    // Every tile runs the same steps; with nch >= NS every chunk waits at
+    // full depth and refills a slot.
     int g = 0;
-    for (int t = 0; t < ntile; ++t) {
+    while (true) {
 #pragma unroll
         for (int i = 0; i < T::MB; ++i)
 #pragma unroll
@@ -539,13 +548,14 @@ __device__ __forceinline__ void mainloop_persistent(const GemmParams &p, int nti
         phase_c(g, std::false_type{});
         ++g;
         __builtin_amdgcn_s_setprio(0);
-        epilogue(t, acc);
+        epilogue(cur, acc);
         wait_vmcnt<0>();
         barrier();
-        if (t + 1 < ntile) {
+        cur = nxt;
+        if (cur < 0) break;
+        queue.advance(nxt);
 #pragma unroll
-            for (int i = 0; i < NRD; ++i) rd(g % T::NS, 0, i, av0, bv0);
-        }
+        for (int i = 0; i < NRD; ++i) rd(g % T::NS, 0, i, av0, bv0);
     }
 }
 
