@@ -626,18 +626,22 @@ __global__ __launch_bounds__(512, 1) void lmhead_top2_w8p_kernel(e3g::GemmParams
         const int nt = n0 / BIG_BN;
         const int vbase = n0 + wn * T::CW;
         const int nvalid = gp.N - vbase;
+        // a wave whose rows all lie past M (no MFMAs ran for it) selects nothing
+        const bool rows_here = __builtin_amdgcn_readfirstlane(m0 + wm * (BM / 2)) < gp.M;
         uint64_t own[T::MB][2];
+        if (rows_here) {
 #pragma unroll
-        for (int mb = 0; mb < T::MB; ++mb) {
-            float b0, b1;
-            int i0, i1;
-            top2_row<T::NB>(acc[mb], lh, nvalid, b0, i0, b1, i1);
-            own[mb][0] = i0 == NO_COL ? 0 : e3_key(b0, vbase + i0);
-            own[mb][1] = i1 == NO_COL ? 0 : e3_key(b1, vbase + i1);
+            for (int mb = 0; mb < T::MB; ++mb) {
+                float b0, b1;
+                int i0, i1;
+                top2_row<T::NB>(acc[mb], lh, nvalid, b0, i0, b1, i1);
+                own[mb][0] = i0 == NO_COL ? 0 : e3_key(b0, vbase + i0);
+                own[mb][1] = i1 == NO_COL ? 0 : e3_key(b1, vbase + i1);
+            }
         }
         // odd waves hand their lists to the even wave of the same half
         uint64_t *xk = xk_all + ((wm * 2 + (wn >> 1)) * T::MB) * 64;
-        if ((wn & 1) && lh == 0) {
+        if (rows_here && (wn & 1) && lh == 0) {
 #pragma unroll
             for (int mb = 0; mb < T::MB; ++mb) {
                 xk[mb * 64 + 2 * lr] = own[mb][0];
@@ -646,7 +650,7 @@ __global__ __launch_bounds__(512, 1) void lmhead_top2_w8p_kernel(e3g::GemmParams
         }
         // LDS-only barrier: a full one would also wait for the next tile's chunks in flight
         e3_lds_barrier();
-        if (!(wn & 1) && lh == 0) {
+        if (rows_here && !(wn & 1) && lh == 0) {
             const int rec_tile = 2 * nt + (wn >> 1);
 #pragma unroll
             for (int mb = 0; mb < T::MB; ++mb) {
