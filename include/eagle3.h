@@ -346,7 +346,13 @@ int eagle3_silu_mul(const void *gu, int M, int F, int dtype, void *y, void *stre
  * 128 j .. 128 j + 127, the next 128 rows the up rows of the same outputs;
  * eagle3_copy_rows with a row table builds it from [Wg; Wu]); N % 256 == 0;
  * c is y [M, F] with row stride ldc (0: F; a multiple of 8; 16-byte aligned);
- * no residual, no workspace (ws ignored). */
+ * no residual. ws / ws_bytes (optional, device, caller-owned, 16-byte
+ * aligned, at least EAGLE3_PERSIST_WS_BYTES): for large calls with one A
+ * segment and no row gather, the call then runs one work-group per CU that
+ * takes output tiles from counters kept there (the caller must not use the
+ * workspace for anything else while the call runs); results are the same
+ * with or without it. */
+#define EAGLE3_PERSIST_WS_BYTES ((size_t)1024)
 int eagle3_gemm_swiglu(const eagle3_gemm_args *args, void *stream);
 
 /* Rotary embedding, rotate-half convention (reading): in place on x viewed as

@@ -122,9 +122,15 @@ def test_silu_mul(orc, lib, dtype):
     assert rel <= (2e-2 if dtype == "bf16" else 1e-5)
 
 
-@pytest.mark.parametrize("M,F,k", [(1, 128, [64]), (200, 256, [128, 64, 192]), (1000, 384, [256]),
-                                   (640, 512, [4096])])
-def test_gemm_swiglu_fused(orc, lib, M, F, k):
+# (1000, 32768, [128]) with a workspace: 4 x 256 tiles of 256 x 256, so the
+# persistent path runs (one work-group per CU, several tiles each; the last
+# row tile holds 232 rows); (300, 16384, [256]): one tile per work-group, the
+# upper half of the last row tile past M
+@pytest.mark.parametrize("M,F,k,ws", [(1, 128, [64], False), (200, 256, [128, 64, 192], False),
+                                      (1000, 384, [256], False), (640, 512, [4096], False),
+                                      (1000, 32768, [128], True), (1000, 32768, [128], False),
+                                      (300, 16384, [256], True)])
+def test_gemm_swiglu_fused(orc, lib, M, F, k, ws):
     """The fused gate/up projection + gating against the oracle's
     silu_mul(gemm(A, [Wg; Wu])), and bit for bit against the two separate
     calls on the GPU (the weight turned into the paired layout by
@@ -143,7 +149,8 @@ def test_gemm_swiglu_fused(orc, lib, M, F, k):
     wp = torch.empty_like(w)
     lib.eagle3_copy_rows(w, wp, 2 * F, src_rows=lib.pair_gate_up_rows(F, "cuda"))
     y = torch.full((M, F), 3.0, dtype=torch.bfloat16, device="cuda")
-    lib.eagle3_gemm_swiglu(sd, wp, y, a_rows=rd)
+    wsb = torch.full((lib.PERSIST_WS_BYTES,), 0xAB, dtype=torch.uint8, device="cuda") if ws else None
+    lib.eagle3_gemm_swiglu(sd, wp, y, a_rows=rd, ws=wsb)
     gu = torch.empty(M, 2 * F, dtype=torch.bfloat16, device="cuda")
     lib.eagle3_gemm(sd, w, gu, a_rows=rd)
     y2 = torch.empty(M, F, dtype=torch.bfloat16, device="cuda")

@@ -228,10 +228,14 @@ def eagle3_gemm(a, b, c, residual=None, a_rows=None, a_nrows=None, ldc=0, M=None
     _check(_gemm(ctypes.byref(g), _stream(stream)), "eagle3_gemm")
 
 
-def eagle3_gemm_swiglu(a, b, y, a_rows=None, ldc=0, M=None, stream=None):
+PERSIST_WS_BYTES = 1024  # EAGLE3_PERSIST_WS_BYTES
+
+
+def eagle3_gemm_swiglu(a, b, y, a_rows=None, ldc=0, M=None, stream=None, ws=None):
     """y = silu(A . Wg^T) * (A . Wu^T) with b the gate/up weight in paired
-    layout (see pair_gate_up_rows); y [M, N / 2]."""
-    g = _gemm_args(a, b, y, None, a_rows, ldc, M if M is not None else y.shape[0], None)
+    layout (see pair_gate_up_rows); y [M, N / 2]. ws (optional, at least
+    PERSIST_WS_BYTES): room for the tile counters of the persistent path."""
+    g = _gemm_args(a, b, y, None, a_rows, ldc, M if M is not None else y.shape[0], ws)
     _check(_gemm_swiglu(ctypes.byref(g), _stream(stream)), "eagle3_gemm_swiglu")
 
 

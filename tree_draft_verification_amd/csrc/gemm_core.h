@@ -368,6 +368,97 @@ __device__ __forceinline__ void mainloop(const GemmParams &p, int m0, int n0, in
 }
 
 
+// Tile-claim counters of the persistent kernels: one per XCD run, 128 bytes
+// apart, in a caller's workspace, zeroed by ctr_zero_kernel before a pass.
+constexpr int CTR_STRIDE = 32;
+constexpr size_t CTR_BYTES = 8 * CTR_STRIDE * sizeof(uint32_t);
+static_assert(CTR_BYTES <= EAGLE3_PERSIST_WS_BYTES, "the counters fit the documented workspace");
+// a tile claim: a global (not flat) atomic, counted by vmcnt only, so a wait
+// for LDS operations does not wait for a claim in flight
+__device__ __forceinline__ uint32_t claim_tile(uint32_t *ctr) {
+    typedef __attribute__((address_space(1))) uint32_t global_u32;
+    return __hip_atomic_fetch_add((global_u32 *)ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <int UNUSED = 0>
+__global__ void ctr_zero_kernel(uint32_t *ctr) {
+    if (threadIdx.x < 8) ctr[threadIdx.x * CTR_STRIDE] = 0;
+}
+
+// barrier over LDS operations only (no wait for vector memory operations)
+__device__ __forceinline__ void lds_barrier() {
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+}
+
+// Tile queue of the persistent kernels: the tile order is cut into 8
+// runs, one per XCD, each with a claim counter; thread 0 claims for the
+// work-group and broadcasts through LDS. first() and advance() are called by
+// every thread at points with no load in flight.
+struct TileQueue {
+    uint32_t *ctr;
+    int *tq;              // LDS broadcast slots
+    int x, q, r8;         // own run; tiles per run = q (+1 for the first r8 runs)
+    uint32_t pend;        // thread 0: the claim in flight on the own run
+    bool own_left;        // thread 0: the own run may still have tiles
+    __device__ __forceinline__ void init(uint32_t *c, int *slots, int ntiles) {
+        ctr = c; tq = slots;
+        x = blockIdx.x & 7; q = ntiles >> 3; r8 = ntiles & 7;
+        pend = 0; own_left = true;
+    }
+    __device__ __forceinline__ int run_start(int v) const { return v * q + min(v, r8); }
+    __device__ __forceinline__ int run_cnt(int v) const { return q + (v < r8 ? 1 : 0); }
+    // thread 0: a tile from the runs first_run, first_run + 1, ... (waits for each claim)
+    __device__ __forceinline__ int claim(int first_run) {
+        for (int d = 0; d < 8; ++d) {
+            const int v = (first_run + d) & 7;
+            const uint32_t k = claim_tile(ctr + v * CTR_STRIDE);
+            if (k < (uint32_t)run_cnt(v)) return run_start(v) + (int)k;
+        }
+        return -1;
+    }
+    // the claim for the tile after next, read at the next boundary; the
+    // counter's offset is hidden from the compiler, whose rewrite of an atomic
+    // on a uniform address would consume the result at once
+    __device__ __forceinline__ void issue_pending() {
+        int off = x * CTR_STRIDE;
+        __asm__ volatile("" : "+v"(off));
+        if (own_left) pend = claim_tile(ctr + off);
+    }
+    __device__ __forceinline__ void first(int &cur, int &nxt) {
+        if (threadIdx.x == 0) {
+            const int a = claim(x);
+            const int b = a < 0 ? -1 : claim(x);
+            own_left = b >= run_start(x) && b < run_start(x) + run_cnt(x);
+            tq[0] = a;
+            tq[1] = b;
+            if (b >= 0) issue_pending();
+        }
+        lds_barrier();
+        cur = tq[0];
+        nxt = tq[1];
+        lds_barrier();  // the slots are written again at the next boundary
+    }
+    // nxt holds the new current tile; returns the one after it (-1: none)
+    __device__ __forceinline__ void advance(int &nxt) {
+        if (threadIdx.x == 0) {
+            int t = -1;
+            if (own_left && pend < (uint32_t)run_cnt(x)) {
+                t = run_start(x) + (int)pend;
+            } else {
+                own_left = false;
+                t = claim((x + 1) & 7);  // the other runs, then the own run again
+            }
+            if (t >= 0) issue_pending();
+            tq[0] = t;
+        }
+        lds_barrier();
+        nxt = tq[0];
+        lds_barrier();
+    }
+};
+
 // Persistent form of the K loop for one A segment without a row gather (the
 // many-row LM head): the work-group runs tile after tile as `queue` hands
 // them out and the DMA ring runs on across tile boundaries, so the first

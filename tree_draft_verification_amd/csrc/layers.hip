@@ -359,6 +359,90 @@ __global__ __launch_bounds__(256) void commit_kv_kernel(const void *__restrict__
     }
 }
 
+// Persistent form of the SWIGLU tiles for one A segment without a row gather
+// (tile-claim counters in the caller's workspace; see mainloop_persistent):
+// eight waves per 256 x 256 tile with the MFMA operands swapped, so a lane
+// holds one row and 16 columns of each 32 x 32 block. Of the four waves of a
+// row half, waves 0-1 hold the gate values (tile columns 0-127) and waves 2-3
+// the up values of the same outputs in the same lane and register positions.
+// The gating is split between the two waves of a pair, which sit on
+// different SIMDs: per 32-row block the up wave hands its bf16-rounded up
+// values of its first 32 columns to the gate wave and the gate wave its gate
+// values of the second 32 columns to the up wave, through LDS (the ring holds
+// the next tile's chunks); each then writes y = silu(g) * u for its 32
+// columns as 16-byte row pieces, with the same rounding and arithmetic as the
+// other SWIGLU epilogue.
+__global__ __launch_bounds__(512, 1) void gemm_swiglu_persistent_kernel(GemmParams p, uint32_t *ctr) {
+    using T = GTile<256, 4, 8>;
+    constexpr int BM = 256;
+    static_assert(T::MB == 4 && T::NB == 2 && T::CW == 64, "wave tile 128 x 64");
+    __shared__ __attribute__((aligned(1024))) unsigned char ring[T::RING];
+    __shared__ uint32_t ub[2 * 2 * 2 * 8 * 64];  // [row half][pair][from up / from gate][bf16 pair][lane]
+    __shared__ int tq[2];
+    TileQueue queue;
+    queue.init(ctr, tq, p.mt * p.nt);
+    auto tile_at = [&](int t, int &m0, int &n0) {
+        int mt, nt;
+        tile_at_order(t, p.mt, p.nt, mt, nt);
+        m0 = mt * BM;
+        n0 = nt * GBN;
+    };
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int lr = lane & 31, lh = lane >> 5, wm = wave / T::WN, wn = wave % T::WN;
+    uint16_t *cc = (uint16_t *)p.c;
+    uint32_t *pair_slot = ub + ((wm * 2 + (wn & 1)) * 2) * 8 * 64;
+    auto epilogue = [&](int tile, const f32x16_t (&acc)[T::MB][T::NB]) {
+        int m0, n0;
+        tile_at(tile, m0, n0);
+        const bool rows_here = __builtin_amdgcn_readfirstlane(m0 + wm * (BM / 2)) < p.M;
+        const bool up = __builtin_amdgcn_readfirstlane(wn) >= 2;
+        // this wave computes the outputs of block `own` (gate wave: 0, up
+        // wave: 1) and hands its values of the other block to its partner
+        const int own = up ? 1 : 0;
+        uint32_t *to_partner = pair_slot + (up ? 0 : 1) * 8 * 64;
+        const uint32_t *from_partner = pair_slot + (up ? 1 : 0) * 8 * 64;
+        uint16_t *ybase = cc + (n0 >> 1) + (wn & 1) * T::CW + own * 32 + 4 * lh;
+#pragma unroll
+        for (int mb = 0; mb < T::MB; ++mb) {
+            if (rows_here) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float v0 = up ? acc[mb][0][2 * e] : acc[mb][1][2 * e];
+                    const float v1 = up ? acc[mb][0][2 * e + 1] : acc[mb][1][2 * e + 1];
+                    to_partner[e * 64 + lane] = (uint32_t)e3_f32_to_bf16(v0) | ((uint32_t)e3_f32_to_bf16(v1) << 16);
+                }
+            }
+            lds_barrier();
+            const int m = m0 + wm * (BM / 2) + 32 * mb + lr;
+            if (rows_here && m < p.M) {
+                uint16_t *yrow = ybase + (size_t)m * p.ldc;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    // outputs 32 own + 8 q + 4 lh + (0..3) of this pair's 64
+                    const uint32_t w01 = from_partner[(2 * q) * 64 + lane];
+                    const uint32_t w23 = from_partner[(2 * q + 1) * 64 + lane];
+                    const float other[4] = {e3_bf16_to_f32((uint16_t)w01), e3_bf16_to_f32((uint16_t)(w01 >> 16)),
+                                            e3_bf16_to_f32((uint16_t)w23), e3_bf16_to_f32((uint16_t)(w23 >> 16))};
+                    uint16_t y[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float mine = e3_bf16_to_f32(e3_f32_to_bf16(up ? acc[mb][1][4 * q + e]
+                                                                            : acc[mb][0][4 * q + e]));
+                        const float g = up ? other[e] : mine, u = up ? mine : other[e];
+                        y[e] = e3_f32_to_bf16(g / (1.f + expf(-g)) * u);
+                    }
+                    uint2 o;
+                    o.x = (uint32_t)y[0] | ((uint32_t)y[1] << 16);
+                    o.y = (uint32_t)y[2] | ((uint32_t)y[3] << 16);
+                    *reinterpret_cast<uint2 *>(yrow + 8 * q) = o;
+                }
+            }
+            lds_barrier();  // the pair is done before the next block overwrites the slots
+        }
+    };
+    mainloop_persistent<BM, T::NS, true, 8>(p, tile_at, queue, epilogue, ring);
+}
+
 // dst[dst_rows[i]] = src[src_rows[i]] for i < n, 16 bytes per thread; a null
 // table is the identity; rows outside [0, nrows) are skipped.
 __global__ __launch_bounds__(256) void copy_rows_kernel(const uint4 *__restrict__ src,
@@ -513,7 +597,16 @@ extern "C" int eagle3_gemm_swiglu(const eagle3_gemm_args *a, void *stream) {
     p.nt = nt;
     if (t256 >= 4 * cus || (t128 < 2 * cus && t256 >= cus)) {
         p.mt = (a->M + 255) / 256;
-        gemm_bf16_kernel<256, 4, false, true, true><<<p.mt * nt, 256, 0, st>>>(p, 1, nullptr);
+        // persistent work-groups when the workspace can hold the tile counters
+        // (one A segment without a row gather; at least 4 chunks of K)
+        if (a->ws && a->ws_bytes >= EAGLE3_PERSIST_WS_BYTES && e3_aligned16(a->ws) && a->nseg == 1 &&
+            !a->a_rows[0] && K / GBK >= 4) {
+            uint32_t *ctr = (uint32_t *)a->ws;
+            ctr_zero_kernel<<<1, 64, 0, st>>>(ctr);
+            gemm_swiglu_persistent_kernel<<<(int)std::min<long>(t256, cus), 512, 0, st>>>(p, ctr);
+        } else {
+            gemm_bf16_kernel<256, 4, false, true, true><<<p.mt * nt, 256, 0, st>>>(p, 1, nullptr);
+        }
     } else if (t128 >= 2 * cus) {
         p.mt = (a->M + 127) / 128;
         gemm_bf16_kernel<128, 3, false, true, true><<<p.mt * nt, 256, 0, st>>>(p, 1, nullptr);

@@ -51,14 +51,7 @@ struct Partials {
     float *se;      // [M, ntiles]
     uint32_t *ctr;  // tile counters of the persistent top-2 pass, one per XCD, CTR_STRIDE apart
 };
-constexpr int CTR_STRIDE = 32;  // 128 bytes between counters
-// a tile claim: a global (not flat) atomic, counted by vmcnt only, so a wait
-// for LDS operations does not wait for a claim in flight
-__device__ __forceinline__ uint32_t e3_claim(uint32_t *ctr) {
-    typedef __attribute__((address_space(1))) uint32_t global_u32;
-    return __hip_atomic_fetch_add((global_u32 *)ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-constexpr size_t CTR_BYTES = 8 * CTR_STRIDE * sizeof(uint32_t);
+using e3g::CTR_BYTES;
 
 // one record: a row's sorted list over one tile (KK even: 16-byte stores)
 template <int KK>
@@ -515,81 +508,6 @@ __global__ __launch_bounds__(512, 1) void lmhead_top2_w8_kernel(e3g::GemmParams 
     }
 }
 
-// barrier over LDS operations only (no wait for vector memory operations)
-__device__ __forceinline__ void e3_lds_barrier() {
-    __asm__ volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-    __builtin_amdgcn_s_barrier();
-    __asm__ volatile("" ::: "memory");
-}
-
-// Tile queue of the persistent top-2 pass: the tile order is cut into 8
-// runs, one per XCD, each with a claim counter; thread 0 claims for the
-// work-group and broadcasts through LDS. first() and advance() are called by
-// every thread at points with no load in flight.
-struct TileQueue {
-    uint32_t *ctr;
-    int *tq;              // LDS broadcast slots
-    int x, q, r8;         // own run; tiles per run = q (+1 for the first r8 runs)
-    uint32_t pend;        // thread 0: the claim in flight on the own run
-    bool own_left;        // thread 0: the own run may still have tiles
-    __device__ __forceinline__ void init(uint32_t *c, int *slots, int ntiles) {
-        ctr = c; tq = slots;
-        x = blockIdx.x & 7; q = ntiles >> 3; r8 = ntiles & 7;
-        pend = 0; own_left = true;
-    }
-    __device__ __forceinline__ int run_start(int v) const { return v * q + min(v, r8); }
-    __device__ __forceinline__ int run_cnt(int v) const { return q + (v < r8 ? 1 : 0); }
-    // thread 0: a tile from the runs first_run, first_run + 1, ... (waits for each claim)
-    __device__ __forceinline__ int claim(int first_run) {
-        for (int d = 0; d < 8; ++d) {
-            const int v = (first_run + d) & 7;
-            const uint32_t k = e3_claim(ctr + v * CTR_STRIDE);
-            if (k < (uint32_t)run_cnt(v)) return run_start(v) + (int)k;
-        }
-        return -1;
-    }
-    // the claim for the tile after next, read at the next boundary; the
-    // counter's offset is hidden from the compiler, whose rewrite of an atomic
-    // on a uniform address would consume the result at once
-    __device__ __forceinline__ void issue_pending() {
-        int off = x * CTR_STRIDE;
-        __asm__ volatile("" : "+v"(off));
-        if (own_left) pend = e3_claim(ctr + off);
-    }
-    __device__ __forceinline__ void first(int &cur, int &nxt) {
-        if (threadIdx.x == 0) {
-            const int a = claim(x);
-            const int b = a < 0 ? -1 : claim(x);
-            own_left = b >= run_start(x) && b < run_start(x) + run_cnt(x);
-            tq[0] = a;
-            tq[1] = b;
-            if (b >= 0) issue_pending();
-        }
-        e3_lds_barrier();
-        cur = tq[0];
-        nxt = tq[1];
-        e3_lds_barrier();  // the slots are written again at the next boundary
-    }
-    // nxt holds the new current tile; returns the one after it (-1: none)
-    __device__ __forceinline__ void advance(int &nxt) {
-        if (threadIdx.x == 0) {
-            int t = -1;
-            if (own_left && pend < (uint32_t)run_cnt(x)) {
-                t = run_start(x) + (int)pend;
-            } else {
-                own_left = false;
-                t = claim((x + 1) & 7);  // the other runs, then the own run again
-            }
-            if (t >= 0) issue_pending();
-            tq[0] = t;
-        }
-        e3_lds_barrier();
-        nxt = tq[0];
-        e3_lds_barrier();
-    }
-};
-
 // The same top-2 tiles, persistent: one work-group per CU takes tiles from
 // the run of the tile order that belongs to its XCD (work-group w is
 // dispatched to XCD w mod 8), so an XCD's work-groups work on neighbouring
@@ -610,7 +528,7 @@ __global__ __launch_bounds__(512, 1) void lmhead_top2_w8p_kernel(e3g::GemmParams
     __shared__ uint64_t xk_all[2 * 2 * T::MB * 64];
     __shared__ int tq[2];
     static_assert(T::WN == 4 && T::CW == 64, "two waves per 128-column half");
-    TileQueue queue;
+    e3g::TileQueue queue;
     queue.init(p.ctr, tq, gp.mt * gp.nt);
     auto tile_at = [&](int t, int &m0, int &n0) {
         int mt, nt;
@@ -649,7 +567,7 @@ __global__ __launch_bounds__(512, 1) void lmhead_top2_w8p_kernel(e3g::GemmParams
             }
         }
         // LDS-only barrier: a full one would also wait for the next tile's chunks in flight
-        e3_lds_barrier();
+        e3g::lds_barrier();
         if (rows_here && !(wn & 1) && lh == 0) {
             const int rec_tile = 2 * nt + (wn >> 1);
 #pragma unroll
@@ -668,10 +586,6 @@ __global__ __launch_bounds__(512, 1) void lmhead_top2_w8p_kernel(e3g::GemmParams
         // the buffer is written again only after the next tile's K loop and its barriers
     };
     e3g::mainloop_persistent<BM, T::NS, true, 8>(gp, tile_at, queue, epilogue, ring);
-}
-
-__global__ void lmhead_ctr_zero_kernel(uint32_t *ctr) {
-    if (threadIdx.x < 8) ctr[threadIdx.x * CTR_STRIDE] = 0;
 }
 
 template <int KK, bool LSE>
@@ -840,7 +754,7 @@ void launch(const void *hidden, const void *w, int M, int N, int K, int topk, in
         gp.mt = (M + BM - 1) / BM; gp.nt = (N + BIG_BN - 1) / BIG_BN;
         if constexpr (KK == 2 && !LSE) {
             if (K / e3g::GBK >= 4) {  // the persistent loop keeps 4 chunks of one tile in flight
-                lmhead_ctr_zero_kernel<<<1, 64, 0, st>>>(p.ctr);
+                e3g::ctr_zero_kernel<<<1, 64, 0, st>>>(p.ctr);
                 lmhead_top2_w8p_kernel<<<std::min(gp.mt * gp.nt, e3_cu_count()), 512, 0, st>>>(gp, ntiles, p);
             } else
                 lmhead_top2_w8_kernel<<<gp.mt * gp.nt, 512, 0, st>>>(gp, ntiles, p);

@@ -83,9 +83,10 @@ class TargetModel:
         dtc = B_._dtype(E)
         self.lm_ws = torch.empty(max(256, B_.eagle3_lmhead_workspace(M, self.V, self.k, 1, dtc)),
                                  dtype=torch.uint8, device=dv)
-        # K-split workspace of the narrow projections (K and V: few output tiles)
+        # K-split workspace of the narrow projections (K and V: few output tiles),
+        # also the tile counters of the persistent gate/up call
         need = max(B_.eagle3_gemm_workspace([self.h], self.proj[0][1], self.k_rows[0].view(M, self.kvd)),
-                   B_.eagle3_gemm_workspace([self.h], self.proj[0][0], self.q), 256)
+                   B_.eagle3_gemm_workspace([self.h], self.proj[0][0], self.q), B_.PERSIST_WS_BYTES)
         self.gemm_ws = torch.empty(need, dtype=torch.uint8, device=dv)
         self._attn_ws = None
         # optional: a list of (start, end) HIP event pairs per layer for the
@@ -137,7 +138,7 @@ class TargetModel:
             B_.eagle3_rmsnorm(self.x, self.h, eps=self.eps)
             self._ev("gu", i, 0)
             if self.fused_mlp:
-                B_.eagle3_gemm_swiglu([self.h], self.wgu_paired[i], self.f)
+                B_.eagle3_gemm_swiglu([self.h], self.wgu_paired[i], self.f, ws=ws)
             else:
                 B_.eagle3_gemm([self.h], self.w[f"l{i}.wgu"], self.gu, ws=ws)
             self._ev("gu", i, 1)
