@@ -544,7 +544,7 @@ __global__ __launch_bounds__(512, 1) void lmhead_top2_w8p_kernel(e3g::GemmParams
         const int nt = n0 / BIG_BN;
         const int vbase = n0 + wn * T::CW;
         const int nvalid = gp.N - vbase;
-        // a wave whose rows all lie past M (no MFMAs ran for it) selects nothing
+        // a wave whose rows all lie past M selects nothing
         const bool rows_here = __builtin_amdgcn_readfirstlane(m0 + wm * (BM / 2)) < gp.M;
         uint64_t own[T::MB][2];
         if (rows_here) {
