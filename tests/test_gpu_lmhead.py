@@ -30,7 +30,9 @@ def gpu_lmhead(lib, h, w, topk, want_lse=True):
     val = torch.empty((M, topk), dtype=torch.float32, device="cuda")
     gap = torch.empty((M,), dtype=torch.float32, device="cuda")
     lse = torch.empty((M,), dtype=torch.float32, device="cuda") if want_lse else None
-    ws = torch.empty(lib.eagle3_lmhead_workspace(M, N, K, topk, dt), dtype=torch.uint8, device="cuda")
+    # the workspace starts as garbage: the call owns its contents (records,
+    # and the tile-claim counters it clears itself)
+    ws = torch.full((lib.eagle3_lmhead_workspace(M, N, K, topk, dt),), 0xA5, dtype=torch.uint8, device="cuda")
     lib.eagle3_lmhead_argmax(hd, wd, topk, idx, val, gap, lse, ws)
     torch.cuda.synchronize()
     return host(idx), host(val), host(gap), (host(lse) if want_lse else None)
