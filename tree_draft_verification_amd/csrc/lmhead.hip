@@ -325,6 +325,106 @@ __device__ __forceinline__ void top2_row(const f32x16_t (&blk)[NB], int lh, int 
     }
 }
 
+// One lane's top-KK keys (value desc, column asc) and, with LSE, (max, sum
+// of exp) over the first nvalid of its CPL staged columns (column c at
+// rowp[(c0 + c + rot) & 127]), in two passes over the staged row:
+// (1) the KK largest values with multiplicity, by a median-of-three network
+//     (slot s takes the median of slots s - 1 and s and the value, slot 0
+//     the maximum): KK branch-free operations per value, NaN passing over;
+// (2) the columns holding a value >= the KK-th largest, marked in bitmasks
+//     and walked in column order: each takes the first free slot from the
+//     first slot that holds its value, so equal values keep column order and
+//     values equal to the KK-th largest beyond the list are dropped. Only
+//     the marked columns (about KK per lane) run the slot search.
+// Unfilled slots are empty keys (0), as a list that saw fewer values.
+template <int KK, int CPL, bool LSE>
+__device__ __forceinline__ void select_lane(const float *rowp, int c0, int rot, int nvalid, int colbase,
+                                            uint64_t (&L)[KK], float &mx, float &se) {
+    static_assert(KK <= 16 && CPL % 64 == 0, "list and mask sizes");
+    constexpr int NB8 = CPL / 8, NM = CPL / 64;
+    auto load8 = [&](int b, float (&xs)[8]) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const f32x4_t t = *reinterpret_cast<const f32x4_t *>(rowp + ((c0 + b * 8 + 4 * q + rot) & 127));
+            xs[4 * q] = t[0]; xs[4 * q + 1] = t[1]; xs[4 * q + 2] = t[2]; xs[4 * q + 3] = t[3];
+        }
+    };
+    float lv[KK];
+#pragma unroll
+    for (int t = 0; t < KK; ++t) lv[t] = -INFINITY;
+    mx = -INFINITY;
+    se = 0.f;
+#pragma unroll
+    for (int b = 0; b < NB8; ++b) {
+        const int jv = nvalid - b * 8;  // valid columns in this batch
+        if (jv > 0) {
+            float xs[8];
+            load8(b, xs);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                if (i >= jv) xs[i] = -INFINITY;
+                const float x = xs[i];
+#pragma unroll
+                for (int t = KK - 1; t > 0; --t) lv[t] = __builtin_amdgcn_fmed3f(lv[t - 1], lv[t], x);
+                lv[0] = e3_vmax(lv[0], x);
+            }
+            if (LSE) {
+                float bm = xs[0];
+#pragma unroll
+                for (int i = 1; i < 8; ++i) bm = fmaxf(bm, xs[i]);
+                const float nm = fmaxf(mx, bm);
+                if (nm != -INFINITY) {
+                    float sb = 0.f;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) sb += __expf(xs[i] - nm);
+                    se = se * __expf(mx - nm) + sb;
+                    mx = nm;
+                }
+            }
+        }
+    }
+    const float thr = lv[KK - 1];
+    uint64_t cand[NM];
+#pragma unroll
+    for (int w = 0; w < NM; ++w) cand[w] = 0;
+#pragma unroll
+    for (int b = 0; b < NB8; ++b) {
+        const int jv = nvalid - b * 8;
+        if (jv > 0) {
+            float xs[8];
+            load8(b, xs);
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                if (i < jv && xs[i] >= thr) cand[(b * 8 + i) / 64] |= 1ull << ((b * 8 + i) % 64);
+        }
+    }
+    int idx[KK];
+#pragma unroll
+    for (int t = 0; t < KK; ++t) idx[t] = 0;
+    uint32_t taken = 0;
+#pragma unroll
+    for (int w = 0; w < NM; ++w) {
+        uint64_t cm = cand[w];
+        while (cm) {
+            const int col = w * 64 + (int)__builtin_ctzll(cm);
+            cm &= cm - 1;
+            const float v = rowp[(c0 + col + rot) & 127];
+            int s0 = 0;
+#pragma unroll
+            for (int t = 0; t < KK; ++t) s0 += lv[t] > v ? 1 : 0;
+            const uint32_t fr = ~taken & (((1u << KK) - 1u) & ~((1u << s0) - 1u));
+            if (fr) {
+                const int slot = (int)__builtin_ctz(fr);
+                taken |= 1u << slot;
+#pragma unroll
+                for (int t = 0; t < KK; ++t) idx[t] = t == slot ? col : idx[t];
+            }
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < KK; ++t) L[t] = (taken >> t) & 1u ? e3_key(lv[t], colbase + idx[t]) : 0;
+}
+
 template <int BM, int KK, bool LSE>
 __global__ __launch_bounds__(256, BM == 128 ? 2 : 1) void lmhead_big_kernel(e3g::GemmParams gp, int nrec,
                                                                              Partials p) {
@@ -396,43 +496,10 @@ __global__ __launch_bounds__(256, BM == 128 ? 2 : 1) void lmhead_big_kernel(e3g:
                 }
         // a wave's LDS accesses complete in order: the scan below sees the stores
         uint64_t L[KK];
-        e3_kinit<KK>(L);
-        float mx = -INFINITY, se = 0.f;
+        float mx, se;
         const int c0 = CPL * ch;
         const int nvalid = min(CPL, gp.N - vbase - c0);
-        // 8 columns at a time: two 16-byte reads, the batch maximum rescales
-        // the running sum once, then branch-free inserts of the keys that
-        // beat the list's last entry
-        for (int b = 0; b < CPL / 8; ++b) {
-            const int jv = nvalid - b * 8;   // valid columns in this batch
-            if (jv <= 0) break;
-            float xs[8];
-#pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                const f32x4_t t =
-                    *reinterpret_cast<const f32x4_t *>(st + row * 128 + ((c0 + b * 8 + 4 * q + 4 * row) & 127));
-                xs[4 * q] = t[0]; xs[4 * q + 1] = t[1]; xs[4 * q + 2] = t[2]; xs[4 * q + 3] = t[3];
-            }
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                if (i >= jv) xs[i] = -INFINITY;
-                const uint64_t k = i < jv ? e3_key(xs[i], vbase + c0 + b * 8 + i) : 0;
-                if (k > L[KK - 1]) e3_kinsert<KK>(L, k);
-            }
-            if (LSE) {
-                float bm = xs[0];
-#pragma unroll
-                for (int i = 1; i < 8; ++i) bm = fmaxf(bm, xs[i]);
-                const float nm = fmaxf(mx, bm);
-                if (nm != -INFINITY) {
-                    float sb = 0.f;
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) sb += __expf(xs[i] - nm);
-                    se = se * __expf(mx - nm) + sb;
-                    mx = nm;
-                }
-            }
-        }
+        select_lane<KK, CPL, LSE>(st + row * 128, c0, 4 * row, nvalid, vbase + c0, L, mx, se);
         if constexpr (LPR == 2) {
             e3_kmerge_xor<KK>(L, 32);
             if (LSE) {
