@@ -5,7 +5,7 @@ speculative decoding: the tree-verifier method": the target runs once over
 the whole tree with each token attending to the cached context and its
 ancestors, then the accept rule).
 
-Per layer, over M = B * T tree rows: RMSNorm -> Q, K, V projections -> RoPE
+Per layer, over M = B * T tree rows: RMSNorm -> Q and (one GEMM) K, V projections -> RoPE
 at the sequence's cached length + the node's depth -> tree attention over
 that layer's paged prefix plus the ancestor-masked tree rows -> output
 projection + residual -> RMSNorm -> gate/up projection -> SiLU(gate) * up ->
@@ -47,7 +47,8 @@ class TargetModel:
         self.proj = []
         for i in range(layers):
             wqkv = weights[f"l{i}.wqkv"]
-            self.proj.append((wqkv[:self.qd], wqkv[self.qd:self.qd + self.kvd], wqkv[self.qd + self.kvd:]))
+            # (Q rows, the adjacent K and V rows as one weight)
+            self.proj.append((wqkv[:self.qd], wqkv[self.qd:]))
         # bf16: the gate/up weights in the paired layout of the fused
         # projection + gating call (one extra copy of those weights)
         self.fused_mlp = self.dtype == torch.bfloat16 and self.F % 128 == 0
@@ -69,6 +70,11 @@ class TargetModel:
         self.x, self.h = e(M, self.k), e(M, self.k)
         self.q, self.attn = e(M, self.qd), e(M, self.qd)
         self.gu, self.f = e(M, 2 * self.F), e(M, self.F)
+        # K and V projections as one GEMM ([M, 2 kvd], each row K then V),
+        # then each half gathered into its row buffer
+        self.kv = e(M, 2 * self.kvd)
+        self.k_src = torch.arange(0, 2 * M, 2, **i32)
+        self.v_src = torch.arange(1, 2 * M, 2, **i32)
         # tree rows' K (after RoPE) and V of every layer, kept for the commit
         self.k_rows = [e(B, T, Hkv, D) for _ in range(layers)]
         self.v_rows = [e(B, T, Hkv, D) for _ in range(layers)]
@@ -83,9 +89,9 @@ class TargetModel:
         dtc = B_._dtype(E)
         self.lm_ws = torch.empty(max(256, B_.eagle3_lmhead_workspace(M, self.V, self.k, 1, dtc)),
                                  dtype=torch.uint8, device=dv)
-        # K-split workspace of the narrow projections (K and V: few output tiles),
+        # K-split workspace of the projections when they have few output tiles,
         # also the tile counters of the persistent gate/up call
-        need = max(B_.eagle3_gemm_workspace([self.h], self.proj[0][1], self.k_rows[0].view(M, self.kvd)),
+        need = max(B_.eagle3_gemm_workspace([self.h], self.proj[0][1], self.kv),
                    B_.eagle3_gemm_workspace([self.h], self.proj[0][0], self.q), B_.PERSIST_WS_BYTES)
         self.gemm_ws = torch.empty(need, dtype=torch.uint8, device=dv)
         self._attn_ws = None
@@ -123,12 +129,14 @@ class TargetModel:
         for i in range(n_layers):
             if record is not None:
                 record.append(self.x.view(B, T, self.k).clone())
-            wq, wk, wv = self.proj[i]
+            wq, wkv = self.proj[i]
             kr, vr = self.k_rows[i].view(M, self.kvd), self.v_rows[i].view(M, self.kvd)
             B_.eagle3_rmsnorm(self.x, self.h, eps=self.eps)
             B_.eagle3_gemm([self.h], wq, self.q, ws=ws)
-            B_.eagle3_gemm([self.h], wk, kr, ws=ws)
-            B_.eagle3_gemm([self.h], wv, vr, ws=ws)
+            B_.eagle3_gemm([self.h], wkv, self.kv, ws=ws)
+            kv2 = self.kv.view(2 * M, self.kvd)
+            B_.eagle3_copy_rows(kv2, kr, M, src_rows=self.k_src)
+            B_.eagle3_copy_rows(kv2, vr, M, src_rows=self.v_src)
             B_.eagle3_rope(self.q, M, self.Hq, D, self.qd, pos, 0, self.theta)
             B_.eagle3_rope(kr, M, self.Hkv, D, self.kvd, pos, 0, self.theta)
             self._ev("attn", i, 0)
