@@ -460,13 +460,14 @@ struct TileQueue {
 };
 
 // Persistent form of the K loop for one A segment without a row gather (the
-// many-row LM head): the work-group runs tile after tile as `queue` hands
-// them out and the DMA ring runs on across tile boundaries, so the first
-// chunks of a tile are loaded while the previous tile finishes and its
-// epilogue(tile, acc) runs. queue.first(cur, nxt) gives the first two tiles
-// (-1: none) and queue.advance(nxt) the one after the new current tile; both
-// are called by every thread with no load in flight and return the same
-// values in every thread. tile_at(tile, m0, n0) gives a tile's origin.
+// many-row LM head, the fused gate/up projection): the work-group runs tile
+// after tile as `queue` hands them out and the DMA ring runs on across tile
+// boundaries, so the first chunks of a tile are loaded while the previous
+// tile finishes and its epilogue(tile, acc) runs. queue.first(cur, nxt)
+// gives the first two tiles (-1: none) and queue.advance(nxt) the one after
+// the new current tile; both are called by every thread with no load in
+// flight and return the same values in every thread. tile_at(tile, m0, n0)
+// gives a tile's origin.
 // Layout of acc, LDS ring and ordering rule as in mainloop. At a tile
 // boundary every wave waits for all of its outstanding vector memory
 // operations (the epilogue's stores among them) and meets a barrier before
