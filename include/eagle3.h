@@ -308,7 +308,12 @@ int eagle3_vocab_map(const int32_t *ids, int n, const int32_t *vmap, int V_sub, 
  * residual) before the one rounding to bf16. The split count depends on M,
  * so with a workspace a row's rounding can depend on the batch (results stay
  * within the same accuracy). NULL or too small: no split, same results as
- * without.
+ * without. A large bf16 call (one A segment without a row gather, 256 x 256
+ * output tiles at least four times the CU count, N and ldc multiples of 8, c
+ * and residual 16-byte aligned, K >= 128) given at least
+ * EAGLE3_PERSIST_WS_BYTES runs one work-group per CU that takes output tiles
+ * from counters kept in the workspace (the caller must not use it for
+ * anything else while the call runs); its results are the same as without.
  */
 typedef struct eagle3_gemm_args {
     int dtype;
@@ -329,7 +334,9 @@ typedef struct eagle3_gemm_args {
 /* bf16: each A segment (M rows, or a_nrows rows when gathered) must be under
  * 4 GiB (EAGLE3_ERR_UNSUPPORTED otherwise); the same holds for the hidden
  * state of eagle3_lmhead_argmax. */
-/* bytes of workspace the call would use to split K (0: it would not split) */
+/* bytes of workspace the call would use: S * M * N * 4 to split K S ways
+ * (S >= 2), or EAGLE3_PERSIST_WS_BYTES for the tile counters of its
+ * persistent form (a call takes one or neither); 0: it would use none */
 size_t eagle3_gemm_workspace(const eagle3_gemm_args *args);
 
 int eagle3_gemm(const eagle3_gemm_args *args, void *stream);
@@ -398,8 +405,11 @@ int eagle3_commit_kv(const void *k_rows, const void *v_rows, int rows_per_seq, c
  * ahead of each row); E [V, k]; w_fuse [k, 3k]; w_in [k, 2k] (output-major).
  * g is stored (g_out, or the workspace when g_out is NULL) in the storage type
  * before the second FC. bf16 needs k % 64 == 0. The workspace query also
- * covers the K splits of the two GEMMs (see eagle3_gemm); a smaller
- * workspace that still holds g (or none, with g_out) runs them unsplit.
+ * covers the GEMM workspace of the two FCs (K splits or the tile counters of
+ * the persistent form, see eagle3_gemm): it follows g when g lives in the
+ * workspace; with g_out (or in step mode) the whole workspace is the GEMMs'.
+ * The query's size covers both cases. A smaller workspace runs the plain
+ * form: the same results except for the rounding of a K split.
  */
 size_t eagle3_draft_fuse_workspace(int M, int k, int dtype);
 int eagle3_draft_fuse(const void *l, const void *m, const void *h, const void *a_prev, const int32_t *tok,

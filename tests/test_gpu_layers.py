@@ -94,6 +94,73 @@ def test_gemm_split_k_in_place_residual(orc, lib):
     assert (got == unsplit).mean() >= 0.98
 
 
+# Persistent 256-row tiles (a workspace of at least PERSIST_WS_BYTES, one A
+# segment, at least four tiles per CU): (8000, 8200, ...) has 1056 tiles with
+# a ragged N tile and a last row tile whose upper half lies past M;
+# (16384, 4096, ...) exactly 1024; K from the 4-chunk minimum up.
+@pytest.mark.parametrize("M,N,k,res", [(8000, 8200, [256], "separate"), (16384, 4096, [128], None),
+                                       (8000, 8200, [192], "in_place"), (16384, 4096, [512], "separate")])
+def test_gemm_persistent_matches_plain_and_oracle(orc, lib, M, N, k, res):
+    rng = np.random.default_rng(7 * M + N + len(k))
+    segs = [synth.normal_bf16(rng, (M, ks)) for ks in k]
+    B = synth.normal_bf16(rng, (N, sum(k)), 0.05)
+    R = synth.normal_bf16(rng, (M, N)) if res else None
+    A = np.concatenate(segs, axis=1)
+    ref = orc.gemm(A, B, R)
+    sd = [dev(s) for s in segs]
+    Bd = dev(B)
+    c = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    assert lib.eagle3_gemm_workspace(sd, Bd, c) == lib.PERSIST_WS_BYTES
+    ws = torch.full((lib.PERSIST_WS_BYTES,), 0xA5, dtype=torch.uint8, device="cuda")
+    plain = torch.empty_like(c)
+    if res == "in_place":
+        c.copy_(dev(R))
+        plain.copy_(dev(R))
+        lib.eagle3_gemm(sd, Bd, c, residual=c, ws=ws)
+        lib.eagle3_gemm(sd, Bd, plain, residual=plain)
+    else:
+        Rd = dev(R) if res else None
+        lib.eagle3_gemm(sd, Bd, c, residual=Rd, ws=ws)
+        lib.eagle3_gemm(sd, Bd, plain, residual=Rd)
+    torch.cuda.synchronize()
+    got = host(c)
+    assert np.array_equal(got, host(plain))            # the per-tile kernel's arithmetic
+    rel, mx = normwise_rel(got, ref)
+    assert rel <= 2e-2, (rel, mx)
+    d = np.abs(as_f64(got) - as_f64(ref))
+    S = np.abs(as_f64(A)) @ np.abs(as_f64(B)).T + (np.abs(as_f64(R)) if res else 0.0)
+    bad = d > np.maximum(_bf16_ulp(ref), _bf16_ulp(got)) * 1.0001 + 4e-6 * S
+    assert not bad.any(), (int(bad.sum()), np.argwhere(bad)[:5])
+    # the same workspace again for the first 7950 rows (still persistent, a
+    # last tile of 14 rows; every counter zeroed anew) on a zeroed output:
+    # rows past them stay untouched
+    if M == 8000 and res != "in_place":
+        M2 = 7950
+        c2 = torch.zeros_like(c)
+        assert lib.eagle3_gemm_workspace([s[:M2] for s in sd], Bd, c2, M=M2) == lib.PERSIST_WS_BYTES
+        lib.eagle3_gemm([s[:M2] for s in sd], Bd, c2, residual=dev(R)[:M2] if res else None, M=M2, ws=ws)
+        torch.cuda.synchronize()
+        g2 = host(c2)
+        assert np.array_equal(g2[:M2], got[:M2])
+        assert not g2[M2:].view(np.uint16).any()
+
+
+def test_gemm_persistent_taken_only_where_it_applies(lib):
+    """Workspace query: the tile counters for one plain A segment with at
+    least four 256 x 256 tiles per CU; 0 with a row gather, several segments
+    or about one tile per CU (per-tile kernels)."""
+    M, N, k = 8000, 8192, 256
+    bf = dict(dtype=torch.bfloat16, device="cuda")
+    a = [torch.empty(M, k, **bf), torch.empty(50, k, **bf)]
+    rows = [None, torch.zeros(M, dtype=torch.int32, device="cuda")]
+    b = torch.empty(N, 2 * k, **bf)
+    c = torch.empty(M, N, **bf)
+    assert lib.eagle3_gemm_workspace(a[:1], b[:, :k].contiguous(), c) == lib.PERSIST_WS_BYTES
+    assert lib.eagle3_gemm_workspace(a, b, c, a_rows=rows) == 0
+    assert lib.eagle3_gemm_workspace([a[0], a[0]], b, c) == 0
+    assert lib.eagle3_gemm_workspace(a[:1], torch.empty(4096, k, **bf), c[:3904, :4096], M=3904) == 0
+
+
 def test_gemm_f32_and_in_place_residual(orc, lib):
     rng = np.random.default_rng(3)
     M, N, K = 37, 90, 70

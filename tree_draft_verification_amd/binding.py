@@ -215,15 +215,17 @@ def _gemm_args(a, b, c, residual, a_rows, ldc, M, ws):
     return g
 
 
-def eagle3_gemm_workspace(a, b, c, M=None) -> int:
-    """Bytes of workspace eagle3_gemm would use for this call to split K."""
-    return int(_gemm_ws(ctypes.byref(_gemm_args(a, b, c, None, None, 0, M, None))))
+def eagle3_gemm_workspace(a, b, c, M=None, residual=None, a_rows=None) -> int:
+    """Bytes of workspace eagle3_gemm would use for this call: to split K, or
+    PERSIST_WS_BYTES for the tile counters of its persistent form."""
+    return int(_gemm_ws(ctypes.byref(_gemm_args(a, b, c, residual, a_rows, 0, M, None))))
 
 
 def eagle3_gemm(a, b, c, residual=None, a_rows=None, a_nrows=None, ldc=0, M=None, stream=None, ws=None):
     """C = [a_0 | a_1 | ...] . b^T (+ residual); a: list of [rows, k_s] tensors
     (a_rows[s]: optional int32 row gather of segment s; ws: optional workspace
-    that lets a call with few output tiles split K)."""
+    that lets a call with few output tiles split K, or a large one run
+    persistent work-groups: eagle3_gemm_workspace gives the bytes)."""
     g = _gemm_args(a, b, c, residual, a_rows, ldc, M, ws)
     _check(_gemm(ctypes.byref(g), _stream(stream)), "eagle3_gemm")
 

@@ -14,7 +14,7 @@ size_t g_bytes(int M, int k, int dtype) {
     return ((size_t)M * k * esz + 255) & ~(size_t)255;
 }
 
-// K-split workspace of the two FCs (the larger of the two)
+// GEMM workspace of the two FCs (K splits or tile counters; the larger)
 size_t split_bytes(int M, int k, int dtype) {
     eagle3_gemm_args a{};
     a.dtype = dtype; a.M = M; a.N = k;
@@ -44,8 +44,9 @@ extern "C" int eagle3_draft_fuse(const void *l, const void *m, const void *h, co
     if (context && (!l || !m || !h || !w_fuse)) return EAGLE3_ERR_ARG;
     if (!context && (l || m || h)) return EAGLE3_ERR_ARG;
     const void *first = a_prev;
-    // K-split space after the g region, when the caller gave enough
-    const size_t gb = g_bytes(M, k, dtype);
+    // the GEMMs' workspace (K splits or tile counters): after the g region
+    // when g lives in the workspace, else all of it
+    const size_t gb = context && !g_out ? g_bytes(M, k, dtype) : 0;
     void *split_ws = nullptr;
     size_t split_ws_bytes = 0;
     if (ws && ws_bytes > gb) {

@@ -443,6 +443,82 @@ __global__ __launch_bounds__(512, 1) void gemm_swiglu_persistent_kernel(GemmPara
     mainloop_persistent<BM, T::NS, true, 8>(p, tile_at, queue, epilogue, ring);
 }
 
+// Persistent form of the 256-row tiles of the plain product (C = A . B^T,
+// plus the residual with RES) for one A segment without a row gather
+// (tile-claim counters in the caller's workspace; see mainloop_persistent),
+// run on the persistent loop of the many-row LM head: eight waves per 256 x 256 tile with the MFMA operands
+// swapped, so a lane holds one output row and, per 32 x 32 block, the column
+// quads 8 q + 4 lh (q < 4) in registers 4 q .. 4 q + 3. Each quad leaves as
+// one 8-byte store after the residual is added in fp32 and the sum rounded
+// once: the arithmetic of the per-tile kernels, so results are identical.
+// Requires N and ldc multiples of 8 and 16-byte aligned C and residual.
+template <bool RES>
+__global__ __launch_bounds__(512, 1) void gemm_persistent_kernel(GemmParams p, uint32_t *ctr) {
+    using T = GTile<256, 4, 8>;
+    constexpr int BM = 256;
+    static_assert(T::MB == 4 && T::NB == 2 && T::CW == 64, "wave tile 128 x 64");
+    __shared__ __attribute__((aligned(1024))) unsigned char ring[T::RING];
+    __shared__ int tq[2];
+    TileQueue queue;
+    queue.init(ctr, tq, p.mt * p.nt);
+    auto tile_at = [&](int t, int &m0, int &n0) {
+        int mt, nt;
+        tile_at_order(t, p.mt, p.nt, mt, nt);
+        m0 = mt * BM;
+        n0 = nt * GBN;
+    };
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int lr = lane & 31, lh = lane >> 5, wm = wave / T::WN, wn = wave % T::WN;
+    uint16_t *cc = (uint16_t *)p.c;
+    const uint16_t *res = (const uint16_t *)p.res;
+    auto epilogue = [&](int tile, const f32x16_t (&acc)[T::MB][T::NB]) {
+        int m0, n0;
+        tile_at(tile, m0, n0);
+        const int mw = __builtin_amdgcn_readfirstlane(m0 + wm * (BM / 2));
+        if (mw >= p.M) return;  // a last tile's upper half past M
+        const int nw = n0 + wn * T::CW + 4 * lh;
+#pragma unroll
+        for (int mb = 0; mb < T::MB; ++mb) {
+            const int m = mw + 32 * mb + lr;
+            if (m < p.M) {
+                const size_t row = (size_t)m * p.ldc;
+                uint2 rv[T::NB][4];
+                if constexpr (RES) {
+#pragma unroll
+                    for (int nb = 0; nb < T::NB; ++nb)
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const int n = nw + 32 * nb + 8 * q;
+                            rv[nb][q] = n < p.N ? *reinterpret_cast<const uint2 *>(res + row + n) : uint2{0, 0};
+                        }
+                }
+#pragma unroll
+                for (int nb = 0; nb < T::NB; ++nb)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int n = nw + 32 * nb + 8 * q;
+                        if (n < p.N) {
+                            float v[4];
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) v[e] = acc[mb][nb][4 * q + e];
+                            if constexpr (RES) {
+                                v[0] += e3_bf16_to_f32((uint16_t)(rv[nb][q].x & 0xffffu));
+                                v[1] += e3_bf16_to_f32((uint16_t)(rv[nb][q].x >> 16));
+                                v[2] += e3_bf16_to_f32((uint16_t)(rv[nb][q].y & 0xffffu));
+                                v[3] += e3_bf16_to_f32((uint16_t)(rv[nb][q].y >> 16));
+                            }
+                            uint2 o;
+                            o.x = (uint32_t)e3_f32_to_bf16(v[0]) | ((uint32_t)e3_f32_to_bf16(v[1]) << 16);
+                            o.y = (uint32_t)e3_f32_to_bf16(v[2]) | ((uint32_t)e3_f32_to_bf16(v[3]) << 16);
+                            *reinterpret_cast<uint2 *>(cc + row + n) = o;
+                        }
+                    }
+            }
+        }
+    };
+    mainloop_persistent<BM, T::NS, true, 8>(p, tile_at, queue, epilogue, ring);
+}
+
 // dst[dst_rows[i]] = src[src_rows[i]] for i < n, 16 bytes per thread; a null
 // table is the identity; rows outside [0, nrows) are skipped.
 __global__ __launch_bounds__(256) void copy_rows_kernel(const uint4 *__restrict__ src,
@@ -480,12 +556,47 @@ int gemm_k(const eagle3_gemm_args *a) {
     return K;
 }
 
+// Tile shape of an unsplit bf16 call by the amount of work (measured):
+// 256-row tiles once they make four passes over the CUs (most reuse,
+// 65536 x 4096 x 12288: 1.01 vs 0.90 PFLOP/s per-tile); else 128-row tiles
+// two per CU while those fill both slots of every CU (640 x 28672 x 4096:
+// 0.59 vs 0.50); else 256-row tiles if they fill the CUs once (3904 x 4096 x
+// 4096: 0.82 vs 0.72); below that 128-row tiles one per CU with the deeper
+// ring (640 x 4096 x 14336: 0.39 vs 0.33).
+bool gemm_rows256(int M, int N) {
+    const int nt = (N + GBN - 1) / GBN;
+    const long t256 = (long)((M + 255) / 256) * nt, t128 = (long)((M + 127) / 128) * nt;
+    const long cus = e3_cu_count();
+    return t256 >= 4 * cus || (t128 < 2 * cus && t256 >= cus);
+}
+
+// 16-byte row pieces in the output (and the residual)
+bool gemm_vec(const eagle3_gemm_args *a, int ldc) {
+    return a->N % 8 == 0 && ldc % 8 == 0 && e3_aligned16(a->c) && (!a->residual || e3_aligned16(a->residual));
+}
+
+// Whether an unsplit bf16 call runs the persistent 256-row kernel given a
+// workspace for its tile counters: one A segment without a row gather,
+// vector output, at least 4 chunks of K, and 256-row tiles that make at
+// least four passes over the CUs (measured, 65536 x 4096 x 4096..12288 and
+// 65536 x 1024 x 4096: 1.12-1.18 against 0.94-1.07 PFLOP/s per-tile; the
+// queue hands each work-group two tiles at the start, so with about one tile
+// per CU half of the CUs would take two: 3904 x 4096 x 4096, 200 against
+// 128 us).
+bool gemm_persistent(const eagle3_gemm_args *a, int K, int ldc) {
+    if (a->dtype != EAGLE3_BF16 || a->nseg != 1 || a->a_rows[0] || K / GBK < 4 || !gemm_vec(a, ldc)) return false;
+    const long t256 = (long)((a->M + 255) / 256) * ((a->N + GBN - 1) / GBN);
+    return t256 >= 4 * (long)e3_cu_count();
+}
+
 }  // namespace
 
 extern "C" size_t eagle3_gemm_workspace(const eagle3_gemm_args *a) {
     if (!a || a->nseg < 1 || a->nseg > 3 || a->M < 1 || a->N < 1) return 0;
-    const int S = gemm_splits(a, gemm_k(a));
-    return S > 1 ? (size_t)S * a->M * a->N * sizeof(float) : 0;
+    const int K = gemm_k(a);
+    const int S = gemm_splits(a, K);
+    if (S > 1) return (size_t)S * a->M * a->N * sizeof(float);
+    return gemm_persistent(a, K, a->ldc > 0 ? a->ldc : a->N) ? EAGLE3_PERSIST_WS_BYTES : 0;
 }
 
 extern "C" int eagle3_gemm(const eagle3_gemm_args *a, void *stream) {
@@ -528,23 +639,26 @@ extern "C" int eagle3_gemm(const eagle3_gemm_args *a, void *stream) {
                                                                        (const uint16_t *)a->residual,
                                                                        (uint16_t *)a->c, ldc);
     } else if (a->dtype == EAGLE3_BF16) {
-        // Tile shape by the amount of work (measured): 256-row tiles once
-        // they make four passes over the CUs (most reuse, 65536 x 4096 x
-        // 12288: 1.01 vs 0.90 PFLOP/s); else 128-row tiles two per CU while
-        // those fill both slots of every CU (640 x 28672 x 4096: 0.59 vs
-        // 0.50); else 256-row tiles if they fill the CUs once (3904 x 4096 x
-        // 4096: 0.82 vs 0.72); below that 128-row tiles one per CU with the
-        // deeper ring (640 x 4096 x 14336: 0.39 vs 0.33).
         const int nt = (a->N + GBN - 1) / GBN;
         const long t256 = (long)((a->M + 255) / 256) * nt, t128 = (long)((a->M + 127) / 128) * nt;
         const long cus = e3_cu_count();
         p.nt = nt;
-        const bool vec = a->N % 8 == 0 && ldc % 8 == 0 && e3_aligned16(a->c) &&
-                         (!a->residual || e3_aligned16(a->residual));
-        if (t256 >= 4 * cus || (t128 < 2 * cus && t256 >= cus)) {
+        const bool vec = gemm_vec(a, ldc);
+        if (gemm_rows256(a->M, a->N)) {
             p.mt = (a->M + 255) / 256;
-            if (vec) gemm_bf16_kernel<256, 4, false, true><<<p.mt * nt, 256, 0, st>>>(p, 1, nullptr);
-            else gemm_bf16_kernel<256, 4, false><<<p.mt * nt, 256, 0, st>>>(p, 1, nullptr);
+            if (a->ws && a->ws_bytes >= EAGLE3_PERSIST_WS_BYTES && e3_aligned16(a->ws) && gemm_persistent(a, K, ldc)) {
+                // persistent work-groups (one per CU) taking tiles from the
+                // counters in the workspace
+                uint32_t *ctr = (uint32_t *)a->ws;
+                const int grid = (int)std::min<long>(t256, cus);
+                ctr_zero_kernel<<<1, 64, 0, st>>>(ctr);
+                if (a->residual) gemm_persistent_kernel<true><<<grid, 512, 0, st>>>(p, ctr);
+                else gemm_persistent_kernel<false><<<grid, 512, 0, st>>>(p, ctr);
+            } else if (vec) {
+                gemm_bf16_kernel<256, 4, false, true><<<p.mt * nt, 256, 0, st>>>(p, 1, nullptr);
+            } else {
+                gemm_bf16_kernel<256, 4, false><<<p.mt * nt, 256, 0, st>>>(p, 1, nullptr);
+            }
         } else if (t128 >= 2 * cus) {
             p.mt = (a->M + 127) / 128;
             if (vec) gemm_bf16_kernel<128, 3, false, true><<<p.mt * nt, 256, 0, st>>>(p, 1, nullptr);
@@ -595,7 +709,7 @@ extern "C" int eagle3_gemm_swiglu(const eagle3_gemm_args *a, void *stream) {
     const long t256 = (long)((a->M + 255) / 256) * nt, t128 = (long)((a->M + 127) / 128) * nt;
     const long cus = e3_cu_count();
     p.nt = nt;
-    if (t256 >= 4 * cus || (t128 < 2 * cus && t256 >= cus)) {
+    if (gemm_rows256(a->M, a->N)) {
         p.mt = (a->M + 255) / 256;
         // persistent work-groups when the workspace can hold the tile counters
         // (one A segment without a row gather; at least 4 chunks of K)

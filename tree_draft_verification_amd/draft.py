@@ -129,9 +129,10 @@ class DraftHead:
         self.tokens = torch.empty(B, n_drafts + 1, dtype=i32, device=dv)
         self._ctx_bufs = None
         self._ws = None
-        self._gws = None   # K-split workspace of the few-tile GEMMs (shared: one stream)
-        self._fws = torch.empty(max(256, B_.eagle3_draft_fuse_workspace(max(M, B * extend_rows), self.k,
-                                                                        B_._dtype(E))),
+        self._gws = None   # GEMM workspace: K splits or tile counters (shared: one stream)
+        # the fusion's workspace (g, then the FCs' K splits or tile counters)
+        self._fws = torch.empty(max(B_.PERSIST_WS_BYTES,
+                                    B_.eagle3_draft_fuse_workspace(max(M, B * extend_rows), self.k, B_._dtype(E))),
                                 dtype=torch.uint8, device=dv)
         self.R = extend_rows
         if extend_rows:
@@ -167,7 +168,7 @@ class DraftHead:
         self.ctx_tok = ctx_tok
         self.root.copy_(ctx_tok[:, -1])
         B_.eagle3_draft_fuse(ctx_tok.reshape(R), w["embed"], w["w_in"], cb["x"], w_fuse=w["w_fuse"],
-                             l=l.reshape(R, k), m=m.reshape(R, k), h=h.reshape(R, k), g_out=cb["g"])
+                             l=l.reshape(R, k), m=m.reshape(R, k), h=h.reshape(R, k), g_out=cb["g"], ws=self._fws)
         B_.eagle3_rmsnorm(cb["x"], cb["hn"], eps=self.eps)
         self._gemm([cb["hn"]], self.wk, cb["k"])
         self._gemm([cb["hn"]], self.wv, cb["v"])
@@ -190,7 +191,7 @@ class DraftHead:
         self._layer_tail(self.x1, attn, self.a_root, B)
 
     def _gemm(self, a, b, c, residual=None):
-        need = B_.eagle3_gemm_workspace(a, b, c)
+        need = B_.eagle3_gemm_workspace(a, b, c, residual=residual)
         ws = None
         if need:
             if self._gws is None or self._gws.numel() < need:
@@ -210,8 +211,10 @@ class DraftHead:
         self._gemm([attn], w["wo"], x2, residual=x)
         B_.eagle3_rmsnorm(x2, h2, eps=self.eps)
         # the fused projection + gating where the separate projection would
-        # not split K (few rows keep the split, which fills the chip)
-        if self.wgu_paired is not None and not B_.eagle3_gemm_workspace([h2], w["wgu"], gu):
+        # not split K (few rows keep the split, which fills the chip); a split
+        # workspace (at least 2 M N 4 bytes, N = 2F >= 256) exceeds the tile
+        # counters' bytes of a persistent call
+        if self.wgu_paired is not None and B_.eagle3_gemm_workspace([h2], w["wgu"], gu) <= B_.PERSIST_WS_BYTES:
             B_.eagle3_gemm_swiglu([h2], self.wgu_paired, f)
         else:
             self._gemm([h2], w["wgu"], gu)
