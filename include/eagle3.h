@@ -309,8 +309,8 @@ int eagle3_vocab_map(const int32_t *ids, int n, const int32_t *vmap, int V_sub, 
  * so with a workspace a row's rounding can depend on the batch (results stay
  * within the same accuracy). NULL or too small: no split, same results as
  * without. A large bf16 call (one A segment without a row gather, 256 x 256
- * output tiles at least four times the CU count, N and ldc multiples of 8, c
- * and residual 16-byte aligned, K >= 128) given at least
+ * output tiles at least four times the CU count or as many as the CUs, N and
+ * ldc multiples of 8, c and residual 16-byte aligned, K >= 128) given at least
  * EAGLE3_PERSIST_WS_BYTES runs one work-group per CU that takes output tiles
  * from counters kept in the workspace (the caller must not use it for
  * anything else while the call runs); its results are the same as without.

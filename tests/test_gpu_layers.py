@@ -95,11 +95,12 @@ def test_gemm_split_k_in_place_residual(orc, lib):
 
 
 # Persistent 256-row tiles (a workspace of at least PERSIST_WS_BYTES, one A
-# segment, at least four tiles per CU): (8000, 8200, ...) has 1056 tiles with
-# a ragged N tile and a last row tile whose upper half lies past M;
-# (16384, 4096, ...) exactly 1024; K from the 4-chunk minimum up.
+# segment, at least four tiles per CU or one; 256 CUs): (8000, 8200, ...) has
+# 1056 tiles with a ragged N tile and a last row tile whose upper half lies
+# past M; (16384, 4096, ...) exactly 1024; (3904, 4096, ...) 256, one per
+# work-group, with a last row tile of 64 rows; K from the 4-chunk minimum up.
 @pytest.mark.parametrize("M,N,k,res", [(8000, 8200, [256], "separate"), (16384, 4096, [128], None),
-                                       (8000, 8200, [192], "in_place"), (16384, 4096, [512], "separate")])
+                                       (8000, 8200, [192], "in_place"), (3904, 4096, [512], "separate")])
 def test_gemm_persistent_matches_plain_and_oracle(orc, lib, M, N, k, res):
     rng = np.random.default_rng(7 * M + N + len(k))
     segs = [synth.normal_bf16(rng, (M, ks)) for ks in k]
@@ -147,8 +148,9 @@ def test_gemm_persistent_matches_plain_and_oracle(orc, lib, M, N, k, res):
 
 def test_gemm_persistent_taken_only_where_it_applies(lib):
     """Workspace query: the tile counters for one plain A segment with at
-    least four 256 x 256 tiles per CU; 0 with a row gather, several segments
-    or about one tile per CU (per-tile kernels)."""
+    least four 256 x 256 tiles per CU or one; 0 with a row gather, several
+    segments or two tiles per CU (per-tile kernels)."""
+    assert torch.cuda.get_device_properties(0).multi_processor_count == 256
     M, N, k = 8000, 8192, 256
     bf = dict(dtype=torch.bfloat16, device="cuda")
     a = [torch.empty(M, k, **bf), torch.empty(50, k, **bf)]
@@ -158,7 +160,9 @@ def test_gemm_persistent_taken_only_where_it_applies(lib):
     assert lib.eagle3_gemm_workspace(a[:1], b[:, :k].contiguous(), c) == lib.PERSIST_WS_BYTES
     assert lib.eagle3_gemm_workspace(a, b, c, a_rows=rows) == 0
     assert lib.eagle3_gemm_workspace([a[0], a[0]], b, c) == 0
-    assert lib.eagle3_gemm_workspace(a[:1], torch.empty(4096, k, **bf), c[:3904, :4096], M=3904) == 0
+    assert lib.eagle3_gemm_workspace(a[:1], torch.empty(4096, k, **bf), c[:3904, :4096], M=3904) == \
+        lib.PERSIST_WS_BYTES
+    assert lib.eagle3_gemm_workspace(a[:1], torch.empty(4096, k, **bf), c[:, :4096]) == 0   # 512 tiles
 
 
 def test_gemm_f32_and_in_place_residual(orc, lib):

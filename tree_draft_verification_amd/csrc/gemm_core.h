@@ -395,16 +395,19 @@ __device__ __forceinline__ void lds_barrier() {
 // Tile queue of the persistent kernels: the tile order is cut into 8
 // runs, one per XCD, each with a claim counter; thread 0 claims for the
 // work-group and broadcasts through LDS. first() and advance() are called by
-// every thread at points with no load in flight.
+// every thread at points with no load in flight. A work-group claims its
+// second tile at the start, unless there are no more tiles than work-groups
+// (then each takes one).
 struct TileQueue {
     uint32_t *ctr;
     int *tq;              // LDS broadcast slots
     int x, q, r8;         // own run; tiles per run = q (+1 for the first r8 runs)
+    int ntiles;           // tiles of the pass
     uint32_t pend;        // thread 0: the claim in flight on the own run
     bool own_left;        // thread 0: the own run may still have tiles
     __device__ __forceinline__ void init(uint32_t *c, int *slots, int ntiles) {
         ctr = c; tq = slots;
-        x = blockIdx.x & 7; q = ntiles >> 3; r8 = ntiles & 7;
+        x = blockIdx.x & 7; q = ntiles >> 3; r8 = ntiles & 7; this->ntiles = ntiles;
         pend = 0; own_left = true;
     }
     __device__ __forceinline__ int run_start(int v) const { return v * q + min(v, r8); }
@@ -429,7 +432,7 @@ struct TileQueue {
     __device__ __forceinline__ void first(int &cur, int &nxt) {
         if (threadIdx.x == 0) {
             const int a = claim(x);
-            const int b = a < 0 ? -1 : claim(x);
+            const int b = a < 0 || ntiles <= (int)gridDim.x ? -1 : claim(x);
             own_left = b >= run_start(x) && b < run_start(x) + run_cnt(x);
             tq[0] = a;
             tq[1] = b;
@@ -460,7 +463,7 @@ struct TileQueue {
 };
 
 // Persistent form of the K loop for one A segment without a row gather (the
-// many-row LM head, the fused gate/up projection): the work-group runs tile
+// many-row LM head, the fused gate/up projection, the plain bf16 product): the work-group runs tile
 // after tile as `queue` hands them out and the DMA ring runs on across tile
 // boundaries, so the first chunks of a tile are loaded while the previous
 // tile finishes and its epilogue(tile, acc) runs. queue.first(cur, nxt)

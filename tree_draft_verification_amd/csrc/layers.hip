@@ -578,15 +578,15 @@ bool gemm_vec(const eagle3_gemm_args *a, int ldc) {
 // Whether an unsplit bf16 call runs the persistent 256-row kernel given a
 // workspace for its tile counters: one A segment without a row gather,
 // vector output, at least 4 chunks of K, and 256-row tiles that make at
-// least four passes over the CUs (measured, 65536 x 4096 x 4096..12288 and
-// 65536 x 1024 x 4096: 1.12-1.18 against 0.94-1.07 PFLOP/s per-tile; the
-// queue hands each work-group two tiles at the start, so with about one tile
-// per CU half of the CUs would take two: 3904 x 4096 x 4096, 200 against
-// 128 us).
+// least four passes over the CUs or at most one (measured against the
+// per-tile kernel: 65536 x 4096 x 4096..12288 and 65536 x 1024 x 4096
+// 1.10-1.18 against 0.94-1.07 PFLOP/s; one tile per CU, 3904 x 4096 x 14336
+// 407 against 448-460 us, 3904 x 4096 x 4096 alike). In between, the queue's
+// start (two tiles per work-group) would leave CUs idle.
 bool gemm_persistent(const eagle3_gemm_args *a, int K, int ldc) {
     if (a->dtype != EAGLE3_BF16 || a->nseg != 1 || a->a_rows[0] || K / GBK < 4 || !gemm_vec(a, ldc)) return false;
-    const long t256 = (long)((a->M + 255) / 256) * ((a->N + GBN - 1) / GBN);
-    return t256 >= 4 * (long)e3_cu_count();
+    const long t256 = (long)((a->M + 255) / 256) * ((a->N + GBN - 1) / GBN), cus = e3_cu_count();
+    return t256 >= 4 * cus || t256 <= cus;
 }
 
 }  // namespace
