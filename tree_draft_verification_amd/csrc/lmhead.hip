@@ -692,25 +692,31 @@ __global__ __launch_bounds__(256) void lmhead_f32_kernel(const float *__restrict
 }
 
 template <int KK, bool LSE>
-__global__ __launch_bounds__(256) void lmhead_merge_kernel(int ntiles, Partials p, int topk, int32_t *__restrict__ idx,
-                                                           float *__restrict__ val, float *__restrict__ gap,
-                                                           float *__restrict__ lse) {
-    __shared__ uint64_t sk[4][KK];
-    __shared__ float smx[4], sse[4];
-    const int m = blockIdx.x;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+__global__ __launch_bounds__(256) void lmhead_merge_kernel(int M, int ntiles, Partials p, int topk,
+                                                           int32_t *__restrict__ idx, float *__restrict__ val,
+                                                           float *__restrict__ gap, float *__restrict__ lse) {
+    // one wave per row, four rows per work-group: lane l merges the records
+    // l, l + 64, ... into its own list, then the wave's 64 lists meet in a
+    // butterfly (the list and the row's (max, sum-exp) do not depend on the
+    // order in which records meet, up to the rounding of the sum)
+    const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (m >= M) return;  // the whole wave
     uint64_t L[KK];
     e3_kinit<KK>(L);
     float mx = -INFINITY, se = 0.f;
-    // two records per thread and step, both loaded before either is merged
-    // (a 128256-row head at 256 rows per tile has 501 records per row: one
-    // memory round trip instead of two)
-    for (int t0 = threadIdx.x; t0 < ntiles; t0 += 512) {
-        uint64_t rk[2][KK];
-        float rmx[2] = {-INFINITY, -INFINITY}, rse[2] = {0.f, 0.f};
+    // four records per lane and step, all loaded before any is merged (a
+    // 128256-row head has 501 or 1002 records per row: four memory round
+    // trips per lane)
+    constexpr int U = 4;
+    for (int t0 = lane; t0 < ntiles; t0 += 64 * U) {
+        uint64_t rk[U][KK];
+        float rmx[U], rse[U];
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int t = t0 + 256 * u;
+        for (int u = 0; u < U; ++u) {
+            const int t = t0 + 64 * u;
+            rmx[u] = -INFINITY;
+            rse[u] = 0.f;
 #pragma unroll
             for (int s = 0; s < KK; ++s) rk[u][s] = 0;  // below every key: never enters
             if (t < ntiles) {
@@ -726,7 +732,7 @@ __global__ __launch_bounds__(256) void lmhead_merge_kernel(int ntiles, Partials 
             }
         }
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
+        for (int u = 0; u < U; ++u) {
             // a record is sorted: once an entry cannot enter, none after it can
 #pragma unroll
             for (int s = 0; s < KK; ++s) {
@@ -745,21 +751,6 @@ __global__ __launch_bounds__(256) void lmhead_merge_kernel(int ntiles, Partials 
         }
     }
     if (lane == 0) {
-#pragma unroll
-        for (int s = 0; s < KK; ++s) sk[wave][s] = L[s];
-        smx[wave] = mx; sse[wave] = se;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        for (int wv = 1; wv < 4; ++wv) {
-#pragma unroll
-            for (int s = 0; s < KK; ++s) {
-                const uint64_t k = sk[wv][s];
-                if (!(k > L[KK - 1])) break;
-                e3_kinsert<KK>(L, k);
-            }
-            if (LSE) e3_lse_combine(mx, se, smx[wv], sse[wv]);
-        }
 #pragma unroll
         for (int s = 0; s < KK; ++s) {
             if (s < topk) {
@@ -840,7 +831,7 @@ void launch(const void *hidden, const void *w, int M, int N, int K, int topk, in
         dim3 grid((M + 15) / 16, ntiles);
         lmhead_f32_kernel<KK, LSE><<<grid, 256, 0, st>>>((const float *)hidden, (const float *)w, M, N, K, ntiles, p);
     }
-    lmhead_merge_kernel<KK, LSE><<<M, 256, 0, st>>>(ntiles, p, topk, idx, val, gap, lse);
+    lmhead_merge_kernel<KK, LSE><<<(M + 3) / 4, 256, 0, st>>>(M, ntiles, p, topk, idx, val, gap, lse);
 }
 
 template <int KK>
